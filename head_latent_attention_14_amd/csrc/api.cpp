@@ -1,0 +1,185 @@
+// C ABI of libmla: argument validation, launch planning, workspace layout
+// and launch sequencing on the caller's stream. No call here allocates,
+// synchronises or keeps state; every check runs before the first HIP call.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/libmla.h"
+#include "internal.h"
+
+namespace mla {
+
+static constexpr int kTargetCUs = 256;        // MI355X compute units
+static constexpr int kMaxHeads = 1024;
+static constexpr int kMaxSeqs = 1 << 20;
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DecodePlan make_plan(int ct, int B, int H) {
+  DecodePlan p{};
+  if (ct == kF32) {
+    p.hb = 1; p.ds = 4; p.nstage = 2;
+  } else if (H % 64 == 0) {
+    p.hb = 4; p.ds = 1; p.nstage = 3;
+  } else if (H % 32 == 0) {
+    p.hb = 2; p.ds = 2; p.nstage = 4;
+  } else {
+    p.hb = 1; p.ds = 4; p.nstage = 4;
+  }
+  p.head_groups = H / (16 * p.hb);
+  int w = kTargetCUs / p.head_groups;
+  w = w < 8 ? 8 : (w / 8) * 8;                 // a multiple of the 8 XCDs
+  p.workers = w;
+  p.nslot = (int64_t)w + B;
+  (void)B;
+  return p;
+}
+
+WorkspaceLayout workspace_layout(int ct, int B, int H) {
+  const DecodePlan p = make_plan(ct, B, H);
+  WorkspaceLayout l{};
+  size_t off = 0;
+  l.prefix = off;  off = align256(off + sizeof(int64_t) * ((size_t)B + 1));
+  l.q_lat = off;   off = align256(off + (size_t)B * H * MLA_D_C * (ct == kF32 ? 4 : 2));
+  l.part_o = off;  off = align256(off + (size_t)p.nslot * H * MLA_D_C * 4);
+  l.part_ml = off; off = align256(off + (size_t)p.nslot * H * 2 * 4);
+  l.total = off;
+  return l;
+}
+
+}  // namespace mla
+
+using namespace mla;
+
+static bool valid_dtype(int d) {
+  return d == MLA_DTYPE_F32 || d == MLA_DTYPE_BF16 || d == MLA_DTYPE_FP8_E4M3;
+}
+
+// supported (cache, activation) dtype pairs
+static bool supported_pair(int cache, int act) {
+  return (cache == MLA_DTYPE_F32 && act == MLA_DTYPE_F32) ||
+         (cache == MLA_DTYPE_BF16 && act == MLA_DTYPE_BF16) ||
+         (cache == MLA_DTYPE_FP8_E4M3 && act == MLA_DTYPE_BF16);
+}
+
+static int cache_type(int dtype) {
+  return dtype == MLA_DTYPE_F32 ? kF32 : (dtype == MLA_DTYPE_BF16 ? kBF16 : kFP8);
+}
+
+static mla_status_t check_cache(const mla_cache_t* c) {
+  if (!c) return MLA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(c->dtype)) return MLA_ERR_INVALID_ARGUMENT;
+  if (c->d_c != MLA_D_C || c->d_r != MLA_D_R) return MLA_ERR_INVALID_ARGUMENT;
+  if (c->num_seqs < 1 || c->total_rows < 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (c->num_seqs > kMaxSeqs) return MLA_ERR_UNSUPPORTED;
+  if (!c->rows || !c->seq_start || !c->seq_capacity) return MLA_ERR_INVALID_ARGUMENT;
+  if (c->dtype == MLA_DTYPE_FP8_E4M3 && !c->row_scale) return MLA_ERR_INVALID_ARGUMENT;
+  return MLA_OK;
+}
+
+extern "C" {
+
+int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported dtype combination or size";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime or launch error";
+  }
+  return "unknown status";
+}
+
+mla_status_t mla_append(const mla_cache_t* cache, const void* h, int32_t n_tok, int32_t d_model,
+                        const void* w_dkv, const void* w_kr, mla_dtype_t act_dtype,
+                        const int32_t* tok_seq, const int32_t* tok_pos, float rope_base,
+                        void* stream) {
+  mla_status_t st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (!valid_dtype(act_dtype)) return MLA_ERR_INVALID_ARGUMENT;
+  if (n_tok < 0 || d_model <= 0 || d_model % 64 != 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARGUMENT;
+  if (!supported_pair(cache->dtype, act_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (n_tok == 0) return MLA_OK;
+  if (!h || !w_dkv || !w_kr || !tok_seq || !tok_pos) return MLA_ERR_INVALID_ARGUMENT;
+
+  AppendArgs a{};
+  a.rows = cache->rows;
+  a.row_scale = cache->row_scale;
+  a.seq_start = cache->seq_start;
+  a.seq_cap = cache->seq_capacity;
+  a.num_seqs = cache->num_seqs;
+  a.h = h;
+  a.w_dkv = w_dkv;
+  a.w_kr = w_kr;
+  a.tok_seq = tok_seq;
+  a.tok_pos = tok_pos;
+  a.n_tok = n_tok;
+  a.d_model = d_model;
+  for (int i = 0; i < MLA_D_R / 2; ++i)
+    a.inv_freq[i] = pow((double)rope_base, -2.0 * i / (double)MLA_D_R);
+  hipError_t e = launch_append(cache_type(cache->dtype), a, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_decode_workspace_size(int32_t num_seqs, int32_t n_heads, mla_dtype_t cache_dtype,
+                                       mla_dtype_t act_dtype, size_t* bytes) {
+  if (!bytes) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_seqs < 1 || n_heads < 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(cache_dtype) || !valid_dtype(act_dtype)) return MLA_ERR_INVALID_ARGUMENT;
+  if (!supported_pair(cache_dtype, act_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (n_heads % 16 != 0 || n_heads > kMaxHeads || num_seqs > kMaxSeqs) return MLA_ERR_UNSUPPORTED;
+  *bytes = workspace_layout(cache_type(cache_dtype), num_seqs, n_heads).total;
+  return MLA_OK;
+}
+
+mla_status_t mla_decode(const mla_cache_t* cache, const int32_t* seq_len, const void* q_nope,
+                        const void* q_pe, const void* w_uk, const void* w_uv,
+                        mla_dtype_t act_dtype, int32_t n_heads, float softmax_scale, void* out,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status_t st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (!valid_dtype(act_dtype)) return MLA_ERR_INVALID_ARGUMENT;
+  if (!seq_len || !q_nope || !q_pe || !w_uk || !w_uv || !out || !workspace)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (n_heads < 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (!supported_pair(cache->dtype, act_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (n_heads % 16 != 0 || n_heads > kMaxHeads) return MLA_ERR_UNSUPPORTED;
+  const int ct = cache_type(cache->dtype);
+  const int B = cache->num_seqs;
+  const WorkspaceLayout wl = workspace_layout(ct, B, n_heads);
+  if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+  char* ws = (char*)workspace;
+  DecodeArgs a{};
+  a.rows = cache->rows;
+  a.row_scale = cache->row_scale;
+  a.seq_start = cache->seq_start;
+  a.seq_cap = cache->seq_capacity;
+  a.seq_len = seq_len;
+  a.B = B;
+  a.H = n_heads;
+  a.q_nope = q_nope;
+  a.q_pe = q_pe;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.out = out;
+  a.lse = lse;
+  a.softmax_scale = softmax_scale;
+  a.prefix = (int64_t*)(ws + wl.prefix);
+  a.q_lat = ws + wl.q_lat;
+  a.part_o = (float*)(ws + wl.part_o);
+  a.part_ml = (float*)(ws + wl.part_ml);
+  const DecodePlan plan = make_plan(ct, B, n_heads);
+  hipError_t e = launch_decode(ct, plan, a, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// mla_append: compress hidden states into latent cache rows.
+//
+// row = (W_DKV h) || RoPE(W_KR h, pos), stored at seq_start[seq] + pos
+// (discosf explainer, "long-context bottleneck": only the compressed latent
+// c_KV is cached; "decoupled RoPE": a separate 64-wide key carries RoPE and is
+// shared by all heads, adding d_R elements per token).
+//
+// One workgroup owns 16 tokens and 48 of the 576 output columns (three
+// 16-row MFMA blocks; all 576 for the fp8 cache, whose per-row scale needs
+// the whole row). Its four waves split the d_model contraction and reduce
+// through LDS.
+#include <math.h>
+
+#include <type_traits>
+
+#include "common.h"
+#include "internal.h"
+
+namespace mla {
+
+constexpr int kColGroup = 48;                  // columns per group
+constexpr int kNumGroups = kDrow / kColGroup;  // 12
+
+template <int CT>
+__global__ void __launch_bounds__(256)
+mla_append_kernel(AppendArgs a) {
+  using E = typename std::conditional<CT == kF32, float, __bf16>::type;
+  constexpr bool FP8 = (CT == kFP8);
+  __shared__ float red[4][3][16][16];          // [wave][mblock][row j][token]
+  __shared__ float rowt[16][kDrow + 4];        // fp32 rows of the 16 tokens
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int tok0 = blockIdx.x * 16;
+  const int D = a.d_model;
+
+  const int tok_b = tok0 + l16 < a.n_tok ? tok0 + l16 : a.n_tok - 1;   // clamped B-operand token
+  const E* hrow = (const E*)a.h + (int64_t)tok_b * D;
+
+  const int cg_begin = FP8 ? 0 : blockIdx.y;
+  const int cg_end = FP8 ? kNumGroups : blockIdx.y + 1;
+  for (int cg = cg_begin; cg < cg_end; ++cg) {
+    f32x4 acc[3];
+#pragma unroll
+    for (int mb = 0; mb < 3; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const E* wrow[3];
+#pragma unroll
+    for (int mb = 0; mb < 3; ++mb) {
+      const int j = cg * kColGroup + mb * 16 + l16;      // output column of this lane's A row
+      wrow[mb] = (j < kDc) ? (const E*)a.w_dkv + (int64_t)j * D
+                           : (const E*)a.w_kr + (int64_t)(j - kDc) * D;
+    }
+    if constexpr (CT == kF32) {
+      for (int k = 4 * wave; k < D; k += 16) {
+        const float bv = hrow[k + g];
+#pragma unroll
+        for (int mb = 0; mb < 3; ++mb) acc[mb] = mfma_f32_k4(wrow[mb][k + g], bv, acc[mb]);
+      }
+    } else {
+      for (int k = 32 * wave; k < D; k += 128) {
+        const bf16x8 bv = *(const bf16x8*)(hrow + k + 8 * g);
+#pragma unroll
+        for (int mb = 0; mb < 3; ++mb)
+          acc[mb] = mfma_bf16_k32(*(const bf16x8*)(wrow[mb] + k + 8 * g), bv, acc[mb]);
+      }
+    }
+    // lane holds column cg*48 + 16mb + 4g + r of token l16
+#pragma unroll
+    for (int mb = 0; mb < 3; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][mb][4 * g + r][l16] = acc[mb][r];
+    __syncthreads();
+    for (int i = tid; i < 3 * 16 * 16; i += 256) {
+      const int mb = i >> 8, j = (i >> 4) & 15, t = i & 15;
+      rowt[t][cg * kColGroup + mb * 16 + j] =
+          red[0][mb][j][t] + red[1][mb][j][t] + red[2][mb][j][t] + red[3][mb][j][t];
+    }
+    __syncthreads();
+  }
+
+  // ---------------- RoPE on columns 512..575 (pairs 2i, 2i+1) ----------------
+  const int c_lo = FP8 ? 0 : blockIdx.y * kColGroup;
+  const int c_hi = FP8 ? kDrow : c_lo + kColGroup;
+  for (int i = tid; i < 16 * 32; i += 256) {
+    const int t = i >> 5, pr = i & 31;
+    const int col = kDc + 2 * pr;
+    const int tok = tok0 + t;
+    if (col < c_lo || col >= c_hi || tok >= a.n_tok) continue;
+    const double phi = (double)a.tok_pos[tok] * a.inv_freq[pr];
+    double sn, cs;
+    sincos(phi, &sn, &cs);
+    const double x0 = rowt[t][col], x1 = rowt[t][col + 1];
+    rowt[t][col] = (float)(x0 * cs - x1 * sn);
+    rowt[t][col + 1] = (float)(x0 * sn + x1 * cs);
+  }
+  __syncthreads();
+
+  // ---------------- store ----------------
+  if constexpr (!FP8) {
+    for (int i = tid; i < 16 * kColGroup; i += 256) {
+      const int t = i / kColGroup, c = c_lo + (i - t * kColGroup);
+      const int tok = tok0 + t;
+      if (tok >= a.n_tok) continue;
+      const int s = a.tok_seq[tok], pos = a.tok_pos[tok];
+      if (s < 0 || s >= a.num_seqs || pos < 0 || pos >= a.seq_cap[s]) continue;
+      const int64_t row = a.seq_start[s] + pos;
+      if constexpr (CT == kF32)
+        ((float*)a.rows)[row * kDrow + c] = rowt[t][c];
+      else
+        ((uint16_t*)a.rows)[row * kDrow + c] = f32_to_bf16_bits(rowt[t][c]);
+    }
+  } else {
+    // one token per 16 lanes: amax, scale, then 36 codes per lane
+    const int t = tid >> 4, sl = tid & 15;
+    const int tok = tok0 + t;
+    float amax = 0.f;
+    for (int c = sl; c < kDrow; c += 16) amax = __builtin_fmaxf(amax, __builtin_fabsf(rowt[t][c]));
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, shfl_xor_f(amax, off));
+    const float scale = amax > 0.f ? amax / 448.f : 1.f;
+    bool ok = tok < a.n_tok;
+    int s = 0, pos = 0;
+    if (ok) {
+      s = a.tok_seq[tok];
+      pos = a.tok_pos[tok];
+      ok = (s >= 0 && s < a.num_seqs && pos >= 0 && pos < a.seq_cap[s]);
+    }
+    if (ok) {
+      const int64_t row = a.seq_start[s] + pos;
+      uint32_t* dst = (uint32_t*)((uint8_t*)a.rows + row * kDrow);
+      for (int q4 = sl; q4 < kDrow / 4; q4 += 16) {
+        const float* v = &rowt[t][4 * q4];
+        dst[q4] = f32x4_to_fp8x4_sat(v[0] / scale, v[1] / scale, v[2] / scale, v[3] / scale);
+      }
+      if (sl == 0) a.row_scale[row] = scale;
+    }
+  }
+}
+
+hipError_t launch_append(int ct, const AppendArgs& a, hipStream_t s) {
+  dim3 grid((a.n_tok + 15) / 16, ct == kFP8 ? 1 : kNumGroups);
+  switch (ct) {
+    case kF32: hipLaunchKernelGGL(mla_append_kernel<kF32>, grid, dim3(256), 0, s, a); break;
+    case kBF16: hipLaunchKernelGGL(mla_append_kernel<kBF16>, grid, dim3(256), 0, s, a); break;
+    case kFP8: hipLaunchKernelGGL(mla_append_kernel<kFP8>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,201 @@
+// Device-side helpers shared by the libmla kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kDc = 512;
+constexpr int kDr = 64;
+constexpr int kDrow = 576;
+constexpr int kDnope = 128;
+constexpr int kDv = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers. Lane layout (checked on gfx950): for the 16x16 shapes lane l
+// supplies row (A) / column (B) l%16 and a run of K elements chosen by l/16;
+// the 4 results of lane l are D[4*(l/16) + r][l%16], r = 0..3.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma_bf16_k32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  // round to nearest even; NaN kept quiet
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
+  u32x4 u;
+  u[0] = pack_bf16x2(v[0], v[1]);
+  u[1] = pack_bf16x2(v[2], v[3]);
+  u[2] = pack_bf16x2(v[4], v[5]);
+  u[3] = pack_bf16x2(v[6], v[7]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// four e4m3fn codes (one dword) -> four exact bf16 values (two dwords).
+// Every e4m3fn value is exactly representable in bf16, so truncating the
+// fp32 value's low half is exact.
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t codes) {
+  auto a = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
+  auto b = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
+  uint2 r;
+  r.x = (__builtin_bit_cast(uint32_t, a[0]) >> 16) | (__builtin_bit_cast(uint32_t, a[1]) & 0xffff0000u);
+  r.y = (__builtin_bit_cast(uint32_t, b[0]) >> 16) | (__builtin_bit_cast(uint32_t, b[1]) & 0xffff0000u);
+  return r;
+}
+
+// fp32 -> e4m3fn code, round to nearest even, saturating at +-448
+// (the hardware conversion rounds to nearest even but does not saturate).
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4_sat(float a, float b, float c, float d) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.f), 448.f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.f), 448.f);
+  c = __builtin_fminf(__builtin_fmaxf(c, -448.f), 448.f);
+  d = __builtin_fminf(__builtin_fmaxf(d, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  int lane = __lane_id();
+  int src = lane ^ mask;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float max_over_groups(float v) {   // lanes l, l^16, l^32, l^48
+  v = __builtin_fmaxf(v, shfl_xor_f(v, 16));
+  v = __builtin_fmaxf(v, shfl_xor_f(v, 32));
+  return v;
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+  v += shfl_xor_f(v, 16);
+  v += shfl_xor_f(v, 32);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// LDS access
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x8 lds_read_b128(const char* lds_base, uint32_t byte_off) {
+  return *reinterpret_cast<const bf16x8*>(lds_base + byte_off);
+}
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16
+// lanes, result element q of lane j is the 16-bit value at
+// addr(lane 4q + j/4) + 2*(j%4): each quad of source lanes supplies a 4x4
+// block that arrives transposed.
+__device__ __forceinline__ s16x4 lds_read_tr16(const char* lds_base, uint32_t byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(lds_base + byte_off));
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS. Lane i's 16 bytes land at
+// lds_wave_base + 16*i; lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void async_copy16(const void* gsrc, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void async_copy4(const void* gsrc, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_wave_base, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
+}
+// Wait until at most K*PER copies are outstanding, K = min(younger, KMAX),
+// choosing the immediate at run time from a wave-uniform `younger`.
+template <int PER, int KMAX>
+__device__ __forceinline__ void wait_tiles(int younger) {
+  if constexpr (KMAX <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (younger >= KMAX) wait_vmcnt<KMAX * PER>();
+    else wait_tiles<PER, KMAX - 1>(younger);
+  }
+}
+
+// Workgroup barrier that does not wait for outstanding global loads: LDS
+// operations of this wave complete first (lgkmcnt(0)), vmcnt is left alone
+// so asynchronous global->LDS copies of later tiles stay in flight. The empty
+// asm keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Read a value that is constant for the whole launch through the constant
+// address space, so a wave-uniform index becomes a scalar load (lgkmcnt)
+// instead of a vector load that would be counted with the async copies.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(v & 0xffffffff));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
+  return ((int64_t)hi << 32) | (uint32_t)lo;
+}
+
+// ---------------------------------------------------------------------------
+// work partition shared by the attention and merge kernels: worker w of W
+// owns positions [start(w), start(w+1)) of the concatenation of all
+// sequences' tokens, start(w) = floor(w * T / W).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t worker_start(int64_t w, int64_t W, int64_t T) {
+  return (w * T) / W;
+}
+// largest b in [0, B) with prefix[b] <= pos (prefix is non-decreasing,
+// prefix[0] = 0, prefix[B] = T); callers pass pos < T
+__device__ __forceinline__ int find_seq(const int64_t* prefix, int B, int64_t pos) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (ld_const(prefix, mid) <= pos) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+// largest w in [0, W) with start(w) <= pos
+__device__ __forceinline__ int64_t find_worker(int64_t pos, int64_t W, int64_t T) {
+  int64_t w = (pos * W) / T;
+  if (w >= W) w = W - 1;
+  while (w + 1 < W && worker_start(w + 1, W, T) <= pos) ++w;
+  while (w > 0 && worker_start(w, W, T) > pos) --w;
+  return w;
+}
+
+}  // namespace mla

@@ -1,0 +1,78 @@
+// Host-side interface between the C ABI (api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+enum CacheType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+// ---------------------------------------------------------------- append
+struct AppendArgs {
+  void* rows;                 // [total_rows][576] cache storage
+  float* row_scale;           // [total_rows] (fp8 only)
+  const int64_t* seq_start;   // [B]
+  const int32_t* seq_cap;     // [B]
+  int32_t num_seqs;
+  const void* h;              // [n_tok][d_model]
+  const void* w_dkv;          // [512][d_model]
+  const void* w_kr;           // [64][d_model]
+  const int32_t* tok_seq;     // [n_tok]
+  const int32_t* tok_pos;     // [n_tok]
+  int32_t n_tok;
+  int32_t d_model;
+  double inv_freq[32];        // rope_base^(-2i/64), fp64
+};
+hipError_t launch_append(int cache_type, const AppendArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- decode
+// Launch plan: fixed by (cache type, B, H) so that the workspace size can be
+// computed on the host without seeing the device-resident lengths.
+struct DecodePlan {
+  int hb;        // 16-head blocks per workgroup (waves sharing one cache tile)
+  int ds;        // value-dimension splits per head block (waves per head block)
+  int nstage;    // cache tiles in flight per workgroup (LDS ring depth)
+  int workers;   // W: token ranges of the concatenated sequences
+  int head_groups;  // H / (16 * hb)
+  int64_t nslot;    // partial-result slots: W + B
+};
+DecodePlan make_plan(int cache_type, int B, int H);
+
+struct WorkspaceLayout {
+  size_t prefix;     // int64 [B+1] prefix sums of clamped lengths
+  size_t q_lat;      // [B][H][512] bf16 (f32 for the f32 path)
+  size_t part_o;     // f32 [nslot][H][512] unnormalised partial outputs
+  size_t part_ml;    // f32 [nslot][H][2] running max (log2 domain) and sum
+  size_t total;
+};
+WorkspaceLayout workspace_layout(int cache_type, int B, int H);
+
+struct DecodeArgs {
+  // cache
+  const void* rows;
+  const float* row_scale;
+  const int64_t* seq_start;
+  const int32_t* seq_cap;
+  const int32_t* seq_len;
+  int32_t B;
+  int32_t H;
+  // activations / weights (bf16 or f32)
+  const void* q_nope;
+  const void* q_pe;
+  const void* w_uk;
+  const void* w_uv;
+  void* out;
+  float* lse;
+  float softmax_scale;
+  // workspace views
+  int64_t* prefix;
+  void* q_lat;
+  float* part_o;
+  float* part_ml;
+};
+hipError_t launch_decode(int cache_type, const DecodePlan& plan, const DecodeArgs& a,
+                         hipStream_t s);
+
+}  // namespace mla

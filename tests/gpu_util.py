@@ -1,0 +1,73 @@
+"""Helpers shared by the GPU tests: move a synthetic problem to the device,
+run libmla on it, and compare with the oracle."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import workloads as W
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 4e-2}     # rel-L2 bounds on o[B,H,128]
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class DeviceProblem:
+    def __init__(self, p: W.Problem, device="cuda"):
+        import head_latent_attention_14_amd as mla
+        self.mla = mla
+        self.p = p
+        dev = torch.device(device)
+        self.dev = dev
+        rows = p.rows.to(dev)
+        scale = p.row_scale.to(dev) if p.row_scale is not None else None
+        self.cache = mla.LatentCache(rows=rows, seq_start=torch.from_numpy(p.seq_start).to(dev),
+                                     seq_capacity=torch.from_numpy(p.seq_capacity).to(dev),
+                                     row_scale=scale)
+        self.seq_len = torch.from_numpy(p.seq_len).to(dev)
+        self.q_nope = p.q_nope.to(dev)
+        self.q_pe = p.q_pe.to(dev)
+        self.w_uk = p.w_uk.to(dev)
+        self.w_uv = p.w_uv.to(dev)
+        B, H = p.q_nope.shape[:2]
+        self.B, self.H = B, H
+        self.out = torch.empty(B, H, 128, dtype=p.q_nope.dtype, device=dev)
+        self.lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+        self.ws = mla.alloc_workspace(self.cache, H, p.q_nope.dtype)
+        if p.h is not None:
+            self.h = p.h.to(dev)
+            self.w_dkv = p.w_dkv.to(dev)
+            self.w_kr = p.w_kr.to(dev)
+            self.tok_seq = torch.from_numpy(p.tok_seq).to(dev)
+            self.tok_pos = torch.from_numpy(p.tok_pos).to(dev)
+
+    def append(self):
+        self.mla.mla_append(self.cache, self.h, self.w_dkv, self.w_kr, self.tok_seq, self.tok_pos,
+                            self.p.wl.rope_base)
+
+    def decode(self, poison=False):
+        if poison:
+            self.out.fill_(float("nan"))
+            self.lse.fill_(float("nan"))
+            self.ws.fill_(0xFF)        # NaN patterns in every fp32 slot
+        self.mla.mla_decode(self.cache, self.seq_len, self.q_nope, self.q_pe, self.w_uk, self.w_uv,
+                            1.0 / math.sqrt(192.0), self.out, self.lse, self.ws)
+
+    def step(self, poison=False):
+        if self.p.h is not None:
+            self.append()
+        self.decode(poison)
+        torch.cuda.synchronize()
+        return self.out.to(torch.float64).cpu().numpy(), self.lse.to(torch.float64).cpu().numpy()
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))

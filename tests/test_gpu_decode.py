@@ -1,0 +1,139 @@
+"""GPU parity of mla_decode (and mla_append where the workload has it)
+against the fp64 oracle, through the C ABI.
+
+Small cases run the oracle on every output; full-size cases (the workload
+shapes the benchmark uses) compare sampled (sequence, head) outputs, which
+the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle.problem import OracleView
+from tests.gpu_util import TOL, DeviceProblem, log, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+SMALL_LENGTHS = {
+    # ragged: 1 token, a partial tile, several tiles with a ragged tail
+    16: [1, 37, 300, 64],
+    128: [1, 33, 200],
+}
+
+
+def _small(name, lengths=None, seed=None):
+    wl = W.WORKLOADS[name]
+    lengths = np.array(lengths if lengths is not None else SMALL_LENGTHS[wl.H])
+    return W.make_problem(wl, seed=seed, B=len(lengths), lengths=lengths)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_decode_small_all_outputs(name):
+    p = _small(name)
+    log(f"[decode small] {name} lengths={p.seq_len.tolist()} H={p.wl.H}")
+    dp = DeviceProblem(p)
+    o, lse = dp.step(poison=True)
+    ro, rl = OracleView(p).decode()
+    err = rel_l2(o, ro)
+    log(f"  rel-L2 {err:.3e} (bound {TOL[p.wl.cache]}), lse max abs {np.abs(lse - rl).max():.3e}")
+    assert np.all(np.isfinite(o))
+    assert err <= TOL[p.wl.cache]
+    assert np.abs(lse - rl).max() <= 50 * TOL[p.wl.cache]
+    # every sequence on its own meets the bound too
+    for b in range(p.q_nope.shape[0]):
+        assert rel_l2(o[b], ro[b]) <= TOL[p.wl.cache], b
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_decode_full_size_sampled(name):
+    wl = W.WORKLOADS[name]
+    p = W.make_problem(wl)
+    log(f"[decode full] {name} B={wl.B} H={wl.H} T={p.T}")
+    dp = DeviceProblem(p)
+    o, lse = dp.step(poison=True)
+    rng = np.random.default_rng(100 + wl.index)
+    B, H = wl.B, wl.H
+    n = 6 if name == "long_bf16" else 16
+    pairs = [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(n)]
+    pairs += [(0, 0), (B - 1, H - 1)]
+    pairs = sorted(set(pairs))
+    ro, rl = OracleView(p).decode(pairs)
+    got = np.stack([o[b, h] for b, h in pairs])
+    gl = np.array([lse[b, h] for b, h in pairs])
+    err = rel_l2(got, ro)
+    log(f"  sampled {len(pairs)} pairs rel-L2 {err:.3e} lse max abs {np.abs(gl - rl).max():.3e}")
+    assert np.all(np.isfinite(o))
+    assert err <= TOL[wl.cache]
+    assert np.abs(gl - rl).max() <= 50 * TOL[wl.cache]
+
+
+def test_decode_deterministic_and_repeatable():
+    p = _small("v2lite_bf16", lengths=[700, 5, 1300])
+    dp = DeviceProblem(p)
+    dp.decode(poison=True)
+    a = dp.out.clone()
+    la = dp.lse.clone()
+    dp.decode(poison=True)
+    assert torch.equal(a, dp.out) and torch.equal(la, dp.lse)
+
+
+def test_nan_in_one_sequence_stays_there():
+    p = _small("v2_bf16", lengths=[90, 150, 40])
+    s1 = int(p.seq_start[1])
+    p.rows[s1 + 17, 3] = float("nan")
+    dp = DeviceProblem(p)
+    o, _ = dp.step()
+    assert np.all(np.isnan(o[1]))
+    assert np.all(np.isfinite(o[0])) and np.all(np.isfinite(o[2]))
+    ro, _ = OracleView(p).decode([(0, h) for h in range(128)] + [(2, h) for h in range(128)])
+    assert rel_l2(np.concatenate([o[0], o[2]]), ro) <= TOL["bf16"]
+
+
+def test_canary_rows_poisoned_do_not_leak():
+    # rows past each sequence's length hold huge values and NaN; output unchanged
+    p = _small("v2lite_bf16", lengths=[33, 64, 2])
+    mask = torch.from_numpy(W.canary_mask(p))
+    p.rows[mask] = float("nan")
+    dp = DeviceProblem(p)
+    o, lse = dp.step()
+    ro, rl = OracleView(p).decode()
+    assert np.all(np.isfinite(o)) and rel_l2(o, ro) <= TOL["bf16"]
+
+
+def test_zero_and_clamped_lengths():
+    p = _small("v2lite_bf16", lengths=[5, 40, 9])
+    dp = DeviceProblem(p)
+    # sequence 0 gets length 0, sequence 2 asks for more rows than it owns
+    dp.seq_len.copy_(torch.tensor([0, 40, 10_000], dtype=torch.int32))
+    dp.decode(poison=True)
+    torch.cuda.synchronize()
+    o = dp.out.double().cpu().numpy()
+    lse = dp.lse.double().cpu().numpy()
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    p2 = W.make_problem(W.WORKLOADS["v2lite_bf16"], B=3, lengths=np.array([5, 40, 9]))
+    p2.seq_len = np.array([1, 40, int(p.seq_capacity[2])], dtype=np.int32)
+    ro, _ = OracleView(p2).decode([(1, h) for h in range(16)] + [(2, h) for h in range(16)])
+    assert rel_l2(np.concatenate([o[1], o[2]]), ro) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("B", [1, 17, 300])
+def test_many_and_few_sequences(B):
+    rng = np.random.default_rng(B)
+    lengths = rng.integers(1, 200, size=B)
+    p = W.make_problem(W.WORKLOADS["v2lite_bf16"], seed=B, B=B, lengths=lengths)
+    log(f"[decode B={B}] T={p.T}")
+    dp = DeviceProblem(p)
+    o, _ = dp.step()
+    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(B, size=24), rng.integers(16, size=24))]
+    ro, _ = OracleView(p).decode(sorted(set(pairs)))
+    got = np.stack([o[b, h] for b, h in sorted(set(pairs))])
+    assert rel_l2(got, ro) <= TOL["bf16"]
+
+
+def test_other_head_counts():
+    for H in [32, 64]:
+        p = W.make_problem(W.WORKLOADS["v2_bf16"], B=2, lengths=np.array([77, 300]), H=H)
+        dp = DeviceProblem(p)
+        o, _ = dp.step()
+        ro, _ = OracleView(p).decode()
+        assert rel_l2(o, ro) <= TOL["bf16"], H
