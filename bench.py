@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of one MLA decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: mla_append of one
+new token per sequence, then mla_decode (absorb W_UK, attention over the
+latent cache, merge + W_UV) for every sequence. The default workload is the
+DeepSeek-V2-Lite-shaped decode (B=64, H=16, L ~ U[1024, 4096], bf16 cache,
+d_model 2048). Inputs are synthetic and seeded; several replicas of the
+cache and weights are rotated so each step reads its cache from HBM, not
+from the 256 MB Infinity Cache.
+
+Prints one JSON line. `value` is the step's algorithmic bytes (cache rows,
+weights, activations and outputs the method must move) per second.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode latent-cache GB/s + TFLOP/s, % of MI355X roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["head_latent_attention_14_amd/csrc/decode_attn.hip",
+                  "head_latent_attention_14_amd/csrc/common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter runs, if
+    they were taken on the current kernel source for this workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get(workload)
+    if not r or r.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return r.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="v2lite_bf16")
+    ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 2x the MALL")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(p, seconds: float):
+    """Time the fp64 oracle on whole sequences of the same problem until about
+    `seconds` of CPU work; report its rate in the metric's unit."""
+    from oracle import mla as omla
+    from oracle.problem import OracleView
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        blas_threads = None
+    view = OracleView(p)
+    B, H = p.q_nope.shape[:2]
+    e_c = {"f32": 4, "bf16": 2, "fp8": 1}[p.wl.cache] + 0
+    sf = 4 if p.wl.cache == "fp8" else 0
+    e_a = {"f32": 4, "bf16": 2}[p.wl.act]
+    t0 = time.perf_counter()
+    done = 0
+    tokens = 0
+    while done < B and time.perf_counter() - t0 < seconds:
+        view.decode([(done, h) for h in range(H)])
+        tokens += int(p.seq_len[done])
+        done += 1
+    el = time.perf_counter() - t0
+    # the sample's share of the step's algorithmic bytes
+    by = tokens * (576 * e_c + sf) + 2 * H * 128 * 512 * e_a + done * H * (192 + 128) * e_a
+    cores = len(os.sched_getaffinity(0))
+    return {"value": by / el / 1e9, "unit": "GB/s", "cores": blas_threads or cores,
+            "kind": "oracle",
+            "sample": f"fp64 unabsorbed oracle on sequences 0..{done - 1} of {B} "
+                      f"(all {H} heads, {tokens} cached tokens, {el:.1f} s, "
+                      f"{cores} host cores visible)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_latent_attention_14_amd as mla
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    p = W.make_problem(wl)
+    B, H = wl.B, wl.H
+    T = p.T
+    ab = W.algorithmic_bytes(p)
+    fl = W.algorithmic_flops(p)
+    e_a = {"f32": 4, "bf16": 2}[wl.act]
+    e_c = {"f32": 4, "bf16": 2, "fp8": 1}[wl.cache]
+    append_bytes = 0
+    if wl.append:
+        # h, W_DKV, W_KR read; one row written per token
+        append_bytes = B * wl.d_model * e_a + 576 * wl.d_model * e_a + B * 576 * e_c
+    step_bytes = ab["total"] + append_bytes
+    step_flops = fl["total"] + (2 * B * wl.d_model * 576 if wl.append else 0)
+    attn_bytes = ab["cache"]             # per attention launch: the latent rows streamed once
+
+    # ---- replicas so that every step reads its inputs from HBM ----
+    per_rep = p.rows.numel() * p.rows.element_size() + ab["weights"]
+    R = args.replicas or max(2, math.ceil(2 * 256e6 / per_rep) + 1)
+    reps = []
+    for r in range(R):
+        rows = p.rows.to(dev)
+        cache = mla.LatentCache(rows=rows, seq_start=torch.from_numpy(p.seq_start).to(dev),
+                                seq_capacity=torch.from_numpy(p.seq_capacity).to(dev),
+                                row_scale=p.row_scale.to(dev) if p.row_scale is not None else None)
+        rep = dict(cache=cache, seq_len=torch.from_numpy(p.seq_len).to(dev),
+                   q_nope=p.q_nope.to(dev), q_pe=p.q_pe.to(dev), w_uk=p.w_uk.to(dev),
+                   w_uv=p.w_uv.to(dev),
+                   out=torch.empty(B, H, 128, dtype=p.q_nope.dtype, device=dev),
+                   lse=torch.empty(B, H, dtype=torch.float32, device=dev))
+        rep["ws"] = mla.alloc_workspace(cache, H, p.q_nope.dtype)
+        if wl.append:
+            rep.update(h=p.h.to(dev), w_dkv=p.w_dkv.to(dev), w_kr=p.w_kr.to(dev),
+                       tok_seq=torch.from_numpy(p.tok_seq).to(dev),
+                       tok_pos=torch.from_numpy(p.tok_pos).to(dev))
+        reps.append(rep)
+    scale = 1.0 / math.sqrt(192.0)
+    stream = torch.cuda.current_stream()
+
+    def dec_args(r):
+        return (r["cache"], r["seq_len"], r["q_nope"], r["q_pe"], r["w_uk"], r["w_uv"], scale,
+                r["out"], r["lse"], r["ws"])
+
+    def step(i, ev=None):
+        r = reps[i % R]
+        if wl.append:
+            mla.mla_append(r["cache"], r["h"], r["w_dkv"], r["w_kr"], r["tok_seq"], r["tok_pos"],
+                           wl.rope_base)
+        a = dec_args(r)
+        mla.mla_decode_absorb(*a)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_decode_attend(*a)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.mla_decode_combine(*a)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    gpu_ms = start.elapsed_time(end) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg_ms = float(np.mean(attn_ms))
+    ms = max(wall_ms, gpu_ms)
+
+    value = step_bytes / (ms * 1e-3) / 1e9
+    attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-cache/bf16"}[wl.cache],
+        "data": "synthetic (seeded normal draws; random-init weights of the DeepSeek-V2(-Lite) "
+                "MLA shapes)",
+        "config": {"workload": f"{wl.name}: MLA decode step, append {'1 token/seq + ' if wl.append else ''}"
+                               f"decode, B={B}, H={H}, L~U[{wl.lo},{wl.hi}], {wl.cache} latent cache",
+                   "B": B, "H": H, "T": T, "d_c": 512, "d_r": 64,
+                   "d_model": wl.d_model if wl.append else None, "replicas": R},
+        "tflops": round(step_flops / (ms * 1e-3) / 1e12, 3),
+        "attended_tokens_per_s": round(T / (ms * 1e-3), 1),
+        "step_bytes": int(step_bytes),
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "mla_attn_kernel",
+                     "kernel_avg_us": round(attn_avg_ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": int(attn_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,8 +30,9 @@ MLA_DTYPE_FP8_E4M3 = 2
 
 D_C, D_R, D_ROW, D_NOPE, D_V = 512, 64, 576, 128, 128
 
-EXPORTED = ["mla_append", "mla_decode_workspace_size", "mla_decode", "mla_status_string",
-            "mla_abi_version"]
+EXPORTED = ["mla_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_absorb",
+            "mla_decode_attend", "mla_decode_combine", "mla_status_string", "mla_abi_version"]
+DECODE_STAGES = ["mla_decode_absorb", "mla_decode_attend", "mla_decode_combine"]
 
 
 class mla_cache_t(ctypes.Structure):
@@ -48,11 +49,11 @@ class mla_cache_t(ctypes.Structure):
     ]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libmla.so not built at {LIB_PATH}; run "
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"libmla.so not built at {path}; run "
                           "`python -m head_latent_attention_14_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                             ctypes.c_size_t)
     C = ctypes.POINTER(mla_cache_t)
@@ -61,8 +62,10 @@ def _load():
     lib.mla_decode_workspace_size.argtypes = [I32, I32, ctypes.c_int, ctypes.c_int,
                                               ctypes.POINTER(SZ)]
     lib.mla_decode_workspace_size.restype = ctypes.c_int
-    lib.mla_decode.argtypes = [C, P, P, P, P, P, ctypes.c_int, I32, F32, P, P, P, SZ, P]
-    lib.mla_decode.restype = ctypes.c_int
+    for name in ["mla_decode", "mla_decode_absorb", "mla_decode_attend", "mla_decode_combine"]:
+        fn = getattr(lib, name)
+        fn.argtypes = [C, P, P, P, P, P, ctypes.c_int, I32, F32, P, P, P, SZ, P]
+        fn.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -173,18 +176,39 @@ def alloc_workspace(cache: LatentCache, n_heads: int, act_dtype: torch.dtype,
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device or cache.rows.device)
 
 
-def mla_decode(cache: LatentCache, seq_len: torch.Tensor, q_nope: torch.Tensor,
-               q_pe: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
-               softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
-               workspace: torch.Tensor, stream=None) -> None:
-    """o[B,H,128] (and lse[B,H]) of MLA decode over the latent cache (see libmla.h)."""
+def _decode_call(name, cache, seq_len, q_nope, q_pe, w_uk, w_uv, softmax_scale, out, lse,
+                 workspace, stream=None):
     if seq_len.dtype != torch.int32:
         raise TypeError("seq_len must be int32")
     if lse is not None and lse.dtype != torch.float32:
         raise TypeError("lse must be float32")
     B, H, _ = q_nope.shape
     st = ctypes.byref(cache.struct())
-    _check(lib.mla_decode(st, _ptr(seq_len), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
-                          dtype_code(q_nope.dtype), H, float(softmax_scale), _ptr(out),
-                          _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)),
-           "mla_decode")
+    _check(getattr(lib, name)(st, _ptr(seq_len), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk),
+                              _ptr(w_uv), dtype_code(q_nope.dtype), H, float(softmax_scale),
+                              _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                              _stream(stream)), name)
+
+
+def mla_decode(cache: LatentCache, seq_len: torch.Tensor, q_nope: torch.Tensor,
+               q_pe: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
+               softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
+               workspace: torch.Tensor, stream=None) -> None:
+    """o[B,H,128] (and lse[B,H]) of MLA decode over the latent cache (see libmla.h)."""
+    _decode_call("mla_decode", cache, seq_len, q_nope, q_pe, w_uk, w_uv, softmax_scale, out,
+                 lse, workspace, stream)
+
+
+def mla_decode_absorb(*args, **kw) -> None:
+    """Stage 1 of mla_decode (same arguments)."""
+    _decode_call("mla_decode_absorb", *args, **kw)
+
+
+def mla_decode_attend(*args, **kw) -> None:
+    """Stage 2 of mla_decode (same arguments)."""
+    _decode_call("mla_decode_attend", *args, **kw)
+
+
+def mla_decode_combine(*args, **kw) -> None:
+    """Stage 3 of mla_decode (same arguments)."""
+    _decode_call("mla_decode_combine", *args, **kw)

@@ -24,6 +24,9 @@ COMMON = [
     # no packed-fp32 VALU instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    # MFMA accumulators in ordinary VGPRs: the softmax rescale and the partial
+    # stores then touch them without AGPR<->VGPR copies every tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

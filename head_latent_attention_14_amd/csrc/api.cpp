@@ -138,10 +138,11 @@ mla_status_t mla_decode_workspace_size(int32_t num_seqs, int32_t n_heads, mla_dt
   return MLA_OK;
 }
 
-mla_status_t mla_decode(const mla_cache_t* cache, const int32_t* seq_len, const void* q_nope,
-                        const void* q_pe, const void* w_uk, const void* w_uv,
-                        mla_dtype_t act_dtype, int32_t n_heads, float softmax_scale, void* out,
-                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len,
+                                const void* q_nope, const void* q_pe, const void* w_uk,
+                                const void* w_uv, mla_dtype_t act_dtype, int32_t n_heads,
+                                float softmax_scale, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream, int stage) {
   mla_status_t st = check_cache(cache);
   if (st != MLA_OK) return st;
   if (!valid_dtype(act_dtype)) return MLA_ERR_INVALID_ARGUMENT;
@@ -178,8 +179,22 @@ mla_status_t mla_decode(const mla_cache_t* cache, const int32_t* seq_len, const 
   a.part_o = (float*)(ws + wl.part_o);
   a.part_ml = (float*)(ws + wl.part_ml);
   const DecodePlan plan = make_plan(ct, B, n_heads);
-  hipError_t e = launch_decode(ct, plan, a, (hipStream_t)stream);
+  hipError_t e = launch_decode(ct, plan, a, (hipStream_t)stream, stage);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
+
+#define MLA_DECODE_ENTRY(NAME, STAGE)                                                        \
+  mla_status_t NAME(const mla_cache_t* cache, const int32_t* seq_len, const void* q_nope,  \
+                    const void* q_pe, const void* w_uk, const void* w_uv,                   \
+                    mla_dtype_t act_dtype, int32_t n_heads, float softmax_scale, void* out, \
+                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {    \
+    return decode_impl(cache, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads,        \
+                       softmax_scale, out, lse, workspace, workspace_bytes, stream, STAGE); \
+  }
+
+MLA_DECODE_ENTRY(mla_decode, 0)
+MLA_DECODE_ENTRY(mla_decode_absorb, 1)
+MLA_DECODE_ENTRY(mla_decode_attend, 2)
+MLA_DECODE_ENTRY(mla_decode_combine, 3)
 
 }  // extern "C"

@@ -60,7 +60,22 @@ mla_append_kernel(AppendArgs a) {
         for (int mb = 0; mb < 3; ++mb) acc[mb] = mfma_f32_k4(wrow[mb][k + g], bv, acc[mb]);
       }
     } else {
-      for (int k = 32 * wave; k < D; k += 128) {
+      // four k-steps per round, all loads of a round issued before its MFMAs
+      int k = 32 * wave;
+      for (; k + 3 * 128 < D; k += 4 * 128) {
+        bf16x8 bv[4], av[4][3];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          bv[u] = *(const bf16x8*)(hrow + k + 128 * u + 8 * g);
+#pragma unroll
+          for (int mb = 0; mb < 3; ++mb) av[u][mb] = *(const bf16x8*)(wrow[mb] + k + 128 * u + 8 * g);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int mb = 0; mb < 3; ++mb) acc[mb] = mfma_bf16_k32(av[u][mb], bv[u], acc[mb]);
+      }
+      for (; k < D; k += 128) {
         const bf16x8 bv = *(const bf16x8*)(hrow + k + 8 * g);
 #pragma unroll
         for (int mb = 0; mb < 3; ++mb)

@@ -37,18 +37,15 @@ __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, const f32x4& c) {
 // ---------------------------------------------------------------------------
 // conversions
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
-  // round to nearest even; NaN kept quiet
-  uint32_t u = __builtin_bit_cast(uint32_t, x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
-  return __builtin_bit_cast(float, (uint32_t)b << 16);
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32 per pair)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
   u32x4 u;
@@ -61,13 +58,16 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
 
 // four e4m3fn codes (one dword) -> four exact bf16 values (two dwords).
 // Every e4m3fn value is exactly representable in bf16, so truncating the
-// fp32 value's low half is exact.
+// fp32 value's low half is exact. (Vector elements are copied to scalars
+// before __builtin_bit_cast: applied to an element expression such as a[1]
+// the builtin reads element 0.)
 __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t codes) {
-  auto a = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
-  auto b = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
+  const float a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
   uint2 r;
-  r.x = (__builtin_bit_cast(uint32_t, a[0]) >> 16) | (__builtin_bit_cast(uint32_t, a[1]) & 0xffff0000u);
-  r.y = (__builtin_bit_cast(uint32_t, b[0]) >> 16) | (__builtin_bit_cast(uint32_t, b[1]) & 0xffff0000u);
+  r.x = (__builtin_bit_cast(uint32_t, a0) >> 16) | (__builtin_bit_cast(uint32_t, a1) & 0xffff0000u);
+  r.y = (__builtin_bit_cast(uint32_t, b0) >> 16) | (__builtin_bit_cast(uint32_t, b1) & 0xffff0000u);
   return r;
 }
 
@@ -91,15 +91,54 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   int src = lane ^ mask;
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
 }
-__device__ __forceinline__ float max_over_groups(float v) {   // lanes l, l^16, l^32, l^48
-  v = __builtin_fmaxf(v, shfl_xor_f(v, 16));
-  v = __builtin_fmaxf(v, shfl_xor_f(v, 32));
-  return v;
+// Reductions over the four lanes l, l^16, l^32, l^48 that hold one MFMA
+// column. v_permlane32_swap / v_permlane16_swap (gfx950) hand each lane the
+// pair {x[l], x[l^32]} and {x[l], x[l^16]} (checked on gfx950), so each step
+// is VALU work with no LDS round trip.
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  const unsigned a0 = a[0], a1 = a[1];
+  v = __builtin_fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+  const auto b = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  const unsigned b0 = b[0], b1 = b[1];
+  return __builtin_fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
 }
 __device__ __forceinline__ float sum_over_groups(float v) {
-  v += shfl_xor_f(v, 16);
-  v += shfl_xor_f(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  const unsigned a0 = a[0], a1 = a[1];
+  v = __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
+  const auto b = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                  __builtin_bit_cast(unsigned, v), false, false);
+  const unsigned b0 = b[0], b1 = b[1];
+  return __builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1);
+}
+
+// Eight transposing LDS reads (ds_read_b64_tr_b16, gfx950) at one per-lane
+// address plus compile-time offsets, completed inside the same asm block:
+// the compiler never sees a load in flight. (Through the builtin the
+// compiler would wait for every asynchronous global->LDS copy first.)
+// Within each group of 16 lanes, element q of lane j comes from the 16-bit
+// value at addr(lane 4q + j/4) + 2*(j%4).
+template <int O0, int O1, int O2, int O3, int O4, int O5, int O6, int O7>
+__device__ __forceinline__ void lds_tr16_x8(uint32_t addr, s16x4& r0, s16x4& r1, s16x4& r2,
+                                            s16x4& r3, s16x4& r4, s16x4& r5, s16x4& r6,
+                                            s16x4& r7) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%9\n"
+      "ds_read_b64_tr_b16 %1, %8 offset:%10\n"
+      "ds_read_b64_tr_b16 %2, %8 offset:%11\n"
+      "ds_read_b64_tr_b16 %3, %8 offset:%12\n"
+      "ds_read_b64_tr_b16 %4, %8 offset:%13\n"
+      "ds_read_b64_tr_b16 %5, %8 offset:%14\n"
+      "ds_read_b64_tr_b16 %6, %8 offset:%15\n"
+      "ds_read_b64_tr_b16 %7, %8 offset:%16\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(addr), "i"(O0), "i"(O1), "i"(O2), "i"(O3), "i"(O4), "i"(O5), "i"(O6), "i"(O7)
+      : "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -124,6 +163,21 @@ __device__ __forceinline__ void async_copy16(const void* gsrc, char* lds_wave_ba
 }
 __device__ __forceinline__ void async_copy4(const void* gsrc, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_wave_base, 4, 0, 0);
+}
+
+// The same copies through a buffer resource: the 64-bit base sits in scalar
+// registers and each lane only supplies a 32-bit byte offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ void buffer_copy16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buffer_copy4(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                             char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 4, voff, 0, 0, 0);
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:

@@ -33,36 +33,30 @@ struct AttnParams {
   float scale_log2;          // softmax_scale * log2(e)
 };
 
+// Per cache dtype: bytes of a stored row, bytes of a padded LDS row, and
+// tokens per tile. Rows in LDS are padded by 16 bytes so that the 16 rows one
+// MFMA operand read touches start on different banks; every operand read is
+// then a per-lane base plus a compile-time offset.
 template <int CT> struct Tr;
-template <> struct Tr<kBF16> { static constexpr int kRowBytes = 1152, kTile = 32; };
-template <> struct Tr<kFP8> { static constexpr int kRowBytes = 576, kTile = 32; };
-template <> struct Tr<kF32> { static constexpr int kRowBytes = 2304, kTile = 16; };
-
-// XOR swizzle of the 16-byte chunk index inside an LDS row: rows 576, 1152
-// or 2304 bytes apart start on the same bank, so chunk j of row r is stored
-// at j ^ swz(r) to spread the 16 rows one MFMA operand read touches over the
-// banks. The XOR stays inside aligned groups of 8 chunks (4 for the 36-chunk
-// fp8 rows), so it never leaves the row.
-template <int RB>
-__device__ __forceinline__ int swz(int r) {
-  return (RB % 128 == 0) ? ((r >> 1) & 7) : ((r >> 1) & 3);
-}
-
-template <int RB>
-__device__ __forceinline__ uint32_t lds_off(int r, int chunk, int within = 0) {
-  return (uint32_t)(r * RB + ((chunk ^ swz<RB>(r)) << 4) + within);
-}
+template <> struct Tr<kBF16> { static constexpr int kRowBytes = 1152, kPad = 1168, kTile = 32; };
+template <> struct Tr<kFP8> { static constexpr int kRowBytes = 576, kPad = 592, kTile = 32; };
+template <> struct Tr<kF32> { static constexpr int kRowBytes = 2304, kPad = 2320, kTile = 16; };
+constexpr int kConvPad = 1168;   // padded bf16 row of the widened fp8 tile
+constexpr float kSlack = 8.f;    // lazy-rescale slack of the running max (log2 units)
 
 struct Cursor {
-  int b;          // sequence
-  int64_t t;      // first token of the tile, local to the sequence
-  int64_t t_end;  // end of this worker's segment of the sequence (local)
+  int b;            // sequence
+  int64_t t;        // first token of the tile, local to the sequence
+  int64_t t_end;    // end of this worker's segment of the sequence (local)
+  int64_t row0;     // cache row of token t
 };
 
 // Move to the next tile of this worker's token range; false when done.
 template <int TILE>
-__device__ __forceinline__ bool advance(Cursor& c, const int64_t* prefix, int B, int64_t r_hi) {
+__device__ __forceinline__ bool advance(Cursor& c, const int64_t* prefix, const int64_t* seq_start,
+                                        int B, int64_t r_hi) {
   c.t += TILE;
+  c.row0 += TILE;
   if (c.t < c.t_end) return true;
   int b = c.b + 1;
   while (b < B && ld_const(prefix, b + 1) == ld_const(prefix, b)) ++b;   // skip empty sequences
@@ -72,7 +66,17 @@ __device__ __forceinline__ bool advance(Cursor& c, const int64_t* prefix, int B,
   c.t = 0;
   const int64_t pb = ld_const(prefix, b), pe = ld_const(prefix, b + 1);
   c.t_end = (pe < r_hi ? pe : r_hi) - pb;
+  c.row0 = ld_const(seq_start, b);
   return true;
+}
+
+// Value operands of four 16-dim blocks starting at block NB0: the low half
+// covers tile rows 0..15, the high half rows 16..31 (row pitch TP bytes).
+template <int TP, int NB0>
+__device__ __forceinline__ void pv_read4(uint32_t addr, s16x4* lo, s16x4* hi) {
+  lds_tr16_x8<NB0 * 32, 16 * TP + NB0 * 32, (NB0 + 1) * 32, 16 * TP + (NB0 + 1) * 32,
+              (NB0 + 2) * 32, 16 * TP + (NB0 + 2) * 32, (NB0 + 3) * 32, 16 * TP + (NB0 + 3) * 32>(
+      addr, lo[0], hi[0], lo[1], hi[1], lo[2], hi[2], lo[3], hi[3]);
 }
 
 template <int CT, int HB, int DS, int NSTAGE>
@@ -81,17 +85,26 @@ mla_attn_kernel(AttnParams p) {
   constexpr int NW = HB * DS;
   constexpr int TILE = Tr<CT>::kTile;
   constexpr int RB = Tr<CT>::kRowBytes;
-  constexpr int STAGE_DATA = TILE * RB;
+  constexpr int RP = Tr<CT>::kPad;
+  constexpr int SPR = RP / 16;                           // 16-byte slots per padded row
+  constexpr int NCH = (TILE * RP + 1023) / 1024;         // 1 KB wave copies per tile
+  constexpr int STAGE_DATA = NCH * 1024;
   constexpr int STAGE_BYTES = STAGE_DATA + (CT == kFP8 ? 256 : 0);
-  constexpr int NCH = STAGE_DATA / 1024;                 // 1 KB wave copies per tile
-  constexpr int CPR = RB / 16;                           // 16-byte chunks per row
-  constexpr int CONV_BYTES = (CT == kFP8) ? TILE * 1152 : 0;
+  constexpr int CONV_BYTES = (CT == kFP8) ? TILE * kConvPad : 0;
+  constexpr int NCOPY = NCH + (CT == kFP8 ? 1 : 0);      // fp8 adds the row-scale copy
+  constexpr int CPW = (NCOPY + NW - 1) / NW;             // copies per wave per tile
   constexpr int DSLICE = kDc / DS;
   constexpr int NB = DSLICE / 16;
-  static_assert(STAGE_DATA % 1024 == 0, "tile must be whole 1 KB copies");
+  // Split scores: with one 16-head block shared by four waves, wave w
+  // computes the scores of token block (w & 1) over half of the 576-wide
+  // contraction (w >> 1) and the four fp32 partials meet in LDS, so each
+  // score MFMA and each tile read for scores happens once per workgroup.
+  constexpr bool SK = (CT != kF32) && HB == 1 && DS == 4;
+  constexpr int SX_BYTES = SK ? 4096 : 0;
   static_assert(NSTAGE >= 2, "ring needs two stages");
+  static_assert(NCOPY > NW, "a repeated copy needs an earlier copy of the same wave");
 
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + CONV_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + CONV_BYTES + SX_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -109,12 +122,24 @@ mla_attn_kernel(AttnParams p) {
   const int64_t r_hi = worker_start(w + 1, W, T);
   if (r_lo >= r_hi) return;                              // whole workgroup
 
-  // Every wave issues CPW asynchronous copies per tile (the fp8 row scales
-  // are one extra copy; a wave with nothing left repeats its previous copy),
-  // so the number of copies in flight per tile is a compile-time constant.
-  constexpr int NCOPY = NCH + (CT == kFP8 ? 1 : 0);
-  constexpr int CPW = (NCOPY + NW - 1) / NW;
-  static_assert(NCOPY > NW, "a repeated copy needs an earlier copy of the same wave");
+  // ---- this wave's copies: LDS slot -> (row, byte in row) of the tile ----
+  // slot s = id*64 + lane of the padded stage holds row s / SPR, chunk
+  // s % SPR; the pad chunk and slots past the tile repeat valid data.
+  int cp_row[CPW], cp_col[CPW], cp_lds[CPW];
+  uint32_t cp_off[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    int id = wave + i * NW;
+    if (id >= NCOPY) id -= NW;                           // repeat this wave's previous copy
+    cp_lds[i] = uniform(id);
+    const int s = id * 64 + lane;
+    int r = s / SPR, c = s - (s / SPR) * SPR;
+    if (c >= RB / 16) c = RB / 16 - 1;
+    if (r >= TILE) r = TILE - 1;
+    cp_row[i] = r;
+    cp_col[i] = c * 16;
+    cp_off[i] = (uint32_t)(r * RB + c * 16);
+  }
 
   Cursor c0;
   c0.b = uniform(find_seq(p.prefix, B, r_lo));
@@ -122,35 +147,44 @@ mla_attn_kernel(AttnParams p) {
     const int64_t pb = ld_const(p.prefix, c0.b), pe = ld_const(p.prefix, c0.b + 1);
     c0.t = r_lo - pb;
     c0.t_end = (pe < r_hi ? pe : r_hi) - pb;
+    c0.row0 = ld_const(p.seq_start, c0.b) + c0.t;
   }
 
   auto issue = [&](const Cursor& c, int stage) {
-    const int64_t row0 = ld_const(p.seq_start, c.b) + c.t;
     const int64_t left = c.t_end - c.t;
     const int nvalid = left < TILE ? (int)left : TILE;
+    const auto rsrc = make_rsrc(p.rows + c.row0 * RB, (uint32_t)(TILE * RB));
     char* sb = smem + stage * STAGE_BYTES;
+    if (nvalid == TILE) {
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      int id = wave + i * NW;
-      if (id >= NCOPY) id -= NW;                         // repeat this wave's previous copy
-      if (id < NCH) {
-        const int pos = id * 64 + lane;
-        const int r = pos / CPR;
-        const int jp = pos - r * CPR;
-        const int j = jp ^ swz<RB>(r);
-        const int rr = r < nvalid ? r : nvalid - 1;      // pad rows repeat a valid row
-        async_copy16(p.rows + (row0 + rr) * RB + j * 16, sb + id * 1024);
-      } else {
-        const int r = lane & (TILE - 1);
-        const int rr = r < nvalid ? r : nvalid - 1;
-        async_copy4(p.row_scale + row0 + rr, sb + STAGE_DATA);
+      for (int i = 0; i < CPW; ++i) {
+        if (NCOPY == NCH || cp_lds[i] < NCH) buffer_copy16(rsrc, cp_off[i], sb + cp_lds[i] * 1024);
+      }
+    } else {
+      // last tile of a segment: rows past the end repeat the last valid row
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const int r = cp_row[i] < nvalid ? cp_row[i] : nvalid - 1;
+        if (NCOPY == NCH || cp_lds[i] < NCH)
+          buffer_copy16(rsrc, (uint32_t)(r * RB + cp_col[i]), sb + cp_lds[i] * 1024);
+      }
+    }
+    if constexpr (CT == kFP8) {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        if (cp_lds[i] == NCH) {
+          const auto srsrc = make_rsrc(p.row_scale + c.row0, (uint32_t)(TILE * 4));
+          const int r = (lane & (TILE - 1)) < nvalid ? (lane & (TILE - 1)) : nvalid - 1;
+          buffer_copy4(srsrc, (uint32_t)(r * 4), sb + STAGE_DATA);
+        }
       }
     }
   };
 
   // ---- per-lane query fragments (B operand of the score MFMA) ----
   typedef typename std::conditional<CT == kF32, float, bf16x8>::type QFrag;
-  constexpr int NQ = (CT == kF32) ? kDrow / 4 : kDrow / 32;
+  constexpr int NQ = (CT == kF32) ? kDrow / 4 : (SK ? 9 : kDrow / 32);
+  const int k_first = SK ? 9 * (wave >> 1) : 0;          // first 32-wide k-step of this wave
   QFrag q[NQ];
   auto load_q = [&](int b) {
     const int64_t base = ((int64_t)b * H + h);
@@ -165,9 +199,11 @@ mla_attn_kernel(AttnParams p) {
       const __bf16* ql = (const __bf16*)p.q_lat + base * kDc;
       const __bf16* qp = (const __bf16*)p.q_pe + base * kDr;
 #pragma unroll
-      for (int ks = 0; ks < kDc / 32; ++ks) q[ks] = *(const bf16x8*)(ql + 32 * ks + 8 * g);
-      q[16] = *(const bf16x8*)(qp + 8 * g);
-      q[17] = *(const bf16x8*)(qp + 32 + 8 * g);
+      for (int i = 0; i < NQ; ++i) {
+        const int ks = k_first + i;                      // k-steps 16, 17 are the RoPE part
+        q[i] = ks < 16 ? *(const bf16x8*)(ql + 32 * ks + 8 * g)
+                       : *(const bf16x8*)(qp + 32 * (ks - 16) + 8 * g);
+      }
     }
   };
 
@@ -183,7 +219,7 @@ mla_attn_kernel(AttnParams p) {
     if (lvalid) {
       issue(lc, i);
       ++issued;
-      lvalid = advance<TILE>(lc, p.prefix, B, r_hi);
+      lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
     }
   }
 
@@ -194,6 +230,15 @@ mla_attn_kernel(AttnParams p) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // per-lane operand bases (bytes from the tile start)
+  constexpr int TP = (CT == kFP8) ? kConvPad : RP;       // row pitch of the tile computed on
+  const uint32_t s_base = (uint32_t)(l16 * TP + g * 16);                   // score A rows
+  const uint32_t v_base = (uint32_t)(4 * g * TP + (ds * DSLICE + l16) * (CT == kF32 ? 4 : 2));
+  // transposing value reads: source lane (g, l16) points at row 4g + l16/4,
+  // dims ds*DSLICE + 4*(l16%4) .. +3 of the tile computed on
+  const uint32_t tr_lane = (uint32_t)((4 * g + (l16 >> 2)) * TP + 2 * ds * DSLICE + 8 * (l16 & 3));
+  s16x4 vlo[8], vhi[8];
+
   Cursor cc = c0;
   int it = 0;
   while (true) {
@@ -202,7 +247,7 @@ mla_attn_kernel(AttnParams p) {
     if (lvalid) {
       issue(lc, issued % NSTAGE);
       ++issued;
-      lvalid = advance<TILE>(lc, p.prefix, B, r_hi);
+      lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
     }
     const char* stage = smem + (it % NSTAGE) * STAGE_BYTES;
     const int64_t left = cc.t_end - cc.t;
@@ -214,14 +259,12 @@ mla_attn_kernel(AttnParams p) {
       char* conv = smem + NSTAGE * STAGE_BYTES;
       for (int i = threadIdx.x; i < TILE * 36; i += 64 * NW) {   // 16-code chunks
         const int r = i / 36;
-        const int j = i - r * 36;                        // fp8 chunk (16 codes)
-        const u32x4 v = *(const u32x4*)(stage + lds_off<576>(r, j));
+        const int j = i - r * 36;
+        const u32x4 v = *(const u32x4*)(stage + r * RP + j * 16);
         const uint2 c0 = fp8x4_to_bf16x4(v[0]), c1 = fp8x4_to_bf16x4(v[1]);
         const uint2 c2 = fp8x4_to_bf16x4(v[2]), c3 = fp8x4_to_bf16x4(v[3]);
-        const u32x4 lo = {c0.x, c0.y, c1.x, c1.y};
-        const u32x4 hi = {c2.x, c2.y, c3.x, c3.y};
-        *(u32x4*)(conv + lds_off<1152>(r, 2 * j)) = lo;
-        *(u32x4*)(conv + lds_off<1152>(r, 2 * j + 1)) = hi;
+        *(u32x4*)(conv + r * kConvPad + j * 32) = u32x4{c0.x, c0.y, c1.x, c1.y};
+        *(u32x4*)(conv + r * kConvPad + j * 32 + 16) = u32x4{c2.x, c2.y, c3.x, c3.y};
       }
       barrier_lds();
       tb = conv;
@@ -229,14 +272,66 @@ mla_attn_kernel(AttnParams p) {
 
     if constexpr (CT != kF32) {
       // ---------------- scores: two 16-token blocks ----------------
+      const uint32_t tr_addr = (uint32_t)(size_t)tb + tr_lane;
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      const char* sa = tb + s_base;
+      if constexpr (SK) {
+        // this wave: token block (wave & 1), k-steps [k_first, k_first + 9)
+        const char* sk = sa + (wave & 1) * 16 * TP + k_first * 64;
+        bf16x8 av[9];
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const int j = 4 * ks + g;
-        const bf16x8 a0 = lds_read_b128(tb, lds_off<1152>(l16, j));
-        const bf16x8 a1 = lds_read_b128(tb, lds_off<1152>(16 + l16, j));
-        s0 = mfma_bf16_k32(a0, q[ks], s0);
-        s1 = mfma_bf16_k32(a1, q[ks], s1);
+        for (int j = 0; j < 9; ++j) av[j] = *(const bf16x8*)(sk + j * 64);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 pa = {0.f, 0.f, 0.f, 0.f}, pc = {0.f, 0.f, 0.f, 0.f};   // two independent chains
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+          if (j & 1) pc = mfma_bf16_k32(av[j], q[j], pc);
+          else pa = mfma_bf16_k32(av[j], q[j], pa);
+        }
+        // value operands of this tile, read while the score MFMAs run
+        if constexpr (NB == 8) {
+          pv_read4<TP, 0>(tr_addr, vlo, vhi);
+          pv_read4<TP, 4>(tr_addr, vlo + 4, vhi + 4);
+        }
+        const f32x4 part = pa + pc;
+        char* sx = smem + NSTAGE * STAGE_BYTES + CONV_BYTES;
+        *(f32x4*)(sx + wave * 1024 + lane * 16) = part;
+        barrier_lds();
+        const f32x4 p0 = *(const f32x4*)(sx + 0 * 1024 + lane * 16);
+        const f32x4 p1 = *(const f32x4*)(sx + 1 * 1024 + lane * 16);
+        const f32x4 p2 = *(const f32x4*)(sx + 2 * 1024 + lane * 16);
+        const f32x4 p3 = *(const f32x4*)(sx + 3 * 1024 + lane * 16);
+        s0 = p0 + p2;
+        s1 = p1 + p3;
+      } else {
+      // operands in three batches of 6 k-steps, double-buffered: the reads
+      // of batch i+1 are in flight while batch i feeds the MFMAs
+      constexpr int KB = 6;
+      bf16x8 abuf[2][2 * KB];
+      auto load_batch = [&](int buf, int kb) {
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          abuf[buf][2 * j] = *(const bf16x8*)(sa + (kb * KB + j) * 64);
+          abuf[buf][2 * j + 1] = *(const bf16x8*)(sa + 16 * TP + (kb * KB + j) * 64);
+        }
+      };
+      auto mfma_batch = [&](int buf, int kb) {
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          s0 = mfma_bf16_k32(abuf[buf][2 * j], q[kb * KB + j], s0);
+          s1 = mfma_bf16_k32(abuf[buf][2 * j + 1], q[kb * KB + j], s1);
+        }
+      };
+      load_batch(0, 0);
+      load_batch(1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_batch(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_batch(0, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_batch(1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_batch(0, 2);
       }
       float sc[8];
       float tsc[8];                                      // fp8 row scales (1 otherwise)
@@ -251,58 +346,70 @@ mla_attn_kernel(AttnParams p) {
           tsc[r] = 1.f;
           tsc[4 + r] = 1.f;
         }
-        sc[r] = t0 < nvalid ? s0[r] * (p.scale_log2 * tsc[r]) : -INFINITY;
-        sc[4 + r] = t1 < nvalid ? s1[r] * (p.scale_log2 * tsc[4 + r]) : -INFINITY;
+        sc[r] = s0[r] * (p.scale_log2 * tsc[r]);
+        sc[4 + r] = s1[r] * (p.scale_log2 * tsc[4 + r]);
+      }
+      if (nvalid < TILE) {                               // tail tile: mask rows past the end
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (4 * g + r >= nvalid) sc[r] = -INFINITY;
+          if (16 + 4 * g + r >= nvalid) sc[4 + r] = -INFINITY;
+        }
       }
       float tmax = sc[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) tmax = __builtin_fmaxf(tmax, sc[i]);
       tmax = max_over_groups(tmax);
-      const float m_new = __builtin_fmaxf(m_run, tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
+      // Lazy rescaling: the reference max moves only when a score exceeds it
+      // by more than 2^kSlack, so p = 2^(s - m_run) <= 2^kSlack stays finite
+      // and the accumulators are rescaled rarely (the result is unchanged:
+      // o and l always share the reference m_run).
+      if (__any(tmax > m_run + kSlack)) {
+        const float m_new = __builtin_fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[nb] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float pv[8];
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float e = exp2f(sc[i] - m_use);
+        const float e = __builtin_amdgcn_exp2f(sc[i] - m_use);
         psum += e;
         pv[i] = e * tsc[i];                              // fp8: value scale folded into P
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[nb] *= alpha;
-      }
+      l_run += psum;
       const bf16x8 pb = pack_bf16x8(pv);
 
       // ---------------- values: O^T += tile^T P^T ----------------
-      // A operand (tile^T): lane (d, g) needs c_t[d] for t = 4g+q and 16+4g+q,
-      // q = 0..3. Read as 16-bit values; the transposing LDS read would make
-      // the compiler wait for every copy in flight.
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int d = ds * DSLICE + nb * 16 + l16;
-        const uint32_t cb = (uint32_t)((d >> 3) << 4) + (d & 7) * 2;
-        s16x8 a8;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r0 = 4 * g + q, r1 = 16 + 4 * g + q;
-          a8[q] = *(const short*)(tb + r0 * 1152 + (cb ^ (swz<1152>(r0) << 4)));
-          a8[4 + q] = *(const short*)(tb + r1 * 1152 + (cb ^ (swz<1152>(r1) << 4)));
-        }
+      // A operand (tile^T): lane (d, g) holds c_t[d] for t = 4g+q (low half)
+      // and 16+4g+q (high half), from transposing LDS reads.
+      auto pv_mfma = [&](int nb, const s16x4& lo, const s16x4& hi) {
+        const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         o[nb] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a8), pb, o[nb]);
+      };
+      if constexpr (SK && NB == 8) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) pv_mfma(nb, vlo[nb], vhi[nb]);
+      } else {
+        static_assert(NB % 4 == 0, "value blocks come in groups of four");
+#pragma unroll
+        for (int n0 = 0; n0 < NB; n0 += 4) {
+          s16x4 lo[4], hi[4];
+          pv_read4<TP, 0>(tr_addr + n0 * 32, lo, hi);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) pv_mfma(n0 + k, lo[k], hi[k]);
+        }
       }
     } else {
       // ---------------- f32 cache: one 16-token block ----------------
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+      const char* sa = tb + (l16 * RP + g * 4);
 #pragma unroll
-      for (int ks = 0; ks < kDrow / 4; ++ks) {
-        const int e = 4 * ks + g;
-        const float a = *(const float*)(tb + lds_off<2304>(l16, e >> 2, (e & 3) * 4));
-        s0 = mfma_f32_k4(a, q[ks], s0);
-      }
+      for (int ks = 0; ks < kDrow / 4; ++ks) s0 = mfma_f32_k4(*(const float*)(sa + ks * 16), q[ks], s0);
       float sc[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[r] = (4 * g + r) < nvalid ? s0[r] * p.scale_log2 : -INFINITY;
@@ -322,15 +429,12 @@ mla_attn_kernel(AttnParams p) {
       m_run = m_new;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) o[nb] *= alpha;
+      const char* va = tb + v_base;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int d = ds * DSLICE + nb * 16 + l16;
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = *(const float*)(tb + lds_off<2304>(4 * g + r, d >> 2, (d & 3) * 4));
-          o[nb] = mfma_f32_k4(a, pv[r], o[nb]);
-        }
-      }
+        for (int r = 0; r < 4; ++r)
+          o[nb] = mfma_f32_k4(*(const float*)(va + r * RP + nb * 64), pv[r], o[nb]);
     }
 
     // ---------------- segment end: write the partial ----------------
@@ -350,7 +454,7 @@ mla_attn_kernel(AttnParams p) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (!advance<TILE>(cc, p.prefix, B, r_hi)) break;
+    if (!advance<TILE>(cc, p.prefix, p.seq_start, B, r_hi)) break;
     if (seg_end) {
       load_q(cc.b);
       wait_vmcnt<0>();

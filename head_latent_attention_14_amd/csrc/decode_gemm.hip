@@ -32,7 +32,6 @@ struct GemmParams {
 };
 
 constexpr int kNT = 64;       // output columns per workgroup (one 16-wide block per wave)
-constexpr int kKC = 128;      // weight rows staged per K chunk
 
 // inclusive prefix of clamped lengths, written by one wave
 __device__ void build_prefix(const GemmParams& p) {
@@ -63,8 +62,11 @@ __device__ void build_prefix(const GemmParams& p) {
   }
 }
 
-// AT: kF32 or kBF16 (element type of x, w, y); MODE 0 = absorb, 1 = project
-template <int AT, int MODE, int KD, int ND, int NBT>
+// Y[b][h][:] = X[b][h][:] . W[h] for one head (blockIdx.y), 64 output columns
+// (blockIdx.x) and 16*NBT batch rows (blockIdx.z). AT: kF32 or kBF16, the
+// element type of x, w and y. The weight slice W[h][0:KD][n0:n0+64] is
+// staged in LDS KC rows at a time.
+template <int AT, int KD, int ND, int NBT, int KC>
 __global__ void __launch_bounds__(256)
 mla_headgemm_kernel(GemmParams p) {
   using E = typename std::conditional<AT == kF32, float, __bf16>::type;
@@ -72,7 +74,10 @@ mla_headgemm_kernel(GemmParams p) {
   constexpr int BT = 16 * NBT;                        // batch rows per workgroup
   constexpr int WROW = kNT * ES + 16;                 // LDS stride of a weight row
   constexpr int XROW = KD * ES + 16;                  // LDS stride of an X row
-  __shared__ __attribute__((aligned(16))) char w_lds[kKC * WROW];
+  constexpr int XP = BT * KD * ES / 16;               // 16-byte pieces of the X tile
+  constexpr int WP = KC * kNT * ES / 16;              // 16-byte pieces of one weight chunk
+  static_assert(XP % 256 == 0 && WP % 256 == 0, "whole rounds of 16-byte pieces");
+  __shared__ __attribute__((aligned(16))) char w_lds[KC * WROW];
   __shared__ __attribute__((aligned(16))) char x_lds[BT * XROW];
 
   const int tid = threadIdx.x;
@@ -85,79 +90,55 @@ mla_headgemm_kernel(GemmParams p) {
   const int b0 = blockIdx.z * BT;
   const int H = p.H, B = p.B;
 
-  if constexpr (MODE == 0) {
-    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && wave == 0) build_prefix(p);
-  }
+  if (p.seq_len && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && wave == 0)
+    build_prefix(p);
 
-  // ---------------- X tile -> LDS ----------------
-  if constexpr (MODE == 0) {
-    // q_nope rows: KD elements each, 16-byte pieces
+  // ---------------- X tile -> LDS (all loads issued before the stores) ----------------
+  {
     constexpr int PPR = KD * ES / 16;
-    for (int i = tid; i < BT * PPR; i += 256) {
+    u32x4 v[XP / 256];
+#pragma unroll
+    for (int k = 0; k < XP / 256; ++k) {
+      const int i = tid + 256 * k;
       const int r = i / PPR, c = i - r * PPR;
       const int b = b0 + r;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (b < B) v = *(const u32x4*)((const char*)p.x + (((int64_t)b * H + h) * KD) * ES + c * 16);
-      *(u32x4*)(x_lds + r * XROW + c * 16) = v;
+      v[k] = u32x4{0u, 0u, 0u, 0u};
+      if (b < B) v[k] = *(const u32x4*)((const char*)p.x + (((int64_t)b * H + h) * KD) * ES + c * 16);
     }
-  } else {
-    // merge the split partials of each (b, h) into the normalised o_lat row
-    const int64_t T = p.prefix[B];
-    const int64_t W = p.workers;
-    for (int r = 0; r < BT; ++r) {
-      const int b = b0 + r;
-      float acc0 = 0.f, acc1 = 0.f;                   // elements 2*tid, 2*tid+1
-      float mmax = -INFINITY, lsum = 0.f;
-      if (b < B) {
-        const int64_t P0 = p.prefix[b], P1 = p.prefix[b + 1];
-        if (P1 > P0) {
-          const int64_t wf = find_worker(P0, W, T), wl = find_worker(P1 - 1, W, T);
-          for (int64_t w = wf; w <= wl; ++w) {
-            if (worker_start(w, W, T) == worker_start(w + 1, W, T)) continue;
-            mmax = __builtin_fmaxf(mmax, p.part_ml[((w + b) * H + h) * 2]);
-          }
-          for (int64_t w = wf; w <= wl; ++w) {
-            if (worker_start(w, W, T) == worker_start(w + 1, W, T)) continue;
-            const int64_t s = (w + b) * H + h;
-            const float e = exp2f(p.part_ml[s * 2] - mmax);
-            lsum += e * p.part_ml[s * 2 + 1];
-            const float2 v = *(const float2*)(p.part_o + s * kDc + 2 * tid);
-            acc0 += e * v.x;
-            acc1 += e * v.y;
-          }
-          const float inv = 1.f / lsum;
-          acc0 *= inv;
-          acc1 *= inv;
-        }
-        if (p.lse && tid == 0 && blockIdx.x == 0)
-          p.lse[(int64_t)b * H + h] = (lsum > 0.f) ? (mmax + __log2f(lsum)) * kLn2 : -INFINITY;
-      }
-      if constexpr (AT == kF32) {
-        *(float2*)(x_lds + r * XROW + 8 * tid) = make_float2(acc0, acc1);
-      } else {
-        *(uint32_t*)(x_lds + r * XROW + 4 * tid) = pack_bf16x2(acc0, acc1);
-      }
+#pragma unroll
+    for (int k = 0; k < XP / 256; ++k) {
+      const int i = tid + 256 * k;
+      const int r = i / PPR, c = i - r * PPR;
+      *(u32x4*)(x_lds + r * XROW + c * 16) = v[k];
     }
   }
 
-  // ---------------- GEMM over K chunks ----------------
   f32x4 acc[NBT];
 #pragma unroll
   for (int i = 0; i < NBT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < KD; k0 += kKC) {
-    __syncthreads();                                   // X ready / previous chunk consumed
-    constexpr int PPR = kNT * ES / 16;                 // 16-byte pieces per weight row
-    for (int i = tid; i < kKC * PPR; i += 256) {
-      const int r = i / PPR, c = i - r * PPR;
-      const u32x4 v = *(const u32x4*)((const char*)p.w +
-                                       (((int64_t)h * KD + k0 + r) * ND + n0) * ES + c * 16);
-      *(u32x4*)(w_lds + r * WROW + c * 16) = v;
+  for (int k0 = 0; k0 < KD; k0 += KC) {
+    if (k0) __syncthreads();                           // previous chunk consumed
+    {
+      constexpr int PPR = kNT * ES / 16;
+      u32x4 v[WP / 256];
+#pragma unroll
+      for (int k = 0; k < WP / 256; ++k) {
+        const int i = tid + 256 * k;
+        const int r = i / PPR, c = i - r * PPR;
+        v[k] = *(const u32x4*)((const char*)p.w + (((int64_t)h * KD + k0 + r) * ND + n0) * ES + c * 16);
+      }
+#pragma unroll
+      for (int k = 0; k < WP / 256; ++k) {
+        const int i = tid + 256 * k;
+        const int r = i / PPR, c = i - r * PPR;
+        *(u32x4*)(w_lds + r * WROW + c * 16) = v[k];
+      }
     }
     __syncthreads();
     if constexpr (AT == kF32) {
 #pragma unroll 4
-      for (int kk = 0; kk < kKC; kk += 4) {
+      for (int kk = 0; kk < KC; kk += 4) {
         const float a = *(const float*)(w_lds + (kk + g) * WROW + (16 * wave + l16) * 4);
 #pragma unroll
         for (int nb = 0; nb < NBT; ++nb) {
@@ -167,7 +148,7 @@ mla_headgemm_kernel(GemmParams p) {
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < kKC; kk += 32) {
+      for (int kk = 0; kk < KC; kk += 32) {
         // A = W^T block: lane (n, g) gets W[kk + 8g + 0..7][16*wave + n]
         const int rs = kk + 8 * g + (l16 >> 2);
         const int cb = (16 * wave + 4 * (l16 & 3)) * 2;
@@ -202,48 +183,121 @@ mla_headgemm_kernel(GemmParams p) {
   }
 }
 
-template <int AT, int MODE, int KD, int ND, int NBT>
+// Log-sum-exp merge of the split partials of one (b, h) per wave:
+//   M = max_s m_s,  l = sum_s 2^(m_s - M) l_s,
+//   o_lat = sum_s 2^(m_s - M) o_s / l   (written in the activation dtype),
+//   lse = (M + log2 l) ln 2.
+// A sequence of length 0 gets o_lat = 0 and lse = -inf.
+template <int AT>
+__global__ void __launch_bounds__(256)
+mla_merge_kernel(GemmParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int B = p.B, H = p.H;
+  if (pair >= (int64_t)B * H) return;
+  const int b = (int)(pair / H), h = (int)(pair - (int64_t)b * H);
+  const int64_t T = ld_const(p.prefix, B);
+  const int64_t W = p.workers;
+  const int64_t P0 = ld_const(p.prefix, b), P1 = ld_const(p.prefix, b + 1);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float mmax = -INFINITY, lsum = 0.f;
+  if (P1 > P0) {
+    const int64_t wf = find_worker(P0, W, T), wl = find_worker(P1 - 1, W, T);
+    for (int64_t w = wf; w <= wl; ++w) {
+      if (worker_start(w, W, T) == worker_start(w + 1, W, T)) continue;
+      mmax = __builtin_fmaxf(mmax, ld_const(p.part_ml, ((w + b) * H + h) * 2));
+    }
+#pragma unroll 4
+    for (int64_t w = wf; w <= wl; ++w) {
+      if (worker_start(w, W, T) == worker_start(w + 1, W, T)) continue;
+      const int64_t s = (w + b) * H + h;
+      const float e = exp2f(ld_const(p.part_ml, s * 2) - mmax);
+      lsum += e * ld_const(p.part_ml, s * 2 + 1);
+      const f32x4 v0 = *(const f32x4*)(p.part_o + s * kDc + 8 * lane);
+      const f32x4 v1 = *(const f32x4*)(p.part_o + s * kDc + 8 * lane + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += e * v0[i];
+        acc[4 + i] += e * v1[i];
+      }
+    }
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= inv;
+  }
+  if (p.lse && lane == 0) p.lse[pair] = (lsum > 0.f) ? (mmax + __log2f(lsum)) * kLn2 : -INFINITY;
+  char* dst = (char*)p.y + (pair * kDc + 8 * lane) * (AT == kF32 ? 4 : 2);
+  if constexpr (AT == kF32) {
+    *(f32x4*)dst = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4*)(dst + 16) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else {
+    *(bf16x8*)dst = pack_bf16x8(acc);
+  }
+}
+
+template <int AT, int KD, int ND, int NBT, int KC>
 static hipError_t launch_gemm_t(const GemmParams& prm, hipStream_t s) {
   constexpr int BT = 16 * NBT;
   dim3 grid(ND / kNT, prm.H, (prm.B + BT - 1) / BT);
-  hipLaunchKernelGGL((mla_headgemm_kernel<AT, MODE, KD, ND, NBT>), grid, dim3(256), 0, s, prm);
+  hipLaunchKernelGGL((mla_headgemm_kernel<AT, KD, ND, NBT, KC>), grid, dim3(256), 0, s, prm);
   return hipGetLastError();
 }
 
 hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s);
 
-hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s) {
-  GemmParams g{};
-  g.B = a.B;
-  g.H = a.H;
-  g.workers = plan.workers;
-  g.prefix = a.prefix;
-  g.seq_len = a.seq_len;
-  g.seq_cap = a.seq_cap;
+hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hipStream_t s,
+                         int stage) {
   const bool f32 = (ct == kF32);
+  hipError_t e = hipSuccess;
   // 1. absorb W_UK into the query; build the length prefix
-  g.x = a.q_nope;
-  g.w = a.w_uk;
-  g.y = a.q_lat;
-  hipError_t e = f32 ? launch_gemm_t<kF32, 0, kDnope, kDc, 1>(g, s)
-                     : launch_gemm_t<kBF16, 0, kDnope, kDc, 4>(g, s);
-  if (e != hipSuccess) return e;
+  if (stage == 0 || stage == 1) {
+    GemmParams g{};
+    g.B = a.B;
+    g.H = a.H;
+    g.workers = plan.workers;
+    g.prefix = a.prefix;
+    g.seq_len = a.seq_len;
+    g.seq_cap = a.seq_cap;
+    g.x = a.q_nope;
+    g.w = a.w_uk;
+    g.y = a.q_lat;
+    e = f32 ? launch_gemm_t<kF32, kDnope, kDc, 1, kDnope>(g, s)
+            : launch_gemm_t<kBF16, kDnope, kDc, 4, kDnope>(g, s);
+    if (e != hipSuccess) return e;
+  }
   // 2. attention over the latent rows -> split partials
-  e = launch_attn(ct, plan, a, s);
-  if (e != hipSuccess) return e;
-  // 3. merge the partials and apply W_UV
+  if (stage == 0 || stage == 2) {
+    e = launch_attn(ct, plan, a, s);
+    if (e != hipSuccess) return e;
+  }
+  if (stage != 0 && stage != 3) return e;
+  // 3. merge the partials (into the q_lat buffer, free once attention is
+  //    done) and apply W_UV
   GemmParams m{};
   m.B = a.B;
   m.H = a.H;
   m.workers = plan.workers;
   m.prefix = a.prefix;
-  m.w = a.w_uv;
-  m.y = a.out;
+  m.y = a.q_lat;
   m.lse = a.lse;
   m.part_o = a.part_o;
   m.part_ml = a.part_ml;
-  return f32 ? launch_gemm_t<kF32, 1, kDc, kDv, 1>(m, s)
-             : launch_gemm_t<kBF16, 1, kDc, kDv, 2>(m, s);
+  const int64_t pairs = (int64_t)a.B * a.H;
+  dim3 mgrid((unsigned)((pairs + 3) / 4));
+  if (f32)
+    hipLaunchKernelGGL(mla_merge_kernel<kF32>, mgrid, dim3(256), 0, s, m);
+  else
+    hipLaunchKernelGGL(mla_merge_kernel<kBF16>, mgrid, dim3(256), 0, s, m);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GemmParams g{};
+  g.B = a.B;
+  g.H = a.H;
+  g.x = a.q_lat;
+  g.w = a.w_uv;
+  g.y = a.out;
+  return f32 ? launch_gemm_t<kF32, kDc, kDv, 1, 128>(g, s)
+             : launch_gemm_t<kBF16, kDc, kDv, 4, kDc>(g, s);
 }
 
 }  // namespace mla

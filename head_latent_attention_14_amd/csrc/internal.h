@@ -72,7 +72,9 @@ struct DecodeArgs {
   float* part_o;
   float* part_ml;
 };
+// stage: 1 = absorb (+ length prefix), 2 = attention, 3 = merge + W_UV,
+// 0 = all three
 hipError_t launch_decode(int cache_type, const DecodePlan& plan, const DecodeArgs& a,
-                         hipStream_t s);
+                         hipStream_t s, int stage);
 
 }  // namespace mla

@@ -159,6 +159,39 @@ mla_status_t mla_decode(const mla_cache_t* cache, const int32_t* seq_len,
                         void* out, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The three stages mla_decode runs, exposed so a caller can time or
+ * interleave them. Same arguments and rules as mla_decode; calling
+ * absorb, attend and combine in this order on one stream with the same
+ * workspace equals one mla_decode call. The workspace carries the
+ * intermediate results between the stages:
+ *   absorb  -- q_lat = W_UK[h]^T q_nope for every (b, h), and the prefix sums
+ *              of the clamped lengths that partition the work (discosf
+ *              explainer, "long-context bottleneck": W_UK folds into the query);
+ *   attend  -- streams the latent rows once and writes, per token range, the
+ *              running max, sum and unnormalised sum_t p_t c_t (split-K);
+ *   combine -- merges the ranges of each sequence and applies W_UV (W_UV folds
+ *              into the output), writing out and lse.
+ */
+mla_status_t mla_decode_absorb(const mla_cache_t* cache, const int32_t* seq_len,
+                               const void* q_nope, const void* q_pe,
+                               const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
+                               int32_t n_heads, float softmax_scale,
+                               void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+mla_status_t mla_decode_attend(const mla_cache_t* cache, const int32_t* seq_len,
+                               const void* q_nope, const void* q_pe,
+                               const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
+                               int32_t n_heads, float softmax_scale,
+                               void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+mla_status_t mla_decode_combine(const mla_cache_t* cache, const int32_t* seq_len,
+                                const void* q_nope, const void* q_pe,
+                                const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
+                                int32_t n_heads, float softmax_scale,
+                                void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static English text for a status code (host). */
 const char* mla_status_string(mla_status_t status);
 

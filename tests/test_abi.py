@@ -24,6 +24,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"mla_append", "mla_decode_workspace_size", "mla_decode",
+                          "mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
                           "mla_status_string", "mla_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -93,6 +94,16 @@ def test_decode_validation():
     # too small a workspace
     need = mla.mla_decode_workspace_size(4, 16, E.MLA_DTYPE_BF16, E.MLA_DTYPE_BF16)
     assert _decode(_cache(), ws_bytes=need - 1) == E.MLA_ERR_WORKSPACE_TOO_SMALL
+    # the stage entry points validate the same way
+    for name in mla.DECODE_STAGES:
+        fn = getattr(lib, name)
+        assert fn(None, FAKE, FAKE, FAKE, FAKE, FAKE, E.MLA_DTYPE_BF16, 16, 0.07, FAKE, None,
+                  FAKE, 1 << 40, None) == E.MLA_ERR_INVALID_ARGUMENT
+        c = _cache()
+        assert fn(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, E.MLA_DTYPE_BF16, 24, 0.07,
+                  FAKE, None, FAKE, 1 << 40, None) == E.MLA_ERR_UNSUPPORTED
+        assert fn(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, E.MLA_DTYPE_BF16, 16, 0.07,
+                  FAKE, None, FAKE, need - 1, None) == E.MLA_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_workspace_size_query():

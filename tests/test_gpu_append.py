@@ -1,0 +1,207 @@
+"""GPU parity of mla_append against the oracle, through the C ABI.
+
+RoPE indexing is checked exactly: with unit inputs the stored pair i of the
+RoPE key is (cos(pos*theta_i), sin(pos*theta_i)), so its angle must equal
+pos*theta_i reduced mod 2*pi (computed in fp64) to within 1e-6 rad, at
+positions up to 131071; the written slot must be seq_start + pos and every
+other row must keep its bytes."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import mla as omla
+from oracle.numerics import e4m3_decode
+from tests.gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _mla():
+    import head_latent_attention_14_amd as mla
+    return mla
+
+
+def _cache(dtype, caps, fill=None):
+    mla = _mla()
+    caps = np.asarray(caps, dtype=np.int64)
+    starts = np.concatenate([[0], np.cumsum(caps)[:-1]])
+    total = int(caps.sum())
+    if dtype == "fp8":
+        rows = torch.randint(0, 0x7E, (total, 576), dtype=torch.uint8)
+        scale = torch.rand(total) + 0.5
+    else:
+        rows = torch.randn(total, 576).to(W.TORCH_DTYPE[dtype])
+        scale = None
+    cache = mla.LatentCache(rows=rows.cuda(), seq_start=torch.from_numpy(starts).cuda(),
+                            seq_capacity=torch.from_numpy(caps.astype(np.int32)).cuda(),
+                            row_scale=scale.cuda() if scale is not None else None)
+    return cache, starts
+
+
+def _append(cache, h, wd, wk, seq, pos, base):
+    mla = _mla()
+    mla.mla_append(cache, h.cuda(), wd.cuda(), wk.cuda(),
+                   torch.tensor(seq, dtype=torch.int32).cuda(),
+                   torch.tensor(pos, dtype=torch.int32).cuda(), base)
+    torch.cuda.synchronize()
+
+
+def test_rope_indexing_exact_unit_probe():
+    dm = 64
+    positions = [0, 1, 2, 3, 100, 4095, 4096, 65535, 100000, 131071]
+    n = len(positions)
+    cache, starts = _cache("f32", [131072, 17])
+    before = cache.rows.clone()
+    h = torch.zeros(n, dm)
+    h[:, 0] = 1.0
+    wd = torch.zeros(512, dm)
+    wd[7, 0] = 1.0                               # c_KV element 7 = 1 exactly
+    wk = torch.zeros(64, dm)
+    wk[0::2, 0] = 1.0                            # k = (1, 0, 1, 0, ...): every pair unit
+    _append(cache, h, wd, wk, [0] * n, positions, 10000.0)
+    rows = cache.rows.cpu().double().numpy()
+    inv = omla.rope_inv_freq(10000.0)
+    worst = 0.0
+    for p in positions:
+        r = rows[int(starts[0]) + p]
+        assert r[7] == 1.0 and np.count_nonzero(r[:512]) == 1
+        for i in range(32):
+            ang = math.atan2(r[512 + 2 * i + 1], r[512 + 2 * i])
+            want = math.remainder(p * float(inv[i]), 2 * math.pi)
+            d = abs(math.remainder(ang - want, 2 * math.pi))
+            worst = max(worst, d)
+            assert d < 1e-6, (p, i, ang, want)
+    log(f"  worst RoPE angle error {worst:.2e} rad")
+    # only the addressed rows changed
+    changed = np.nonzero(np.any(_bits(before) != _bits(cache.rows), axis=1))[0]
+    assert sorted(changed.tolist()) == sorted(int(starts[0]) + p for p in positions)
+
+
+def _bits(t):
+    """Raw bits of a device tensor as a numpy integer array (any dtype)."""
+    t = t.cpu().contiguous()
+    return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()]).numpy()
+
+
+def _dot_bound(h, wd, wk, pos, base):
+    """Per-element bound on |fp32 result - exact|: the device accumulates
+    products in fp32, so its error is at most a small multiple of
+    2^-24 * sum_k |h_k w_k| (taken 2^-18 * S here, generous); the RoPE pair
+    mixes two such sums."""
+    ah, ad, ak = np.abs(h), np.abs(wd), np.abs(wk)
+    S = np.concatenate([ah @ ad.T, ah @ ak.T], axis=1)
+    pair = S[:, 512:].reshape(-1, 32, 2).sum(axis=2)
+    S[:, 512:] = np.repeat(pair, 2, axis=1)
+    return S * 2.0 ** -18
+
+
+def _near_tie_bf16(x, bound):
+    """True where the exact x lies within `bound` of a bf16 rounding midpoint."""
+    _, e = np.frexp(x)
+    ulp = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    mid = (np.floor(np.abs(x) / ulp) + 0.5) * ulp
+    return np.abs(np.abs(x) - mid) <= bound
+
+
+@pytest.mark.parametrize("n_tok", [1, 5, 37, 64])
+def test_append_bf16_values_and_slots(n_tok):
+    rng = np.random.default_rng(n_tok)
+    dm = 2048
+    B = 8
+    caps = rng.integers(40, 300, size=B)
+    cache, starts = _cache("bf16", caps)
+    before = cache.rows.clone()
+    h = torch.from_numpy(rng.standard_normal((n_tok, dm)).astype(np.float32)).bfloat16()
+    wd = torch.from_numpy((rng.standard_normal((512, dm)) / math.sqrt(dm)).astype(np.float32)).bfloat16()
+    wk = torch.from_numpy((rng.standard_normal((64, dm)) / math.sqrt(dm)).astype(np.float32)).bfloat16()
+    # distinct slots
+    slots = rng.choice([(b, p) for b in range(B) for p in range(int(caps[b]))], size=n_tok,
+                       replace=False)
+    seq = [int(s[0]) for s in slots]
+    pos = [int(s[1]) for s in slots]
+    _append(cache, h, wd, wk, seq, pos, 10000.0)
+    exact = omla.append_rows_exact(h.double().numpy(), wd.double().numpy(), wk.double().numpy(),
+                                   np.array(pos, dtype=np.float64), 10000.0)
+    stored, _, _ = omla.quantize_rows(exact, "bf16")
+    rows = cache.rows.cpu().double().numpy()
+    got = np.stack([rows[int(starts[s]) + p] for s, p in zip(seq, pos)])
+    bound = _dot_bound(h.double().numpy(), wd.double().numpy(), wk.double().numpy(), pos,
+                       10000.0)
+    tie = _near_tie_bf16(exact, bound)
+    mism = (got != stored) & ~tie
+    log(f"  n_tok={n_tok}: {int((got != stored).sum())} of {got.size} differ, "
+        f"{int(tie.sum())} near ties, {int(mism.sum())} off-tie mismatches")
+    assert not mism.any()
+    # near ties may land on either neighbour, never further than the fp32
+    # accumulation error allows
+    assert np.all(np.abs(got - exact) <= np.ldexp(1.0, np.frexp(exact)[1] - 8) + bound)
+    changed = np.nonzero(np.any(_bits(before) != _bits(cache.rows), axis=1))[0]
+    assert set(changed.tolist()) <= {int(starts[s]) + p for s, p in zip(seq, pos)}
+
+
+def test_append_fp8_codes_and_scales():
+    rng = np.random.default_rng(3)
+    dm = 512
+    n_tok = 40
+    cache, starts = _cache("fp8", [64, 64])
+    h = torch.from_numpy(rng.standard_normal((n_tok, dm)).astype(np.float32)).bfloat16()
+    wd = torch.from_numpy((rng.standard_normal((512, dm)) * rng.uniform(0.01, 0.2)).astype(np.float32)).bfloat16()
+    wk = torch.from_numpy((rng.standard_normal((64, dm)) * 0.05).astype(np.float32)).bfloat16()
+    seq = [i % 2 for i in range(n_tok)]
+    pos = [i // 2 for i in range(n_tok)]
+    _append(cache, h, wd, wk, seq, pos, 10000.0)
+    exact = omla.append_rows_exact(h.double().numpy(), wd.double().numpy(), wk.double().numpy(),
+                                   np.array(pos, dtype=np.float64), 10000.0)
+    codes_ref, scale_ref, deq_ref = omla.quantize_rows(exact, "fp8")
+    rows = cache.rows.cpu().numpy()
+    sc = cache.row_scale.cpu().double().numpy()
+    idx = [int(starts[s]) + p for s, p in zip(seq, pos)]
+    got_codes = rows[idx]
+    got_scale = sc[idx]
+    assert np.allclose(got_scale, scale_ref, rtol=1e-5, atol=0)
+    got = e4m3_decode(got_codes) * got_scale[:, None]
+    # a code may differ from the oracle's only where x/scale is near a rounding midpoint
+    v = exact / scale_ref[:, None]
+    _, e = np.frexp(np.abs(v))
+    q = np.ldexp(1.0, np.maximum(e, -5) - 4)
+    t = np.abs(v) / q
+    tie = np.abs((t - np.floor(t)) - 0.5) < 0.02
+    diff = e4m3_decode(got_codes) != e4m3_decode(codes_ref)
+    log(f"  fp8 append: {int(diff.sum())} of {diff.size} codes differ ({int((diff & ~tie).sum())} off-tie)")
+    assert not (diff & ~tie).any()
+    rel = np.linalg.norm(got - exact) / np.linalg.norm(exact)
+    assert rel <= 4e-2
+
+
+def test_append_skips_invalid_tokens():
+    cache, starts = _cache("bf16", [10, 10])
+    before = cache.rows.clone()
+    dm = 64
+    h = torch.randn(4, dm).bfloat16()
+    wd = torch.randn(512, dm).bfloat16()
+    wk = torch.randn(64, dm).bfloat16()
+    # seq out of range, pos out of range (negative and >= capacity), one valid token
+    _append(cache, h, wd, wk, [2, 0, 1, 1], [0, -1, 10, 3], 10000.0)
+    changed = np.nonzero(np.any(_bits(before) != _bits(cache.rows), axis=1))[0]
+    assert changed.tolist() == [int(starts[1]) + 3]
+
+
+def test_append_then_decode_end_to_end_full_size():
+    # the V2-Lite-shaped step: append one token per sequence, decode over it
+    from oracle.problem import OracleView
+    from tests.gpu_util import DeviceProblem, rel_l2
+    p = W.make_problem(W.WORKLOADS["v2lite_bf16"])
+    dp = DeviceProblem(p)
+    o, _ = dp.step()
+    view = OracleView(p)
+    stored, _, _ = view.append_stored
+    rows = dp.cache.rows.cpu().double().numpy()
+    got = np.stack([rows[int(p.seq_start[b]) + int(p.tok_pos[b])] for b in range(p.wl.B)])
+    assert rel_l2(got, stored) < 4e-3
+    # the appended token is the last one of each sequence: check every head of 4 sequences
+    pairs = [(b, h) for b in (0, 17, 40, 63) for h in range(16)]
+    ro, _ = view.decode(pairs)
+    assert rel_l2(np.stack([o[b, h] for b, h in pairs]), ro) <= 2e-2
