@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (the known-size "
+                         "reference that scales hardware byte counters), then exit")
     return ap.parse_args()
 
 
@@ -111,6 +114,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_reference:
+        n = args.copy_reference << 20
+        x = torch.ones(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_reference_bytes": n, "launches": 5}))
+        return
     import head_latent_attention_14_amd as mla
     import workloads as W
 

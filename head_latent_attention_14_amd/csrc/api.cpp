@@ -43,6 +43,10 @@ WorkspaceLayout workspace_layout(int ct, int B, int H) {
   WorkspaceLayout l{};
   size_t off = 0;
   l.prefix = off;  off = align256(off + sizeof(int64_t) * ((size_t)B + 1));
+  l.starts = off;  off = align256(off + sizeof(int64_t) * ((size_t)p.workers + 1));
+  l.wseq = off;    off = align256(off + sizeof(int32_t) * (size_t)p.workers);
+  l.wfirst = off;  off = align256(off + sizeof(int32_t) * (size_t)B);
+  l.wlast = off;   off = align256(off + sizeof(int32_t) * (size_t)B);
   l.q_lat = off;   off = align256(off + (size_t)B * H * MLA_D_C * (ct == kF32 ? 4 : 2));
   l.part_o = off;  off = align256(off + (size_t)p.nslot * H * MLA_D_C * 4);
   l.part_ml = off; off = align256(off + (size_t)p.nslot * H * 2 * 4);
@@ -175,6 +179,10 @@ static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len
   a.lse = lse;
   a.softmax_scale = softmax_scale;
   a.prefix = (int64_t*)(ws + wl.prefix);
+  a.starts = (int64_t*)(ws + wl.starts);
+  a.wseq = (int32_t*)(ws + wl.wseq);
+  a.wfirst = (int32_t*)(ws + wl.wfirst);
+  a.wlast = (int32_t*)(ws + wl.wlast);
   a.q_lat = ws + wl.q_lat;
   a.part_o = (float*)(ws + wl.part_o);
   a.part_ml = (float*)(ws + wl.part_ml);

@@ -5,10 +5,6 @@
 // c_KV is cached; "decoupled RoPE": a separate 64-wide key carries RoPE and is
 // shared by all heads, adding d_R elements per token).
 //
-// One workgroup owns 16 tokens and 48 of the 576 output columns (three
-// 16-row MFMA blocks; all 576 for the fp8 cache, whose per-row scale needs
-// the whole row). Its four waves split the d_model contraction and reduce
-// through LDS.
 #include <math.h>
 
 #include <type_traits>
@@ -18,16 +14,22 @@
 
 namespace mla {
 
-constexpr int kColGroup = 48;                  // columns per group
-constexpr int kNumGroups = kDrow / kColGroup;  // 12
+constexpr int kColGroup = 16;                  // columns per group (one MFMA block)
+constexpr int kNumGroups = kDrow / kColGroup;  // 36
 
+// One workgroup computes 16 output columns (all 576 for the fp8 cache, whose
+// per-row scale needs the whole row) for 16 tokens; its four waves split the
+// d_model contraction into quarters and reduce through LDS.
 template <int CT>
 __global__ void __launch_bounds__(256)
 mla_append_kernel(AppendArgs a) {
   using E = typename std::conditional<CT == kF32, float, __bf16>::type;
   constexpr bool FP8 = (CT == kFP8);
-  __shared__ float red[4][3][16][16];          // [wave][mblock][row j][token]
-  __shared__ float rowt[16][kDrow + 4];        // fp32 rows of the 16 tokens
+  constexpr int KPL = (CT == kF32) ? 1 : 8;        // k elements per lane per MFMA
+  constexpr int KSTEP = 4 * KPL;                   // k per MFMA
+  constexpr int U = 16;                            // MFMAs per load round
+  __shared__ float red[4][16][16];                 // [wave][column][token]
+  __shared__ float rowt[16][kDrow + 4];            // fp32 rows of the 16 tokens
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -36,6 +38,7 @@ mla_append_kernel(AppendArgs a) {
   const int g = lane >> 4;
   const int tok0 = blockIdx.x * 16;
   const int D = a.d_model;
+  const int nks = D / KSTEP;                       // k-steps of the contraction
 
   const int tok_b = tok0 + l16 < a.n_tok ? tok0 + l16 : a.n_tok - 1;   // clamped B-operand token
   const E* hrow = (const E*)a.h + (int64_t)tok_b * D;
@@ -43,55 +46,44 @@ mla_append_kernel(AppendArgs a) {
   const int cg_begin = FP8 ? 0 : blockIdx.y;
   const int cg_end = FP8 ? kNumGroups : blockIdx.y + 1;
   for (int cg = cg_begin; cg < cg_end; ++cg) {
-    f32x4 acc[3];
+    const int j = cg * kColGroup + l16;            // output column of this lane's A row
+    const E* wrow = (j < kDc) ? (const E*)a.w_dkv + (int64_t)j * D
+                              : (const E*)a.w_kr + (int64_t)(j - kDc) * D;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // wave w takes k-steps w, w+4, w+8, ...; one round issues the loads of U
+    // of its k-steps, then their MFMAs
+    for (int ks0 = wave; ks0 < nks; ks0 += 4 * U) {
+      if constexpr (CT == kF32) {
+        float av[U], bv[U];
 #pragma unroll
-    for (int mb = 0; mb < 3; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const E* wrow[3];
-#pragma unroll
-    for (int mb = 0; mb < 3; ++mb) {
-      const int j = cg * kColGroup + mb * 16 + l16;      // output column of this lane's A row
-      wrow[mb] = (j < kDc) ? (const E*)a.w_dkv + (int64_t)j * D
-                           : (const E*)a.w_kr + (int64_t)(j - kDc) * D;
-    }
-    if constexpr (CT == kF32) {
-      for (int k = 4 * wave; k < D; k += 16) {
-        const float bv = hrow[k + g];
-#pragma unroll
-        for (int mb = 0; mb < 3; ++mb) acc[mb] = mfma_f32_k4(wrow[mb][k + g], bv, acc[mb]);
-      }
-    } else {
-      // four k-steps per round, all loads of a round issued before its MFMAs
-      int k = 32 * wave;
-      for (; k + 3 * 128 < D; k += 4 * 128) {
-        bf16x8 bv[4], av[4][3];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          bv[u] = *(const bf16x8*)(hrow + k + 128 * u + 8 * g);
-#pragma unroll
-          for (int mb = 0; mb < 3; ++mb) av[u][mb] = *(const bf16x8*)(wrow[mb] + k + 128 * u + 8 * g);
+        for (int u = 0; u < U; ++u) {
+          const int ks = ks0 + 4 * u;
+          const int k = ks * KSTEP + g;
+          av[u] = ks < nks ? wrow[k] : 0.f;
+          bv[u] = ks < nks ? hrow[k] : 0.f;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < U; ++u) acc = mfma_f32_k4(av[u], bv[u], acc);
+      } else {
+        bf16x8 av[U], bv[U];
 #pragma unroll
-          for (int mb = 0; mb < 3; ++mb) acc[mb] = mfma_bf16_k32(av[u][mb], bv[u], acc[mb]);
-      }
-      for (; k < D; k += 128) {
-        const bf16x8 bv = *(const bf16x8*)(hrow + k + 8 * g);
+        for (int u = 0; u < U; ++u) {
+          const int ks = ks0 + 4 * u;
+          const int k = ks * KSTEP + 8 * g;
+          av[u] = ks < nks ? *(const bf16x8*)(wrow + k) : bf16x8{};
+          bv[u] = ks < nks ? *(const bf16x8*)(hrow + k) : bf16x8{};
+        }
 #pragma unroll
-        for (int mb = 0; mb < 3; ++mb)
-          acc[mb] = mfma_bf16_k32(*(const bf16x8*)(wrow[mb] + k + 8 * g), bv, acc[mb]);
+        for (int u = 0; u < U; ++u) acc = mfma_bf16_k32(av[u], bv[u], acc);
       }
     }
-    // lane holds column cg*48 + 16mb + 4g + r of token l16
+    // lane holds column cg*16 + 4g + r of token l16
 #pragma unroll
-    for (int mb = 0; mb < 3; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][mb][4 * g + r][l16] = acc[mb][r];
+    for (int r = 0; r < 4; ++r) red[wave][4 * g + r][l16] = acc[r];
     __syncthreads();
-    for (int i = tid; i < 3 * 16 * 16; i += 256) {
-      const int mb = i >> 8, j = (i >> 4) & 15, t = i & 15;
-      rowt[t][cg * kColGroup + mb * 16 + j] =
-          red[0][mb][j][t] + red[1][mb][j][t] + red[2][mb][j][t] + red[3][mb][j][t];
+    {
+      const int c = tid >> 4, t = tid & 15;
+      rowt[t][cg * kColGroup + c] = red[0][c][t] + red[1][c][t] + red[2][c][t] + red[3][c][t];
     }
     __syncthreads();
   }
@@ -99,33 +91,37 @@ mla_append_kernel(AppendArgs a) {
   // ---------------- RoPE on columns 512..575 (pairs 2i, 2i+1) ----------------
   const int c_lo = FP8 ? 0 : blockIdx.y * kColGroup;
   const int c_hi = FP8 ? kDrow : c_lo + kColGroup;
-  for (int i = tid; i < 16 * 32; i += 256) {
-    const int t = i >> 5, pr = i & 31;
-    const int col = kDc + 2 * pr;
-    const int tok = tok0 + t;
-    if (col < c_lo || col >= c_hi || tok >= a.n_tok) continue;
-    const double phi = (double)a.tok_pos[tok] * a.inv_freq[pr];
-    double sn, cs;
-    sincos(phi, &sn, &cs);
-    const double x0 = rowt[t][col], x1 = rowt[t][col + 1];
-    rowt[t][col] = (float)(x0 * cs - x1 * sn);
-    rowt[t][col + 1] = (float)(x0 * sn + x1 * cs);
+  if (c_hi > kDc) {
+    for (int i = tid; i < 16 * 32; i += 256) {
+      const int t = i >> 5, pr = i & 31;
+      const int col = kDc + 2 * pr;
+      const int tok = tok0 + t;
+      if (col < c_lo || col >= c_hi || tok >= a.n_tok) continue;
+      const double phi = (double)a.tok_pos[tok] * a.inv_freq[pr];
+      double sn, cs;
+      sincos(phi, &sn, &cs);
+      const double x0 = rowt[t][col], x1 = rowt[t][col + 1];
+      rowt[t][col] = (float)(x0 * cs - x1 * sn);
+      rowt[t][col + 1] = (float)(x0 * sn + x1 * cs);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---------------- store ----------------
   if constexpr (!FP8) {
-    for (int i = tid; i < 16 * kColGroup; i += 256) {
-      const int t = i / kColGroup, c = c_lo + (i - t * kColGroup);
+    {
+      const int t = tid >> 4, c = c_lo + (tid & 15);
       const int tok = tok0 + t;
-      if (tok >= a.n_tok) continue;
-      const int s = a.tok_seq[tok], pos = a.tok_pos[tok];
-      if (s < 0 || s >= a.num_seqs || pos < 0 || pos >= a.seq_cap[s]) continue;
-      const int64_t row = a.seq_start[s] + pos;
-      if constexpr (CT == kF32)
-        ((float*)a.rows)[row * kDrow + c] = rowt[t][c];
-      else
-        ((uint16_t*)a.rows)[row * kDrow + c] = f32_to_bf16_bits(rowt[t][c]);
+      if (tok < a.n_tok) {
+        const int s = a.tok_seq[tok], pos = a.tok_pos[tok];
+        if (s >= 0 && s < a.num_seqs && pos >= 0 && pos < a.seq_cap[s]) {
+          const int64_t row = a.seq_start[s] + pos;
+          if constexpr (CT == kF32)
+            ((float*)a.rows)[row * kDrow + c] = rowt[t][c];
+          else
+            ((uint16_t*)a.rows)[row * kDrow + c] = f32_to_bf16_bits(rowt[t][c]);
+        }
+      }
     }
   } else {
     // one token per 16 lanes: amax, scale, then 36 codes per lane

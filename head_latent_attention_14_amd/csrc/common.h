@@ -225,31 +225,4 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return ((int64_t)hi << 32) | (uint32_t)lo;
 }
 
-// ---------------------------------------------------------------------------
-// work partition shared by the attention and merge kernels: worker w of W
-// owns positions [start(w), start(w+1)) of the concatenation of all
-// sequences' tokens, start(w) = floor(w * T / W).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int64_t worker_start(int64_t w, int64_t W, int64_t T) {
-  return (w * T) / W;
-}
-// largest b in [0, B) with prefix[b] <= pos (prefix is non-decreasing,
-// prefix[0] = 0, prefix[B] = T); callers pass pos < T
-__device__ __forceinline__ int find_seq(const int64_t* prefix, int B, int64_t pos) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (ld_const(prefix, mid) <= pos) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-// largest w in [0, W) with start(w) <= pos
-__device__ __forceinline__ int64_t find_worker(int64_t pos, int64_t W, int64_t T) {
-  int64_t w = (pos * W) / T;
-  if (w >= W) w = W - 1;
-  while (w + 1 < W && worker_start(w + 1, W, T) <= pos) ++w;
-  while (w > 0 && worker_start(w, W, T) > pos) --w;
-  return w;
-}
-
 }  // namespace mla

@@ -24,6 +24,8 @@ struct AttnParams {
   const float* row_scale;
   const int64_t* seq_start;
   const int64_t* prefix;     // [B+1]
+  const int64_t* starts;     // [W+1]
+  const int32_t* wseq;       // [W]
   const void* q_lat;         // [B][H][512]  bf16 (f32 for the f32 cache)
   const void* q_pe;          // [B][H][64]
   float* part_o;             // [nslot][H][512]
@@ -115,11 +117,9 @@ mla_attn_kernel(AttnParams p) {
   const int H = p.H;
   const int B = p.B;
   const int h = (blockIdx.y * HB + hb) * 16 + l16;       // head of this lane
-  const int64_t W = gridDim.x;
   const int64_t w = blockIdx.x;
-  const int64_t T = ld_const(p.prefix, B);
-  const int64_t r_lo = worker_start(w, W, T);
-  const int64_t r_hi = worker_start(w + 1, W, T);
+  const int64_t r_lo = ld_const(p.starts, w);
+  const int64_t r_hi = ld_const(p.starts, w + 1);
   if (r_lo >= r_hi) return;                              // whole workgroup
 
   // ---- this wave's copies: LDS slot -> (row, byte in row) of the tile ----
@@ -142,7 +142,7 @@ mla_attn_kernel(AttnParams p) {
   }
 
   Cursor c0;
-  c0.b = uniform(find_seq(p.prefix, B, r_lo));
+  c0.b = ld_const(p.wseq, w);
   {
     const int64_t pb = ld_const(p.prefix, c0.b), pe = ld_const(p.prefix, c0.b + 1);
     c0.t = r_lo - pb;
@@ -479,6 +479,8 @@ hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipS
   prm.row_scale = a.row_scale;
   prm.seq_start = a.seq_start;
   prm.prefix = a.prefix;
+  prm.starts = a.starts;
+  prm.wseq = a.wseq;
   prm.q_lat = a.q_lat;
   prm.q_pe = a.q_pe;
   prm.part_o = a.part_o;

@@ -23,7 +23,11 @@ struct GemmParams {
   float* lse;                 // project: [B][H] or null
   const float* part_o;        // project: [nslot][H][512]
   const float* part_ml;       // project: [nslot][H][2]
-  int64_t* prefix;            // [B+1] (written by absorb, read by project)
+  int64_t* prefix;            // [B+1] (written by the plan block of absorb)
+  int64_t* starts;            // [W+1]
+  int32_t* wseq;              // [W]
+  int32_t* wfirst;            // [B]
+  int32_t* wlast;             // [B]
   const int32_t* seq_len;     // absorb: [B]
   const int32_t* seq_cap;     // absorb: [B]
   int32_t B;
@@ -33,32 +37,77 @@ struct GemmParams {
 
 constexpr int kNT = 64;       // output columns per workgroup (one 16-wide block per wave)
 
-// inclusive prefix of clamped lengths, written by one wave
-__device__ void build_prefix(const GemmParams& p) {
-  const int lane = threadIdx.x & 63;
-  int64_t carry = 0;
-  if (lane == 0) p.prefix[0] = 0;
-  for (int b0 = 0; b0 < p.B; b0 += 64) {
-    const int b = b0 + lane;
-    int64_t v = 0;
-    if (b < p.B) {
-      int L = p.seq_len[b];
-      const int cap = p.seq_cap[b];
-      L = L < 0 ? 0 : (L > cap ? cap : L);
-      v = L;
-    }
+// The work plan, built by one extra workgroup of the absorb launch so the
+// attention and merge kernels need no divisions or searches:
+//   prefix[b]  = sum of the clamped lengths of sequences < b (prefix[B] = T)
+//   starts[w]  = floor(w * T / W): worker w streams positions [starts[w], starts[w+1])
+//                of the concatenation of all sequences
+//   wseq[w]    = the sequence holding position starts[w] (non-empty workers)
+//   wfirst[b], wlast[b] = first and last worker that touch sequence b
+//                (wlast < wfirst for an empty sequence)
+__device__ void build_plan(const GemmParams& p) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int B = p.B;
+  const int64_t W = p.workers;
+  if (tid < 64) {
+    int64_t carry = 0;
+    if (lane == 0) p.prefix[0] = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int b = b0 + lane;
+      int64_t v = 0;
+      if (b < B) {
+        int L = p.seq_len[b];
+        const int cap = p.seq_cap[b];
+        v = L < 0 ? 0 : (L > cap ? cap : L);
+      }
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int src = lane - off;
-      const int lo = __builtin_amdgcn_ds_bpermute((src < 0 ? lane : src) << 2, (int)(v & 0xffffffff));
-      const int hi = __builtin_amdgcn_ds_bpermute((src < 0 ? lane : src) << 2, (int)(v >> 32));
-      const int64_t u = ((int64_t)hi << 32) | (uint32_t)lo;
-      if (src >= 0) v += u;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int src = lane - off;
+        const int lo = __builtin_amdgcn_ds_bpermute((src < 0 ? lane : src) << 2, (int)(v & 0xffffffff));
+        const int hi = __builtin_amdgcn_ds_bpermute((src < 0 ? lane : src) << 2, (int)(v >> 32));
+        const int64_t u = ((int64_t)hi << 32) | (uint32_t)lo;
+        if (src >= 0) v += u;
+      }
+      if (b < B) p.prefix[b + 1] = carry + v;
+      const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffff), 63);
+      const int hi = __builtin_amdgcn_readlane((int)(v >> 32), 63);
+      carry += ((int64_t)hi << 32) | (uint32_t)lo;
     }
-    if (b < p.B) p.prefix[b + 1] = carry + v;
-    const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffff), 63);
-    const int hi = __builtin_amdgcn_readlane((int)(v >> 32), 63);
-    carry += ((int64_t)hi << 32) | (uint32_t)lo;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const volatile int64_t* prefix = p.prefix;
+  const int64_t T = prefix[B];
+  for (int64_t w = tid; w <= W; w += 256) p.starts[w] = (w * T) / W;
+  // first sequence of each worker: largest b with prefix[b] <= starts[w]
+  for (int64_t w = tid; w < W; w += 256) {
+    const int64_t pos = (w * T) / W;
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (prefix[mid] <= pos) lo = mid; else hi = mid - 1;
+    }
+    p.wseq[w] = lo;
+  }
+  // first and last worker of each sequence: largest w with starts[w] <= pos
+  auto worker_of = [&](int64_t pos) -> int {
+    int64_t w = T > 0 ? (pos * W) / T : 0;
+    if (w >= W) w = W - 1;
+    while (w + 1 < W && ((w + 1) * T) / W <= pos) ++w;
+    while (w > 0 && (w * T) / W > pos) --w;
+    return (int)w;
+  };
+  for (int b = tid; b < B; b += 256) {
+    const int64_t P0 = prefix[b], P1 = prefix[b + 1];
+    if (P1 > P0) {
+      p.wfirst[b] = worker_of(P0);
+      p.wlast[b] = worker_of(P1 - 1);
+    } else {
+      p.wfirst[b] = 0;
+      p.wlast[b] = -1;
+    }
   }
 }
 
@@ -90,8 +139,10 @@ mla_headgemm_kernel(GemmParams p) {
   const int b0 = blockIdx.z * BT;
   const int H = p.H, B = p.B;
 
-  if (p.seq_len && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && wave == 0)
-    build_prefix(p);
+  if (p.seq_len && blockIdx.z == gridDim.z - 1) {       // the extra plan workgroup
+    if (blockIdx.x == 0 && blockIdx.y == 0) build_plan(p);
+    return;
+  }
 
   // ---------------- X tile -> LDS (all loads issued before the stores) ----------------
   {
@@ -196,30 +247,44 @@ mla_merge_kernel(GemmParams p) {
   const int B = p.B, H = p.H;
   if (pair >= (int64_t)B * H) return;
   const int b = (int)(pair / H), h = (int)(pair - (int64_t)b * H);
-  const int64_t T = ld_const(p.prefix, B);
-  const int64_t W = p.workers;
-  const int64_t P0 = ld_const(p.prefix, b), P1 = ld_const(p.prefix, b + 1);
+  const int64_t wf = ld_const(p.wfirst, b), wl = ld_const(p.wlast, b);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float mmax = -INFINITY, lsum = 0.f;
-  if (P1 > P0) {
-    const int64_t wf = find_worker(P0, W, T), wl = find_worker(P1 - 1, W, T);
-    for (int64_t w = wf; w <= wl; ++w) {
-      if (worker_start(w, W, T) == worker_start(w + 1, W, T)) continue;
-      mmax = __builtin_fmaxf(mmax, ld_const(p.part_ml, ((w + b) * H + h) * 2));
-    }
-#pragma unroll 4
-    for (int64_t w = wf; w <= wl; ++w) {
-      if (worker_start(w, W, T) == worker_start(w + 1, W, T)) continue;
-      const int64_t s = (w + b) * H + h;
-      const float e = exp2f(ld_const(p.part_ml, s * 2) - mmax);
-      lsum += e * ld_const(p.part_ml, s * 2 + 1);
-      const f32x4 v0 = *(const f32x4*)(p.part_o + s * kDc + 8 * lane);
-      const f32x4 v1 = *(const f32x4*)(p.part_o + s * kDc + 8 * lane + 4);
+  if (wl >= wf) {
+    // rounds of up to RU slots: every load of a round is issued before any
+    // of its values is used; rounds combine with an online rescale
+    constexpr int RU = 8;
+    for (int64_t w0 = wf; w0 <= wl; w0 += RU) {
+      float m[RU], l[RU];
+      f32x4 v0[RU], v1[RU];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] += e * v0[i];
-        acc[4 + i] += e * v1[i];
+      for (int u = 0; u < RU; ++u) {
+        const int64_t w = w0 + u;
+        const bool ok = w <= wl && ld_const(p.starts, w) != ld_const(p.starts, w + 1);
+        const int64_t s = ((ok ? w : wf) + b) * H + h;
+        m[u] = ok ? ld_const(p.part_ml, s * 2) : -INFINITY;
+        l[u] = ok ? ld_const(p.part_ml, s * 2 + 1) : 0.f;
+        v0[u] = *(const f32x4*)(p.part_o + s * kDc + 8 * lane);
+        v1[u] = *(const f32x4*)(p.part_o + s * kDc + 8 * lane + 4);
       }
+      float rmax = mmax;
+#pragma unroll
+      for (int u = 0; u < RU; ++u) rmax = __builtin_fmaxf(rmax, m[u]);
+      const float alpha = (mmax == -INFINITY) ? 0.f : exp2f(mmax - rmax);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        const float e = (m[u] == -INFINITY) ? 0.f : exp2f(m[u] - rmax);
+        lsum += e * l[u];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i] += e * v0[u][i];
+          acc[4 + i] += e * v1[u][i];
+        }
+      }
+      mmax = rmax;
     }
     const float inv = 1.f / lsum;
 #pragma unroll
@@ -238,7 +303,8 @@ mla_merge_kernel(GemmParams p) {
 template <int AT, int KD, int ND, int NBT, int KC>
 static hipError_t launch_gemm_t(const GemmParams& prm, hipStream_t s) {
   constexpr int BT = 16 * NBT;
-  dim3 grid(ND / kNT, prm.H, (prm.B + BT - 1) / BT);
+  // absorb (seq_len given) gets one more z slice whose first block builds the plan
+  dim3 grid(ND / kNT, prm.H, (prm.B + BT - 1) / BT + (prm.seq_len ? 1 : 0));
   hipLaunchKernelGGL((mla_headgemm_kernel<AT, KD, ND, NBT, KC>), grid, dim3(256), 0, s, prm);
   return hipGetLastError();
 }
@@ -256,6 +322,10 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
     g.H = a.H;
     g.workers = plan.workers;
     g.prefix = a.prefix;
+    g.starts = a.starts;
+    g.wseq = a.wseq;
+    g.wfirst = a.wfirst;
+    g.wlast = a.wlast;
     g.seq_len = a.seq_len;
     g.seq_cap = a.seq_cap;
     g.x = a.q_nope;
@@ -278,6 +348,9 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
   m.H = a.H;
   m.workers = plan.workers;
   m.prefix = a.prefix;
+  m.starts = a.starts;
+  m.wfirst = a.wfirst;
+  m.wlast = a.wlast;
   m.y = a.q_lat;
   m.lse = a.lse;
   m.part_o = a.part_o;
@@ -297,7 +370,7 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
   g.w = a.w_uv;
   g.y = a.out;
   return f32 ? launch_gemm_t<kF32, kDc, kDv, 1, 128>(g, s)
-             : launch_gemm_t<kBF16, kDc, kDv, 4, kDc>(g, s);
+             : launch_gemm_t<kBF16, kDc, kDv, 1, kDc>(g, s);
 }
 
 }  // namespace mla

@@ -42,6 +42,10 @@ DecodePlan make_plan(int cache_type, int B, int H);
 
 struct WorkspaceLayout {
   size_t prefix;     // int64 [B+1] prefix sums of clamped lengths
+  size_t starts;     // int64 [W+1] first stream position of each worker (and T)
+  size_t wseq;       // int32 [W] first sequence of each worker
+  size_t wfirst;     // int32 [B] first worker of each sequence
+  size_t wlast;      // int32 [B] last worker of each sequence (-1 if empty)
   size_t q_lat;      // [B][H][512] bf16 (f32 for the f32 path)
   size_t part_o;     // f32 [nslot][H][512] unnormalised partial outputs
   size_t part_ml;    // f32 [nslot][H][2] running max (log2 domain) and sum
@@ -68,6 +72,10 @@ struct DecodeArgs {
   float softmax_scale;
   // workspace views
   int64_t* prefix;
+  int64_t* starts;
+  int32_t* wseq;
+  int32_t* wfirst;
+  int32_t* wlast;
   void* q_lat;
   float* part_o;
   float* part_ml;
