@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["api.cpp", "append.hip", "decode_attn.hip", "decode_gemm.hip"]
+SOURCES = ["api.cpp", "append.hip", "decode_attn.hip", "decode_attn_stream.hip", "decode_gemm.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

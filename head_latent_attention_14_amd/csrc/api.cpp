@@ -20,16 +20,24 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 DecodePlan make_plan(int ct, int B, int H) {
   DecodePlan p{};
-  if (ct == kF32) {
-    p.hb = 1; p.ds = 4; p.nstage = 2;
-  } else if (H % 64 == 0) {
-    p.hb = 4; p.ds = 1; p.nstage = 3;
-  } else if (H % 32 == 0) {
-    p.hb = 2; p.ds = 2; p.nstage = 4;
+  if (ct != kF32 && H % 32 == 0) {
+    // pair kernel: up to 128 heads (8 waves) per workgroup; the ring depth is
+    // what fits in LDS beside the score-exchange buffer
+    p.pair = true;
+    p.np = (H % 128 == 0) ? 4 : (H % 64 == 0) ? 2 : 1;
+    p.nstage = (ct == kFP8 || p.np == 1) ? 4 : 3;
+    p.head_groups = H / (32 * p.np);
+  } else if (ct == kBF16) {
+    // 16-head blocks over a bf16 cache: the streaming kernel
+    p.stream = true;
+    p.nstage = 3;
+    p.head_groups = H / 16;
   } else {
-    p.hb = 1; p.ds = 4; p.nstage = 4;
+    p.hb = 1;
+    p.ds = 4;
+    p.nstage = (ct == kF32) ? 2 : 4;
+    p.head_groups = H / 16;
   }
-  p.head_groups = H / (16 * p.hb);
   int w = kTargetCUs / p.head_groups;
   w = w < 8 ? 8 : (w / 8) * 8;                 // a multiple of the 8 XCDs
   p.workers = w;

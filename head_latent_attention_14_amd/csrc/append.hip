@@ -30,6 +30,8 @@ mla_append_kernel(AppendArgs a) {
   constexpr int U = 16;                            // MFMAs per load round
   __shared__ float red[4][16][16];                 // [wave][column][token]
   __shared__ float rowt[16][kDrow + 4];            // fp32 rows of the 16 tokens
+  __shared__ int64_t trow[16];                     // cache row of each token (-1: skip)
+  __shared__ int tpos[16];                         // RoPE position of each token
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -39,6 +41,34 @@ mla_append_kernel(AppendArgs a) {
   const int tok0 = blockIdx.x * 16;
   const int D = a.d_model;
   const int nks = D / KSTEP;                       // k-steps of the contraction
+
+  // Slot of each of the 16 tokens (token -> sequence -> first row and
+  // capacity): two batches of independent scalar loads, issued by wave 0
+  // once its contraction loads are in flight, so the chain overlaps them.
+  auto find_slots = [&]() {
+    int sq[16], ps[16], cap[16];
+    int64_t st[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int tok = tok0 + t < a.n_tok ? tok0 + t : a.n_tok - 1;
+      sq[t] = ld_const(a.tok_seq, tok);
+      ps[t] = ld_const(a.tok_pos, tok);
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int sc = (sq[t] >= 0 && sq[t] < a.num_seqs) ? sq[t] : 0;
+      cap[t] = ld_const(a.seq_cap, sc);
+      st[t] = ld_const(a.seq_start, sc);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const bool ok = sq[t] >= 0 && sq[t] < a.num_seqs && ps[t] >= 0 && ps[t] < cap[t];
+        trow[t] = ok ? st[t] + ps[t] : -1;
+        tpos[t] = ps[t];
+      }
+    }
+  };
 
   const int tok_b = tok0 + l16 < a.n_tok ? tok0 + l16 : a.n_tok - 1;   // clamped B-operand token
   const E* hrow = (const E*)a.h + (int64_t)tok_b * D;
@@ -62,6 +92,7 @@ mla_append_kernel(AppendArgs a) {
           av[u] = ks < nks ? wrow[k] : 0.f;
           bv[u] = ks < nks ? hrow[k] : 0.f;
         }
+        if (wave == 0 && cg == cg_begin && ks0 == 0) find_slots();
 #pragma unroll
         for (int u = 0; u < U; ++u) acc = mfma_f32_k4(av[u], bv[u], acc);
       } else {
@@ -73,6 +104,7 @@ mla_append_kernel(AppendArgs a) {
           av[u] = ks < nks ? *(const bf16x8*)(wrow + k) : bf16x8{};
           bv[u] = ks < nks ? *(const bf16x8*)(hrow + k) : bf16x8{};
         }
+        if (wave == 0 && cg == cg_begin && ks0 == 0) find_slots();
 #pragma unroll
         for (int u = 0; u < U; ++u) acc = mfma_bf16_k32(av[u], bv[u], acc);
       }
@@ -97,9 +129,14 @@ mla_append_kernel(AppendArgs a) {
       const int col = kDc + 2 * pr;
       const int tok = tok0 + t;
       if (col < c_lo || col >= c_hi || tok >= a.n_tok) continue;
-      const double phi = (double)a.tok_pos[tok] * a.inv_freq[pr];
+      // angle in fp64, reduced to [-pi, pi] with a two-term 2*pi
+      // (Cody-Waite) before the sine and cosine
+      const double phi = (double)tpos[t] * a.inv_freq[pr];
+      const double kq = rint(phi * 0.15915494309189535);          // 1 / (2 pi)
+      double red_phi = fma(-kq, 6.283185307179586, phi);          // 2 pi, leading part
+      red_phi = fma(-kq, 2.4492935982947064e-16, red_phi);        // 2 pi, trailing part
       double sn, cs;
-      sincos(phi, &sn, &cs);
+      sincos(red_phi, &sn, &cs);
       const double x0 = rowt[t][col], x1 = rowt[t][col + 1];
       rowt[t][col] = (float)(x0 * cs - x1 * sn);
       rowt[t][col + 1] = (float)(x0 * sn + x1 * cs);
@@ -113,9 +150,8 @@ mla_append_kernel(AppendArgs a) {
       const int t = tid >> 4, c = c_lo + (tid & 15);
       const int tok = tok0 + t;
       if (tok < a.n_tok) {
-        const int s = a.tok_seq[tok], pos = a.tok_pos[tok];
-        if (s >= 0 && s < a.num_seqs && pos >= 0 && pos < a.seq_cap[s]) {
-          const int64_t row = a.seq_start[s] + pos;
+        const int64_t row = trow[t];
+        if (row >= 0) {
           if constexpr (CT == kF32)
             ((float*)a.rows)[row * kDrow + c] = rowt[t][c];
           else
@@ -132,15 +168,8 @@ mla_append_kernel(AppendArgs a) {
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, shfl_xor_f(amax, off));
     const float scale = amax > 0.f ? amax / 448.f : 1.f;
-    bool ok = tok < a.n_tok;
-    int s = 0, pos = 0;
-    if (ok) {
-      s = a.tok_seq[tok];
-      pos = a.tok_pos[tok];
-      ok = (s >= 0 && s < a.num_seqs && pos >= 0 && pos < a.seq_cap[s]);
-    }
-    if (ok) {
-      const int64_t row = a.seq_start[s] + pos;
+    const int64_t row = tok < a.n_tok ? trow[t] : -1;
+    if (row >= 0) {
       uint32_t* dst = (uint32_t*)((uint8_t*)a.rows + row * kDrow);
       for (int q4 = sl; q4 < kDrow / 4; q4 += 16) {
         const float* v = &rowt[t][4 * q4];

@@ -219,6 +219,13 @@ __device__ __forceinline__ T ld_const(const T* p, int64_t i) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// A copy of v the compiler cannot see through: values derived from it are
+// recomputed where they are used instead of being hoisted out of a loop into
+// registers that stay live across it.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
   const int lo = __builtin_amdgcn_readfirstlane((int)(v & 0xffffffff));
   const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));

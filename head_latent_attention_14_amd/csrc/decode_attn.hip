@@ -14,72 +14,9 @@
 // to a partial slot; the merge kernel combines the slots of each sequence.
 #include <type_traits>
 
-#include "common.h"
-#include "internal.h"
+#include "attn_tile.h"
 
 namespace mla {
-
-struct AttnParams {
-  const char* rows;
-  const float* row_scale;
-  const int64_t* seq_start;
-  const int64_t* prefix;     // [B+1]
-  const int64_t* starts;     // [W+1]
-  const int32_t* wseq;       // [W]
-  const void* q_lat;         // [B][H][512]  bf16 (f32 for the f32 cache)
-  const void* q_pe;          // [B][H][64]
-  float* part_o;             // [nslot][H][512]
-  float* part_ml;            // [nslot][H][2]
-  int32_t B;
-  int32_t H;
-  float scale_log2;          // softmax_scale * log2(e)
-};
-
-// Per cache dtype: bytes of a stored row, bytes of a padded LDS row, and
-// tokens per tile. Rows in LDS are padded by 16 bytes so that the 16 rows one
-// MFMA operand read touches start on different banks; every operand read is
-// then a per-lane base plus a compile-time offset.
-template <int CT> struct Tr;
-template <> struct Tr<kBF16> { static constexpr int kRowBytes = 1152, kPad = 1168, kTile = 32; };
-template <> struct Tr<kFP8> { static constexpr int kRowBytes = 576, kPad = 592, kTile = 32; };
-template <> struct Tr<kF32> { static constexpr int kRowBytes = 2304, kPad = 2320, kTile = 16; };
-constexpr int kConvPad = 1168;   // padded bf16 row of the widened fp8 tile
-constexpr float kSlack = 8.f;    // lazy-rescale slack of the running max (log2 units)
-
-struct Cursor {
-  int b;            // sequence
-  int64_t t;        // first token of the tile, local to the sequence
-  int64_t t_end;    // end of this worker's segment of the sequence (local)
-  int64_t row0;     // cache row of token t
-};
-
-// Move to the next tile of this worker's token range; false when done.
-template <int TILE>
-__device__ __forceinline__ bool advance(Cursor& c, const int64_t* prefix, const int64_t* seq_start,
-                                        int B, int64_t r_hi) {
-  c.t += TILE;
-  c.row0 += TILE;
-  if (c.t < c.t_end) return true;
-  int b = c.b + 1;
-  while (b < B && ld_const(prefix, b + 1) == ld_const(prefix, b)) ++b;   // skip empty sequences
-  b = uniform(b);
-  if (b >= B || ld_const(prefix, b) >= r_hi) return false;
-  c.b = b;
-  c.t = 0;
-  const int64_t pb = ld_const(prefix, b), pe = ld_const(prefix, b + 1);
-  c.t_end = (pe < r_hi ? pe : r_hi) - pb;
-  c.row0 = ld_const(seq_start, b);
-  return true;
-}
-
-// Value operands of four 16-dim blocks starting at block NB0: the low half
-// covers tile rows 0..15, the high half rows 16..31 (row pitch TP bytes).
-template <int TP, int NB0>
-__device__ __forceinline__ void pv_read4(uint32_t addr, s16x4* lo, s16x4* hi) {
-  lds_tr16_x8<NB0 * 32, 16 * TP + NB0 * 32, (NB0 + 1) * 32, 16 * TP + (NB0 + 1) * 32,
-              (NB0 + 2) * 32, 16 * TP + (NB0 + 2) * 32, (NB0 + 3) * 32, 16 * TP + (NB0 + 3) * 32>(
-      addr, lo[0], hi[0], lo[1], hi[1], lo[2], hi[2], lo[3], hi[3]);
-}
 
 template <int CT, int HB, int DS, int NSTAGE>
 __global__ void __launch_bounds__(64 * HB * DS)
@@ -88,13 +25,10 @@ mla_attn_kernel(AttnParams p) {
   constexpr int TILE = Tr<CT>::kTile;
   constexpr int RB = Tr<CT>::kRowBytes;
   constexpr int RP = Tr<CT>::kPad;
-  constexpr int SPR = RP / 16;                           // 16-byte slots per padded row
-  constexpr int NCH = (TILE * RP + 1023) / 1024;         // 1 KB wave copies per tile
-  constexpr int STAGE_DATA = NCH * 1024;
-  constexpr int STAGE_BYTES = STAGE_DATA + (CT == kFP8 ? 256 : 0);
+  constexpr int STAGE_DATA = TileCopy<CT, NW>::STAGE_DATA;
+  constexpr int STAGE_BYTES = TileCopy<CT, NW>::STAGE_BYTES;
   constexpr int CONV_BYTES = (CT == kFP8) ? TILE * kConvPad : 0;
-  constexpr int NCOPY = NCH + (CT == kFP8 ? 1 : 0);      // fp8 adds the row-scale copy
-  constexpr int CPW = (NCOPY + NW - 1) / NW;             // copies per wave per tile
+  constexpr int CPW = TileCopy<CT, NW>::CPW;             // copies per wave per tile
   constexpr int DSLICE = kDc / DS;
   constexpr int NB = DSLICE / 16;
   // Split scores: with one 16-head block shared by four waves, wave w
@@ -104,7 +38,7 @@ mla_attn_kernel(AttnParams p) {
   constexpr bool SK = (CT != kF32) && HB == 1 && DS == 4;
   constexpr int SX_BYTES = SK ? 4096 : 0;
   static_assert(NSTAGE >= 2, "ring needs two stages");
-  static_assert(NCOPY > NW, "a repeated copy needs an earlier copy of the same wave");
+  static_assert(CT == kF32 || SK, "bf16/fp8 caches: one 16-head block over four waves");
 
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + CONV_BYTES + SX_BYTES];
 
@@ -122,24 +56,8 @@ mla_attn_kernel(AttnParams p) {
   const int64_t r_hi = ld_const(p.starts, w + 1);
   if (r_lo >= r_hi) return;                              // whole workgroup
 
-  // ---- this wave's copies: LDS slot -> (row, byte in row) of the tile ----
-  // slot s = id*64 + lane of the padded stage holds row s / SPR, chunk
-  // s % SPR; the pad chunk and slots past the tile repeat valid data.
-  int cp_row[CPW], cp_col[CPW], cp_lds[CPW];
-  uint32_t cp_off[CPW];
-#pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    int id = wave + i * NW;
-    if (id >= NCOPY) id -= NW;                           // repeat this wave's previous copy
-    cp_lds[i] = uniform(id);
-    const int s = id * 64 + lane;
-    int r = s / SPR, c = s - (s / SPR) * SPR;
-    if (c >= RB / 16) c = RB / 16 - 1;
-    if (r >= TILE) r = TILE - 1;
-    cp_row[i] = r;
-    cp_col[i] = c * 16;
-    cp_off[i] = (uint32_t)(r * RB + c * 16);
-  }
+  TileCopy<CT, NW> cp;
+  cp.init(wave, lane);
 
   Cursor c0;
   c0.b = ld_const(p.wseq, w);
@@ -149,36 +67,8 @@ mla_attn_kernel(AttnParams p) {
     c0.t_end = (pe < r_hi ? pe : r_hi) - pb;
     c0.row0 = ld_const(p.seq_start, c0.b) + c0.t;
   }
-
   auto issue = [&](const Cursor& c, int stage) {
-    const int64_t left = c.t_end - c.t;
-    const int nvalid = left < TILE ? (int)left : TILE;
-    const auto rsrc = make_rsrc(p.rows + c.row0 * RB, (uint32_t)(TILE * RB));
-    char* sb = smem + stage * STAGE_BYTES;
-    if (nvalid == TILE) {
-#pragma unroll
-      for (int i = 0; i < CPW; ++i) {
-        if (NCOPY == NCH || cp_lds[i] < NCH) buffer_copy16(rsrc, cp_off[i], sb + cp_lds[i] * 1024);
-      }
-    } else {
-      // last tile of a segment: rows past the end repeat the last valid row
-#pragma unroll
-      for (int i = 0; i < CPW; ++i) {
-        const int r = cp_row[i] < nvalid ? cp_row[i] : nvalid - 1;
-        if (NCOPY == NCH || cp_lds[i] < NCH)
-          buffer_copy16(rsrc, (uint32_t)(r * RB + cp_col[i]), sb + cp_lds[i] * 1024);
-      }
-    }
-    if constexpr (CT == kFP8) {
-#pragma unroll
-      for (int i = 0; i < CPW; ++i) {
-        if (cp_lds[i] == NCH) {
-          const auto srsrc = make_rsrc(p.row_scale + c.row0, (uint32_t)(TILE * 4));
-          const int r = (lane & (TILE - 1)) < nvalid ? (lane & (TILE - 1)) : nvalid - 1;
-          buffer_copy4(srsrc, (uint32_t)(r * 4), sb + STAGE_DATA);
-        }
-      }
-    }
+    cp.issue(p.rows, p.row_scale, c, smem + stage * STAGE_BYTES, lane);
   };
 
   // ---- per-lane query fragments (B operand of the score MFMA) ----
@@ -244,8 +134,15 @@ mla_attn_kernel(AttnParams p) {
   while (true) {
     wait_tiles<CPW, NSTAGE - 2>(issued - 1 - it);       // this wave's copies of tile `it` landed
     barrier_lds();                                       // tile `it` visible; stage it-1 free
+    // bf16/fp8: the next tile's copies are spread over the score steps so the
+    // wave is not stalled on the memory pipeline by a burst of them
+    const bool do_copy = lvalid;
+    typename TileCopy<CT, NW>::Pending pend;
     if (lvalid) {
-      issue(lc, issued % NSTAGE);
+      if constexpr (CT == kF32)
+        issue(lc, issued % NSTAGE);
+      else
+        pend = cp.prepare(p.rows, p.row_scale, lc, smem + (issued % NSTAGE) * STAGE_BYTES);
       ++issued;
       lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
     }
@@ -257,15 +154,7 @@ mla_attn_kernel(AttnParams p) {
     if constexpr (CT == kFP8) {
       // widen the fp8 codes to bf16 once for all waves
       char* conv = smem + NSTAGE * STAGE_BYTES;
-      for (int i = threadIdx.x; i < TILE * 36; i += 64 * NW) {   // 16-code chunks
-        const int r = i / 36;
-        const int j = i - r * 36;
-        const u32x4 v = *(const u32x4*)(stage + r * RP + j * 16);
-        const uint2 c0 = fp8x4_to_bf16x4(v[0]), c1 = fp8x4_to_bf16x4(v[1]);
-        const uint2 c2 = fp8x4_to_bf16x4(v[2]), c3 = fp8x4_to_bf16x4(v[3]);
-        *(u32x4*)(conv + r * kConvPad + j * 32) = u32x4{c0.x, c0.y, c1.x, c1.y};
-        *(u32x4*)(conv + r * kConvPad + j * 32 + 16) = u32x4{c2.x, c2.y, c3.x, c3.y};
-      }
+      widen_fp8_tile<64 * NW>(stage, conv);
       barrier_lds();
       tb = conv;
     }
@@ -275,7 +164,7 @@ mla_attn_kernel(AttnParams p) {
       const uint32_t tr_addr = (uint32_t)(size_t)tb + tr_lane;
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
       const char* sa = tb + s_base;
-      if constexpr (SK) {
+      {
         // this wave: token block (wave & 1), k-steps [k_first, k_first + 9)
         const char* sk = sa + (wave & 1) * 16 * TP + k_first * 64;
         bf16x8 av[9];
@@ -287,12 +176,15 @@ mla_attn_kernel(AttnParams p) {
         for (int j = 0; j < 9; ++j) {
           if (j & 1) pc = mfma_bf16_k32(av[j], q[j], pc);
           else pa = mfma_bf16_k32(av[j], q[j], pa);
+          if (do_copy) {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i)
+              if (i * 9 / CPW == j) cp.copy(pend, i);
+          }
         }
         // value operands of this tile, read while the score MFMAs run
-        if constexpr (NB == 8) {
-          pv_read4<TP, 0>(tr_addr, vlo, vhi);
-          pv_read4<TP, 4>(tr_addr, vlo + 4, vhi + 4);
-        }
+        pv_read4<TP, 0>(tr_addr, vlo, vhi);
+        pv_read4<TP, 4>(tr_addr, vlo + 4, vhi + 4);
         const f32x4 part = pa + pc;
         char* sx = smem + NSTAGE * STAGE_BYTES + CONV_BYTES;
         *(f32x4*)(sx + wave * 1024 + lane * 16) = part;
@@ -303,35 +195,6 @@ mla_attn_kernel(AttnParams p) {
         const f32x4 p3 = *(const f32x4*)(sx + 3 * 1024 + lane * 16);
         s0 = p0 + p2;
         s1 = p1 + p3;
-      } else {
-      // operands in three batches of 6 k-steps, double-buffered: the reads
-      // of batch i+1 are in flight while batch i feeds the MFMAs
-      constexpr int KB = 6;
-      bf16x8 abuf[2][2 * KB];
-      auto load_batch = [&](int buf, int kb) {
-#pragma unroll
-        for (int j = 0; j < KB; ++j) {
-          abuf[buf][2 * j] = *(const bf16x8*)(sa + (kb * KB + j) * 64);
-          abuf[buf][2 * j + 1] = *(const bf16x8*)(sa + 16 * TP + (kb * KB + j) * 64);
-        }
-      };
-      auto mfma_batch = [&](int buf, int kb) {
-#pragma unroll
-        for (int j = 0; j < KB; ++j) {
-          s0 = mfma_bf16_k32(abuf[buf][2 * j], q[kb * KB + j], s0);
-          s1 = mfma_bf16_k32(abuf[buf][2 * j + 1], q[kb * KB + j], s1);
-        }
-      };
-      load_batch(0, 0);
-      load_batch(1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_batch(0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      load_batch(0, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_batch(1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_batch(0, 2);
       }
       float sc[8];
       float tsc[8];                                      // fp8 row scales (1 otherwise)
@@ -391,19 +254,8 @@ mla_attn_kernel(AttnParams p) {
         const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         o[nb] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a8), pb, o[nb]);
       };
-      if constexpr (SK && NB == 8) {
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) pv_mfma(nb, vlo[nb], vhi[nb]);
-      } else {
-        static_assert(NB % 4 == 0, "value blocks come in groups of four");
-#pragma unroll
-        for (int n0 = 0; n0 < NB; n0 += 4) {
-          s16x4 lo[4], hi[4];
-          pv_read4<TP, 0>(tr_addr + n0 * 32, lo, hi);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) pv_mfma(n0 + k, lo[k], hi[k]);
-        }
-      }
+      for (int nb = 0; nb < 8; ++nb) pv_mfma(nb, vlo[nb], vhi[nb]);
     } else {
       // ---------------- f32 cache: one 16-token block ----------------
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
@@ -463,7 +315,298 @@ mla_attn_kernel(AttnParams p) {
   }
 }
 
+// Pair kernel, for head counts that are multiples of 32 (bf16 or fp8 cache).
+// Two waves share 32 heads (two 16-head MFMA blocks): for the scores each
+// wave contracts one half of the 576-wide rows (k-steps 0..8 or 9..17) and
+// the two fp32 partials meet in LDS; for the values each wave accumulates
+// one half of the 512 latent dims. Every tile operand a wave reads from LDS
+// then feeds two MFMAs (one per head block), and the per-wave registers are
+// 72 for the query half and 128 for the output half, so NP pairs (up to 128
+// heads) run as 2*NP waves of one workgroup, two waves per SIMD at NP = 4,
+// and each tile is fetched from HBM once for all of them.
+template <int CT, int NP, int NSTAGE>
+__global__ void __launch_bounds__(128 * NP)
+mla_attn_pair_kernel(AttnParams p) {
+  static_assert(CT == kBF16 || CT == kFP8, "pair kernel: bf16 or fp8 cache");
+  constexpr int NW = 2 * NP;
+  constexpr int TILE = 32;
+  constexpr int RP = Tr<CT>::kPad;
+  constexpr int STAGE_DATA = TileCopy<CT, NW>::STAGE_DATA;
+  constexpr int STAGE_BYTES = TileCopy<CT, NW>::STAGE_BYTES;
+  constexpr int CPW = TileCopy<CT, NW>::CPW;
+  constexpr int CONV_BYTES = (CT == kFP8) ? TILE * kConvPad : 0;
+  constexpr int X_BYTES = NW * 4096;                     // one 32x32 fp32 partial per wave
+  constexpr int TP = (CT == kFP8) ? kConvPad : RP;       // row pitch of the tile computed on
+  static_assert(NSTAGE >= 2, "ring needs two stages");
+  static_assert(Tr<CT>::kTile == TILE, "32-token tiles");
+
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + CONV_BYTES + X_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int half = wave & 1;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int H = p.H;
+  const int B = p.B;
+  const int hp = (blockIdx.y * NP + (wave >> 1)) * 32;  // first head of the pair
+  const int64_t w = blockIdx.x;
+  const int64_t r_lo = ld_const(p.starts, w);
+  const int64_t r_hi = ld_const(p.starts, w + 1);
+  if (r_lo >= r_hi) return;                              // whole workgroup
+
+  TileCopy<CT, NW> cp;
+  cp.init(wave, lane);
+  Cursor c0;
+  c0.b = ld_const(p.wseq, w);
+  {
+    const int64_t pb = ld_const(p.prefix, c0.b), pe = ld_const(p.prefix, c0.b + 1);
+    c0.t = r_lo - pb;
+    c0.t_end = (pe < r_hi ? pe : r_hi) - pb;
+    c0.row0 = ld_const(p.seq_start, c0.b) + c0.t;
+  }
+  auto issue = [&](const Cursor& c, int stage) {
+    cp.issue(p.rows, p.row_scale, c, smem + stage * STAGE_BYTES, lane);
+  };
+
+  // query fragments (B operand of the score MFMA): head block hb, k-step 9*half + j
+  bf16x8 q[2][9];
+  auto load_q = [&](int b) {
+    const int ln = opaque(lane);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int64_t base = (int64_t)b * H + hp + 16 * hb + (ln & 15);
+      const __bf16* ql = (const __bf16*)p.q_lat + base * kDc + 8 * (ln >> 4);
+      const __bf16* qp = (const __bf16*)p.q_pe + base * kDr + 8 * (ln >> 4);
+#pragma unroll
+      for (int j = 0; j < 9; ++j) {
+        const int ks = 9 * half + j;                     // k-steps 16, 17 are the RoPE part
+        const __bf16* src = ks < 16 ? ql + 32 * ks : qp + 32 * (ks - 16);
+        q[hb][j] = *(const bf16x8*)src;
+      }
+    }
+  };
+  load_q(c0.b);
+  wait_vmcnt<0>();
+
+  Cursor lc = c0;
+  bool lvalid = true;
+  int issued = 0;
+#pragma unroll
+  for (int i = 0; i < NSTAGE - 1; ++i) {
+    if (lvalid) {
+      issue(lc, i);
+      ++issued;
+      lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
+    }
+  }
+
+  float m_run[2] = {-INFINITY, -INFINITY};   // running max per head block (log2 domain)
+  float l_run[2] = {0.f, 0.f};               // this lane's share of the running sums
+  f32x4 o[2][16];                            // O^T: dims 256*half + 16*nb + 4g + r, head l16
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // score A operand: tile row l16 (+16 for the second token block), k-step 9*half
+  const uint32_t s_base = (uint32_t)(l16 * TP + g * 16 + half * 9 * 64);
+  // transposing value reads: source lane (g, l16) points at row 4g + l16/4,
+  // dims 256*half + 4*(l16%4) .. +3
+  const uint32_t tr_lane = (uint32_t)((4 * g + (l16 >> 2)) * TP + 2 * 256 * half + 8 * (l16 & 3));
+  char* xbuf = smem + NSTAGE * STAGE_BYTES + CONV_BYTES;
+
+  Cursor cc = c0;
+  int it = 0;
+  while (true) {
+    wait_tiles<CPW, NSTAGE - 2>(issued - 1 - it);       // this wave's copies of tile `it` landed
+    barrier_lds();                                       // tile visible; stage it-1 and xbuf free
+    // the next tile's copies go out in five groups, one after each score batch
+    const bool do_copy = lvalid;
+    typename TileCopy<CT, NW>::Pending pend;
+    if (do_copy) {
+      pend = cp.prepare(p.rows, p.row_scale, lc, smem + (issued % NSTAGE) * STAGE_BYTES);
+      ++issued;
+      lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
+    }
+    auto copy_group = [&](int grp) {
+      if (do_copy) {
+#pragma unroll
+        for (int i = grp * CPW / 5; i < (grp + 1) * CPW / 5; ++i) cp.copy(pend, i);
+      }
+    };
+    const char* stage = smem + (it % NSTAGE) * STAGE_BYTES;
+    const int64_t left = cc.t_end - cc.t;
+    const int nvalid = left < TILE ? (int)left : TILE;
+    const char* tb = stage;
+    if constexpr (CT == kFP8) {
+      char* conv = smem + NSTAGE * STAGE_BYTES;
+      widen_fp8_tile<64 * NW>(stage, conv);
+      barrier_lds();
+      tb = conv;
+    }
+
+    // ---------------- scores: this wave's half of the contraction ----------------
+    f32x4 acc[2][2];                                     // [token block][head block]
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const char* sa = tb + s_base;
+    // operands in batches of two k-steps (the last batch has one)
+#pragma unroll
+    for (int k0 = 0; k0 < 9; k0 += 2) {
+      constexpr int KB = 2;
+      bf16x8 a0[KB], a1[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if (k0 + j < 9) {
+          a0[j] = *(const bf16x8*)(sa + (k0 + j) * 64);
+          a1[j] = *(const bf16x8*)(sa + 16 * TP + (k0 + j) * 64);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if (k0 + j < 9) {
+          acc[0][0] = mfma_bf16_k32(a0[j], q[0][k0 + j], acc[0][0]);
+          acc[0][1] = mfma_bf16_k32(a0[j], q[1][k0 + j], acc[0][1]);
+          acc[1][0] = mfma_bf16_k32(a1[j], q[0][k0 + j], acc[1][0]);
+          acc[1][1] = mfma_bf16_k32(a1[j], q[1][k0 + j], acc[1][1]);
+        }
+      }
+      copy_group(k0 / 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // exchange partials with the other wave of the pair (a + b == b + a, so
+    // both waves hold bit-identical scores and take identical decisions)
+    char* xw = xbuf + wave * 4096 + lane * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(f32x4*)(xw + i * 1024) = acc[i >> 1][i & 1];
+    barrier_lds();
+    const char* xp = xbuf + (wave ^ 1) * 4096 + lane * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i >> 1][i & 1] += *(const f32x4*)(xp + i * 1024);
+
+    // ---------------- online softmax per head block ----------------
+    float tsc[8];                                        // fp8 row scales (1 otherwise)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (CT == kFP8) {
+        const float* scl = (const float*)(stage + STAGE_DATA);
+        tsc[r] = scl[4 * g + r];
+        tsc[4 + r] = scl[16 + 4 * g + r];
+      } else {
+        tsc[r] = 1.f;
+        tsc[4 + r] = 1.f;
+      }
+    }
+    float sc[2][8];
+    float tmax[2];
+    bool grow = false;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[hb][r] = acc[0][hb][r] * (p.scale_log2 * tsc[r]);
+        sc[hb][4 + r] = acc[1][hb][r] * (p.scale_log2 * tsc[4 + r]);
+      }
+      if (nvalid < TILE) {                               // tail tile: mask rows past the end
+        const int g4 = 4 * (opaque(lane) >> 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (g4 >= nvalid - r) sc[hb][r] = -INFINITY;
+          if (g4 >= nvalid - 16 - r) sc[hb][4 + r] = -INFINITY;
+        }
+      }
+      float t = sc[hb][0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) t = __builtin_fmaxf(t, sc[hb][i]);
+      tmax[hb] = max_over_groups(t);
+      grow = grow || (tmax[hb] > m_run[hb] + kSlack);
+    }
+    // lazy rescale: the reference max moves only when a score exceeds it by
+    // more than 2^kSlack (o and l always share the reference)
+    if (__any(grow)) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const float m_new = __builtin_fmaxf(m_run[hb], tmax[hb]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[hb] - m_new);
+        l_run[hb] *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) o[hb][nb] *= alpha;
+        m_run[hb] = m_new;
+      }
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float m_use = (m_run[hb] == -INFINITY) ? 0.f : m_run[hb];
+      float pv[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float e = __builtin_amdgcn_exp2f(sc[hb][i] - m_use);
+        psum += e;
+        pv[i] = e * tsc[i];                              // fp8: value scale folded into P
+      }
+      l_run[hb] += psum;
+      pb[hb] = pack_bf16x8(pv);
+    }
+
+    // ---------------- values: O^T += tile^T P^T, this wave's 256 dims ----------------
+    const uint32_t tr_addr = (uint32_t)(size_t)tb + tr_lane;
+#pragma unroll
+    for (int n0 = 0; n0 < 16; n0 += 4) {
+      s16x4 lo[4], hi[4];
+      pv_read4<TP, 0>(tr_addr + n0 * 32, lo, hi);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const s16x8 a8 = {lo[k][0], lo[k][1], lo[k][2], lo[k][3], hi[k][0], hi[k][1], hi[k][2], hi[k][3]};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+        o[0][n0 + k] = mfma_bf16_k32(a, pb[0], o[0][n0 + k]);
+        o[1][n0 + k] = mfma_bf16_k32(a, pb[1], o[1][n0 + k]);
+      }
+    }
+
+    // ---------------- segment end: write the partial ----------------
+    const bool seg_end = (cc.t + TILE >= cc.t_end);
+    if (seg_end) {
+      const int64_t slot = w + cc.b;
+      const int ln = opaque(lane);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const float lsum = sum_over_groups(l_run[hb]);
+        const int h = hp + 16 * hb + (ln & 15);
+        float* po = p.part_o + (slot * H + h) * kDc + 256 * half + 4 * (ln >> 4);
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) *(f32x4*)(po + nb * 16) = o[hb][nb];
+        if (half == 0 && (ln >> 4) == 0) {
+          p.part_ml[(slot * H + h) * 2 + 0] = m_run[hb];
+          p.part_ml[(slot * H + h) * 2 + 1] = lsum;
+        }
+        m_run[hb] = -INFINITY;
+        l_run[hb] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    if (!advance<TILE>(cc, p.prefix, p.seq_start, B, r_hi)) break;
+    if (seg_end) {
+      load_q(cc.b);
+      wait_vmcnt<0>();
+    }
+    ++it;
+  }
+}
+
 // ------------------------------------------------------------------ launch
+template <int CT, int NP, int NSTAGE>
+static hipError_t launch_pair_t(const AttnParams& prm, int workers, int head_groups,
+                                hipStream_t s) {
+  dim3 grid(workers, head_groups);
+  dim3 block(128 * NP);
+  hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE>), grid, block, 0, s, prm);
+  return hipGetLastError();
+}
+
 template <int CT, int HB, int DS, int NSTAGE>
 static hipError_t launch_attn_t(const AttnParams& prm, int workers, int head_groups,
                                 hipStream_t s) {
@@ -489,16 +632,23 @@ hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipS
   prm.H = a.H;
   prm.scale_log2 = a.softmax_scale * kLog2e;
   const int W = plan.workers, G = plan.head_groups;
+  if (plan.stream) return launch_attn_stream(plan, prm, s);
 #define MLA_CASE(CT_, HB_, DS_, NS_)                                              \
-  if (ct == CT_ && plan.hb == HB_ && plan.ds == DS_ && plan.nstage == NS_)        \
+  if (!plan.pair && ct == CT_ && plan.hb == HB_ && plan.ds == DS_ && plan.nstage == NS_) \
     return launch_attn_t<CT_, HB_, DS_, NS_>(prm, W, G, s);
+#define MLA_PAIR(CT_, NP_, NS_)                                                   \
+  if (plan.pair && ct == CT_ && plan.np == NP_ && plan.nstage == NS_)             \
+    return launch_pair_t<CT_, NP_, NS_>(prm, W, G, s);
   MLA_CASE(kF32, 1, 4, 2)
   MLA_CASE(kBF16, 1, 4, 4)
-  MLA_CASE(kBF16, 2, 2, 4)
-  MLA_CASE(kBF16, 4, 1, 3)
   MLA_CASE(kFP8, 1, 4, 4)
-  MLA_CASE(kFP8, 2, 2, 4)
-  MLA_CASE(kFP8, 4, 1, 3)
+  MLA_PAIR(kBF16, 4, 3)
+  MLA_PAIR(kBF16, 2, 3)
+  MLA_PAIR(kBF16, 1, 4)
+  MLA_PAIR(kFP8, 4, 4)
+  MLA_PAIR(kFP8, 2, 4)
+  MLA_PAIR(kFP8, 1, 4)
+#undef MLA_PAIR
 #undef MLA_CASE
   return hipErrorInvalidValue;
 }

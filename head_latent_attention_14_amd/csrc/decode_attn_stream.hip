@@ -1,0 +1,306 @@
+// Streaming MLA decode attention for one 16-head block per workgroup (the
+// DeepSeek-V2-Lite shape) over a bf16 latent cache.
+//
+// Same contractions as decode_attn.hip (discosf explainer, "long-context
+// bottleneck": W_UK folds into the query, W_UV into the output, so both
+// products read the 576-wide latent rows):
+//   scores  S^T[t][h] = c_t . q_lat[h] + k_pe_t . q_pe[h]
+//   values  O^T[d][h] += sum_t c_t[d] p[t][h]
+//
+// With 16 heads the arithmetic per cached byte is small and the kernel is
+// bound by the stream of latent rows from HBM. An asynchronous global->LDS
+// copy holds the issuing wave until the memory pipeline accepts it, so one
+// wave of the workgroup issues every copy and four other waves only compute:
+//   copy wave   waits for tile t, joins the barrier, issues tile t+NSTAGE-1
+//               (and, on the last tile of a sequence segment, the next
+//               sequence's queries into the other of two LDS query buffers)
+//   compute q   scores of all 32 tokens of the tile for the 16 heads (each
+//               compute wave does them, which costs little at 16 heads), the
+//               online softmax (identical in the four waves), and the values
+//               for latent dims 128q..128q+127.
+// Each wave writes its quarter of a segment's partial itself, so a tile needs
+// one barrier and nothing is exchanged between waves.
+#include "attn_tile.h"
+
+namespace mla {
+
+template <int NSTAGE>
+__global__ void __launch_bounds__(320)
+mla_attn_stream_kernel(AttnParams p) {
+  constexpr int CT = kBF16;
+  constexpr int TILE = 32;
+  constexpr int RB = Tr<CT>::kRowBytes;
+  constexpr int TP = Tr<CT>::kPad;
+  using TC = TileCopy<CT, 1>;                            // all copies from one wave
+  constexpr int STAGE_BYTES = TC::STAGE_BYTES;
+  constexpr int NCOPY = TC::NCOPY;                       // 37 one-kilobyte copies per tile
+  // queries of a segment in LDS: 16 rows of q_lat at the padded row pitch
+  // (one 1 KB copy each) and the 16 q_pe rows of 128 bytes (two 1 KB copies),
+  // whose eight 16-byte chunks are stored XOR-swizzled by (row / 2) so the
+  // sixteen rows one operand read touches fall on different banks
+  constexpr int QLAT_BYTES = 16 * TP;
+  constexpr int QBUF = QLAT_BYTES + 16 * 128;
+  constexpr int NQCOPY = 16 + 2;
+  static_assert(NCOPY * (NSTAGE - 2) < 64 && NCOPY + NQCOPY < 64,
+                "outstanding copies must fit the vmcnt counter");
+  static_assert(Tr<CT>::kTile == TILE, "32-token tiles");
+
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + 2 * QBUF];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const bool copier = (wave == 4);
+  const int dq = wave & 3;                               // latent quarter of a compute wave
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int H = p.H;
+  const int B = p.B;
+  const int64_t w = blockIdx.x;
+  const int64_t r_lo = ld_const(p.starts, w);
+  const int64_t r_hi = ld_const(p.starts, w + 1);
+  if (r_lo >= r_hi) return;                              // whole workgroup
+
+  Cursor c0;
+  c0.b = ld_const(p.wseq, w);
+  {
+    const int64_t pb = ld_const(p.prefix, c0.b), pe = ld_const(p.prefix, c0.b + 1);
+    c0.t = r_lo - pb;
+    c0.t_end = (pe < r_hi ? pe : r_hi) - pb;
+    c0.row0 = ld_const(p.seq_start, c0.b) + c0.t;
+  }
+  char* qlds = smem + NSTAGE * STAGE_BYTES;             // two query buffers (segment parity)
+
+  // ---- copy wave: copy i moves stage slots 64i..64i+63; slot s holds
+  // padded row s / SPR, 16-byte chunk s % SPR (the pad chunk repeats the
+  // last one). The row and chunk of this lane advance by 64 slots per copy,
+  // which wraps the chunk at most once since 64 < SPR. ----
+  constexpr int SPR = TP / 16;
+  static_assert(SPR > 64, "one wrap per copy");
+  auto issue = [&](const Cursor& c, int stage) {
+    const int64_t left = c.t_end - c.t;
+    const int nvalid = left < TILE ? (int)left : TILE;
+    const auto rsrc = make_rsrc(p.rows + c.row0 * RB, (uint32_t)(TILE * RB));
+    char* sb = smem + stage * STAGE_BYTES;
+    int row = 0, chunk = opaque(lane);                   // slot `lane` of copy 0
+#pragma unroll
+    for (int i = 0; i < NCOPY; ++i) {
+      int r = row < nvalid ? row : nvalid - 1;           // rows past the end repeat the last one
+      r = r < TILE ? r : TILE - 1;
+      const int ch = chunk < RB / 16 ? chunk : RB / 16 - 1;
+      buffer_copy16(rsrc, (uint32_t)(r * RB + ch * 16), sb + i * 1024);
+      chunk += 64;
+      if (chunk >= SPR) {
+        chunk -= SPR;
+        ++row;
+      }
+    }
+  };
+  // the 16 heads' queries of sequence b into query buffer `buf`
+  auto issue_q = [&](int b, int buf) {
+    char* qb = qlds + buf * QBUF;
+    const int64_t h0 = (int64_t)b * H + blockIdx.y * 16;
+    const auto ql = make_rsrc((const char*)p.q_lat + h0 * kDc * 2, 16 * kDc * 2);
+    const auto qp = make_rsrc((const char*)p.q_pe + h0 * kDr * 2, 16 * kDr * 2);
+    const int ln = opaque(lane);
+    const uint32_t lo = (uint32_t)ln * 16;
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) buffer_copy16(ql, hh * 1024 + lo, qb + hh * TP);
+    // LDS chunk ln of copy k holds row 8k + ln/8, position ln%8, which stores
+    // chunk (ln%8) ^ (row/2 % 8) of that row
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int row = 8 * k + (ln >> 3);
+      const int src = (ln & 7) ^ ((row >> 1) & 7);
+      buffer_copy16(qp, (uint32_t)(row * 128 + src * 16), qb + QLAT_BYTES + k * 1024);
+    }
+  };
+
+  // score A operand: tile row l16 (+16 for the second token block), k-run 8g
+  const uint32_t s_base = (uint32_t)(l16 * TP + g * 16);
+  // value A operand (transposing reads): source lane (g, l16) points at row
+  // 4g + l16/4, dims 128*dq + 4*(l16%4) .. +3; the low half of a read holds
+  // c_t[128*dq + 16*nb + l16] for t = 4g + q, the high half t = 16 + 4g + q
+  const uint32_t tr_lane = (uint32_t)((4 * g + (l16 >> 2)) * TP + 2 * 128 * dq + 8 * (l16 & 3));
+  // query operand (B of the score MFMA): lane (h, g) takes head h's k-run
+  // 8g..8g+7 of each k-step
+  const uint32_t q_lat_lane = (uint32_t)(l16 * TP + 16 * g);
+  const uint32_t q_pe_lane = (uint32_t)(QLAT_BYTES + l16 * 128);
+
+  // The two roles run separate loops over the same tiles, so they meet at
+  // the same barriers: one per tile.
+  Cursor cc = c0;
+  int it = 0;
+  int qpar = 0;                                          // query buffer of the current segment
+  if (copier) {
+    Cursor lc = c0;
+    bool lvalid = true;
+    int issued = 0;
+    issue_q(c0.b, 0);
+#pragma unroll
+    for (int i = 0; i < NSTAGE - 1; ++i) {
+      if (lvalid) {
+        issue(lc, i);
+        ++issued;
+        lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
+      }
+    }
+    while (true) {
+      wait_tiles<NCOPY, NSTAGE - 2>(issued - 1 - it);
+      barrier_lds();                                     // tile `it` (and its queries) visible
+      const bool seg_end = (cc.t + TILE >= cc.t_end);
+      Cursor nx = cc;
+      const bool more = advance<TILE>(nx, p.prefix, p.seq_start, B, r_hi);
+      // the next segment's queries go out before this round's tile copies,
+      // so the wait before the next barrier covers them
+      if (seg_end && more) issue_q(nx.b, qpar ^ 1);
+      if (lvalid) {
+        issue(lc, issued % NSTAGE);
+        ++issued;
+        lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
+      }
+      if (!more) break;
+      if (seg_end) qpar ^= 1;
+      cc = nx;
+      ++it;
+    }
+    return;
+  }
+
+  // ---------------- compute waves: one pass per sequence segment ----------------
+  bool more = true;
+  while (more) {
+    // first tile of the segment: its queries are in LDS buffer qpar once the
+    // barrier has passed; they stay in registers for the whole segment
+    barrier_lds();
+    bf16x8 q[18];
+    {
+      const char* qb = qlds + qpar * QBUF;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) q[ks] = *(const bf16x8*)(qb + q_lat_lane + ks * 64);
+#pragma unroll
+      for (int ks = 16; ks < 18; ++ks) {
+        const int c = 4 * (ks - 16) + g;                 // logical 16-byte chunk of the q_pe row
+        q[ks] = *(const bf16x8*)(qb + q_pe_lane + 16 * (c ^ ((l16 >> 1) & 7)));
+      }
+    }
+    float m_run = -INFINITY;   // running max of this lane's head (log2 domain)
+    float l_run = 0.f;         // this lane's share of the running sum
+    f32x4 o[8];                // O^T: dims 128*dq + 16*nb + 4g + r, head l16
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool seg_end = false;
+    bool first = true;
+    while (!seg_end) {
+      if (!first) barrier_lds();                         // tile `it` visible
+      first = false;
+      const int64_t left = cc.t_end - cc.t;
+      const int nvalid = left < TILE ? (int)left : TILE;
+      seg_end = (cc.t + TILE >= cc.t_end);
+      const char* tbase = smem + (it % NSTAGE) * STAGE_BYTES;
+
+      // ---------------- scores of the 32 tokens ----------------
+      // operands in two batches of nine k-steps
+      const char* sa = tbase + s_base;
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < 18; k0 += 9) {
+        bf16x8 a0[9], a1[9];
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+          a0[j] = *(const bf16x8*)(sa + (k0 + j) * 64);
+          a1[j] = *(const bf16x8*)(sa + 16 * TP + (k0 + j) * 64);
+        }
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+          s0 = mfma_bf16_k32(a0[j], q[k0 + j], s0);
+          s1 = mfma_bf16_k32(a1[j], q[k0 + j], s1);
+        }
+      }
+      // value operands of this tile, read while the score MFMAs run
+      s16x4 vlo[8], vhi[8];
+      const uint32_t tr_addr = (uint32_t)(size_t)tbase + tr_lane;
+      lds_tr16_x8<0, 16 * TP, 32, 16 * TP + 32, 64, 16 * TP + 64, 96, 16 * TP + 96>(
+          tr_addr, vlo[0], vhi[0], vlo[1], vhi[1], vlo[2], vhi[2], vlo[3], vhi[3]);
+      lds_tr16_x8<128, 16 * TP + 128, 160, 16 * TP + 160, 192, 16 * TP + 192, 224, 16 * TP + 224>(
+          tr_addr, vlo[4], vhi[4], vlo[5], vhi[5], vlo[6], vhi[6], vlo[7], vhi[7]);
+
+      // ---------------- online softmax over the tile ----------------
+      float sc[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[r] = s0[r] * p.scale_log2;
+        sc[4 + r] = s1[r] * p.scale_log2;
+      }
+      if (nvalid < TILE) {                               // tail tile: mask rows past the end
+        const int t4 = 4 * (opaque(lane) >> 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (t4 >= nvalid - r) sc[r] = -INFINITY;
+          if (t4 >= nvalid - 16 - r) sc[4 + r] = -INFINITY;
+        }
+      }
+      float tmax = sc[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) tmax = __builtin_fmaxf(tmax, sc[i]);
+      tmax = max_over_groups(tmax);
+      // lazy rescale: the reference max moves only when a score exceeds it by
+      // more than 2^kSlack (o and l always share the reference)
+      if (__any(tmax > m_run + kSlack)) {
+        const float m_new = __builtin_fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) o[nb] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
+        l_run += pv[i];
+      }
+      // B operand (32 tokens x 16 heads): lane (h, g) holds p for tokens
+      // 4g..4g+3 and 16+4g..16+4g+3, the order of the value operand's halves
+      const bf16x8 pb = pack_bf16x8(pv);
+
+      // ---------------- values: O^T += tile^T P^T, this wave's 128 dims ----------------
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const s16x8 a8 = {vlo[nb][0], vlo[nb][1], vlo[nb][2], vlo[nb][3],
+                          vhi[nb][0], vhi[nb][1], vhi[nb][2], vhi[nb][3]};
+        o[nb] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a8), pb, o[nb]);
+      }
+      if (!seg_end) {
+        advance<TILE>(cc, p.prefix, p.seq_start, B, r_hi);   // stays in this segment
+        ++it;
+      }
+    }
+    // ---------------- segment end: this wave's quarter of the partial ----------------
+    {
+      const float lsum = sum_over_groups(l_run);
+      const int64_t slot = w + cc.b;
+      const int ln = opaque(lane);
+      const int hh = blockIdx.y * 16 + (ln & 15);
+      float* po = p.part_o + (slot * H + hh) * kDc + 128 * dq + 4 * (ln >> 4);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) *(f32x4*)(po + nb * 16) = o[nb];
+      if (dq == 0 && (ln >> 4) == 0) {
+        p.part_ml[(slot * H + hh) * 2 + 0] = m_run;
+        p.part_ml[(slot * H + hh) * 2 + 1] = lsum;
+      }
+    }
+    more = advance<TILE>(cc, p.prefix, p.seq_start, B, r_hi);
+    ++it;
+    qpar ^= 1;
+  }
+}
+
+hipError_t launch_attn_stream(const DecodePlan& plan, const AttnParams& prm, hipStream_t s) {
+  if (plan.nstage != 3) return hipErrorInvalidValue;
+  dim3 grid(plan.workers, plan.head_groups);
+  hipLaunchKernelGGL(mla_attn_stream_kernel<3>, grid, dim3(320), 0, s, prm);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -45,19 +45,30 @@ constexpr int kNT = 64;       // output columns per workgroup (one 16-wide block
 //   wseq[w]    = the sequence holding position starts[w] (non-empty workers)
 //   wfirst[b], wlast[b] = first and last worker that touch sequence b
 //                (wlast < wfirst for an empty sequence)
-__device__ void build_plan(const GemmParams& p) {
+// With P = prefix[b], floor(w T / W) >= P exactly when w >= ceil(P W / T), so
+// sequence b holds the starts of workers [ceil(P_b W/T), ceil(P_{b+1} W/T)),
+// its first worker is ceil((P_b + 1) W / T) - 1 and its last ceil(P_{b+1} W / T) - 1:
+// every entry is a closed form of the prefix sums, which stay in LDS
+// (`lds`, room for `lds_n` values) when they fit.
+__device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int B = p.B;
   const int64_t W = p.workers;
+  const bool in_lds = B + 1 <= lds_n;
   if (tid < 64) {
     int64_t carry = 0;
-    if (lane == 0) p.prefix[0] = 0;
+    if (lane == 0) {
+      p.prefix[0] = 0;
+      if (in_lds) lds[0] = 0;
+    }
     for (int b0 = 0; b0 < B; b0 += 64) {
       const int b = b0 + lane;
       int64_t v = 0;
       if (b < B) {
-        int L = p.seq_len[b];
+        const int L = p.seq_len[b];
         const int cap = p.seq_cap[b];
         v = L < 0 ? 0 : (L > cap ? cap : L);
       }
@@ -69,41 +80,33 @@ __device__ void build_plan(const GemmParams& p) {
         const int64_t u = ((int64_t)hi << 32) | (uint32_t)lo;
         if (src >= 0) v += u;
       }
-      if (b < B) p.prefix[b + 1] = carry + v;
+      if (b < B) {
+        p.prefix[b + 1] = carry + v;
+        if (in_lds) lds[b + 1] = carry + v;
+      }
       const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffff), 63);
       const int hi = __builtin_amdgcn_readlane((int)(v >> 32), 63);
       carry += ((int64_t)hi << 32) | (uint32_t)lo;
     }
+    if (!in_lds && lane == 0) lds[0] = carry;            // T for the other waves
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const volatile int64_t* prefix = p.prefix;
-  const int64_t T = prefix[B];
+  const volatile int64_t* gpref = p.prefix;
+  auto prefix = [&](int b) -> int64_t { return in_lds ? lds[b] : gpref[b]; };
+  const int64_t T = in_lds ? lds[B] : lds[0];
   for (int64_t w = tid; w <= W; w += 256) p.starts[w] = (w * T) / W;
-  // first sequence of each worker: largest b with prefix[b] <= starts[w]
-  for (int64_t w = tid; w < W; w += 256) {
-    const int64_t pos = (w * T) / W;
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (prefix[mid] <= pos) lo = mid; else hi = mid - 1;
-    }
-    p.wseq[w] = lo;
+  if (T == 0) {
+    for (int64_t w = tid; w < W; w += 256) p.wseq[w] = 0;
   }
-  // first and last worker of each sequence: largest w with starts[w] <= pos
-  auto worker_of = [&](int64_t pos) -> int {
-    int64_t w = T > 0 ? (pos * W) / T : 0;
-    if (w >= W) w = W - 1;
-    while (w + 1 < W && ((w + 1) * T) / W <= pos) ++w;
-    while (w > 0 && (w * T) / W > pos) --w;
-    return (int)w;
-  };
   for (int b = tid; b < B; b += 256) {
-    const int64_t P0 = prefix[b], P1 = prefix[b + 1];
+    const int64_t P0 = prefix(b), P1 = prefix(b + 1);
     if (P1 > P0) {
-      p.wfirst[b] = worker_of(P0);
-      p.wlast[b] = worker_of(P1 - 1);
+      const int64_t wlo = ceil_div64(P0 * W, T), whi = ceil_div64(P1 * W, T);
+      for (int64_t w = wlo; w < whi; ++w) p.wseq[w] = b;
+      p.wfirst[b] = (int)(ceil_div64((P0 + 1) * W, T) - 1);
+      p.wlast[b] = (int)(whi - 1);
     } else {
       p.wfirst[b] = 0;
       p.wlast[b] = -1;
@@ -140,7 +143,8 @@ mla_headgemm_kernel(GemmParams p) {
   const int H = p.H, B = p.B;
 
   if (p.seq_len && blockIdx.z == gridDim.z - 1) {       // the extra plan workgroup
-    if (blockIdx.x == 0 && blockIdx.y == 0) build_plan(p);
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+      build_plan(p, (int64_t*)w_lds, (int)(sizeof(w_lds) / 8));
     return;
   }
 
@@ -253,35 +257,49 @@ mla_merge_kernel(GemmParams p) {
   if (wl >= wf) {
     // rounds of up to RU slots: every load of a round is issued before any
     // of its values is used; rounds combine with an online rescale
+    // Every address of a round depends only on wf and wl, so all its loads
+    // are in flight together; a slot counts only if its worker's range is
+    // non-empty (an empty worker writes nothing), which is applied by
+    // selection once the data is back.
     constexpr int RU = 8;
     for (int64_t w0 = wf; w0 <= wl; w0 += RU) {
       float m[RU], l[RU];
+      int64_t st0[RU], st1[RU];
       f32x4 v0[RU], v1[RU];
 #pragma unroll
       for (int u = 0; u < RU; ++u) {
-        const int64_t w = w0 + u;
-        const bool ok = w <= wl && ld_const(p.starts, w) != ld_const(p.starts, w + 1);
-        const int64_t s = ((ok ? w : wf) + b) * H + h;
-        m[u] = ok ? ld_const(p.part_ml, s * 2) : -INFINITY;
-        l[u] = ok ? ld_const(p.part_ml, s * 2 + 1) : 0.f;
+        const int64_t w = (w0 + u <= wl) ? w0 + u : wl;
+        const int64_t s = (w + b) * H + h;
+        st0[u] = ld_const(p.starts, w);
+        st1[u] = ld_const(p.starts, w + 1);
+        m[u] = ld_const(p.part_ml, s * 2);
+        l[u] = ld_const(p.part_ml, s * 2 + 1);
         v0[u] = *(const f32x4*)(p.part_o + s * kDc + 8 * lane);
         v1[u] = *(const f32x4*)(p.part_o + s * kDc + 8 * lane + 4);
       }
+      bool ok[RU];
       float rmax = mmax;
 #pragma unroll
-      for (int u = 0; u < RU; ++u) rmax = __builtin_fmaxf(rmax, m[u]);
+      for (int u = 0; u < RU; ++u) {
+        ok[u] = (w0 + u <= wl) && st0[u] != st1[u];
+        if (ok[u]) rmax = __builtin_fmaxf(rmax, m[u]);
+      }
       const float alpha = (mmax == -INFINITY) ? 0.f : exp2f(mmax - rmax);
       lsum *= alpha;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] *= alpha;
 #pragma unroll
       for (int u = 0; u < RU; ++u) {
-        const float e = (m[u] == -INFINITY) ? 0.f : exp2f(m[u] - rmax);
-        lsum += e * l[u];
+        if (ok[u]) {
+          // a segment whose scores were all NaN keeps m = -inf and l = NaN:
+          // weight 0, and 0 * NaN carries the NaN into the result
+          const float e = (m[u] == -INFINITY) ? 0.f : exp2f(m[u] - rmax);
+          lsum += e * l[u];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[i] += e * v0[u][i];
-          acc[4 + i] += e * v1[u][i];
+          for (int i = 0; i < 4; ++i) {
+            acc[i] += e * v0[u][i];
+            acc[4 + i] += e * v1[u][i];
+          }
         }
       }
       mmax = rmax;

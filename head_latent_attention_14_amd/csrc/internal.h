@@ -31,11 +31,14 @@ hipError_t launch_append(int cache_type, const AppendArgs& a, hipStream_t s);
 // Launch plan: fixed by (cache type, B, H) so that the workspace size can be
 // computed on the host without seeing the device-resident lengths.
 struct DecodePlan {
-  int hb;        // 16-head blocks per workgroup (waves sharing one cache tile)
-  int ds;        // value-dimension splits per head block (waves per head block)
+  bool pair;     // pair kernel (two waves per 32 heads) instead of the block kernel
+  bool stream;   // streaming kernel (one copy wave + four compute waves per 16 heads)
+  int np;        // pair kernel: 32-head pairs per workgroup
+  int hb;        // block kernel: 16-head blocks per workgroup
+  int ds;        // block kernel: value-dimension splits per head block
   int nstage;    // cache tiles in flight per workgroup (LDS ring depth)
   int workers;   // W: token ranges of the concatenated sequences
-  int head_groups;  // H / (16 * hb)
+  int head_groups;  // workgroups sharing one token range (H / heads per workgroup)
   int64_t nslot;    // partial-result slots: W + B
 };
 DecodePlan make_plan(int cache_type, int B, int H);
