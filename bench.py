@@ -10,7 +10,13 @@ cache and weights are rotated so each step reads its cache from HBM, not
 from the 256 MB Infinity Cache.
 
 Prints one JSON line. `value` is the step's algorithmic bytes (cache rows,
-weights, activations and outputs the method must move) per second.
+weights, activations and outputs the method must move) per second, over a
+timed region of whole steps with events only at its ends. The attention
+kernel's own duration (the roofline entry) is then measured over the same
+number of steps with HIP events on the launch stream around each attention
+launch (those events add a little to the step, so they stay out of the timed
+region). A second workload (the 128-head V2 shape by default) is measured the
+same way and reported under "secondary".
 """
 from __future__ import annotations
 
@@ -31,6 +37,8 @@ if ROOT not in sys.path:
 METRIC = "MLA decode latent-cache GB/s + TFLOP/s, % of MI355X roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["head_latent_attention_14_amd/csrc/decode_attn.hip",
+                  "head_latent_attention_14_amd/csrc/decode_attn_stream.hip",
+                  "head_latent_attention_14_amd/csrc/attn_tile.h",
                   "head_latent_attention_14_amd/csrc/common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 
@@ -63,6 +71,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="v2lite_bf16")
+    ap.add_argument("--secondary", default="v2_bf16",
+                    help="a second workload measured the same way and reported under "
+                         "'secondary' (empty: none)")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 2x the MALL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -106,6 +117,98 @@ def cpu_baseline(p, seconds: float):
                       f"{cores} host cores visible)"}
 
 
+def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0):
+    """Time `steps` decode steps of workload `name` (append when the workload
+    has it, then absorb -> attend -> combine). Returns the measurements."""
+    wl = W.WORKLOADS[name]
+    dev = torch.device("cuda", 0)
+    p = W.make_problem(wl)
+    B, H = wl.B, wl.H
+    ab = W.algorithmic_bytes(p)
+    fl = W.algorithmic_flops(p)
+    e_a = {"f32": 4, "bf16": 2}[wl.act]
+    e_c = {"f32": 4, "bf16": 2, "fp8": 1}[wl.cache]
+    append_bytes = 0
+    if wl.append:
+        # h, W_DKV, W_KR read; one row written per token
+        append_bytes = B * wl.d_model * e_a + 576 * wl.d_model * e_a + B * 576 * e_c
+    step_bytes = ab["total"] + append_bytes
+    step_flops = fl["total"] + (2 * B * wl.d_model * 576 if wl.append else 0)
+
+    # ---- replicas so that every step reads its inputs from HBM, not the 256 MB MALL ----
+    per_rep = p.rows.numel() * p.rows.element_size() + ab["weights"]
+    R = replicas or max(2, math.ceil(2 * 256e6 / per_rep) + 1)
+    scale = 1.0 / math.sqrt(192.0)
+    stream = torch.cuda.current_stream()
+    reps = []
+    for _ in range(R):
+        rows = p.rows.to(dev)
+        cache = mla.LatentCache(rows=rows, seq_start=torch.from_numpy(p.seq_start).to(dev),
+                                seq_capacity=torch.from_numpy(p.seq_capacity).to(dev),
+                                row_scale=p.row_scale.to(dev) if p.row_scale is not None else None)
+        r = dict(cache=cache, seq_len=torch.from_numpy(p.seq_len).to(dev),
+                 q_nope=p.q_nope.to(dev), q_pe=p.q_pe.to(dev), w_uk=p.w_uk.to(dev),
+                 w_uv=p.w_uv.to(dev),
+                 out=torch.empty(B, H, 128, dtype=p.q_nope.dtype, device=dev),
+                 lse=torch.empty(B, H, dtype=torch.float32, device=dev))
+        r["ws"] = mla.alloc_workspace(cache, H, p.q_nope.dtype)
+        # arguments marshalled once per replica: a step is a few foreign calls
+        r["dec"] = mla.PreparedDecode(r["cache"], r["seq_len"], r["q_nope"], r["q_pe"], r["w_uk"],
+                                      r["w_uv"], scale, r["out"], r["lse"], r["ws"], stream)
+        if wl.append:
+            r.update(h=p.h.to(dev), w_dkv=p.w_dkv.to(dev), w_kr=p.w_kr.to(dev),
+                     tok_seq=torch.from_numpy(p.tok_seq).to(dev),
+                     tok_pos=torch.from_numpy(p.tok_pos).to(dev))
+            r["app"] = mla.PreparedAppend(r["cache"], r["h"], r["w_dkv"], r["w_kr"], r["tok_seq"],
+                                          r["tok_pos"], wl.rope_base, stream)
+        reps.append(r)
+
+    def step(i, ev=None):
+        r = reps[i % R]
+        if wl.append:
+            r["app"]()
+        d = r["dec"]
+        if ev is None:
+            d()
+        else:
+            d.absorb()
+            ev[0].record(stream)
+            d.attend()
+            ev[1].record(stream)
+            d.combine()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: `steps` whole steps, events only at its two ends
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / steps
+    gpu_ms = start.elapsed_time(end) / steps
+    ms = max(wall_ms, gpu_ms)
+
+    # the attention kernel's own duration over the same number of steps, with
+    # events recorded on the launch stream around each attention launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        step(warmup + steps + i, evs[i])
+    torch.cuda.synchronize()
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    del reps
+    torch.cuda.empty_cache()
+    return dict(wl=wl, p=p, T=p.T, B=B, H=H, R=R, ms=ms, step_bytes=step_bytes,
+                step_flops=step_flops, attn_bytes=ab["cache"], attn_ms=attn_ms)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -126,89 +229,11 @@ def main():
     import head_latent_attention_14_amd as mla
     import workloads as W
 
-    wl = W.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
-    p = W.make_problem(wl)
-    B, H = wl.B, wl.H
-    T = p.T
-    ab = W.algorithmic_bytes(p)
-    fl = W.algorithmic_flops(p)
-    e_a = {"f32": 4, "bf16": 2}[wl.act]
-    e_c = {"f32": 4, "bf16": 2, "fp8": 1}[wl.cache]
-    append_bytes = 0
-    if wl.append:
-        # h, W_DKV, W_KR read; one row written per token
-        append_bytes = B * wl.d_model * e_a + 576 * wl.d_model * e_a + B * 576 * e_c
-    step_bytes = ab["total"] + append_bytes
-    step_flops = fl["total"] + (2 * B * wl.d_model * 576 if wl.append else 0)
-    attn_bytes = ab["cache"]             # per attention launch: the latent rows streamed once
-
-    # ---- replicas so that every step reads its inputs from HBM ----
-    per_rep = p.rows.numel() * p.rows.element_size() + ab["weights"]
-    R = args.replicas or max(2, math.ceil(2 * 256e6 / per_rep) + 1)
-    reps = []
-    for r in range(R):
-        rows = p.rows.to(dev)
-        cache = mla.LatentCache(rows=rows, seq_start=torch.from_numpy(p.seq_start).to(dev),
-                                seq_capacity=torch.from_numpy(p.seq_capacity).to(dev),
-                                row_scale=p.row_scale.to(dev) if p.row_scale is not None else None)
-        rep = dict(cache=cache, seq_len=torch.from_numpy(p.seq_len).to(dev),
-                   q_nope=p.q_nope.to(dev), q_pe=p.q_pe.to(dev), w_uk=p.w_uk.to(dev),
-                   w_uv=p.w_uv.to(dev),
-                   out=torch.empty(B, H, 128, dtype=p.q_nope.dtype, device=dev),
-                   lse=torch.empty(B, H, dtype=torch.float32, device=dev))
-        rep["ws"] = mla.alloc_workspace(cache, H, p.q_nope.dtype)
-        if wl.append:
-            rep.update(h=p.h.to(dev), w_dkv=p.w_dkv.to(dev), w_kr=p.w_kr.to(dev),
-                       tok_seq=torch.from_numpy(p.tok_seq).to(dev),
-                       tok_pos=torch.from_numpy(p.tok_pos).to(dev))
-        reps.append(rep)
-    scale = 1.0 / math.sqrt(192.0)
-    stream = torch.cuda.current_stream()
-
-    def dec_args(r):
-        return (r["cache"], r["seq_len"], r["q_nope"], r["q_pe"], r["w_uk"], r["w_uv"], scale,
-                r["out"], r["lse"], r["ws"])
-
-    def step(i, ev=None):
-        r = reps[i % R]
-        if wl.append:
-            mla.mla_append(r["cache"], r["h"], r["w_dkv"], r["w_kr"], r["tok_seq"], r["tok_pos"],
-                           wl.rope_base)
-        a = dec_args(r)
-        mla.mla_decode_absorb(*a)
-        if ev is not None:
-            ev[0].record(stream)
-        mla.mla_decode_attend(*a)
-        if ev is not None:
-            ev[1].record(stream)
-        mla.mla_decode_combine(*a)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    end.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-    gpu_ms = start.elapsed_time(end) / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
-    attn_avg_ms = float(np.mean(attn_ms))
-    ms = max(wall_ms, gpu_ms)
-
-    value = step_bytes / (ms * 1e-3) / 1e9
-    attn_gbs = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    m = measure(mla, W, torch, args.workload, args.steps, args.warmup, args.replicas)
+    wl, ms = m["wl"], m["ms"]
+    value = m["step_bytes"] / (ms * 1e-3) / 1e9
+    attn_gbs = m["attn_bytes"] / (m["attn_ms"] * 1e-3) / 1e9
     traffic = recorded_traffic(args.workload)
     out = {
         "metric": METRIC,
@@ -225,19 +250,35 @@ def main():
         "data": "synthetic (seeded normal draws; random-init weights of the DeepSeek-V2(-Lite) "
                 "MLA shapes)",
         "config": {"workload": f"{wl.name}: MLA decode step, append {'1 token/seq + ' if wl.append else ''}"
-                               f"decode, B={B}, H={H}, L~U[{wl.lo},{wl.hi}], {wl.cache} latent cache",
-                   "B": B, "H": H, "T": T, "d_c": 512, "d_r": 64,
-                   "d_model": wl.d_model if wl.append else None, "replicas": R},
-        "tflops": round(step_flops / (ms * 1e-3) / 1e12, 3),
-        "attended_tokens_per_s": round(T / (ms * 1e-3), 1),
-        "step_bytes": int(step_bytes),
+                               f"decode, B={m['B']}, H={m['H']}, L~U[{wl.lo},{wl.hi}], {wl.cache} latent cache",
+                   "B": m["B"], "H": m["H"], "T": m["T"], "d_c": 512, "d_r": 64,
+                   "d_model": wl.d_model if wl.append else None, "replicas": m["R"]},
+        "tflops": round(m["step_flops"] / (ms * 1e-3) / 1e12, 3),
+        "attended_tokens_per_s": round(m["T"] / (ms * 1e-3), 1),
+        "step_bytes": int(m["step_bytes"]),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "mla_attn_kernel",
-                     "kernel_avg_us": round(attn_avg_ms * 1e3, 3),
-                     "algorithmic_bytes_per_launch": int(attn_bytes)},
+                     "traffic": traffic, "kernel": "attention (mla_decode_attend)",
+                     "kernel_avg_us": round(m["attn_ms"] * 1e3, 3),
+                     "algorithmic_bytes_per_launch": int(m["attn_bytes"])},
     }
+    if args.secondary and args.secondary != args.workload:
+        s = measure(mla, W, torch, args.secondary, args.steps, args.warmup)
+        sw = s["wl"]
+        s_attn = s["attn_bytes"] / (s["attn_ms"] * 1e-3) / 1e9
+        out["secondary"] = {
+            "workload": f"{sw.name}: MLA decode step, B={s['B']}, H={s['H']}, "
+                        f"L~U[{sw.lo},{sw.hi}], {sw.cache} latent cache",
+            "ms_per_step": round(s["ms"], 5),
+            "value_GBps": round(s["step_bytes"] / (s["ms"] * 1e-3) / 1e9, 2),
+            "tflops": round(s["step_flops"] / (s["ms"] * 1e-3) / 1e12, 3),
+            "hbm_frac_step": round(s["step_bytes"] / (s["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "attention_kernel_us": round(s["attn_ms"] * 1e3, 3),
+            "attention_GBps": round(s_attn, 2),
+            "attention_hbm_frac": round(s_attn / HBM_PEAK_GBS, 4),
+        }
     if not args.no_cpu_baseline:
+        p = W.make_problem(wl)
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None

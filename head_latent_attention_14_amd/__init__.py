@@ -212,3 +212,60 @@ def mla_decode_attend(*args, **kw) -> None:
 def mla_decode_combine(*args, **kw) -> None:
     """Stage 3 of mla_decode (same arguments)."""
     _decode_call("mla_decode_combine", *args, **kw)
+
+
+class PreparedDecode:
+    """mla_decode and its three stages with the arguments marshalled once.
+
+    For callers that run the same decode over the same tensors many times
+    (a serving loop over fixed buffers, a benchmark): the per-call cost is one
+    foreign call with precomputed pointers. The tensors are kept alive by this
+    object; changing their contents between calls is fine, reallocating them
+    is not."""
+
+    def __init__(self, cache: LatentCache, seq_len: torch.Tensor, q_nope: torch.Tensor,
+                 q_pe: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                 softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
+                 workspace: torch.Tensor, stream=None):
+        if seq_len.dtype != torch.int32:
+            raise TypeError("seq_len must be int32")
+        if lse is not None and lse.dtype != torch.float32:
+            raise TypeError("lse must be float32")
+        B, H, _ = q_nope.shape
+        self._keep = (cache, seq_len, q_nope, q_pe, w_uk, w_uv, out, lse, workspace)
+        self._st = cache.struct()
+        self._args = (ctypes.byref(self._st), _ptr(seq_len), _ptr(q_nope), _ptr(q_pe),
+                      _ptr(w_uk), _ptr(w_uv), dtype_code(q_nope.dtype), H,
+                      float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                      workspace.numel(), _stream(stream))
+
+    def __call__(self) -> None:
+        _check(lib.mla_decode(*self._args), "mla_decode")
+
+    def absorb(self) -> None:
+        _check(lib.mla_decode_absorb(*self._args), "mla_decode_absorb")
+
+    def attend(self) -> None:
+        _check(lib.mla_decode_attend(*self._args), "mla_decode_attend")
+
+    def combine(self) -> None:
+        _check(lib.mla_decode_combine(*self._args), "mla_decode_combine")
+
+
+class PreparedAppend:
+    """mla_append with the arguments marshalled once (see PreparedDecode)."""
+
+    def __init__(self, cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor,
+                 w_kr: torch.Tensor, tok_seq: torch.Tensor, tok_pos: torch.Tensor,
+                 rope_base: float, stream=None):
+        if tok_seq.dtype != torch.int32 or tok_pos.dtype != torch.int32:
+            raise TypeError("tok_seq and tok_pos must be int32")
+        n_tok, d_model = h.shape
+        self._keep = (cache, h, w_dkv, w_kr, tok_seq, tok_pos)
+        self._st = cache.struct()
+        self._args = (ctypes.byref(self._st), _ptr(h), n_tok, d_model, _ptr(w_dkv), _ptr(w_kr),
+                      dtype_code(h.dtype), _ptr(tok_seq), _ptr(tok_pos), float(rope_base),
+                      _stream(stream))
+
+    def __call__(self) -> None:
+        _check(lib.mla_append(*self._args), "mla_append")

@@ -46,6 +46,12 @@ mla_attn_stream_kernel(AttnParams p) {
   static_assert(Tr<CT>::kTile == TILE, "32-token tiles");
 
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + 2 * QBUF];
+  // per stage: the tile's sequence, valid rows, whether it ends its segment,
+  // whether another tile follows, and the following segment's sequence
+  struct TileMeta {
+    int b, nvalid, seg_end, more, next_b;
+  };
+  __shared__ TileMeta meta[NSTAGE];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -127,46 +133,47 @@ mla_attn_stream_kernel(AttnParams p) {
   const uint32_t q_pe_lane = (uint32_t)(QLAT_BYTES + l16 * 128);
 
   // The two roles run separate loops over the same tiles, so they meet at
-  // the same barriers: one per tile.
-  Cursor cc = c0;
-  int it = 0;
-  int qpar = 0;                                          // query buffer of the current segment
+  // the same barriers: one per tile. Only the copy wave walks the sequences
+  // (its cursor runs NSTAGE-1 tiles ahead); it records each tile's place in
+  // the stream next to the tile, so the compute waves read it from LDS.
   if (copier) {
     Cursor lc = c0;
     bool lvalid = true;
     int issued = 0;
+    auto issue_tile = [&](int stage) {
+      const int64_t left = lc.t_end - lc.t;
+      const int nvalid = left < TILE ? (int)left : TILE;
+      const int b = lc.b;
+      const bool seg_end = (lc.t + TILE >= lc.t_end);
+      issue(lc, stage);
+      ++issued;
+      lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
+      if (lane == 0) meta[stage] = TileMeta{b, nvalid, seg_end ? 1 : 0, lvalid ? 1 : 0, lc.b};
+    };
     issue_q(c0.b, 0);
 #pragma unroll
-    for (int i = 0; i < NSTAGE - 1; ++i) {
-      if (lvalid) {
-        issue(lc, i);
-        ++issued;
-        lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
-      }
-    }
+    for (int i = 0; i < NSTAGE - 1; ++i)
+      if (lvalid) issue_tile(i);
+    int it = 0;
+    int qpar = 0;                                        // query buffer of the current segment
     while (true) {
       wait_tiles<NCOPY, NSTAGE - 2>(issued - 1 - it);
       barrier_lds();                                     // tile `it` (and its queries) visible
-      const bool seg_end = (cc.t + TILE >= cc.t_end);
-      Cursor nx = cc;
-      const bool more = advance<TILE>(nx, p.prefix, p.seq_start, B, r_hi);
+      const TileMeta m = meta[it % NSTAGE];
       // the next segment's queries go out before this round's tile copies,
       // so the wait before the next barrier covers them
-      if (seg_end && more) issue_q(nx.b, qpar ^ 1);
-      if (lvalid) {
-        issue(lc, issued % NSTAGE);
-        ++issued;
-        lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
-      }
-      if (!more) break;
-      if (seg_end) qpar ^= 1;
-      cc = nx;
+      if (m.seg_end && m.more) issue_q(uniform(m.next_b), qpar ^ 1);
+      if (lvalid) issue_tile(issued % NSTAGE);
+      if (!m.more) break;
+      if (m.seg_end) qpar ^= 1;
       ++it;
     }
     return;
   }
 
   // ---------------- compute waves: one pass per sequence segment ----------------
+  int it = 0;
+  int qpar = 0;
   bool more = true;
   while (more) {
     // first tile of the segment: its queries are in LDS buffer qpar once the
@@ -188,16 +195,18 @@ mla_attn_stream_kernel(AttnParams p) {
     f32x4 o[8];                // O^T: dims 128*dq + 16*nb + 4g + r, head l16
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int seg_b = 0;
     bool seg_end = false;
     bool first = true;
     while (!seg_end) {
       if (!first) barrier_lds();                         // tile `it` visible
       first = false;
-      const int64_t left = cc.t_end - cc.t;
-      const int nvalid = left < TILE ? (int)left : TILE;
-      seg_end = (cc.t + TILE >= cc.t_end);
+      const TileMeta m = meta[it % NSTAGE];
+      const int nvalid = uniform(m.nvalid);
+      seg_end = uniform(m.seg_end) != 0;
+      more = uniform(m.more) != 0;
+      seg_b = uniform(m.b);
       const char* tbase = smem + (it % NSTAGE) * STAGE_BYTES;
-
       // ---------------- scores of the 32 tokens ----------------
       // operands in two batches of nine k-steps
       const char* sa = tbase + s_base;
@@ -271,15 +280,12 @@ mla_attn_stream_kernel(AttnParams p) {
                           vhi[nb][0], vhi[nb][1], vhi[nb][2], vhi[nb][3]};
         o[nb] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a8), pb, o[nb]);
       }
-      if (!seg_end) {
-        advance<TILE>(cc, p.prefix, p.seq_start, B, r_hi);   // stays in this segment
-        ++it;
-      }
+      ++it;
     }
     // ---------------- segment end: this wave's quarter of the partial ----------------
     {
       const float lsum = sum_over_groups(l_run);
-      const int64_t slot = w + cc.b;
+      const int64_t slot = w + seg_b;
       const int ln = opaque(lane);
       const int hh = blockIdx.y * 16 + (ln & 15);
       float* po = p.part_o + (slot * H + hh) * kDc + 128 * dq + 4 * (ln >> 4);
@@ -290,8 +296,6 @@ mla_attn_stream_kernel(AttnParams p) {
         p.part_ml[(slot * H + hh) * 2 + 1] = lsum;
       }
     }
-    more = advance<TILE>(cc, p.prefix, p.seq_start, B, r_hi);
-    ++it;
     qpar ^= 1;
   }
 }

@@ -4,6 +4,8 @@ against the fp64 oracle, through the C ABI.
 Small cases run the oracle on every output; full-size cases (the workload
 shapes the benchmark uses) compare sampled (sequence, head) outputs, which
 the oracle computes one by one."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -139,3 +141,24 @@ def test_other_head_counts():
         o, _ = dp.step()
         ro, _ = OracleView(p).decode()
         assert rel_l2(o, ro) <= TOL["bf16"], H
+
+
+def test_prepared_calls_match_direct_calls():
+    # the prepared binding marshals the same arguments once; results are bitwise equal
+    import head_latent_attention_14_amd as mla
+    p = _small("v2lite_bf16", lengths=[100, 37, 260])
+    dp = DeviceProblem(p)
+    o_direct, l_direct = dp.step()
+    dp.out.zero_()
+    dp.lse.zero_()
+    pd = mla.PreparedDecode(dp.cache, dp.seq_len, dp.q_nope, dp.q_pe, dp.w_uk, dp.w_uv,
+                            1.0 / math.sqrt(192.0), dp.out, dp.lse, dp.ws)
+    pd.absorb()
+    pd.attend()
+    pd.combine()
+    torch.cuda.synchronize()
+    assert np.array_equal(dp.out.double().cpu().numpy(), o_direct)
+    pd()
+    torch.cuda.synchronize()
+    assert np.array_equal(dp.out.double().cpu().numpy(), o_direct)
+    assert np.array_equal(dp.lse.double().cpu().numpy(), l_direct)
