@@ -56,7 +56,7 @@ WorkspaceLayout workspace_layout(int ct, int B, int H) {
   l.wfirst = off;  off = align256(off + sizeof(int32_t) * (size_t)B);
   l.wlast = off;   off = align256(off + sizeof(int32_t) * (size_t)B);
   l.q_lat = off;   off = align256(off + (size_t)B * H * MLA_D_C * (ct == kF32 ? 4 : 2));
-  l.part_o = off;  off = align256(off + (size_t)p.nslot * H * MLA_D_C * 4);
+  l.part_o = off;  off = align256(off + (size_t)p.nslot * H * MLA_D_C * (ct == kF32 ? 4 : 2));
   l.part_ml = off; off = align256(off + (size_t)p.nslot * H * 2 * 4);
   l.total = off;
   return l;
@@ -192,7 +192,7 @@ static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len
   a.wfirst = (int32_t*)(ws + wl.wfirst);
   a.wlast = (int32_t*)(ws + wl.wlast);
   a.q_lat = ws + wl.q_lat;
-  a.part_o = (float*)(ws + wl.part_o);
+  a.part_o = (void*)(ws + wl.part_o);
   a.part_ml = (float*)(ws + wl.part_ml);
   const DecodePlan plan = make_plan(ct, B, n_heads);
   hipError_t e = launch_decode(ct, plan, a, (hipStream_t)stream, stage);

@@ -17,7 +17,7 @@ struct AttnParams {
   const int32_t* wseq;       // [W]
   const void* q_lat;         // [B][H][512]  bf16 (f32 for the f32 cache)
   const void* q_pe;          // [B][H][64]
-  float* part_o;             // [nslot][H][512]
+  void* part_o;              // [nslot][H][512] o/l: fp32 (f32 cache) or bf16
   float* part_ml;            // [nslot][H][2]
   int32_t B;
   int32_t H;
@@ -192,6 +192,25 @@ __device__ __forceinline__ void pv_read4(uint32_t addr, s16x4* lo, s16x4* hi) {
               (NB0 + 2) * 32, 16 * TP + (NB0 + 2) * 32, (NB0 + 3) * 32, 16 * TP + (NB0 + 3) * 32>(
       addr, lo[0], hi[0], lo[1], hi[1], lo[2], hi[2], lo[3], hi[3]);
 }
+
+// Store four consecutive values (dims d..d+3 of one head) of a segment's
+// normalised partial output o / l: fp32 for the f32 cache, bf16 otherwise
+// (the normalised partial is a convex combination of cached rows, so one bf16
+// rounding of it is of the size of the rounding of the bf16 output itself).
+template <int CT>
+__device__ __forceinline__ void store_part4(void* part_o, int64_t elem, const f32x4& v, float inv_l) {
+  const f32x4 x = v * inv_l;
+  if constexpr (CT == kF32) {
+    *(f32x4*)((float*)part_o + elem) = x;
+  } else {
+    uint2 u;
+    u.x = pack_bf16x2(x[0], x[1]);
+    u.y = pack_bf16x2(x[2], x[3]);
+    *(uint2*)((uint16_t*)part_o + elem) = u;
+  }
+}
+// 1 / l for the normalisation (0 for an empty sum; NaN stays NaN)
+__device__ __forceinline__ float inv_or_zero(float l) { return l != 0.f ? 1.f / l : 0.f; }
 
 // Launcher of the streaming kernel (decode_attn_stream.hip).
 hipError_t launch_attn_stream(const DecodePlan& plan, const AttnParams& prm, hipStream_t s);

@@ -294,9 +294,10 @@ mla_attn_kernel(AttnParams p) {
     if (seg_end) {
       const float lsum = sum_over_groups(l_run);
       const int64_t slot = w + cc.b;
-      float* po = p.part_o + (slot * H + h) * kDc + ds * DSLICE + 4 * g;
+      const float inv = inv_or_zero(lsum);
+      const int64_t po = (slot * H + h) * kDc + ds * DSLICE + 4 * g;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) *(f32x4*)(po + nb * 16) = o[nb];
+      for (int nb = 0; nb < NB; ++nb) store_part4<CT>(p.part_o, po + nb * 16, o[nb], inv);
       if (ds == 0 && g == 0) {
         p.part_ml[(slot * H + h) * 2 + 0] = m_run;
         p.part_ml[(slot * H + h) * 2 + 1] = lsum;
@@ -575,9 +576,10 @@ mla_attn_pair_kernel(AttnParams p) {
       for (int hb = 0; hb < 2; ++hb) {
         const float lsum = sum_over_groups(l_run[hb]);
         const int h = hp + 16 * hb + (ln & 15);
-        float* po = p.part_o + (slot * H + h) * kDc + 256 * half + 4 * (ln >> 4);
+        const float inv = inv_or_zero(lsum);
+        const int64_t po = (slot * H + h) * kDc + 256 * half + 4 * (ln >> 4);
 #pragma unroll
-        for (int nb = 0; nb < 16; ++nb) *(f32x4*)(po + nb * 16) = o[hb][nb];
+        for (int nb = 0; nb < 16; ++nb) store_part4<CT>(p.part_o, po + nb * 16, o[hb][nb], inv);
         if (half == 0 && (ln >> 4) == 0) {
           p.part_ml[(slot * H + h) * 2 + 0] = m_run[hb];
           p.part_ml[(slot * H + h) * 2 + 1] = lsum;

@@ -288,9 +288,10 @@ mla_attn_stream_kernel(AttnParams p) {
       const int64_t slot = w + seg_b;
       const int ln = opaque(lane);
       const int hh = blockIdx.y * 16 + (ln & 15);
-      float* po = p.part_o + (slot * H + hh) * kDc + 128 * dq + 4 * (ln >> 4);
+      const float inv = inv_or_zero(lsum);
+      const int64_t po = (slot * H + hh) * kDc + 128 * dq + 4 * (ln >> 4);
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) *(f32x4*)(po + nb * 16) = o[nb];
+      for (int nb = 0; nb < 8; ++nb) store_part4<CT>(p.part_o, po + nb * 16, o[nb], inv);
       if (dq == 0 && (ln >> 4) == 0) {
         p.part_ml[(slot * H + hh) * 2 + 0] = m_run;
         p.part_ml[(slot * H + hh) * 2 + 1] = lsum;

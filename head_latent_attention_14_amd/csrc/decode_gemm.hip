@@ -21,8 +21,8 @@ struct GemmParams {
   const void* w;              // [H][KD][ND]
   void* y;                    // absorb: q_lat [B][H][512]; project: out [B][H][128]
   float* lse;                 // project: [B][H] or null
-  const float* part_o;        // project: [nslot][H][512]
-  const float* part_ml;       // project: [nslot][H][2]
+  const void* part_o;         // merge: [nslot][H][512] o/l, f32 (f32 path) or bf16
+  const float* part_ml;       // merge: [nslot][H][2] (m, l)
   int64_t* prefix;            // [B+1] (written by the plan block of absorb)
   int64_t* starts;            // [W+1]
   int32_t* wseq;              // [W]
@@ -238,9 +238,10 @@ mla_headgemm_kernel(GemmParams p) {
   }
 }
 
-// Log-sum-exp merge of the split partials of one (b, h) per wave:
-//   M = max_s m_s,  l = sum_s 2^(m_s - M) l_s,
-//   o_lat = sum_s 2^(m_s - M) o_s / l   (written in the activation dtype),
+// Log-sum-exp merge of the split partials of one (b, h) per wave. Slot s
+// holds the normalised output u_s = o_s / l_s of its segment with (m_s, l_s):
+//   M = max_s m_s,  w_s = 2^(m_s - M) l_s,  l = sum_s w_s,
+//   o_lat = sum_s w_s u_s / l   (written in the activation dtype),
 //   lse = (M + log2 l) ln 2.
 // A sequence of length 0 gets o_lat = 0 and lse = -inf.
 template <int AT>
@@ -274,8 +275,18 @@ mla_merge_kernel(GemmParams p) {
         st1[u] = ld_const(p.starts, w + 1);
         m[u] = ld_const(p.part_ml, s * 2);
         l[u] = ld_const(p.part_ml, s * 2 + 1);
-        v0[u] = *(const f32x4*)(p.part_o + s * kDc + 8 * lane);
-        v1[u] = *(const f32x4*)(p.part_o + s * kDc + 8 * lane + 4);
+        if constexpr (AT == kF32) {
+          const float* po = (const float*)p.part_o + s * kDc + 8 * lane;
+          v0[u] = *(const f32x4*)po;
+          v1[u] = *(const f32x4*)(po + 4);
+        } else {
+          const u32x4 r = *(const u32x4*)((const uint16_t*)p.part_o + s * kDc + 8 * lane);
+          const uint32_t r0 = r[0], r1 = r[1], r2 = r[2], r3 = r[3];
+          v0[u] = f32x4{__builtin_bit_cast(float, r0 << 16), __builtin_bit_cast(float, r0 & 0xffff0000u),
+                        __builtin_bit_cast(float, r1 << 16), __builtin_bit_cast(float, r1 & 0xffff0000u)};
+          v1[u] = f32x4{__builtin_bit_cast(float, r2 << 16), __builtin_bit_cast(float, r2 & 0xffff0000u),
+                        __builtin_bit_cast(float, r3 << 16), __builtin_bit_cast(float, r3 & 0xffff0000u)};
+        }
       }
       bool ok[RU];
       float rmax = mmax;
@@ -292,9 +303,9 @@ mla_merge_kernel(GemmParams p) {
       for (int u = 0; u < RU; ++u) {
         if (ok[u]) {
           // a segment whose scores were all NaN keeps m = -inf and l = NaN:
-          // weight 0, and 0 * NaN carries the NaN into the result
-          const float e = (m[u] == -INFINITY) ? 0.f : exp2f(m[u] - rmax);
-          lsum += e * l[u];
+          // weight 0 * NaN, which carries the NaN into the result
+          const float e = ((m[u] == -INFINITY) ? 0.f : exp2f(m[u] - rmax)) * l[u];
+          lsum += e;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             acc[i] += e * v0[u][i];

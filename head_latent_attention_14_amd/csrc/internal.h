@@ -50,7 +50,7 @@ struct WorkspaceLayout {
   size_t wfirst;     // int32 [B] first worker of each sequence
   size_t wlast;      // int32 [B] last worker of each sequence (-1 if empty)
   size_t q_lat;      // [B][H][512] bf16 (f32 for the f32 path)
-  size_t part_o;     // f32 [nslot][H][512] unnormalised partial outputs
+  size_t part_o;     // [nslot][H][512] normalised partial outputs: f32 (f32 path) or bf16
   size_t part_ml;    // f32 [nslot][H][2] running max (log2 domain) and sum
   size_t total;
 };
@@ -80,7 +80,7 @@ struct DecodeArgs {
   int32_t* wfirst;
   int32_t* wlast;
   void* q_lat;
-  float* part_o;
+  void* part_o;
   float* part_ml;
 };
 // stage: 1 = absorb (+ length prefix), 2 = attention, 3 = merge + W_UV,
