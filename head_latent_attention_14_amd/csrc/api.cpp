@@ -12,7 +12,6 @@
 
 namespace mla {
 
-static constexpr int kTargetCUs = 256;        // MI355X compute units
 static constexpr int kMaxHeads = 1024;
 static constexpr int kMaxSeqs = 1 << 20;
 

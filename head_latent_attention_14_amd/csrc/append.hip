@@ -180,11 +180,143 @@ mla_append_kernel(AppendArgs a) {
   }
 }
 
+// BF16 cache and activations: the same 16 columns x 16 tokens per workgroup,
+// with both operands staged in LDS by asynchronous 1 KB copies. A wave copy
+// covers 512 contiguous elements of one weight or hidden row, so every HBM
+// request is a full contiguous kilobyte (loading MFMA operands straight from
+// memory would touch 16 rows 2*d_model bytes apart per instruction). The
+// contraction runs in stages of KC elements, two stages in LDS; rows are
+// padded by 16 bytes so the 16 rows of an operand read fall on distinct banks.
+__global__ void __launch_bounds__(256)
+mla_append_bf16_kernel(AppendArgs a) {
+  constexpr int KC = 1024;                 // contraction elements per stage
+  constexpr int RS = KC * 2 + 16;          // padded LDS row (bytes)
+  constexpr int OPND = 16 * RS;            // 16 rows of one operand
+  constexpr int STAGE = 2 * OPND;          // weight rows, then hidden rows
+  constexpr int NST = 2;
+  __shared__ __attribute__((aligned(1024))) char stg[NST * STAGE];
+  __shared__ float red[4][16][17];         // [wave][column][token]
+  __shared__ float rowt[16][17];           // [token][column]
+  __shared__ float2 rot[16][8];            // (cos, sin) per token and pair (RoPE groups)
+  __shared__ int64_t trow[16];
+  __shared__ int tpos[16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int tok0 = blockIdx.x * 16;
+  const int j0 = blockIdx.y * kColGroup;   // first output column
+  const int D = a.d_model;
+  const int nch = (D + KC - 1) / KC;
+
+  const __bf16* wbase = (j0 < kDc) ? (const __bf16*)a.w_dkv + (int64_t)j0 * D
+                                   : (const __bf16*)a.w_kr + (int64_t)(j0 - kDc) * D;
+  const int nh = (a.n_tok - tok0 < 16) ? a.n_tok - tok0 : 16;
+  // rows past the last token read as zeros (buffer range check)
+  const auto rw = make_rsrc(wbase, (uint32_t)(16 * D * 2));
+  const auto rh = make_rsrc((const __bf16*)a.h + (int64_t)tok0 * D, (uint32_t)(nh * D * 2));
+
+  // stage c: copy i (wave-uniform) = operand i/32, row (i/2)%16, half i%2 of the KC slice
+  auto issue = [&](int c) {
+    const int k0 = c * KC;
+    char* sb = stg + (c % NST) * STAGE;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = wave + 4 * u;
+      const int op = i >> 5, r = (i >> 1) & 15, pc = i & 1;
+      if (k0 + pc * 512 >= D) continue;
+      const uint32_t voff = (uint32_t)(((r * D) + k0 + pc * 512) * 2 + lane * 16);
+      buffer_copy16(op ? rh : rw, voff, sb + op * OPND + r * RS + pc * 1024);
+    }
+  };
+  issue(0);
+  if (nch > 1) issue(1);
+
+  // token slots (wave 0) and, for the RoPE columns, the rotation of every
+  // (token, pair): angle in fp64, reduced to [-pi, pi] with a two-term 2*pi
+  // (Cody-Waite), then sine and cosine of the reduced angle in fp32
+  if (wave == 0) {
+    const int t = (tok0 + l16 < a.n_tok) ? tok0 + l16 : a.n_tok - 1;
+    const int sq = a.tok_seq[t];
+    const int ps = a.tok_pos[t];
+    const int sc = (sq >= 0 && sq < a.num_seqs) ? sq : 0;
+    const int cap = a.seq_cap[sc];
+    const int64_t st = a.seq_start[sc];
+    if (g == 0) {
+      const bool ok = sq >= 0 && sq < a.num_seqs && ps >= 0 && ps < cap;
+      trow[l16] = ok ? st + ps : -1;
+      tpos[l16] = ps;
+    }
+    if (j0 >= kDc) {
+      const int i0 = (j0 - kDc) / 2;       // first pair of this column group
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int pr = g + 4 * pass;       // pairs g, g + 4 for the lanes of group g
+        const double f0 = a.inv_freq[i0 + 4 * pass + 0], f1 = a.inv_freq[i0 + 4 * pass + 1];
+        const double f2 = a.inv_freq[i0 + 4 * pass + 2], f3 = a.inv_freq[i0 + 4 * pass + 3];
+        const double f = g == 0 ? f0 : g == 1 ? f1 : g == 2 ? f2 : f3;
+        const double phi = (double)ps * f;
+        const double kq = rint(phi * 0.15915494309189535);         // 1 / (2 pi)
+        double rp = fma(-kq, 6.283185307179586, phi);              // 2 pi, leading part
+        rp = fma(-kq, 2.4492935982947064e-16, rp);                 // 2 pi, trailing part
+        float sn, cs;
+        sincosf((float)rp, &sn, &cs);
+        rot[l16][pr] = make_float2(cs, sn);
+      }
+    }
+  }
+
+  // ---------------- contraction ----------------
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nch; ++c) {
+    wait_vmcnt<0>();
+    __syncthreads();                                   // stage c visible to all waves
+    const int k0 = c * KC;
+    const int nks = ((D - k0) < KC ? (D - k0) : KC) / 32;
+    const char* sb = stg + (c % NST) * STAGE;
+    const char* pa = sb + l16 * RS + g * 16;
+    const char* pb = pa + OPND;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {                      // wave w takes k-steps 8w .. 8w+7
+      const int ks = 8 * wave + u;
+      if (ks < nks) acc = mfma_bf16_k32(*(const bf16x8*)(pa + ks * 64), *(const bf16x8*)(pb + ks * 64), acc);
+    }
+    if (c + NST < nch) {
+      __syncthreads();                                 // stage c consumed
+      issue(c + NST);
+    }
+  }
+  // lane holds column j0 + 4g + r of token l16
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][4 * g + r][l16] = acc[r];
+  __syncthreads();
+  {
+    const int cc = tid >> 4, t = tid & 15;
+    rowt[t][cc] = red[0][cc][t] + red[1][cc][t] + red[2][cc][t] + red[3][cc][t];
+  }
+  __syncthreads();
+  if (j0 >= kDc && tid < 128) {                        // RoPE: pair pr of token t
+    const int t = tid >> 3, pr = tid & 7;
+    const float2 cs = rot[t][pr];
+    const float x0 = rowt[t][2 * pr], x1 = rowt[t][2 * pr + 1];
+    rowt[t][2 * pr] = x0 * cs.x - x1 * cs.y;
+    rowt[t][2 * pr + 1] = x0 * cs.y + x1 * cs.x;
+  }
+  __syncthreads();
+  {
+    const int t = tid >> 4, cc = tid & 15;
+    if (tok0 + t < a.n_tok && trow[t] >= 0)
+      ((uint16_t*)a.rows)[trow[t] * kDrow + j0 + cc] = f32_to_bf16_bits(rowt[t][cc]);
+  }
+}
+
 hipError_t launch_append(int ct, const AppendArgs& a, hipStream_t s) {
   dim3 grid((a.n_tok + 15) / 16, ct == kFP8 ? 1 : kNumGroups);
   switch (ct) {
     case kF32: hipLaunchKernelGGL(mla_append_kernel<kF32>, grid, dim3(256), 0, s, a); break;
-    case kBF16: hipLaunchKernelGGL(mla_append_kernel<kBF16>, grid, dim3(256), 0, s, a); break;
+    case kBF16: hipLaunchKernelGGL(mla_append_bf16_kernel, grid, dim3(256), 0, s, a); break;
     case kFP8: hipLaunchKernelGGL(mla_append_kernel<kFP8>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }

@@ -398,8 +398,17 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
   g.x = a.q_lat;
   g.w = a.w_uv;
   g.y = a.out;
-  return f32 ? launch_gemm_t<kF32, kDc, kDv, 1, 128>(g, s)
-             : launch_gemm_t<kBF16, kDc, kDv, 1, kDc>(g, s);
+  if (f32) return launch_gemm_t<kF32, kDc, kDv, 1, 128>(g, s);
+  // 16 or 32 batch rows per workgroup, whichever loads fewer bytes per CU:
+  // each workgroup reads a 64 KB weight slice and 16 KB of merged output per
+  // 16 rows, and every 256 workgroups share the CUs once more
+  auto per_cu = [&](int nbt) {
+    const int64_t wgs = (int64_t)(kDv / kNT) * a.H * ((a.B + 16 * nbt - 1) / (16 * nbt));
+    const int64_t rounds = (wgs + kTargetCUs - 1) / kTargetCUs;
+    return rounds * (64 + 16 * nbt);
+  };
+  return per_cu(2) < per_cu(1) ? launch_gemm_t<kBF16, kDc, kDv, 2, kDc>(g, s)
+                               : launch_gemm_t<kBF16, kDc, kDv, 1, kDc>(g, s);
 }
 
 }  // namespace mla

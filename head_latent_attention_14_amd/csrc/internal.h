@@ -9,6 +9,8 @@ namespace mla {
 
 enum CacheType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
+constexpr int kTargetCUs = 256;   // MI355X compute units
+
 // ---------------------------------------------------------------- append
 struct AppendArgs {
   void* rows;                 // [total_rows][576] cache storage
