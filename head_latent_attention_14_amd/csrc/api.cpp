@@ -37,6 +37,7 @@ DecodePlan make_plan(int ct, int B, int H) {
     p.nstage = (ct == kF32) ? 2 : 4;
     p.head_groups = H / 16;
   }
+  p.tile = (ct == kF32) ? 16 : 32;
   int w = kTargetCUs / p.head_groups;
   w = w < 8 ? 8 : (w / 8) * 8;                 // a multiple of the 8 XCDs
   p.workers = w;
@@ -49,7 +50,7 @@ WorkspaceLayout workspace_layout(int ct, int B, int H) {
   const DecodePlan p = make_plan(ct, B, H);
   WorkspaceLayout l{};
   size_t off = 0;
-  l.prefix = off;  off = align256(off + sizeof(int64_t) * ((size_t)B + 1));
+  l.seqinfo = off; off = align256(off + sizeof(SeqInfo) * (size_t)B);
   l.starts = off;  off = align256(off + sizeof(int64_t) * ((size_t)p.workers + 1));
   l.wseq = off;    off = align256(off + sizeof(int32_t) * (size_t)p.workers);
   l.wfirst = off;  off = align256(off + sizeof(int32_t) * (size_t)B);
@@ -185,7 +186,7 @@ static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len
   a.out = out;
   a.lse = lse;
   a.softmax_scale = softmax_scale;
-  a.prefix = (int64_t*)(ws + wl.prefix);
+  a.seqinfo = (SeqInfo*)(ws + wl.seqinfo);
   a.starts = (int64_t*)(ws + wl.starts);
   a.wseq = (int32_t*)(ws + wl.wseq);
   a.wfirst = (int32_t*)(ws + wl.wfirst);

@@ -11,9 +11,8 @@ namespace mla {
 struct AttnParams {
   const char* rows;
   const float* row_scale;
-  const int64_t* seq_start;
-  const int64_t* prefix;     // [B+1]
-  const int64_t* starts;     // [W+1]
+  const SeqInfo* seqinfo;    // [B]
+  const int64_t* starts;     // [W+1] in tiles
   const int32_t* wseq;       // [W]
   const void* q_lat;         // [B][H][512]  bf16 (f32 for the f32 cache)
   const void* q_pe;          // [B][H][64]
@@ -35,29 +34,60 @@ template <> struct Tr<kF32> { static constexpr int kRowBytes = 2304, kPad = 2320
 constexpr int kConvPad = 1168;   // padded bf16 row of the widened fp8 tile
 constexpr float kSlack = 8.f;    // lazy-rescale slack of the running max (log2 units)
 
+// A worker's position in its tile range: the tile at token t of sequence b.
+// The record of the next sequence with tiles is loaded one segment ahead
+// (lane l holds its 32-bit word l % 8), so moving into it needs no memory
+// access on the way.
 struct Cursor {
   int b;            // sequence
   int64_t t;        // first token of the tile, local to the sequence
   int64_t t_end;    // end of this worker's segment of the sequence (local)
   int64_t row0;     // cache row of token t
+  int nb;           // next sequence with tiles (B: none)
+  int nx;           // this lane's word of seqinfo[nb]
 };
 
-// Move to the next tile of this worker's token range; false when done.
+__device__ __forceinline__ int seqinfo_word(const SeqInfo* si, int b, int lane) {
+  return ((const int*)(si + b))[lane & 7];
+}
+
+// The first tile of worker w's range [r_lo, r_hi) (tiles).
 template <int TILE>
-__device__ __forceinline__ bool advance(Cursor& c, const int64_t* prefix, const int64_t* seq_start,
-                                        int B, int64_t r_hi) {
+__device__ __forceinline__ Cursor cursor_start(const AttnParams& p, int64_t w, int64_t r_lo,
+                                               int64_t r_hi, int lane) {
+  Cursor c;
+  c.b = ld_const(p.wseq, w);
+  const SeqInfo* si = p.seqinfo + c.b;
+  const int64_t t0 = ld_const(&si->tile0, 0), t1 = ld_const(&si->tile1, 0);
+  const int64_t len = ld_const(&si->len, 0);
+  const int64_t se = t1 < r_hi ? t1 : r_hi;
+  c.t = (r_lo - t0) * TILE;
+  c.t_end = (se - t0) * TILE < len ? (se - t0) * TILE : len;
+  c.row0 = ld_const(&si->row0, 0) + c.t;
+  c.nb = ld_const(&si->next, 0);
+  c.nx = c.nb < p.B ? seqinfo_word(p.seqinfo, c.nb, opaque(lane)) : 0;
+  return c;
+}
+
+// Move to the next tile of the worker's range; false when done.
+template <int TILE>
+__device__ __forceinline__ bool advance(Cursor& c, const AttnParams& p, int64_t r_hi, int lane) {
   c.t += TILE;
   c.row0 += TILE;
   if (c.t < c.t_end) return true;
-  int b = c.b + 1;
-  while (b < B && ld_const(prefix, b + 1) == ld_const(prefix, b)) ++b;   // skip empty sequences
-  b = uniform(b);
-  if (b >= B || ld_const(prefix, b) >= r_hi) return false;
-  c.b = b;
+  if (c.nb >= p.B) return false;
+  const int64_t t0 = __builtin_amdgcn_readlane(c.nx, 3);
+  if (t0 >= r_hi) return false;
+  const int64_t t1 = __builtin_amdgcn_readlane(c.nx, 4);
+  const int64_t len = __builtin_amdgcn_readlane(c.nx, 2);
+  const int64_t se = t1 < r_hi ? t1 : r_hi;
+  c.b = c.nb;
   c.t = 0;
-  const int64_t pb = ld_const(prefix, b), pe = ld_const(prefix, b + 1);
-  c.t_end = (pe < r_hi ? pe : r_hi) - pb;
-  c.row0 = ld_const(seq_start, b);
+  c.t_end = (se - t0) * TILE < len ? (se - t0) * TILE : len;
+  c.row0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(c.nx, 1) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane(c.nx, 0));
+  c.nb = __builtin_amdgcn_readlane(c.nx, 5);
+  if (c.nb < p.B) c.nx = seqinfo_word(p.seqinfo, c.nb, opaque(lane));
   return true;
 }
 

@@ -59,14 +59,7 @@ mla_attn_kernel(AttnParams p) {
   TileCopy<CT, NW> cp;
   cp.init(wave, lane);
 
-  Cursor c0;
-  c0.b = ld_const(p.wseq, w);
-  {
-    const int64_t pb = ld_const(p.prefix, c0.b), pe = ld_const(p.prefix, c0.b + 1);
-    c0.t = r_lo - pb;
-    c0.t_end = (pe < r_hi ? pe : r_hi) - pb;
-    c0.row0 = ld_const(p.seq_start, c0.b) + c0.t;
-  }
+  const Cursor c0 = cursor_start<TILE>(p, w, r_lo, r_hi, lane);
   auto issue = [&](const Cursor& c, int stage) {
     cp.issue(p.rows, p.row_scale, c, smem + stage * STAGE_BYTES, lane);
   };
@@ -109,7 +102,7 @@ mla_attn_kernel(AttnParams p) {
     if (lvalid) {
       issue(lc, i);
       ++issued;
-      lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
+      lvalid = advance<TILE>(lc, p, r_hi, lane);
     }
   }
 
@@ -144,7 +137,7 @@ mla_attn_kernel(AttnParams p) {
       else
         pend = cp.prepare(p.rows, p.row_scale, lc, smem + (issued % NSTAGE) * STAGE_BYTES);
       ++issued;
-      lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
+      lvalid = advance<TILE>(lc, p, r_hi, lane);
     }
     const char* stage = smem + (it % NSTAGE) * STAGE_BYTES;
     const int64_t left = cc.t_end - cc.t;
@@ -307,7 +300,7 @@ mla_attn_kernel(AttnParams p) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (!advance<TILE>(cc, p.prefix, p.seq_start, B, r_hi)) break;
+    if (!advance<TILE>(cc, p, r_hi, lane)) break;
     if (seg_end) {
       load_q(cc.b);
       wait_vmcnt<0>();
@@ -358,14 +351,7 @@ mla_attn_pair_kernel(AttnParams p) {
 
   TileCopy<CT, NW> cp;
   cp.init(wave, lane);
-  Cursor c0;
-  c0.b = ld_const(p.wseq, w);
-  {
-    const int64_t pb = ld_const(p.prefix, c0.b), pe = ld_const(p.prefix, c0.b + 1);
-    c0.t = r_lo - pb;
-    c0.t_end = (pe < r_hi ? pe : r_hi) - pb;
-    c0.row0 = ld_const(p.seq_start, c0.b) + c0.t;
-  }
+  const Cursor c0 = cursor_start<TILE>(p, w, r_lo, r_hi, lane);
   auto issue = [&](const Cursor& c, int stage) {
     cp.issue(p.rows, p.row_scale, c, smem + stage * STAGE_BYTES, lane);
   };
@@ -398,7 +384,7 @@ mla_attn_pair_kernel(AttnParams p) {
     if (lvalid) {
       issue(lc, i);
       ++issued;
-      lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
+      lvalid = advance<TILE>(lc, p, r_hi, lane);
     }
   }
 
@@ -428,7 +414,7 @@ mla_attn_pair_kernel(AttnParams p) {
     if (do_copy) {
       pend = cp.prepare(p.rows, p.row_scale, lc, smem + (issued % NSTAGE) * STAGE_BYTES);
       ++issued;
-      lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
+      lvalid = advance<TILE>(lc, p, r_hi, lane);
     }
     auto copy_group = [&](int grp) {
       if (do_copy) {
@@ -590,7 +576,7 @@ mla_attn_pair_kernel(AttnParams p) {
         for (int nb = 0; nb < 16; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
-    if (!advance<TILE>(cc, p.prefix, p.seq_start, B, r_hi)) break;
+    if (!advance<TILE>(cc, p, r_hi, lane)) break;
     if (seg_end) {
       load_q(cc.b);
       wait_vmcnt<0>();
@@ -622,8 +608,7 @@ hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipS
   AttnParams prm;
   prm.rows = (const char*)a.rows;
   prm.row_scale = a.row_scale;
-  prm.seq_start = a.seq_start;
-  prm.prefix = a.prefix;
+  prm.seqinfo = a.seqinfo;
   prm.starts = a.starts;
   prm.wseq = a.wseq;
   prm.q_lat = a.q_lat;

@@ -14,12 +14,17 @@
 //   copy wave   waits for tile t, joins the barrier, issues tile t+NSTAGE-1
 //               (and, on the last tile of a sequence segment, the next
 //               sequence's queries into the other of two LDS query buffers)
-//   compute q   scores of all 32 tokens of the tile for the 16 heads (each
-//               compute wave does them, which costs little at 16 heads), the
-//               online softmax (identical in the four waves), and the values
-//               for latent dims 128q..128q+127.
-// Each wave writes its quarter of a segment's partial itself, so a tile needs
-// one barrier and nothing is exchanged between waves.
+//   compute q   its share of the 18 k-steps of the scores (5, 4, 5, 4), the
+//               fp32 partial to LDS, a barrier, the sum of the four partials
+//               in a fixed order (so the four waves hold bit-identical
+//               scores), the online softmax, and the values for latent dims
+//               128q..128q+127.
+// A tile takes two barriers: the tile is visible (A), the score partials are
+// (B). The copy wave issues a few copies of a later tile between them and the
+// rest after B, so the compute waves rarely wait for it at B. Each wave
+// writes its quarter of a segment's partial itself.
+#include <type_traits>
+
 #include "attn_tile.h"
 
 namespace mla {
@@ -45,7 +50,9 @@ mla_attn_stream_kernel(AttnParams p) {
                 "outstanding copies must fit the vmcnt counter");
   static_assert(Tr<CT>::kTile == TILE, "32-token tiles");
 
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + 2 * QBUF];
+  constexpr int XBUF = 4 * 2048;                         // score partials, 2 KB per compute wave
+  constexpr int NEARLY = 8;                              // copies issued between barriers A and B
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + 2 * QBUF + XBUF];
   // per stage: the tile's sequence, valid rows, whether it ends its segment,
   // whether another tile follows, and the following segment's sequence
   struct TileMeta {
@@ -66,15 +73,9 @@ mla_attn_stream_kernel(AttnParams p) {
   const int64_t r_hi = ld_const(p.starts, w + 1);
   if (r_lo >= r_hi) return;                              // whole workgroup
 
-  Cursor c0;
-  c0.b = ld_const(p.wseq, w);
-  {
-    const int64_t pb = ld_const(p.prefix, c0.b), pe = ld_const(p.prefix, c0.b + 1);
-    c0.t = r_lo - pb;
-    c0.t_end = (pe < r_hi ? pe : r_hi) - pb;
-    c0.row0 = ld_const(p.seq_start, c0.b) + c0.t;
-  }
+  const Cursor c0 = cursor_start<TILE>(p, w, r_lo, r_hi, lane);
   char* qlds = smem + NSTAGE * STAGE_BYTES;             // two query buffers (segment parity)
+  char* xbuf = qlds + 2 * QBUF;
 
   // ---- copy wave: copy i moves stage slots 64i..64i+63; slot s holds
   // padded row s / SPR, 16-byte chunk s % SPR (the pad chunk repeats the
@@ -82,25 +83,40 @@ mla_attn_stream_kernel(AttnParams p) {
   // which wraps the chunk at most once since 64 < SPR. ----
   constexpr int SPR = TP / 16;
   static_assert(SPR > 64, "one wrap per copy");
-  auto issue = [&](const Cursor& c, int stage) {
+  struct Copies {
+    __amdgpu_buffer_rsrc_t rsrc;
+    char* sb;
+    int nvalid, row, chunk;
+  };
+  auto prepare = [&](const Cursor& c, int stage) {
     const int64_t left = c.t_end - c.t;
-    const int nvalid = left < TILE ? (int)left : TILE;
-    const auto rsrc = make_rsrc(p.rows + c.row0 * RB, (uint32_t)(TILE * RB));
-    char* sb = smem + stage * STAGE_BYTES;
-    int row = 0, chunk = opaque(lane);                   // slot `lane` of copy 0
+    Copies k;
+    k.nvalid = left < TILE ? (int)left : TILE;
+    k.rsrc = make_rsrc(p.rows + c.row0 * RB, (uint32_t)(TILE * RB));
+    k.sb = smem + stage * STAGE_BYTES;
+    k.row = 0;
+    k.chunk = opaque(lane);                              // slot `lane` of copy 0
+    return k;
+  };
+  // copies [I0, I1) of a tile
+  auto copies = [&](Copies& k, auto i0c, auto i1c) {
+    constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
 #pragma unroll
-    for (int i = 0; i < NCOPY; ++i) {
-      int r = row < nvalid ? row : nvalid - 1;           // rows past the end repeat the last one
+    for (int i = I0; i < I1; ++i) {
+      int r = k.row < k.nvalid ? k.row : k.nvalid - 1;   // rows past the end repeat the last one
       r = r < TILE ? r : TILE - 1;
-      const int ch = chunk < RB / 16 ? chunk : RB / 16 - 1;
-      buffer_copy16(rsrc, (uint32_t)(r * RB + ch * 16), sb + i * 1024);
-      chunk += 64;
-      if (chunk >= SPR) {
-        chunk -= SPR;
-        ++row;
+      const int ch = k.chunk < RB / 16 ? k.chunk : RB / 16 - 1;
+      buffer_copy16(k.rsrc, (uint32_t)(r * RB + ch * 16), k.sb + i * 1024);
+      k.chunk += 64;
+      if (k.chunk >= SPR) {
+        k.chunk -= SPR;
+        ++k.row;
       }
     }
   };
+  using I0_ = std::integral_constant<int, 0>;
+  using IE_ = std::integral_constant<int, NEARLY>;
+  using IN_ = std::integral_constant<int, NCOPY>;
   // the 16 heads' queries of sequence b into query buffer `buf`
   auto issue_q = [&](int b, int buf) {
     char* qb = qlds + buf * QBUF;
@@ -121,8 +137,10 @@ mla_attn_stream_kernel(AttnParams p) {
     }
   };
 
+  // this compute wave's k-steps of the scores: [ks_lo, ks_hi) of 18
+  const int ks_lo = (dq * 9 + 1) / 2, ks_hi = (dq * 9 + 10) / 2;
   // score A operand: tile row l16 (+16 for the second token block), k-run 8g
-  const uint32_t s_base = (uint32_t)(l16 * TP + g * 16);
+  const uint32_t s_base = (uint32_t)(l16 * TP + g * 16 + ks_lo * 64);
   // value A operand (transposing reads): source lane (g, l16) points at row
   // 4g + l16/4, dims 128*dq + 4*(l16%4) .. +3; the low half of a read holds
   // c_t[128*dq + 16*nb + l16] for t = 4g + q, the high half t = 16 + 4g + q
@@ -140,30 +158,42 @@ mla_attn_stream_kernel(AttnParams p) {
     Cursor lc = c0;
     bool lvalid = true;
     int issued = 0;
-    auto issue_tile = [&](int stage) {
-      const int64_t left = lc.t_end - lc.t;
-      const int nvalid = left < TILE ? (int)left : TILE;
+    // the tile at the cursor: copies [0, NEARLY) now, the rest by finish_tile
+    auto finish_tile = [&](Copies& k, int stage) {
+      copies(k, IE_{}, IN_{});
       const int b = lc.b;
       const bool seg_end = (lc.t + TILE >= lc.t_end);
-      issue(lc, stage);
       ++issued;
-      lvalid = advance<TILE>(lc, p.prefix, p.seq_start, B, r_hi);
-      if (lane == 0) meta[stage] = TileMeta{b, nvalid, seg_end ? 1 : 0, lvalid ? 1 : 0, lc.b};
+      lvalid = advance<TILE>(lc, p, r_hi, lane);
+      if (lane == 0) meta[stage] = TileMeta{b, k.nvalid, seg_end ? 1 : 0, lvalid ? 1 : 0, lc.b};
     };
     issue_q(c0.b, 0);
 #pragma unroll
-    for (int i = 0; i < NSTAGE - 1; ++i)
-      if (lvalid) issue_tile(i);
+    for (int i = 0; i < NSTAGE - 1; ++i) {
+      if (lvalid) {
+        Copies k = prepare(lc, i);
+        copies(k, I0_{}, IE_{});
+        finish_tile(k, i);
+      }
+    }
     int it = 0;
     int qpar = 0;                                        // query buffer of the current segment
     while (true) {
       wait_tiles<NCOPY, NSTAGE - 2>(issued - 1 - it);
-      barrier_lds();                                     // tile `it` (and its queries) visible
+      barrier_lds();                                     // A: tile `it` (and its queries) visible
       const TileMeta m = meta[it % NSTAGE];
       // the next segment's queries go out before this round's tile copies,
-      // so the wait before the next barrier covers them
+      // so the wait before the next barrier A covers them
       if (m.seg_end && m.more) issue_q(uniform(m.next_b), qpar ^ 1);
-      if (lvalid) issue_tile(issued % NSTAGE);
+      const bool go = lvalid;
+      const int stage = issued % NSTAGE;
+      Copies k;
+      if (go) {
+        k = prepare(lc, stage);
+        copies(k, I0_{}, IE_{});
+      }
+      barrier_lds();                                     // B: score partials visible
+      if (go) finish_tile(k, stage);
       if (!m.more) break;
       if (m.seg_end) qpar ^= 1;
       ++it;
@@ -179,15 +209,18 @@ mla_attn_stream_kernel(AttnParams p) {
     // first tile of the segment: its queries are in LDS buffer qpar once the
     // barrier has passed; they stay in registers for the whole segment
     barrier_lds();
-    bf16x8 q[18];
+    bf16x8 q[5];                                         // k-steps ks_lo + j
     {
       const char* qb = qlds + qpar * QBUF;
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) q[ks] = *(const bf16x8*)(qb + q_lat_lane + ks * 64);
-#pragma unroll
-      for (int ks = 16; ks < 18; ++ks) {
-        const int c = 4 * (ks - 16) + g;                 // logical 16-byte chunk of the q_pe row
-        q[ks] = *(const bf16x8*)(qb + q_pe_lane + 16 * (c ^ ((l16 >> 1) & 7)));
+      for (int j = 0; j < 5; ++j) {
+        const int ks = ks_lo + j;
+        if (ks < 16) {
+          q[j] = *(const bf16x8*)(qb + q_lat_lane + ks * 64);
+        } else if (ks < 18) {
+          const int c = 4 * (ks - 16) + g;               // logical 16-byte chunk of the q_pe row
+          q[j] = *(const bf16x8*)(qb + q_pe_lane + 16 * (c ^ ((l16 >> 1) & 7)));
+        }
       }
     }
     float m_run = -INFINITY;   // running max of this lane's head (log2 domain)
@@ -207,23 +240,30 @@ mla_attn_stream_kernel(AttnParams p) {
       more = uniform(m.more) != 0;
       seg_b = uniform(m.b);
       const char* tbase = smem + (it % NSTAGE) * STAGE_BYTES;
-      // ---------------- scores of the 32 tokens ----------------
-      // operands in two batches of nine k-steps
+      // ---------------- scores of the 32 tokens: this wave's k-steps ----------------
       const char* sa = tbase + s_base;
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      {
+        bf16x8 a0[5], a1[5];
 #pragma unroll
-      for (int k0 = 0; k0 < 18; k0 += 9) {
-        bf16x8 a0[9], a1[9];
-#pragma unroll
-        for (int j = 0; j < 9; ++j) {
-          a0[j] = *(const bf16x8*)(sa + (k0 + j) * 64);
-          a1[j] = *(const bf16x8*)(sa + 16 * TP + (k0 + j) * 64);
+        for (int j = 0; j < 5; ++j) {
+          if (ks_lo + j < ks_hi) {
+            a0[j] = *(const bf16x8*)(sa + j * 64);
+            a1[j] = *(const bf16x8*)(sa + 16 * TP + j * 64);
+          }
         }
 #pragma unroll
-        for (int j = 0; j < 9; ++j) {
-          s0 = mfma_bf16_k32(a0[j], q[k0 + j], s0);
-          s1 = mfma_bf16_k32(a1[j], q[k0 + j], s1);
+        for (int j = 0; j < 5; ++j) {
+          if (ks_lo + j < ks_hi) {
+            s0 = mfma_bf16_k32(a0[j], q[j], s0);
+            s1 = mfma_bf16_k32(a1[j], q[j], s1);
+          }
         }
+      }
+      {
+        char* xw = xbuf + dq * 2048 + lane * 16;
+        *(f32x4*)xw = s0;
+        *(f32x4*)(xw + 1024) = s1;
       }
       // value operands of this tile, read while the score MFMAs run
       s16x4 vlo[8], vhi[8];
@@ -233,6 +273,26 @@ mla_attn_stream_kernel(AttnParams p) {
       lds_tr16_x8<128, 16 * TP + 128, 160, 16 * TP + 160, 192, 16 * TP + 192, 224, 16 * TP + 224>(
           tr_addr, vlo[4], vhi[4], vlo[5], vhi[5], vlo[6], vhi[6], vlo[7], vhi[7]);
 
+      barrier_lds();                                     // B: the four partials are in LDS
+      {
+        // the same order in every wave: ((p0 + p1) + p2) + p3
+        f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const char* xr = xbuf + u * 2048 + lane * 16;
+          const f32x4 u0 = (u == dq) ? s0 : *(const f32x4*)xr;
+          const f32x4 u1 = (u == dq) ? s1 : *(const f32x4*)(xr + 1024);
+          if (u == 0) {
+            t0 = u0;
+            t1 = u1;
+          } else {
+            t0 += u0;
+            t1 += u1;
+          }
+        }
+        s0 = t0;
+        s1 = t1;
+      }
       // ---------------- online softmax over the tile ----------------
       float sc[8];
 #pragma unroll

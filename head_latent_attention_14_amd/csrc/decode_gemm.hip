@@ -7,8 +7,8 @@
 // The weight's contraction index is its row index, so weight tiles are staged
 // in LDS and fed to the MFMA through transposing LDS reads.
 //
-// The absorb launch also builds the prefix sums of the clamped sequence
-// lengths that the attention and merge kernels partition work with.
+// The absorb launch also builds the work plan that the attention and merge
+// kernels split the sequences' tiles with.
 #include <type_traits>
 
 #include "common.h"
@@ -23,33 +23,38 @@ struct GemmParams {
   float* lse;                 // project: [B][H] or null
   const void* part_o;         // merge: [nslot][H][512] o/l, f32 (f32 path) or bf16
   const float* part_ml;       // merge: [nslot][H][2] (m, l)
-  int64_t* prefix;            // [B+1] (written by the plan block of absorb)
+  SeqInfo* seqinfo;           // [B] (written by the plan block of absorb)
   int64_t* starts;            // [W+1]
   int32_t* wseq;              // [W]
   int32_t* wfirst;            // [B]
   int32_t* wlast;             // [B]
   const int32_t* seq_len;     // absorb: [B]
   const int32_t* seq_cap;     // absorb: [B]
+  const int64_t* seq_start;   // absorb: [B]
   int32_t B;
   int32_t H;
   int32_t workers;            // W of the attention launch
+  int32_t tile;               // tokens per tile of the attention launch
 };
 
 constexpr int kNT = 64;       // output columns per workgroup (one 16-wide block per wave)
 
 // The work plan, built by one extra workgroup of the absorb launch so the
-// attention and merge kernels need no divisions or searches:
-//   prefix[b]  = sum of the clamped lengths of sequences < b (prefix[B] = T)
-//   starts[w]  = floor(w * T / W): worker w streams positions [starts[w], starts[w+1])
-//                of the concatenation of all sequences
-//   wseq[w]    = the sequence holding position starts[w] (non-empty workers)
+// attention and merge kernels need no divisions or searches. Sequence b has
+// n_b = ceil(len_b / tile) tiles (len clamped to [0, capacity]); P_b is the
+// prefix sum of n, NT = P_B, and the tiles of all sequences form one stream:
+//   seqinfo[b] = {first cache row, len_b, P_b, P_(b+1), next sequence with tiles}
+//   starts[w]  = floor(w * NT / W): worker w takes tiles [starts[w], starts[w+1])
+//   wseq[w]    = the sequence holding tile starts[w] (non-empty workers)
 //   wfirst[b], wlast[b] = first and last worker that touch sequence b
 //                (wlast < wfirst for an empty sequence)
-// With P = prefix[b], floor(w T / W) >= P exactly when w >= ceil(P W / T), so
-// sequence b holds the starts of workers [ceil(P_b W/T), ceil(P_{b+1} W/T)),
-// its first worker is ceil((P_b + 1) W / T) - 1 and its last ceil(P_{b+1} W / T) - 1:
-// every entry is a closed form of the prefix sums, which stay in LDS
-// (`lds`, room for `lds_n` values) when they fit.
+// Splitting whole tiles keeps every split inside a sequence on a tile
+// boundary, so the only partial tile of a sequence is its last one.
+// floor(w NT / W) >= P exactly when w >= ceil(P W / NT), so sequence b holds
+// the starts of workers [ceil(P_b W/NT), ceil(P_(b+1) W/NT)), its first
+// worker is ceil((P_b + 1) W / NT) - 1 and its last ceil(P_(b+1) W / NT) - 1:
+// every entry is a closed form of the prefix sums, which stay in LDS (`lds`,
+// room for `lds_n` values) when they fit.
 __device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
@@ -57,21 +62,21 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
   const int lane = tid & 63;
   const int B = p.B;
   const int64_t W = p.workers;
+  const int TL = p.tile;
   const bool in_lds = B + 1 <= lds_n;
   if (tid < 64) {
     int64_t carry = 0;
-    if (lane == 0) {
-      p.prefix[0] = 0;
-      if (in_lds) lds[0] = 0;
-    }
+    if (lane == 0 && in_lds) lds[0] = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
       const int b = b0 + lane;
-      int64_t v = 0;
+      int L = 0;
       if (b < B) {
-        const int L = p.seq_len[b];
+        const int Lr = p.seq_len[b];
         const int cap = p.seq_cap[b];
-        v = L < 0 ? 0 : (L > cap ? cap : L);
+        L = Lr < 0 ? 0 : (Lr > cap ? cap : Lr);
       }
+      const int64_t n = (L + TL - 1) / TL;
+      int64_t v = n;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int src = lane - off;
@@ -81,36 +86,59 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
         if (src >= 0) v += u;
       }
       if (b < B) {
-        p.prefix[b + 1] = carry + v;
+        SeqInfo si;
+        si.row0 = p.seq_start[b];
+        si.len = L;
+        si.tile0 = (int32_t)(carry + v - n);
+        si.tile1 = (int32_t)(carry + v);
+        si.next = B;                                     // set below
+        si.pad[0] = si.pad[1] = 0;
+        p.seqinfo[b] = si;
         if (in_lds) lds[b + 1] = carry + v;
       }
       const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffff), 63);
       const int hi = __builtin_amdgcn_readlane((int)(v >> 32), 63);
       carry += ((int64_t)hi << 32) | (uint32_t)lo;
     }
-    if (!in_lds && lane == 0) lds[0] = carry;            // T for the other waves
+    if (!in_lds && lane == 0) lds[0] = carry;            // NT for the other waves
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const volatile int64_t* gpref = p.prefix;
-  auto prefix = [&](int b) -> int64_t { return in_lds ? lds[b] : gpref[b]; };
-  const int64_t T = in_lds ? lds[B] : lds[0];
-  for (int64_t w = tid; w <= W; w += 256) p.starts[w] = (w * T) / W;
-  if (T == 0) {
+  const volatile int32_t* gtile0 = &p.seqinfo[0].tile0;
+  // P_b for b < B (P_B = NT)
+  auto prefix = [&](int b) -> int64_t {
+    return in_lds ? lds[b] : (int64_t)gtile0[(int64_t)b * (sizeof(SeqInfo) / 4)];
+  };
+  const int64_t NT = in_lds ? lds[B] : lds[0];
+  for (int64_t w = tid; w <= W; w += 256) p.starts[w] = (w * NT) / W;
+  if (NT == 0) {
     for (int64_t w = tid; w < W; w += 256) p.wseq[w] = 0;
   }
   for (int b = tid; b < B; b += 256) {
-    const int64_t P0 = prefix(b), P1 = prefix(b + 1);
+    const int64_t P0 = prefix(b), P1 = (b + 1 < B) ? prefix(b + 1) : NT;
     if (P1 > P0) {
-      const int64_t wlo = ceil_div64(P0 * W, T), whi = ceil_div64(P1 * W, T);
+      const int64_t wlo = ceil_div64(P0 * W, NT), whi = ceil_div64(P1 * W, NT);
       for (int64_t w = wlo; w < whi; ++w) p.wseq[w] = b;
-      p.wfirst[b] = (int)(ceil_div64((P0 + 1) * W, T) - 1);
+      p.wfirst[b] = (int)(ceil_div64((P0 + 1) * W, NT) - 1);
       p.wlast[b] = (int)(whi - 1);
     } else {
       p.wfirst[b] = 0;
       p.wlast[b] = -1;
     }
+    // next sequence with tiles: the largest b' > b with P_b' <= P_(b+1), which
+    // owns tile P_(b+1) (none when P_(b+1) = NT)
+    int nx = B;
+    if (P1 < NT) {
+      int lo = b + 1, hi = B - 1;                        // P_lo <= P1 holds (P_(b+1) = P1)
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (prefix(mid) <= P1) lo = mid;
+        else hi = mid - 1;
+      }
+      nx = lo;
+    }
+    p.seqinfo[b].next = nx;
   }
 }
 
@@ -344,14 +372,16 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
                          int stage) {
   const bool f32 = (ct == kF32);
   hipError_t e = hipSuccess;
-  // 1. absorb W_UK into the query; build the length prefix
+  // 1. absorb W_UK into the query; build the work plan
   if (stage == 0 || stage == 1) {
     GemmParams g{};
     g.B = a.B;
     g.H = a.H;
     g.workers = plan.workers;
-    g.prefix = a.prefix;
+    g.seqinfo = a.seqinfo;
     g.starts = a.starts;
+    g.seq_start = a.seq_start;
+    g.tile = plan.tile;
     g.wseq = a.wseq;
     g.wfirst = a.wfirst;
     g.wlast = a.wlast;
@@ -376,7 +406,7 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
   m.B = a.B;
   m.H = a.H;
   m.workers = plan.workers;
-  m.prefix = a.prefix;
+  m.seqinfo = a.seqinfo;
   m.starts = a.starts;
   m.wfirst = a.wfirst;
   m.wlast = a.wlast;

@@ -30,6 +30,20 @@ struct AppendArgs {
 hipError_t launch_append(int cache_type, const AppendArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- decode
+// Per-sequence record of the work plan (written by the absorb launch, read by
+// the attention kernels). Work is split in tiles: sequence b owns tiles
+// [tile0, tile1) of the stream of all sequences' tiles, ceil(len / tile) of
+// them, the last one possibly partial.
+struct SeqInfo {
+  int64_t row0;     // cache row of the sequence's first token
+  int32_t len;      // length clamped to [0, capacity]
+  int32_t tile0;    // first tile
+  int32_t tile1;    // one past the last tile
+  int32_t next;     // next sequence that has tiles (B: none)
+  int32_t pad[2];
+};
+static_assert(sizeof(SeqInfo) == 32, "one 32-byte record per sequence");
+
 // Launch plan: fixed by (cache type, B, H) so that the workspace size can be
 // computed on the host without seeing the device-resident lengths.
 struct DecodePlan {
@@ -39,15 +53,16 @@ struct DecodePlan {
   int hb;        // block kernel: 16-head blocks per workgroup
   int ds;        // block kernel: value-dimension splits per head block
   int nstage;    // cache tiles in flight per workgroup (LDS ring depth)
-  int workers;   // W: token ranges of the concatenated sequences
+  int tile;      // tokens per tile of the kernel (the unit of the work split)
+  int workers;   // W: tile ranges of the stream of all sequences' tiles
   int head_groups;  // workgroups sharing one token range (H / heads per workgroup)
   int64_t nslot;    // partial-result slots: W + B
 };
 DecodePlan make_plan(int cache_type, int B, int H);
 
 struct WorkspaceLayout {
-  size_t prefix;     // int64 [B+1] prefix sums of clamped lengths
-  size_t starts;     // int64 [W+1] first stream position of each worker (and T)
+  size_t seqinfo;    // SeqInfo [B]
+  size_t starts;     // int64 [W+1] first tile of each worker (and the tile count)
   size_t wseq;       // int32 [W] first sequence of each worker
   size_t wfirst;     // int32 [B] first worker of each sequence
   size_t wlast;      // int32 [B] last worker of each sequence (-1 if empty)
@@ -76,7 +91,7 @@ struct DecodeArgs {
   float* lse;
   float softmax_scale;
   // workspace views
-  int64_t* prefix;
+  SeqInfo* seqinfo;
   int64_t* starts;
   int32_t* wseq;
   int32_t* wfirst;
@@ -85,7 +100,7 @@ struct DecodeArgs {
   void* part_o;
   float* part_ml;
 };
-// stage: 1 = absorb (+ length prefix), 2 = attention, 3 = merge + W_UV,
+// stage: 1 = absorb (+ work plan), 2 = attention, 3 = merge + W_UV,
 // 0 = all three
 hipError_t launch_decode(int cache_type, const DecodePlan& plan, const DecodeArgs& a,
                          hipStream_t s, int stage);
