@@ -12,11 +12,11 @@ from the 256 MB Infinity Cache.
 Prints one JSON line. `value` is the step's algorithmic bytes (cache rows,
 weights, activations and outputs the method must move) per second, over a
 timed region of whole steps with events only at its ends. The attention
-kernel's own duration (the roofline entry) is then measured over the same
-number of steps with HIP events on the launch stream around each attention
-launch (those events add a little to the step, so they stay out of the timed
-region). A second workload (the 128-head V2 shape by default) is measured the
-same way and reported under "secondary".
+kernel's own duration (the roofline entry) is then measured as the same
+number of attention launches back to back on the launch stream, rotating over
+the replicas, between two HIP events. A second workload (the 128-head V2
+shape by default) is measured the same way and reported under "secondary",
+with its attention rate also against the bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 
 METRIC = "MLA decode latent-cache GB/s + TFLOP/s, % of MI355X roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA, MI355X
 KERNEL_SOURCES = ["head_latent_attention_14_amd/csrc/decode_attn.hip",
                   "head_latent_attention_14_amd/csrc/decode_attn_stream.hip",
                   "head_latent_attention_14_amd/csrc/attn_tile.h",
@@ -100,19 +101,20 @@ def cpu_baseline(p, seconds: float):
     sf = 4 if p.wl.cache == "fp8" else 0
     e_a = {"f32": 4, "bf16": 2}[p.wl.act]
     t0 = time.perf_counter()
-    done = 0
+    done = 0           # sequences decoded (passes over the batch repeat it)
     tokens = 0
-    while done < B and time.perf_counter() - t0 < seconds:
-        view.decode([(done, h) for h in range(H)])
-        tokens += int(p.seq_len[done])
+    while time.perf_counter() - t0 < seconds and done < 64 * B:
+        b = done % B
+        view.decode([(b, h) for h in range(H)])
+        tokens += int(p.seq_len[b])
         done += 1
     el = time.perf_counter() - t0
     # the sample's share of the step's algorithmic bytes
-    by = tokens * (576 * e_c + sf) + 2 * H * 128 * 512 * e_a + done * H * (192 + 128) * e_a
+    by = tokens * (576 * e_c + sf) + 2 * H * 128 * 512 * e_a * done / B + done * H * (192 + 128) * e_a
     cores = len(os.sched_getaffinity(0))
     return {"value": by / el / 1e9, "unit": "GB/s", "cores": blas_threads or cores,
             "kind": "oracle",
-            "sample": f"fp64 unabsorbed oracle on sequences 0..{done - 1} of {B} "
+            "sample": f"fp64 unabsorbed oracle, {done} sequence decodes over the {B} sequences "
                       f"(all {H} heads, {tokens} cached tokens, {el:.1f} s, "
                       f"{cores} host cores visible)"}
 
@@ -163,19 +165,11 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
                                           r["tok_pos"], wl.rope_base, stream)
         reps.append(r)
 
-    def step(i, ev=None):
+    def step(i):
         r = reps[i % R]
         if wl.append:
             r["app"]()
-        d = r["dec"]
-        if ev is None:
-            d()
-        else:
-            d.absorb()
-            ev[0].record(stream)
-            d.attend()
-            ev[1].record(stream)
-            d.combine()
+        r["dec"]()
 
     for i in range(warmup):
         step(i)
@@ -195,18 +189,25 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
     gpu_ms = start.elapsed_time(end) / steps
     ms = max(wall_ms, gpu_ms)
 
-    # the attention kernel's own duration over the same number of steps, with
-    # events recorded on the launch stream around each attention launch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(steps):
-        step(warmup + steps + i, evs[i])
+    # the attention kernel's own duration: `steps` launches back to back on the
+    # launch stream, rotating over the replicas (each absorbed first, so every
+    # launch reads its cache from HBM), between two events
+    for r in reps:
+        r["dec"].absorb()
     torch.cuda.synchronize()
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    a0 = torch.cuda.Event(enable_timing=True)
+    a1 = torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for i in range(steps):
+        reps[i % R]["dec"].attend()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = a0.elapsed_time(a1) / steps
     del reps
     torch.cuda.empty_cache()
     return dict(wl=wl, p=p, T=p.T, B=B, H=H, R=R, ms=ms, step_bytes=step_bytes,
-                step_flops=step_flops, attn_bytes=ab["cache"], attn_ms=attn_ms)
+                step_flops=step_flops, attn_bytes=ab["cache"], attn_flops=fl["attention"],
+                attn_ms=attn_ms)
 
 
 def main():
@@ -276,6 +277,9 @@ def main():
             "attention_kernel_us": round(s["attn_ms"] * 1e3, 3),
             "attention_GBps": round(s_attn, 2),
             "attention_hbm_frac": round(s_attn / HBM_PEAK_GBS, 4),
+            "attention_tflops": round(s["attn_flops"] / (s["attn_ms"] * 1e-3) / 1e12, 2),
+            "attention_mfma_frac": round(s["attn_flops"] / (s["attn_ms"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "attention_traffic": recorded_traffic(args.secondary),
         }
     if not args.no_cpu_baseline:
         p = W.make_problem(wl)

@@ -86,7 +86,9 @@ typedef struct {
  *   k      = W_KR  h[n]                  (64 values)
  *   k_pe   = RoPE(k, pos)                pairs (2i, 2i+1), i = 0..31, rotated by
  *                                        pos * rope_base^(-2i/64); the angle is
- *                                        formed in fp64
+ *                                        formed and reduced to [-pi, pi] in fp64,
+ *                                        its sine and cosine taken in fp32 (BF16
+ *                                        cache) or fp64 (F32, FP8_E4M3)
  *   row    = c || k_pe, stored at row seq_start[s] + pos of the cache, where
  *            s = tok_seq[n] and pos = tok_pos[n] (pos is both the slot and the
  *            RoPE position, 0-based within the sequence).
