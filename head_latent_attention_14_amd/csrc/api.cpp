@@ -53,6 +53,7 @@ WorkspaceLayout workspace_layout(int ct, int B, int H) {
   l.seqinfo = off; off = align256(off + sizeof(SeqInfo) * (size_t)B);
   l.starts = off;  off = align256(off + sizeof(int64_t) * ((size_t)p.workers + 1));
   l.wseq = off;    off = align256(off + sizeof(int32_t) * (size_t)p.workers);
+  l.winfo = off;   off = align256(off + sizeof(WorkerInfo) * (size_t)p.workers);
   l.wfirst = off;  off = align256(off + sizeof(int32_t) * (size_t)B);
   l.wlast = off;   off = align256(off + sizeof(int32_t) * (size_t)B);
   l.q_lat = off;   off = align256(off + (size_t)B * H * MLA_D_C * (ct == kF32 ? 4 : 2));
@@ -189,6 +190,7 @@ static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len
   a.seqinfo = (SeqInfo*)(ws + wl.seqinfo);
   a.starts = (int64_t*)(ws + wl.starts);
   a.wseq = (int32_t*)(ws + wl.wseq);
+  a.winfo = (WorkerInfo*)(ws + wl.winfo);
   a.wfirst = (int32_t*)(ws + wl.wfirst);
   a.wlast = (int32_t*)(ws + wl.wlast);
   a.q_lat = ws + wl.q_lat;

@@ -12,8 +12,7 @@ struct AttnParams {
   const char* rows;
   const float* row_scale;
   const SeqInfo* seqinfo;    // [B]
-  const int64_t* starts;     // [W+1] in tiles
-  const int32_t* wseq;       // [W]
+  const WorkerInfo* winfo;   // [W]
   const void* q_lat;         // [B][H][512]  bf16 (f32 for the f32 cache)
   const void* q_pe;          // [B][H][64]
   void* part_o;              // [nslot][H][512] o/l: fp32 (f32 cache) or bf16
@@ -51,21 +50,20 @@ __device__ __forceinline__ int seqinfo_word(const SeqInfo* si, int b, int lane) 
   return ((const int*)(si + b))[lane & 7];
 }
 
-// The first tile of worker w's range [r_lo, r_hi) (tiles).
+// The first tile of worker w (c.b < 0: the worker has none); r_hi receives
+// one past its last tile.
 template <int TILE>
-__device__ __forceinline__ Cursor cursor_start(const AttnParams& p, int64_t w, int64_t r_lo,
-                                               int64_t r_hi, int lane) {
+__device__ __forceinline__ Cursor cursor_start(const AttnParams& p, int64_t w, int lane,
+                                               int64_t& r_hi) {
+  const WorkerInfo* wi = p.winfo + w;
   Cursor c;
-  c.b = ld_const(p.wseq, w);
-  const SeqInfo* si = p.seqinfo + c.b;
-  const int64_t t0 = ld_const(&si->tile0, 0), t1 = ld_const(&si->tile1, 0);
-  const int64_t len = ld_const(&si->len, 0);
-  const int64_t se = t1 < r_hi ? t1 : r_hi;
-  c.t = (r_lo - t0) * TILE;
-  c.t_end = (se - t0) * TILE < len ? (se - t0) * TILE : len;
-  c.row0 = ld_const(&si->row0, 0) + c.t;
-  c.nb = ld_const(&si->next, 0);
-  c.nx = c.nb < p.B ? seqinfo_word(p.seqinfo, c.nb, opaque(lane)) : 0;
+  c.b = ld_const(&wi->b, 0);
+  c.t = ld_const(&wi->t, 0);
+  c.t_end = ld_const(&wi->t_end, 0);
+  c.row0 = ld_const(&wi->row0, 0);
+  c.nb = ld_const(&wi->next, 0);
+  r_hi = ld_const(&wi->r_hi, 0);
+  c.nx = (c.b >= 0 && c.nb < p.B) ? seqinfo_word(p.seqinfo, c.nb, opaque(lane)) : 0;
   return c;
 }
 

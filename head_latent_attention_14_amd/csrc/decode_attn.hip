@@ -52,14 +52,13 @@ mla_attn_kernel(AttnParams p) {
   const int B = p.B;
   const int h = (blockIdx.y * HB + hb) * 16 + l16;       // head of this lane
   const int64_t w = blockIdx.x;
-  const int64_t r_lo = ld_const(p.starts, w);
-  const int64_t r_hi = ld_const(p.starts, w + 1);
-  if (r_lo >= r_hi) return;                              // whole workgroup
+  int64_t r_hi;
+  const Cursor c0 = cursor_start<TILE>(p, w, lane, r_hi);
+  if (c0.b < 0) return;                                  // whole workgroup
 
   TileCopy<CT, NW> cp;
   cp.init(wave, lane);
 
-  const Cursor c0 = cursor_start<TILE>(p, w, r_lo, r_hi, lane);
   auto issue = [&](const Cursor& c, int stage) {
     cp.issue(p.rows, p.row_scale, c, smem + stage * STAGE_BYTES, lane);
   };
@@ -345,13 +344,12 @@ mla_attn_pair_kernel(AttnParams p) {
   const int B = p.B;
   const int hp = (blockIdx.y * NP + (wave >> 1)) * 32;  // first head of the pair
   const int64_t w = blockIdx.x;
-  const int64_t r_lo = ld_const(p.starts, w);
-  const int64_t r_hi = ld_const(p.starts, w + 1);
-  if (r_lo >= r_hi) return;                              // whole workgroup
+  int64_t r_hi;
+  const Cursor c0 = cursor_start<TILE>(p, w, lane, r_hi);
+  if (c0.b < 0) return;                                  // whole workgroup
 
   TileCopy<CT, NW> cp;
   cp.init(wave, lane);
-  const Cursor c0 = cursor_start<TILE>(p, w, r_lo, r_hi, lane);
   auto issue = [&](const Cursor& c, int stage) {
     cp.issue(p.rows, p.row_scale, c, smem + stage * STAGE_BYTES, lane);
   };
@@ -609,8 +607,7 @@ hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipS
   prm.rows = (const char*)a.rows;
   prm.row_scale = a.row_scale;
   prm.seqinfo = a.seqinfo;
-  prm.starts = a.starts;
-  prm.wseq = a.wseq;
+  prm.winfo = a.winfo;
   prm.q_lat = a.q_lat;
   prm.q_pe = a.q_pe;
   prm.part_o = a.part_o;

@@ -69,11 +69,10 @@ mla_attn_stream_kernel(AttnParams p) {
   const int H = p.H;
   const int B = p.B;
   const int64_t w = blockIdx.x;
-  const int64_t r_lo = ld_const(p.starts, w);
-  const int64_t r_hi = ld_const(p.starts, w + 1);
-  if (r_lo >= r_hi) return;                              // whole workgroup
+  int64_t r_hi;
+  const Cursor c0 = cursor_start<TILE>(p, w, lane, r_hi);
+  if (c0.b < 0) return;                                  // whole workgroup
 
-  const Cursor c0 = cursor_start<TILE>(p, w, r_lo, r_hi, lane);
   char* qlds = smem + NSTAGE * STAGE_BYTES;             // two query buffers (segment parity)
   char* xbuf = qlds + 2 * QBUF;
 
@@ -151,14 +150,17 @@ mla_attn_stream_kernel(AttnParams p) {
   const uint32_t q_pe_lane = (uint32_t)(QLAT_BYTES + l16 * 128);
 
   // The two roles run separate loops over the same tiles, so they meet at
-  // the same barriers: one per tile. Only the copy wave walks the sequences
+  // the same barriers: two per tile. Only the copy wave walks the sequences
   // (its cursor runs NSTAGE-1 tiles ahead); it records each tile's place in
-  // the stream next to the tile, so the compute waves read it from LDS.
+  // the stream next to the tile, so the compute waves read it from LDS, and
+  // keeps its own copy of the flags it needs in registers.
+  static_assert(NSTAGE == 3, "the copy wave's flag queue holds two tiles");
   if (copier) {
     Cursor lc = c0;
     bool lvalid = true;
     int issued = 0;
-    // the tile at the cursor: copies [0, NEARLY) now, the rest by finish_tile
+    // flags of an issued tile: segment end (bit 0), another tile follows
+    // (bit 1), the sequence after it (bits 2..)
     auto finish_tile = [&](Copies& k, int stage) {
       copies(k, IE_{}, IN_{});
       const int b = lc.b;
@@ -166,14 +168,18 @@ mla_attn_stream_kernel(AttnParams p) {
       ++issued;
       lvalid = advance<TILE>(lc, p, r_hi, lane);
       if (lane == 0) meta[stage] = TileMeta{b, k.nvalid, seg_end ? 1 : 0, lvalid ? 1 : 0, lc.b};
+      return (seg_end ? 1 : 0) | (lvalid ? 2 : 0) | (lc.b << 2);
     };
     issue_q(c0.b, 0);
-#pragma unroll
-    for (int i = 0; i < NSTAGE - 1; ++i) {
+    int fq0 = 0, fq1 = 0;                                // flags of tiles `it` and `it`+1
+    {
+      Copies k = prepare(lc, 0);
+      copies(k, I0_{}, IE_{});
+      fq0 = finish_tile(k, 0);
       if (lvalid) {
-        Copies k = prepare(lc, i);
+        k = prepare(lc, 1);
         copies(k, I0_{}, IE_{});
-        finish_tile(k, i);
+        fq1 = finish_tile(k, 1);
       }
     }
     int it = 0;
@@ -181,10 +187,11 @@ mla_attn_stream_kernel(AttnParams p) {
     while (true) {
       wait_tiles<NCOPY, NSTAGE - 2>(issued - 1 - it);
       barrier_lds();                                     // A: tile `it` (and its queries) visible
-      const TileMeta m = meta[it % NSTAGE];
+      const int m = fq0;
+      const bool m_seg_end = (m & 1) != 0, m_more = (m & 2) != 0;
       // the next segment's queries go out before this round's tile copies,
       // so the wait before the next barrier A covers them
-      if (m.seg_end && m.more) issue_q(uniform(m.next_b), qpar ^ 1);
+      if (m_seg_end && m_more) issue_q(m >> 2, qpar ^ 1);
       const bool go = lvalid;
       const int stage = issued % NSTAGE;
       Copies k;
@@ -193,9 +200,10 @@ mla_attn_stream_kernel(AttnParams p) {
         copies(k, I0_{}, IE_{});
       }
       barrier_lds();                                     // B: score partials visible
-      if (go) finish_tile(k, stage);
-      if (!m.more) break;
-      if (m.seg_end) qpar ^= 1;
+      fq0 = fq1;
+      if (go) fq1 = finish_tile(k, stage);
+      if (!m_more) break;
+      if (m_seg_end) qpar ^= 1;
       ++it;
     }
     return;

@@ -26,6 +26,7 @@ struct GemmParams {
   SeqInfo* seqinfo;           // [B] (written by the plan block of absorb)
   int64_t* starts;            // [W+1]
   int32_t* wseq;              // [W]
+  WorkerInfo* winfo;          // [W]
   int32_t* wfirst;            // [B]
   int32_t* wlast;             // [B]
   const int32_t* seq_len;     // absorb: [B]
@@ -140,6 +141,33 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
     }
     p.seqinfo[b].next = nx;
   }
+  // each worker's starting point, from the records above
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int64_t w = tid; w < W; w += 256) {
+    const int64_t r_lo = (w * NT) / W, r_hi = ((w + 1) * NT) / W;
+    WorkerInfo wi;
+    wi.r_hi = (int32_t)r_hi;
+    wi.pad = 0;
+    if (r_lo >= r_hi) {
+      wi.row0 = 0;
+      wi.b = -1;
+      wi.t = wi.t_end = 0;
+      wi.next = B;
+    } else {
+      const int b = ((const volatile int32_t*)p.wseq)[w];
+      const volatile SeqInfo* si = p.seqinfo + b;
+      const int64_t t0 = si->tile0, t1 = si->tile1, len = si->len;
+      const int64_t se = t1 < r_hi ? t1 : r_hi;
+      wi.b = b;
+      wi.t = (int32_t)((r_lo - t0) * TL);
+      wi.t_end = (int32_t)((se - t0) * TL < len ? (se - t0) * TL : len);
+      wi.row0 = si->row0 + wi.t;
+      wi.next = si->next;
+    }
+    p.winfo[w] = wi;
+  }
 }
 
 // Y[b][h][:] = X[b][h][:] . W[h] for one head (blockIdx.y), 64 output columns
@@ -176,24 +204,45 @@ mla_headgemm_kernel(GemmParams p) {
     return;
   }
 
-  // ---------------- X tile -> LDS (all loads issued before the stores) ----------------
+  // ---------------- X tile and the first weight chunk -> LDS ----------------
+  // (every load of both is issued before any store, so the two round trips
+  // to memory overlap)
+  constexpr int XPR = KD * ES / 16;                    // 16-byte pieces per X row
+  constexpr int WPR = kNT * ES / 16;                   // 16-byte pieces per weight row
+  auto load_w = [&](int k0, u32x4* v) {
+#pragma unroll
+    for (int k = 0; k < WP / 256; ++k) {
+      const int i = tid + 256 * k;
+      const int r = i / WPR, c = i - r * WPR;
+      v[k] = *(const u32x4*)((const char*)p.w + (((int64_t)h * KD + k0 + r) * ND + n0) * ES + c * 16);
+    }
+  };
+  auto store_w = [&](const u32x4* v) {
+#pragma unroll
+    for (int k = 0; k < WP / 256; ++k) {
+      const int i = tid + 256 * k;
+      const int r = i / WPR, c = i - r * WPR;
+      *(u32x4*)(w_lds + r * WROW + c * 16) = v[k];
+    }
+  };
   {
-    constexpr int PPR = KD * ES / 16;
-    u32x4 v[XP / 256];
+    u32x4 xv[XP / 256], wv[WP / 256];
 #pragma unroll
     for (int k = 0; k < XP / 256; ++k) {
       const int i = tid + 256 * k;
-      const int r = i / PPR, c = i - r * PPR;
+      const int r = i / XPR, c = i - r * XPR;
       const int b = b0 + r;
-      v[k] = u32x4{0u, 0u, 0u, 0u};
-      if (b < B) v[k] = *(const u32x4*)((const char*)p.x + (((int64_t)b * H + h) * KD) * ES + c * 16);
+      xv[k] = u32x4{0u, 0u, 0u, 0u};
+      if (b < B) xv[k] = *(const u32x4*)((const char*)p.x + (((int64_t)b * H + h) * KD) * ES + c * 16);
     }
+    load_w(0, wv);
 #pragma unroll
     for (int k = 0; k < XP / 256; ++k) {
       const int i = tid + 256 * k;
-      const int r = i / PPR, c = i - r * PPR;
-      *(u32x4*)(x_lds + r * XROW + c * 16) = v[k];
+      const int r = i / XPR, c = i - r * XPR;
+      *(u32x4*)(x_lds + r * XROW + c * 16) = xv[k];
     }
+    store_w(wv);
   }
 
   f32x4 acc[NBT];
@@ -201,22 +250,11 @@ mla_headgemm_kernel(GemmParams p) {
   for (int i = 0; i < NBT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int k0 = 0; k0 < KD; k0 += KC) {
-    if (k0) __syncthreads();                           // previous chunk consumed
-    {
-      constexpr int PPR = kNT * ES / 16;
-      u32x4 v[WP / 256];
-#pragma unroll
-      for (int k = 0; k < WP / 256; ++k) {
-        const int i = tid + 256 * k;
-        const int r = i / PPR, c = i - r * PPR;
-        v[k] = *(const u32x4*)((const char*)p.w + (((int64_t)h * KD + k0 + r) * ND + n0) * ES + c * 16);
-      }
-#pragma unroll
-      for (int k = 0; k < WP / 256; ++k) {
-        const int i = tid + 256 * k;
-        const int r = i / PPR, c = i - r * PPR;
-        *(u32x4*)(w_lds + r * WROW + c * 16) = v[k];
-      }
+    if (k0) {
+      u32x4 wv[WP / 256];
+      load_w(k0, wv);
+      __syncthreads();                                 // previous chunk consumed
+      store_w(wv);
     }
     __syncthreads();
     if constexpr (AT == kF32) {
@@ -266,30 +304,25 @@ mla_headgemm_kernel(GemmParams p) {
   }
 }
 
-// Log-sum-exp merge of the split partials of one (b, h) per wave. Slot s
+// Log-sum-exp merge of the split partials of one (b, h) by one wave. Slot s
 // holds the normalised output u_s = o_s / l_s of its segment with (m_s, l_s):
 //   M = max_s m_s,  w_s = 2^(m_s - M) l_s,  l = sum_s w_s,
-//   o_lat = sum_s w_s u_s / l   (written in the activation dtype),
+//   o_lat = sum_s w_s u_s / l,
 //   lse = (M + log2 l) ln 2.
-// A sequence of length 0 gets o_lat = 0 and lse = -inf.
+// Lane l returns dims 8l..8l+7 of o_lat in `acc`. A sequence of length 0
+// gets o_lat = 0 and lse = -inf.
 template <int AT>
-__global__ void __launch_bounds__(256)
-mla_merge_kernel(GemmParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int B = p.B, H = p.H;
-  if (pair >= (int64_t)B * H) return;
-  const int b = (int)(pair / H), h = (int)(pair - (int64_t)b * H);
+__device__ __forceinline__ float merge_row(const GemmParams& p, int b, int h, int lane, float* acc) {
+  const int H = p.H;
   const int64_t wf = ld_const(p.wfirst, b), wl = ld_const(p.wlast, b);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   float mmax = -INFINITY, lsum = 0.f;
   if (wl >= wf) {
-    // rounds of up to RU slots: every load of a round is issued before any
-    // of its values is used; rounds combine with an online rescale
-    // Every address of a round depends only on wf and wl, so all its loads
-    // are in flight together; a slot counts only if its worker's range is
-    // non-empty (an empty worker writes nothing), which is applied by
-    // selection once the data is back.
+    // rounds of up to RU slots: every address of a round depends only on wf
+    // and wl, so all its loads are in flight together; a slot counts only if
+    // its worker's range is non-empty (an empty worker writes nothing),
+    // which is applied by selection once the data is back
     constexpr int RU = 8;
     for (int64_t w0 = wf; w0 <= wl; w0 += RU) {
       float m[RU], l[RU];
@@ -347,7 +380,21 @@ mla_merge_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] *= inv;
   }
-  if (p.lse && lane == 0) p.lse[pair] = (lsum > 0.f) ? (mmax + __log2f(lsum)) * kLn2 : -INFINITY;
+  return (lsum > 0.f) ? (mmax + __log2f(lsum)) * kLn2 : -INFINITY;
+}
+
+// Merge one (b, h) per wave into o_lat (the q_lat buffer) and lse.
+template <int AT>
+__global__ void __launch_bounds__(256)
+mla_merge_kernel(GemmParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int B = p.B, H = p.H;
+  if (pair >= (int64_t)B * H) return;
+  const int b = (int)(pair / H), h = (int)(pair - (int64_t)b * H);
+  float acc[8];
+  const float lse = merge_row<AT>(p, b, h, lane, acc);
+  if (p.lse && lane == 0) p.lse[pair] = lse;
   char* dst = (char*)p.y + (pair * kDc + 8 * lane) * (AT == kF32 ? 4 : 2);
   if constexpr (AT == kF32) {
     *(f32x4*)dst = f32x4{acc[0], acc[1], acc[2], acc[3]};
@@ -379,6 +426,7 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
     g.H = a.H;
     g.workers = plan.workers;
     g.seqinfo = a.seqinfo;
+    g.winfo = a.winfo;
     g.starts = a.starts;
     g.seq_start = a.seq_start;
     g.tile = plan.tile;

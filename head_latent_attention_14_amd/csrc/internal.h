@@ -44,6 +44,19 @@ struct SeqInfo {
 };
 static_assert(sizeof(SeqInfo) == 32, "one 32-byte record per sequence");
 
+// Per-worker record of the work plan: where worker w starts, so that a
+// workgroup knows its first tile from one 32-byte load.
+struct WorkerInfo {
+  int64_t row0;     // cache row of the worker's first token
+  int32_t b;        // its first sequence (-1: the worker has no tiles)
+  int32_t t;        // first token, local to that sequence
+  int32_t t_end;    // end of the first segment (local token)
+  int32_t next;     // next sequence with tiles after b (B: none)
+  int32_t r_hi;     // one past the worker's last tile
+  int32_t pad;
+};
+static_assert(sizeof(WorkerInfo) == 32, "one 32-byte record per worker");
+
 // Launch plan: fixed by (cache type, B, H) so that the workspace size can be
 // computed on the host without seeing the device-resident lengths.
 struct DecodePlan {
@@ -64,6 +77,7 @@ struct WorkspaceLayout {
   size_t seqinfo;    // SeqInfo [B]
   size_t starts;     // int64 [W+1] first tile of each worker (and the tile count)
   size_t wseq;       // int32 [W] first sequence of each worker
+  size_t winfo;      // WorkerInfo [W]
   size_t wfirst;     // int32 [B] first worker of each sequence
   size_t wlast;      // int32 [B] last worker of each sequence (-1 if empty)
   size_t q_lat;      // [B][H][512] bf16 (f32 for the f32 path)
@@ -94,6 +108,7 @@ struct DecodeArgs {
   SeqInfo* seqinfo;
   int64_t* starts;
   int32_t* wseq;
+  WorkerInfo* winfo;
   int32_t* wfirst;
   int32_t* wlast;
   void* q_lat;
