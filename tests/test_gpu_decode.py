@@ -162,3 +162,39 @@ def test_prepared_calls_match_direct_calls():
     torch.cuda.synchronize()
     assert np.array_equal(dp.out.double().cpu().numpy(), o_direct)
     assert np.array_equal(dp.lse.double().cpu().numpy(), l_direct)
+
+
+# Empty sequences between, before and after non-empty ones; lengths of 1, of a
+# whole tile and one past it. Work is split in whole tiles, so these decide
+# where workers start, where their segments end and which sequence follows.
+GAPPY = [0, 0, 1, 0, 32, 0, 0, 33, 64, 0, 1, 0]
+
+
+@pytest.mark.parametrize("name,H", [("v2lite_bf16", 16), ("v2_bf16", 32), ("v2_bf16", 128),
+                                    ("fp8_cache", 16), ("fp8_cache", 128), ("tiny_fp32", 16)])
+def test_empty_sequences_between_others(name, H):
+    wl = W.WORKLOADS[name]
+    make = np.array([max(n, 1) for n in GAPPY])
+    p = W.make_problem(wl, seed=5, B=len(GAPPY), lengths=make, H=H)
+    dp = DeviceProblem(p)
+    dp.seq_len.copy_(torch.tensor(GAPPY, dtype=torch.int32))
+    log(f"[decode gappy] {name} H={H} lengths={GAPPY}")
+    dp.decode(poison=True)
+    torch.cuda.synchronize()
+    o = dp.out.double().cpu().numpy()
+    lse = dp.lse.double().cpu().numpy()
+    empty = [b for b, n in enumerate(GAPPY) if n == 0]
+    full = [b for b, n in enumerate(GAPPY) if n > 0]
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    p2 = W.make_problem(wl, seed=5, B=len(GAPPY), lengths=make, H=H)
+    p2.seq_len = np.array(GAPPY, dtype=np.int32)
+    ro, rl = OracleView(p2, apply_append=False).decode([(b, h) for b in full for h in range(H)])
+    got = np.stack([o[b, h] for b in full for h in range(H)])
+    err = rel_l2(got, ro)
+    log(f"  rel-L2 {err:.3e}")
+    assert err <= TOL[wl.cache]
+    gl = np.array([lse[b, h] for b in full for h in range(H)])
+    assert np.abs(gl - rl).max() <= 50 * TOL[wl.cache]
+    # every non-empty sequence on its own meets the bound too
+    for i, b in enumerate(full):
+        assert rel_l2(got[i * H:(i + 1) * H], ro[i * H:(i + 1) * H]) <= TOL[wl.cache], b
