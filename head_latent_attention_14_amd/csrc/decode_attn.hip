@@ -406,7 +406,7 @@ mla_attn_pair_kernel(AttnParams p) {
   while (true) {
     wait_tiles<CPW, NSTAGE - 2>(issued - 1 - it);       // this wave's copies of tile `it` landed
     barrier_lds();                                       // tile visible; stage it-1 and xbuf free
-    // the next tile's copies go out in five groups, one after each score batch
+    // the next tile's copies go out after this wave's score MFMAs are issued
     const bool do_copy = lvalid;
     typename TileCopy<CT, NW>::Pending pend;
     if (do_copy) {
@@ -414,12 +414,6 @@ mla_attn_pair_kernel(AttnParams p) {
       ++issued;
       lvalid = advance<TILE>(lc, p, r_hi, lane);
     }
-    auto copy_group = [&](int grp) {
-      if (do_copy) {
-#pragma unroll
-        for (int i = grp * CPW / 5; i < (grp + 1) * CPW / 5; ++i) cp.copy(pend, i);
-      }
-    };
     const char* stage = smem + (it % NSTAGE) * STAGE_BYTES;
     const int64_t left = cc.t_end - cc.t;
     const int nvalid = left < TILE ? (int)left : TILE;
@@ -436,29 +430,22 @@ mla_attn_pair_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     const char* sa = tb + s_base;
-    // operands in batches of two k-steps (the last batch has one)
+    // one batch of nine k-steps: the compiler places the 18 operand reads
+    // among the 36 MFMAs as registers allow (measured: batches of two with a
+    // scheduling barrier between them left the matrix unit idle longer)
 #pragma unroll
-    for (int k0 = 0; k0 < 9; k0 += 2) {
-      constexpr int KB = 2;
-      bf16x8 a0[KB], a1[KB];
+    for (int k = 0; k < 9; ++k) {
+      const bf16x8 a0 = *(const bf16x8*)(sa + k * 64);
+      const bf16x8 a1 = *(const bf16x8*)(sa + 16 * TP + k * 64);
+      acc[0][0] = mfma_bf16_k32(a0, q[0][k], acc[0][0]);
+      acc[0][1] = mfma_bf16_k32(a0, q[1][k], acc[0][1]);
+      acc[1][0] = mfma_bf16_k32(a1, q[0][k], acc[1][0]);
+      acc[1][1] = mfma_bf16_k32(a1, q[1][k], acc[1][1]);
+    }
+    // the next tile's copies, after this wave's score work is issued
+    if (do_copy) {
 #pragma unroll
-      for (int j = 0; j < KB; ++j) {
-        if (k0 + j < 9) {
-          a0[j] = *(const bf16x8*)(sa + (k0 + j) * 64);
-          a1[j] = *(const bf16x8*)(sa + 16 * TP + (k0 + j) * 64);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < KB; ++j) {
-        if (k0 + j < 9) {
-          acc[0][0] = mfma_bf16_k32(a0[j], q[0][k0 + j], acc[0][0]);
-          acc[0][1] = mfma_bf16_k32(a0[j], q[1][k0 + j], acc[0][1]);
-          acc[1][0] = mfma_bf16_k32(a1[j], q[0][k0 + j], acc[1][0]);
-          acc[1][1] = mfma_bf16_k32(a1[j], q[1][k0 + j], acc[1][1]);
-        }
-      }
-      copy_group(k0 / 2);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < CPW; ++i) cp.copy(pend, i);
     }
     // exchange partials with the other wave of the pair (a + b == b + a, so
     // both waves hold bit-identical scores and take identical decisions)
