@@ -477,7 +477,7 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
   g.w = a.w_uv;
   g.y = a.out;
   if (f32) return launch_gemm_t<kF32, kDc, kDv, 1, 128>(g, s);
-  // 16 or 32 batch rows per workgroup, whichever loads fewer bytes per CU:
+  // 16, 32 or 64 batch rows per workgroup, whichever loads fewer bytes per CU:
   // each workgroup reads a 64 KB weight slice and 16 KB of merged output per
   // 16 rows, and every 256 workgroups share the CUs once more
   auto per_cu = [&](int nbt) {
@@ -485,8 +485,10 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
     const int64_t rounds = (wgs + kTargetCUs - 1) / kTargetCUs;
     return rounds * (64 + 16 * nbt);
   };
-  return per_cu(2) < per_cu(1) ? launch_gemm_t<kBF16, kDc, kDv, 2, kDc>(g, s)
-                               : launch_gemm_t<kBF16, kDc, kDv, 1, kDc>(g, s);
+  const int64_t c1 = per_cu(1), c2 = per_cu(2), c4 = per_cu(4);
+  if (c4 < c2 && c4 < c1) return launch_gemm_t<kBF16, kDc, kDv, 4, kDc>(g, s);
+  return c2 < c1 ? launch_gemm_t<kBF16, kDc, kDv, 2, kDc>(g, s)
+                 : launch_gemm_t<kBF16, kDc, kDv, 1, kDc>(g, s);
 }
 
 }  // namespace mla
