@@ -3,7 +3,9 @@
 
 A step is one pass of the whole hot path over one batch: mla_append of one
 new token per sequence, then mla_decode (absorb W_UK, attention over the
-latent cache, merge + W_UV) for every sequence. The default workload is the
+latent cache, merge + W_UV) for every sequence. The append and the absorb
+stage go through mla_append_absorb (one launch: neither reads what the other
+writes), then mla_decode_attend and mla_decode_combine. The default workload is the
 DeepSeek-V2-Lite-shaped decode (B=64, H=16, L ~ U[1024, 4096], bf16 cache,
 d_model 2048). Inputs are synthetic and seeded; several replicas of the
 cache and weights are rotated so each step reads its cache from HBM, not
@@ -161,15 +163,23 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
             r.update(h=p.h.to(dev), w_dkv=p.w_dkv.to(dev), w_kr=p.w_kr.to(dev),
                      tok_seq=torch.from_numpy(p.tok_seq).to(dev),
                      tok_pos=torch.from_numpy(p.tok_pos).to(dev))
-            r["app"] = mla.PreparedAppend(r["cache"], r["h"], r["w_dkv"], r["w_kr"], r["tok_seq"],
-                                          r["tok_pos"], wl.rope_base, stream)
+            # the append and the decode's absorb stage in one call (one launch
+            # where it applies), then attend and combine
+            r["app"] = mla.PreparedAppendAbsorb(r["cache"], r["h"], r["w_dkv"], r["w_kr"],
+                                                r["tok_seq"], r["tok_pos"], wl.rope_base,
+                                                r["seq_len"], r["q_nope"], r["q_pe"], r["w_uk"],
+                                                r["w_uv"], scale, r["out"], r["lse"], r["ws"],
+                                                stream)
         reps.append(r)
 
     def step(i):
         r = reps[i % R]
         if wl.append:
             r["app"]()
-        r["dec"]()
+            r["dec"].attend()
+            r["dec"].combine()
+        else:
+            r["dec"]()
 
     for i in range(warmup):
         step(i)

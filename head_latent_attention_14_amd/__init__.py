@@ -31,7 +31,8 @@ MLA_DTYPE_FP8_E4M3 = 2
 D_C, D_R, D_ROW, D_NOPE, D_V = 512, 64, 576, 128, 128
 
 EXPORTED = ["mla_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_absorb",
-            "mla_decode_attend", "mla_decode_combine", "mla_status_string", "mla_abi_version"]
+            "mla_decode_attend", "mla_decode_combine", "mla_append_absorb", "mla_status_string",
+            "mla_abi_version"]
 DECODE_STAGES = ["mla_decode_absorb", "mla_decode_attend", "mla_decode_combine"]
 
 
@@ -66,6 +67,9 @@ def _load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = [C, P, P, P, P, P, ctypes.c_int, I32, F32, P, P, P, SZ, P]
         fn.restype = ctypes.c_int
+    lib.mla_append_absorb.argtypes = [C, P, I32, I32, P, P, P, P, F32,
+                                      P, P, P, P, P, ctypes.c_int, I32, F32, P, P, P, SZ, P]
+    lib.mla_append_absorb.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -160,6 +164,28 @@ def mla_append(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: t
     _check(lib.mla_append(st, _ptr(h), n_tok, d_model, _ptr(w_dkv), _ptr(w_kr),
                           dtype_code(h.dtype), _ptr(tok_seq), _ptr(tok_pos),
                           float(rope_base), _stream(stream)), "mla_append")
+
+
+def mla_append_absorb(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor,
+                      w_kr: torch.Tensor, tok_seq: torch.Tensor, tok_pos: torch.Tensor,
+                      rope_base: float, seq_len: torch.Tensor, q_nope: torch.Tensor,
+                      q_pe: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                      softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
+                      workspace: torch.Tensor, stream=None) -> None:
+    """mla_append then mla_decode_absorb, in one launch where it applies (see libmla.h)."""
+    if tok_seq.dtype != torch.int32 or tok_pos.dtype != torch.int32 or seq_len.dtype != torch.int32:
+        raise TypeError("tok_seq, tok_pos and seq_len must be int32")
+    if lse is not None and lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    n_tok, d_model = h.shape
+    B, H, _ = q_nope.shape
+    st = ctypes.byref(cache.struct())
+    _check(lib.mla_append_absorb(st, _ptr(h), n_tok, d_model, _ptr(w_dkv), _ptr(w_kr),
+                                 _ptr(tok_seq), _ptr(tok_pos), float(rope_base), _ptr(seq_len),
+                                 _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+                                 dtype_code(q_nope.dtype), H, float(softmax_scale), _ptr(out),
+                                 _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "mla_append_absorb")
 
 
 def mla_decode_workspace_size(num_seqs: int, n_heads: int, cache_dtype: int,
@@ -269,3 +295,34 @@ class PreparedAppend:
 
     def __call__(self) -> None:
         _check(lib.mla_append(*self._args), "mla_append")
+
+
+class PreparedAppendAbsorb:
+    """mla_append_absorb with the arguments marshalled once (see PreparedDecode);
+    follow it with PreparedDecode.attend() and .combine() on the same decode
+    arguments to complete the step."""
+
+    def __init__(self, cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor,
+                 w_kr: torch.Tensor, tok_seq: torch.Tensor, tok_pos: torch.Tensor,
+                 rope_base: float, seq_len: torch.Tensor, q_nope: torch.Tensor,
+                 q_pe: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                 softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
+                 workspace: torch.Tensor, stream=None):
+        if (tok_seq.dtype != torch.int32 or tok_pos.dtype != torch.int32
+                or seq_len.dtype != torch.int32):
+            raise TypeError("tok_seq, tok_pos and seq_len must be int32")
+        if lse is not None and lse.dtype != torch.float32:
+            raise TypeError("lse must be float32")
+        n_tok, d_model = h.shape
+        B, H, _ = q_nope.shape
+        self._keep = (cache, h, w_dkv, w_kr, tok_seq, tok_pos, seq_len, q_nope, q_pe, w_uk, w_uv,
+                      out, lse, workspace)
+        self._st = cache.struct()
+        self._args = (ctypes.byref(self._st), _ptr(h), n_tok, d_model, _ptr(w_dkv), _ptr(w_kr),
+                      _ptr(tok_seq), _ptr(tok_pos), float(rope_base), _ptr(seq_len),
+                      _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+                      dtype_code(q_nope.dtype), H, float(softmax_scale), _ptr(out), _ptr(lse),
+                      _ptr(workspace), workspace.numel(), _stream(stream))
+
+    def __call__(self) -> None:
+        _check(lib.mla_append_absorb(*self._args), "mla_append_absorb")

@@ -108,20 +108,22 @@ const char* mla_status_string(mla_status_t s) {
   return "unknown status";
 }
 
-mla_status_t mla_append(const mla_cache_t* cache, const void* h, int32_t n_tok, int32_t d_model,
-                        const void* w_dkv, const void* w_kr, mla_dtype_t act_dtype,
-                        const int32_t* tok_seq, const int32_t* tok_pos, float rope_base,
-                        void* stream) {
+}  // extern "C"
+
+// Validate mla_append's arguments and fill `a` (n_tok == 0 is valid and
+// leaves nothing to launch).
+static mla_status_t append_args(const mla_cache_t* cache, const void* h, int32_t n_tok,
+                                int32_t d_model, const void* w_dkv, const void* w_kr,
+                                mla_dtype_t act_dtype, const int32_t* tok_seq,
+                                const int32_t* tok_pos, float rope_base, AppendArgs& a) {
   mla_status_t st = check_cache(cache);
   if (st != MLA_OK) return st;
   if (!valid_dtype(act_dtype)) return MLA_ERR_INVALID_ARGUMENT;
   if (n_tok < 0 || d_model <= 0 || d_model % 64 != 0) return MLA_ERR_INVALID_ARGUMENT;
   if (!(rope_base > 0.f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARGUMENT;
   if (!supported_pair(cache->dtype, act_dtype)) return MLA_ERR_UNSUPPORTED;
-  if (n_tok == 0) return MLA_OK;
-  if (!h || !w_dkv || !w_kr || !tok_seq || !tok_pos) return MLA_ERR_INVALID_ARGUMENT;
-
-  AppendArgs a{};
+  if (n_tok > 0 && (!h || !w_dkv || !w_kr || !tok_seq || !tok_pos)) return MLA_ERR_INVALID_ARGUMENT;
+  a = AppendArgs{};
   a.rows = cache->rows;
   a.row_scale = cache->row_scale;
   a.seq_start = cache->seq_start;
@@ -136,6 +138,19 @@ mla_status_t mla_append(const mla_cache_t* cache, const void* h, int32_t n_tok, 
   a.d_model = d_model;
   for (int i = 0; i < MLA_D_R / 2; ++i)
     a.inv_freq[i] = pow((double)rope_base, -2.0 * i / (double)MLA_D_R);
+  return MLA_OK;
+}
+
+extern "C" {
+
+mla_status_t mla_append(const mla_cache_t* cache, const void* h, int32_t n_tok, int32_t d_model,
+                        const void* w_dkv, const void* w_kr, mla_dtype_t act_dtype,
+                        const int32_t* tok_seq, const int32_t* tok_pos, float rope_base,
+                        void* stream) {
+  AppendArgs a;
+  const mla_status_t st = append_args(cache, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq,
+                                      tok_pos, rope_base, a);
+  if (st != MLA_OK || n_tok == 0) return st;
   hipError_t e = launch_append(cache_type(cache->dtype), a, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -151,11 +166,14 @@ mla_status_t mla_decode_workspace_size(int32_t num_seqs, int32_t n_heads, mla_dt
   return MLA_OK;
 }
 
-static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len,
+}  // extern "C"
+
+// Validate mla_decode's arguments and fill `a` and the launch plan.
+static mla_status_t decode_args(const mla_cache_t* cache, const int32_t* seq_len,
                                 const void* q_nope, const void* q_pe, const void* w_uk,
                                 const void* w_uv, mla_dtype_t act_dtype, int32_t n_heads,
                                 float softmax_scale, void* out, float* lse, void* workspace,
-                                size_t workspace_bytes, void* stream, int stage) {
+                                size_t workspace_bytes, DecodeArgs& a, DecodePlan& plan) {
   mla_status_t st = check_cache(cache);
   if (st != MLA_OK) return st;
   if (!valid_dtype(act_dtype)) return MLA_ERR_INVALID_ARGUMENT;
@@ -172,7 +190,7 @@ static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len
   if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
   char* ws = (char*)workspace;
-  DecodeArgs a{};
+  a = DecodeArgs{};
   a.rows = cache->rows;
   a.row_scale = cache->row_scale;
   a.seq_start = cache->seq_start;
@@ -196,8 +214,21 @@ static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len
   a.q_lat = ws + wl.q_lat;
   a.part_o = (void*)(ws + wl.part_o);
   a.part_ml = (float*)(ws + wl.part_ml);
-  const DecodePlan plan = make_plan(ct, B, n_heads);
-  hipError_t e = launch_decode(ct, plan, a, (hipStream_t)stream, stage);
+  plan = make_plan(ct, B, n_heads);
+  return MLA_OK;
+}
+
+static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len,
+                                const void* q_nope, const void* q_pe, const void* w_uk,
+                                const void* w_uv, mla_dtype_t act_dtype, int32_t n_heads,
+                                float softmax_scale, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream, int stage) {
+  DecodeArgs a;
+  DecodePlan plan;
+  const mla_status_t st = decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads,
+                                      softmax_scale, out, lse, workspace, workspace_bytes, a, plan);
+  if (st != MLA_OK) return st;
+  hipError_t e = launch_decode(cache_type(cache->dtype), plan, a, (hipStream_t)stream, stage);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -210,9 +241,38 @@ static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len
                        softmax_scale, out, lse, workspace, workspace_bytes, stream, STAGE); \
   }
 
+extern "C" {
+
 MLA_DECODE_ENTRY(mla_decode, 0)
 MLA_DECODE_ENTRY(mla_decode_absorb, 1)
 MLA_DECODE_ENTRY(mla_decode_attend, 2)
 MLA_DECODE_ENTRY(mla_decode_combine, 3)
+
+mla_status_t mla_append_absorb(const mla_cache_t* cache, const void* h, int32_t n_tok,
+                               int32_t d_model, const void* w_dkv, const void* w_kr,
+                               const int32_t* tok_seq, const int32_t* tok_pos, float rope_base,
+                               const int32_t* seq_len, const void* q_nope, const void* q_pe,
+                               const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
+                               int32_t n_heads, float softmax_scale, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  AppendArgs aa;
+  mla_status_t st = append_args(cache, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq, tok_pos,
+                                rope_base, aa);
+  if (st != MLA_OK) return st;
+  DecodeArgs da;
+  DecodePlan plan;
+  st = decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads, softmax_scale, out,
+                   lse, workspace, workspace_bytes, da, plan);
+  if (st != MLA_OK) return st;
+  const int ct = cache_type(cache->dtype);
+  hipError_t e;
+  if (n_tok > 0 && append_absorb_fits(ct, aa, da)) {
+    e = launch_append_absorb(aa, plan, da, (hipStream_t)stream);
+  } else {
+    e = n_tok > 0 ? launch_append(ct, aa, (hipStream_t)stream) : hipSuccess;
+    if (e == hipSuccess) e = launch_decode(ct, plan, da, (hipStream_t)stream, 1);
+  }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
 
 }  // extern "C"

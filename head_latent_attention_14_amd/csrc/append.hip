@@ -9,8 +9,7 @@
 
 #include <type_traits>
 
-#include "common.h"
-#include "internal.h"
+#include "gemm_tile.h"
 
 namespace mla {
 
@@ -187,27 +186,41 @@ mla_append_kernel(AppendArgs a) {
 // memory would touch 16 rows 2*d_model bytes apart per instruction). The
 // contraction runs in stages of KC elements, two stages in LDS; rows are
 // padded by 16 bytes so the 16 rows of an operand read fall on distinct banks.
-__global__ void __launch_bounds__(256)
-mla_append_bf16_kernel(AppendArgs a) {
-  constexpr int KC = 1024;                 // contraction elements per stage
-  constexpr int RS = KC * 2 + 16;          // padded LDS row (bytes)
-  constexpr int OPND = 16 * RS;            // 16 rows of one operand
-  constexpr int STAGE = 2 * OPND;          // weight rows, then hidden rows
-  constexpr int NST = 2;
-  __shared__ __attribute__((aligned(1024))) char stg[NST * STAGE];
-  __shared__ float red[4][16][17];         // [wave][column][token]
-  __shared__ float rowt[16][17];           // [token][column]
-  __shared__ float2 rot[16][8];            // (cos, sin) per token and pair (RoPE groups)
-  __shared__ int64_t trow[16];
-  __shared__ int tpos[16];
+struct AppendBf16Lds {
+  static constexpr int KC = 1024;          // contraction elements per stage
+  static constexpr int RS = KC * 2 + 16;   // padded LDS row (bytes)
+  static constexpr int OPND = 16 * RS;     // 16 rows of one operand
+  static constexpr int STAGE = 2 * OPND;   // weight rows, then hidden rows
+  static constexpr int NST = 2;
+  char stg[NST * STAGE];
+  float red[4][16][17];                    // [wave][column][token]
+  float rowt[16][17];                      // [token][column]
+  float2 rot[16][8];                       // (cos, sin) per token and pair (RoPE groups)
+  int64_t trow[16];
+  int tpos[16];
+};
+
+// One (16 tokens, 16 columns) block: token block tb, column group cg.
+__device__ void append_bf16_block(const AppendArgs& a, int tb, int cg, AppendBf16Lds& L) {
+  constexpr int KC = AppendBf16Lds::KC;
+  constexpr int RS = AppendBf16Lds::RS;
+  constexpr int OPND = AppendBf16Lds::OPND;
+  constexpr int STAGE = AppendBf16Lds::STAGE;
+  constexpr int NST = AppendBf16Lds::NST;
+  char* stg = L.stg;
+  auto& red = L.red;
+  auto& rowt = L.rowt;
+  auto& rot = L.rot;
+  auto& trow = L.trow;
+  auto& tpos = L.tpos;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int g = lane >> 4;
-  const int tok0 = blockIdx.x * 16;
-  const int j0 = blockIdx.y * kColGroup;   // first output column
+  const int tok0 = tb * 16;
+  const int j0 = cg * kColGroup;           // first output column
   const int D = a.d_model;
   const int nch = (D + KC - 1) / KC;
 
@@ -310,6 +323,62 @@ mla_append_bf16_kernel(AppendArgs a) {
     if (tok0 + t < a.n_tok && trow[t] >= 0)
       ((uint16_t*)a.rows)[trow[t] * kDrow + j0 + cc] = f32_to_bf16_bits(rowt[t][cc]);
   }
+}
+
+__global__ void __launch_bounds__(256)
+mla_append_bf16_kernel(AppendArgs a) {
+  __shared__ __attribute__((aligned(1024))) AppendBf16Lds L;
+  append_bf16_block(a, blockIdx.x, blockIdx.y, L);
+}
+
+// Append and the absorb launch of the following decode in one launch (bf16):
+// neither reads what the other writes (the absorb product and the work plan
+// read queries, weights and lengths, not cache rows), so workgroup i issues
+// the loads of absorb tile i, runs append block i while they are in flight,
+// then finishes the absorb tile in the same LDS. The last workgroup builds
+// the plan. Grid: max(append blocks, absorb tiles) + 1 workgroups.
+__global__ void __launch_bounds__(256)
+mla_append_absorb_kernel(AppendArgs a, GemmParams g, int n_app, int n_abs) {
+  using G = AbsorbBf16;
+  __shared__ __attribute__((aligned(1024))) AppendBf16Lds L;
+  static_assert(G::LDS_BYTES <= (int)sizeof(AppendBf16Lds::stg), "absorb tile fits the append stages");
+  const int wg = blockIdx.x;
+  if (wg == (int)gridDim.x - 1) {
+    build_plan(g, (int64_t*)L.stg, (int)(sizeof(L.stg) / 8));
+    return;
+  }
+  const int nxb = kDc / kNT;                             // absorb tiles per (head, batch slice)
+  const bool abs = wg < n_abs;
+  const int n0 = (wg % nxb) * kNT;
+  const int h = (wg / nxb) % g.H;
+  const int b0 = (wg / nxb / g.H) * G::BT;
+  typename G::Regs rg;
+  if (abs) G::load(g, n0, h, b0, rg);
+  if (wg < n_app) {
+    const int ntb = (a.n_tok + 15) / 16;
+    append_bf16_block(a, wg % ntb, wg / ntb, L);
+    __syncthreads();                                     // append done with its stages
+  }
+  if (abs) G::run(g, n0, h, b0, rg, L.stg);
+}
+
+hipError_t launch_append_absorb(const AppendArgs& a, const DecodePlan& plan, const DecodeArgs& d,
+                                hipStream_t s) {
+  const int n_app = ((a.n_tok + 15) / 16) * kNumGroups;
+  const int n_abs = (kDc / kNT) * d.H * ((d.B + AbsorbBf16::BT - 1) / AbsorbBf16::BT);
+  const int n = (n_app > n_abs ? n_app : n_abs) + 1;
+  hipLaunchKernelGGL(mla_append_absorb_kernel, dim3(n), dim3(256), 0, s, a, absorb_params(plan, d),
+                     n_app, n_abs);
+  return hipGetLastError();
+}
+
+// Whether the fused launch applies: bf16 cache and activations, and a grid
+// that fits the CUs in one round (its LDS allows one workgroup per CU).
+bool append_absorb_fits(int cache_type, const AppendArgs& a, const DecodeArgs& d) {
+  if (cache_type != kBF16) return false;
+  const int n_app = ((a.n_tok + 15) / 16) * kNumGroups;
+  const int n_abs = (kDc / kNT) * d.H * ((d.B + AbsorbBf16::BT - 1) / AbsorbBf16::BT);
+  return (n_app > n_abs ? n_app : n_abs) + 1 <= kTargetCUs;
 }
 
 hipError_t launch_append(int ct, const AppendArgs& a, hipStream_t s) {

@@ -120,4 +120,10 @@ struct DecodeArgs {
 hipError_t launch_decode(int cache_type, const DecodePlan& plan, const DecodeArgs& a,
                          hipStream_t s, int stage);
 
+// Append and the absorb stage of the following decode in one launch (bf16
+// cache, and a grid that fits the CUs at once: append_absorb_fits).
+bool append_absorb_fits(int cache_type, const AppendArgs& a, const DecodeArgs& d);
+hipError_t launch_append_absorb(const AppendArgs& a, const DecodePlan& plan, const DecodeArgs& d,
+                                hipStream_t s);
+
 }  // namespace mla

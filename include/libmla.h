@@ -167,11 +167,13 @@ mla_status_t mla_decode(const mla_cache_t* cache, const int32_t* seq_len,
  * absorb, attend and combine in this order on one stream with the same
  * workspace equals one mla_decode call. The workspace carries the
  * intermediate results between the stages:
- *   absorb  -- q_lat = W_UK[h]^T q_nope for every (b, h), and the prefix sums
- *              of the clamped lengths that partition the work (discosf
- *              explainer, "long-context bottleneck": W_UK folds into the query);
- *   attend  -- streams the latent rows once and writes, per token range, the
- *              running max, sum and unnormalised sum_t p_t c_t (split-K);
+ *   absorb  -- q_lat = W_UK[h]^T q_nope for every (b, h), and the work plan
+ *              (tile counts of the clamped lengths, each worker's tile range)
+ *              that partitions the attention (discosf explainer, "long-context
+ *              bottleneck": W_UK folds into the query);
+ *   attend  -- streams the latent rows once and writes, per tile range and
+ *              sequence, the running max, sum and normalised sum_t p_t c_t / l
+ *              (split-K);
  *   combine -- merges the ranges of each sequence and applies W_UV (W_UV folds
  *              into the output), writing out and lse.
  */
@@ -193,6 +195,29 @@ mla_status_t mla_decode_combine(const mla_cache_t* cache, const int32_t* seq_len
                                 int32_t n_heads, float softmax_scale,
                                 void* out, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_append_absorb -- mla_append followed by mla_decode_absorb, in one launch
+ * where it applies (BF16 cache and activations, and a grid that fits the GPU
+ * at once); otherwise the two run one after the other. The absorb product and
+ * the work plan read queries, W_UK and lengths, never cache rows, so the two
+ * do not depend on each other. Arguments: mla_append's (cache, h ... rope_base)
+ * then mla_decode's (seq_len ... stream), with the same meaning, ownership and
+ * rules; both argument sets are validated before anything runs. Calling
+ * mla_decode_attend and mla_decode_combine afterwards with the same decode
+ * arguments and workspace completes the decode step: the result equals
+ * mla_append then mla_decode. For callers that run a decode step right after
+ * appending its token.
+ */
+mla_status_t mla_append_absorb(const mla_cache_t* cache,
+                               const void* h, int32_t n_tok, int32_t d_model,
+                               const void* w_dkv, const void* w_kr,
+                               const int32_t* tok_seq, const int32_t* tok_pos, float rope_base,
+                               const int32_t* seq_len, const void* q_nope, const void* q_pe,
+                               const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
+                               int32_t n_heads, float softmax_scale,
+                               void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static English text for a status code (host). */
 const char* mla_status_string(mla_status_t status);

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"mla_append", "mla_decode_workspace_size", "mla_decode",
                           "mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
-                          "mla_status_string", "mla_abi_version"}
+                          "mla_append_absorb", "mla_status_string", "mla_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert getattr(lib, n) is not None
@@ -144,3 +144,33 @@ def test_append_validation():
     assert _append(_cache(dtype=E.MLA_DTYPE_FP8_E4M3)) == E.MLA_ERR_INVALID_ARGUMENT
     # zero tokens: a no-op that launches nothing
     assert _append(_cache(), n_tok=0) == E.MLA_OK
+
+
+def _append_absorb(cache, n_tok=4, d_model=128, act=mla.MLA_DTYPE_BF16, base=10000.0, H=16,
+                   scale=0.07, ws=FAKE, ws_bytes=1 << 40, null=None):
+    args = dict(h=FAKE, w_dkv=FAKE, w_kr=FAKE, tok_seq=FAKE, tok_pos=FAKE, seq_len=FAKE,
+                q_nope=FAKE, q_pe=FAKE, w_uk=FAKE, w_uv=FAKE, out=FAKE)
+    if null:
+        args[null] = None
+    c = ctypes.byref(cache) if cache is not None else None
+    return lib.mla_append_absorb(c, args["h"], n_tok, d_model, args["w_dkv"], args["w_kr"],
+                                 args["tok_seq"], args["tok_pos"], base, args["seq_len"],
+                                 args["q_nope"], args["q_pe"], args["w_uk"], args["w_uv"], act,
+                                 H, scale, args["out"], None, ws, ws_bytes, None)
+
+
+def test_append_absorb_validation():
+    # both argument sets are checked before anything is launched
+    E = mla
+    assert _append_absorb(None) == E.MLA_ERR_INVALID_ARGUMENT
+    for null in ["h", "w_dkv", "w_kr", "tok_seq", "tok_pos", "seq_len", "q_nope", "q_pe",
+                 "w_uk", "w_uv", "out"]:
+        assert _append_absorb(_cache(), null=null) == E.MLA_ERR_INVALID_ARGUMENT, null
+    assert _append_absorb(_cache(), d_model=100) == E.MLA_ERR_INVALID_ARGUMENT
+    assert _append_absorb(_cache(), base=0.0) == E.MLA_ERR_INVALID_ARGUMENT
+    assert _append_absorb(_cache(), scale=0.0) == E.MLA_ERR_INVALID_ARGUMENT
+    assert _append_absorb(_cache(), H=24) == E.MLA_ERR_UNSUPPORTED
+    assert _append_absorb(_cache(), act=E.MLA_DTYPE_F32) == E.MLA_ERR_UNSUPPORTED
+    assert _append_absorb(_cache(), ws=FAKE + 64) == E.MLA_ERR_INVALID_ARGUMENT
+    need = mla.mla_decode_workspace_size(4, 16, E.MLA_DTYPE_BF16, E.MLA_DTYPE_BF16)
+    assert _append_absorb(_cache(), ws_bytes=need - 1) == E.MLA_ERR_WORKSPACE_TOO_SMALL

@@ -198,3 +198,56 @@ def test_empty_sequences_between_others(name, H):
     # every non-empty sequence on its own meets the bound too
     for i, b in enumerate(full):
         assert rel_l2(got[i * H:(i + 1) * H], ro[i * H:(i + 1) * H]) <= TOL[wl.cache], b
+
+
+def _fused_step(dp, poison=True):
+    import head_latent_attention_14_amd as mla
+    if poison:
+        dp.out.fill_(float("nan"))
+        dp.lse.fill_(float("nan"))
+        dp.ws.fill_(0xFF)
+    scale = 1.0 / math.sqrt(192.0)
+    mla.mla_append_absorb(dp.cache, dp.h, dp.w_dkv, dp.w_kr, dp.tok_seq, dp.tok_pos,
+                          dp.p.wl.rope_base, dp.seq_len, dp.q_nope, dp.q_pe, dp.w_uk, dp.w_uv,
+                          scale, dp.out, dp.lse, dp.ws)
+    mla.mla_decode_attend(dp.cache, dp.seq_len, dp.q_nope, dp.q_pe, dp.w_uk, dp.w_uv, scale,
+                          dp.out, dp.lse, dp.ws)
+    mla.mla_decode_combine(dp.cache, dp.seq_len, dp.q_nope, dp.q_pe, dp.w_uk, dp.w_uv, scale,
+                           dp.out, dp.lse, dp.ws)
+    torch.cuda.synchronize()
+    return (dp.out.double().cpu().numpy(), dp.lse.double().cpu().numpy(),
+            dp.cache.rows.cpu().view(torch.int16).numpy().copy())
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_append_absorb_equals_append_then_decode(full):
+    # one launch for append + absorb (bf16) gives bit-identical rows and outputs
+    wl = W.WORKLOADS["v2lite_bf16"]
+    p = W.make_problem(wl) if full else _small("v2lite_bf16")
+    log(f"[append+absorb] full={full} B={p.q_nope.shape[0]}")
+    a = DeviceProblem(p)
+    o_ref, l_ref = a.step(poison=True)
+    rows_ref = a.cache.rows.cpu().view(torch.int16).numpy().copy()
+    b = DeviceProblem(p)
+    o, l, rows = _fused_step(b)
+    assert np.array_equal(rows, rows_ref)
+    assert np.array_equal(o, o_ref)
+    assert np.array_equal(np.isnan(l), np.isnan(l_ref)) and np.array_equal(l[~np.isnan(l)],
+                                                                            l_ref[~np.isnan(l_ref)])
+    # and against the oracle (append applied)
+    ro, _ = OracleView(p).decode([(0, 0), (p.q_nope.shape[0] - 1, 15)])
+    assert rel_l2(np.stack([o[0, 0], o[-1, 15]]), ro) <= TOL["bf16"]
+
+
+def test_append_absorb_two_launch_path():
+    # a grid too large for one round of CUs (many heads, few tokens) takes
+    # the two-launch path; results still match append then decode bitwise
+    wl = W.WORKLOADS["v2lite_bf16"]
+    p = W.make_problem(wl, B=40, lengths=np.arange(40) * 7 + 1, H=64)
+    a = DeviceProblem(p)
+    o_ref, _ = a.step(poison=True)
+    rows_ref = a.cache.rows.cpu().view(torch.int16).numpy().copy()
+    b = DeviceProblem(p)
+    o, _, rows = _fused_step(b)
+    assert np.array_equal(rows, rows_ref)
+    assert np.array_equal(o, o_ref)
