@@ -38,7 +38,7 @@ mla_headgemm_kernel(GemmParams p) {
 //   lse = (M + log2 l) ln 2.
 // Lane l returns dims 8l..8l+7 of o_lat in `acc`. A sequence of length 0
 // gets o_lat = 0 and lse = -inf.
-template <int AT>
+template <int AT, int RU = 8>
 __device__ __forceinline__ float merge_row(const GemmParams& p, int b, int h, int lane, float* acc) {
   const int H = p.H;
   const int64_t wf = ld_const(p.wfirst, b), wl = ld_const(p.wlast, b);
@@ -50,7 +50,6 @@ __device__ __forceinline__ float merge_row(const GemmParams& p, int b, int h, in
     // and wl, so all its loads are in flight together; a slot counts only if
     // its worker's range is non-empty (an empty worker writes nothing),
     // which is applied by selection once the data is back
-    constexpr int RU = 8;
     for (int64_t w0 = wf; w0 <= wl; w0 += RU) {
       float m[RU], l[RU];
       int64_t st0[RU], st1[RU];
@@ -131,6 +130,73 @@ mla_merge_kernel(GemmParams p) {
   }
 }
 
+// Merge and W_UV in one launch (bf16), for batches whose rows have few
+// partial slots: workgroup (64 output columns, head h, 16 batch rows) with
+// sixteen waves. Each wave merges one row (all its slot loads in one round)
+// while the weight slice is in flight, writes the merged row in bf16 to LDS
+// (the value the separate merge stores), and four waves then multiply. The
+// two column workgroups of a (head, rows) both merge the rows; the first
+// writes lse.
+__global__ void __launch_bounds__(1024)
+mla_combine_kernel(GemmParams p) {
+  using G = HeadGemm<kBF16, kDc, kDv, 1, kDc>;
+  constexpr int TPW = 1024;                            // threads
+  constexpr int WP = kDc * kNT * 2 / 16;               // 16-byte pieces of the weight slice
+  __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+  char* w_lds = lds;
+  char* x_lds = lds + G::W_BYTES;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n0 = blockIdx.x * kNT, h = blockIdx.y, b0 = blockIdx.z * 16;
+  u32x4 wv[WP / TPW];
+#pragma unroll
+  for (int k = 0; k < WP / TPW; ++k) {
+    const int i = tid + TPW * k;
+    const int r = i / G::WPR, c = i - r * G::WPR;
+    wv[k] = *(const u32x4*)((const char*)p.w + (((int64_t)h * kDc + r) * kDv + n0) * 2 + c * 16);
+  }
+  {
+    const int b = b0 + wave;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (b < p.B) {
+      const float lse = merge_row<kBF16, 6>(p, b, h, lane, acc);
+      if (p.lse && blockIdx.x == 0 && lane == 0) p.lse[(int64_t)b * p.H + h] = lse;
+    }
+    *(bf16x8*)(x_lds + wave * G::XROW + 16 * lane) = pack_bf16x8(acc);
+  }
+#pragma unroll
+  for (int k = 0; k < WP / TPW; ++k) {
+    const int i = tid + TPW * k;
+    const int r = i / G::WPR, c = i - r * G::WPR;
+    *(u32x4*)(w_lds + r * G::WROW + c * 16) = wv[k];
+  }
+  __syncthreads();
+  if (wave >= 4) return;
+  const int l16 = lane & 15, g = lane >> 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < kDc; kk += 32) {
+    // A = W^T block: lane (n, g) gets W[kk + 8g + 0..7][16*wave + n]
+    const int rs = kk + 8 * g + (l16 >> 2);
+    const int cb = (16 * wave + 4 * (l16 & 3)) * 2;
+    const s16x4 lo = lds_read_tr16(w_lds, rs * G::WROW + cb);
+    const s16x4 hi = lds_read_tr16(w_lds, (rs + 4) * G::WROW + cb);
+    const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const bf16x8 bv = lds_read_b128(x_lds, l16 * G::XROW + (kk + 8 * g) * 2);
+    acc = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a8), bv, acc);
+  }
+  // lane holds Y[b0 + l16][n0 + 16*wave + 4g + r]
+  const int b = b0 + l16;
+  if (b < p.B) {
+    const int n = n0 + 16 * wave + 4 * g;
+    uint2 v;
+    v.x = pack_bf16x2(acc[0], acc[1]);
+    v.y = pack_bf16x2(acc[2], acc[3]);
+    *(uint2*)((char*)p.y + (((int64_t)b * p.H + h) * kDv + n) * 2) = v;
+  }
+}
+
 template <int AT, int KD, int ND, int NBT, int KC>
 static hipError_t launch_gemm_t(const GemmParams& prm, hipStream_t s) {
   constexpr int BT = 16 * NBT;
@@ -159,8 +225,27 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
     if (e != hipSuccess) return e;
   }
   if (stage != 0 && stage != 3) return e;
-  // 3. merge the partials (into the q_lat buffer, free once attention is
-  //    done) and apply W_UV
+  // 3. merge the partials and apply W_UV: one fused launch (bf16) when the
+  //    sequences have few slots each (one merge round per row, on average)
+  //    and its workgroups fit the CUs at once, else the merge (into the q_lat
+  //    buffer, free once attention is done) and the projection
+  const int64_t comb_wgs = (int64_t)(kDv / kNT) * a.H * ((a.B + 15) / 16);
+  if (!f32 && plan.nslot <= 6 * (int64_t)a.B && comb_wgs <= kTargetCUs) {
+    GemmParams c{};
+    c.B = a.B;
+    c.H = a.H;
+    c.starts = a.starts;
+    c.wfirst = a.wfirst;
+    c.wlast = a.wlast;
+    c.part_o = a.part_o;
+    c.part_ml = a.part_ml;
+    c.lse = a.lse;
+    c.w = a.w_uv;
+    c.y = a.out;
+    hipLaunchKernelGGL(mla_combine_kernel, dim3(kDv / kNT, a.H, (a.B + 15) / 16), dim3(1024), 0, s,
+                       c);
+    return hipGetLastError();
+  }
   GemmParams m{};
   m.B = a.B;
   m.H = a.H;
