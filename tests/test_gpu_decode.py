@@ -251,3 +251,29 @@ def test_append_absorb_two_launch_path():
     o, _, rows = _fused_step(b)
     assert np.array_equal(rows, rows_ref)
     assert np.array_equal(o, o_ref)
+
+
+def test_combine_fused_launch_all_outputs():
+    # 64 short sequences at 16 heads: few slots per sequence, so the merge and
+    # W_UV run as one launch; every output and lse against the oracle, with
+    # two empty sequences among them
+    rng = np.random.default_rng(64)
+    lengths = rng.integers(1, 120, size=64)
+    p = W.make_problem(W.WORKLOADS["v2lite_bf16"], seed=64, B=64, lengths=lengths)
+    dp = DeviceProblem(p)
+    lens = lengths.copy()
+    lens[[5, 40]] = 0
+    dp.seq_len.copy_(torch.from_numpy(lens.astype(np.int32)))
+    dp.decode(poison=True)
+    torch.cuda.synchronize()
+    o = dp.out.double().cpu().numpy()
+    lse = dp.lse.double().cpu().numpy()
+    assert np.all(o[[5, 40]] == 0) and np.all(np.isneginf(lse[[5, 40]]))
+    p2 = W.make_problem(W.WORKLOADS["v2lite_bf16"], seed=64, B=64, lengths=lengths)
+    p2.seq_len = lens.astype(np.int32)
+    full = [b for b in range(64) if lens[b] > 0]
+    ro, rl = OracleView(p2, apply_append=False).decode([(b, h) for b in full for h in range(16)])
+    got = np.stack([o[b, h] for b in full for h in range(16)])
+    assert rel_l2(got, ro) <= TOL["bf16"]
+    gl = np.array([lse[b, h] for b in full for h in range(16)])
+    assert np.abs(gl - rl).max() <= 50 * TOL["bf16"]
