@@ -13,20 +13,22 @@
 
 namespace mla {
 
-// One head-GEMM tile per workgroup: head blockIdx.y, 64 output columns
-// (blockIdx.x), 16*NBT batch rows (blockIdx.z). The absorb launch has one more
-// z slice whose first workgroup builds the plan.
+// One head-GEMM tile per workgroup, numbered (64-column block, head, batch
+// slice of 16*NBT rows) with the column block fastest. The absorb launch has
+// one more workgroup, the last, which builds the plan.
 template <int AT, int KD, int ND, int NBT, int KC>
 __global__ void __launch_bounds__(256)
 mla_headgemm_kernel(GemmParams p) {
   using G = HeadGemm<AT, KD, ND, NBT, KC>;
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
-  if (p.seq_len && blockIdx.z == gridDim.z - 1) {       // the extra plan workgroup
-    if (blockIdx.x == 0 && blockIdx.y == 0) build_plan(p, (int64_t*)lds, (int)(G::W_BYTES / 8));
+  const int i = blockIdx.x;
+  if (p.seq_len && i == (int)gridDim.x - 1) {           // the extra plan workgroup
+    build_plan(p, (int64_t*)lds, (int)(G::W_BYTES / 8));
     return;
   }
+  constexpr int NXB = ND / kNT;
   typename G::Regs rg;
-  const int n0 = blockIdx.x * kNT, h = blockIdx.y, b0 = blockIdx.z * G::BT;
+  const int n0 = (i % NXB) * kNT, h = (i / NXB) % p.H, b0 = (i / NXB / p.H) * G::BT;
   G::load(p, n0, h, b0, rg);
   G::run(p, n0, h, b0, rg, lds);
 }
@@ -200,9 +202,10 @@ mla_combine_kernel(GemmParams p) {
 template <int AT, int KD, int ND, int NBT, int KC>
 static hipError_t launch_gemm_t(const GemmParams& prm, hipStream_t s) {
   constexpr int BT = 16 * NBT;
-  // absorb (seq_len given) gets one more z slice whose first block builds the plan
-  dim3 grid(ND / kNT, prm.H, (prm.B + BT - 1) / BT + (prm.seq_len ? 1 : 0));
-  hipLaunchKernelGGL((mla_headgemm_kernel<AT, KD, ND, NBT, KC>), grid, dim3(256), 0, s, prm);
+  // absorb (seq_len given) gets one more workgroup, which builds the plan
+  const int64_t n = (int64_t)(ND / kNT) * prm.H * ((prm.B + BT - 1) / BT) + (prm.seq_len ? 1 : 0);
+  hipLaunchKernelGGL((mla_headgemm_kernel<AT, KD, ND, NBT, KC>), dim3((unsigned)n), dim3(256), 0, s,
+                     prm);
   return hipGetLastError();
 }
 
@@ -215,8 +218,10 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
   // 1. absorb W_UK into the query; build the work plan
   if (stage == 0 || stage == 1) {
     const GemmParams g = absorb_params(plan, a);
+    // bf16: 64 batch rows per workgroup, 32 for batches of at most 32
     e = f32 ? launch_gemm_t<kF32, kDnope, kDc, 1, kDnope>(g, s)
-            : launch_gemm_t<kBF16, kDnope, kDc, 4, kDnope>(g, s);
+            : (a.B <= 32 ? launch_gemm_t<kBF16, kDnope, kDc, 2, kDnope>(g, s)
+                         : launch_gemm_t<kBF16, kDnope, kDc, 4, kDnope>(g, s));
     if (e != hipSuccess) return e;
   }
   // 2. attention over the latent rows -> split partials

@@ -58,7 +58,11 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
   const int B = p.B;
   const int64_t W = p.workers;
   const int TL = p.tile;
-  const bool in_lds = B + 1 <= lds_n;
+  // LDS (when it fits): P[0..B], then each sequence's first cache row and
+  // clamped length, so the worker records need no second trip to memory
+  const bool in_lds = 3 * (int64_t)B + 1 <= lds_n;
+  int64_t* lrow = lds + B + 1;
+  int64_t* llen = lds + 2 * B + 1;
   if (tid < 64) {
     int64_t carry = 0;
     if (lane == 0 && in_lds) lds[0] = 0;
@@ -89,7 +93,11 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
         si.next = B;                                     // set below
         si.pad[0] = si.pad[1] = 0;
         p.seqinfo[b] = si;
-        if (in_lds) lds[b + 1] = carry + v;
+        if (in_lds) {
+          lds[b + 1] = carry + v;
+          lrow[b] = si.row0;
+          llen[b] = L;
+        }
       }
       const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffff), 63);
       const int hi = __builtin_amdgcn_readlane((int)(v >> 32), 63);
@@ -106,6 +114,16 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
     return in_lds ? lds[b] : (int64_t)gtile0[(int64_t)b * (sizeof(SeqInfo) / 4)];
   };
   const int64_t NT = in_lds ? lds[B] : lds[0];
+  // the sequence holding tile t < NT: the largest b in [lo, B) with P_b <= t
+  auto owner = [&](int lo, int64_t t) {
+    int hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (prefix(mid) <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
   for (int64_t w = tid; w <= W; w += 256) p.starts[w] = (w * NT) / W;
   if (NT == 0) {
     for (int64_t w = tid; w < W; w += 256) p.wseq[w] = 0;
@@ -121,24 +139,15 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
       p.wfirst[b] = 0;
       p.wlast[b] = -1;
     }
-    // next sequence with tiles: the largest b' > b with P_b' <= P_(b+1), which
-    // owns tile P_(b+1) (none when P_(b+1) = NT)
-    int nx = B;
-    if (P1 < NT) {
-      int lo = b + 1, hi = B - 1;                        // P_lo <= P1 holds (P_(b+1) = P1)
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (prefix(mid) <= P1) lo = mid;
-        else hi = mid - 1;
-      }
-      nx = lo;
-    }
-    p.seqinfo[b].next = nx;
+    // next sequence with tiles: the one owning tile P_(b+1) (none when it is NT)
+    p.seqinfo[b].next = (P1 < NT) ? owner(b + 1, P1) : B;
   }
-  // each worker's starting point, from the records above
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (!in_lds) {                                         // the records come back from memory
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  // each worker's starting point
   for (int64_t w = tid; w < W; w += 256) {
     const int64_t r_lo = (w * NT) / W, r_hi = ((w + 1) * NT) / W;
     WorkerInfo wi;
@@ -150,15 +159,31 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
       wi.t = wi.t_end = 0;
       wi.next = B;
     } else {
-      const int b = ((const volatile int32_t*)p.wseq)[w];
-      const volatile SeqInfo* si = p.seqinfo + b;
-      const int64_t t0 = si->tile0, t1 = si->tile1, len = si->len;
+      int b;
+      int64_t t0, t1, len, row0;
+      int nx;
+      if (in_lds) {
+        b = owner(0, r_lo);
+        t0 = lds[b];
+        t1 = lds[b + 1];
+        len = llen[b];
+        row0 = lrow[b];
+        nx = (t1 < NT) ? owner(b + 1, t1) : B;
+      } else {
+        b = ((const volatile int32_t*)p.wseq)[w];
+        const volatile SeqInfo* si = p.seqinfo + b;
+        t0 = si->tile0;
+        t1 = si->tile1;
+        len = si->len;
+        row0 = si->row0;
+        nx = si->next;
+      }
       const int64_t se = t1 < r_hi ? t1 : r_hi;
       wi.b = b;
       wi.t = (int32_t)((r_lo - t0) * TL);
       wi.t_end = (int32_t)((se - t0) * TL < len ? (se - t0) * TL : len);
-      wi.row0 = si->row0 + wi.t;
-      wi.next = si->next;
+      wi.row0 = row0 + wi.t;
+      wi.next = nx;
     }
     p.winfo[w] = wi;
   }

@@ -120,7 +120,7 @@ def test_zero_and_clamped_lengths():
     assert rel_l2(np.concatenate([o[1], o[2]]), ro) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("B", [1, 17, 300])
+@pytest.mark.parametrize("B", [1, 17, 300, 1000])
 def test_many_and_few_sequences(B):
     rng = np.random.default_rng(B)
     lengths = rng.integers(1, 200, size=B)
