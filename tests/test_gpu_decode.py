@@ -277,3 +277,47 @@ def test_combine_fused_launch_all_outputs():
     assert rel_l2(got, ro) <= TOL["bf16"]
     gl = np.array([lse[b, h] for b in full for h in range(16)])
     assert np.abs(gl - rl).max() <= 50 * TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["fp8_cache", "tiny_fp32"])
+def test_append_absorb_other_caches(name):
+    # fp8 and f32 caches take the two-launch path of mla_append_absorb; rows,
+    # row scales and outputs equal mla_append then mla_decode bitwise
+    import head_latent_attention_14_amd as mla
+    wl = W.WORKLOADS[name]
+    lengths = np.array([3, 40, 97])
+    p = W.make_problem(wl, seed=7, B=3, lengths=lengths)
+    rng = np.random.default_rng(7)
+    act = p.q_nope.dtype
+    dm = 256
+    h = torch.from_numpy(rng.standard_normal((3, dm)).astype(np.float32)).to(act).cuda()
+    wd = torch.from_numpy((rng.standard_normal((512, dm)) / 16).astype(np.float32)).to(act).cuda()
+    wk = torch.from_numpy((rng.standard_normal((64, dm)) / 16).astype(np.float32)).to(act).cuda()
+    ts = torch.arange(3, dtype=torch.int32).cuda()
+    tp = torch.from_numpy((lengths - 1).astype(np.int32)).cuda()
+    scale = 1.0 / math.sqrt(192.0)
+    res = []
+    for fused in (False, True):
+        dp = DeviceProblem(p)
+        dp.out.fill_(float("nan"))
+        dp.ws.fill_(0xFF)
+        args = (dp.seq_len, dp.q_nope, dp.q_pe, dp.w_uk, dp.w_uv, scale, dp.out, dp.lse, dp.ws)
+        if fused:
+            mla.mla_append_absorb(dp.cache, h, wd, wk, ts, tp, 10000.0, *args)
+            mla.mla_decode_attend(dp.cache, *args)
+            mla.mla_decode_combine(dp.cache, *args)
+        else:
+            mla.mla_append(dp.cache, h, wd, wk, ts, tp, 10000.0)
+            mla.mla_decode(dp.cache, *args)
+        torch.cuda.synchronize()
+        sc = dp.cache.row_scale.cpu().numpy().copy() if dp.cache.row_scale is not None else None
+        res.append((dp.out.double().cpu().numpy(), _bits_of(dp.cache.rows), sc))
+    (o0, r0, s0), (o1, r1, s1) = res
+    assert np.array_equal(r0, r1)
+    assert s0 is None or np.array_equal(s0, s1)
+    assert np.array_equal(o0, o1) and np.all(np.isfinite(o1))
+
+
+def _bits_of(t):
+    t = t.cpu().contiguous()
+    return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()]).numpy().copy()
