@@ -141,6 +141,35 @@ __device__ __forceinline__ void lds_tr16_x8(uint32_t addr, s16x4& r0, s16x4& r1,
       : "memory");
 }
 
+// Four transposing 8-bit LDS reads (ds_read_b64_tr_b8, gfx950), completed
+// inside the asm block like lds_tr16_x8. Within each group of 16 lanes,
+// byte q of lane j is the byte at addr(lane 2q + j/8) + j%8 (checked on
+// gfx950 with every lane pointing at its own 64-byte row).
+template <int O0, int O1, int O2, int O3>
+__device__ __forceinline__ void lds_tr8_x4(uint32_t addr, uint2& r0, uint2& r1, uint2& r2, uint2& r3) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %4 offset:%5\n"
+      "ds_read_b64_tr_b8 %1, %4 offset:%6\n"
+      "ds_read_b64_tr_b8 %2, %4 offset:%7\n"
+      "ds_read_b64_tr_b8 %3, %4 offset:%8\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(addr), "i"(O0), "i"(O1), "i"(O2), "i"(O3)
+      : "memory");
+}
+
+// Eight e4m3fn codes (bytes 0..7 of v) as eight bf16 values, in order; every
+// e4m3fn value is exact in bf16 and the unit scale leaves it unchanged.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint2 v) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+  const __bf16 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1], c0 = c[0], c1 = c[1], d0 = d[0], d1 = d[1];
+  return bf16x8{a0, a1, b0, b1, c0, c1, d0, d1};
+}
+
 // ---------------------------------------------------------------------------
 // LDS access
 // ---------------------------------------------------------------------------

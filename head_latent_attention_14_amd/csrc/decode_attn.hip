@@ -327,13 +327,13 @@ mla_attn_pair_kernel(AttnParams p) {
   constexpr int STAGE_DATA = TileCopy<CT, NW>::STAGE_DATA;
   constexpr int STAGE_BYTES = TileCopy<CT, NW>::STAGE_BYTES;
   constexpr int CPW = TileCopy<CT, NW>::CPW;
-  constexpr int CONV_BYTES = (CT == kFP8) ? TILE * kConvPad : 0;
   constexpr int X_BYTES = NW * 4096;                     // one 32x32 fp32 partial per wave
-  constexpr int TP = (CT == kFP8) ? kConvPad : RP;       // row pitch of the tile computed on
+  constexpr int TP = RP;                                 // row pitch of the staged tile
+  constexpr int EB = (CT == kFP8) ? 1 : 2;               // bytes per staged element
   static_assert(NSTAGE >= 2, "ring needs two stages");
   static_assert(Tr<CT>::kTile == TILE, "32-token tiles");
 
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + CONV_BYTES + X_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + X_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -395,11 +395,18 @@ mla_attn_pair_kernel(AttnParams p) {
     for (int nb = 0; nb < 16; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // score A operand: tile row l16 (+16 for the second token block), k-step 9*half
-  const uint32_t s_base = (uint32_t)(l16 * TP + g * 16 + half * 9 * 64);
-  // transposing value reads: source lane (g, l16) points at row 4g + l16/4,
-  // dims 256*half + 4*(l16%4) .. +3
-  const uint32_t tr_lane = (uint32_t)((4 * g + (l16 >> 2)) * TP + 2 * 256 * half + 8 * (l16 & 3));
-  char* xbuf = smem + NSTAGE * STAGE_BYTES + CONV_BYTES;
+  const uint32_t s_base = (uint32_t)(l16 * TP + g * 8 * EB + half * 9 * 32 * EB);
+  // transposing value reads. bf16: source lane (g, l16) points at row
+  // 4g + l16/4, dims 256*half + 4*(l16%4) .. +3. fp8: source lane (g, l16)
+  // points at row T(g, l16/2), dims 256*half + 8*(l16%2) .. +7, with
+  // T(g, q) = 4g + q for q < 4 and 16 + 4g + (q - 4) otherwise, so that lane
+  // (n, g) receives dim n of tokens 4g..4g+3 and 16+4g..16+4g+3: the token
+  // order of the bf16 reads and of the P operand
+  const int tq = l16 >> 1;
+  const uint32_t tr_lane =
+      (CT == kFP8) ? (uint32_t)(((tq < 4 ? 4 * g + tq : 16 + 4 * g + tq - 4)) * TP + 256 * half + 8 * (l16 & 1))
+                   : (uint32_t)((4 * g + (l16 >> 2)) * TP + 2 * 256 * half + 8 * (l16 & 3));
+  char* xbuf = smem + NSTAGE * STAGE_BYTES;
 
   Cursor cc = c0;
   int it = 0;
@@ -418,12 +425,6 @@ mla_attn_pair_kernel(AttnParams p) {
     const int64_t left = cc.t_end - cc.t;
     const int nvalid = left < TILE ? (int)left : TILE;
     const char* tb = stage;
-    if constexpr (CT == kFP8) {
-      char* conv = smem + NSTAGE * STAGE_BYTES;
-      widen_fp8_tile<64 * NW>(stage, conv);
-      barrier_lds();
-      tb = conv;
-    }
 
     // ---------------- scores: this wave's half of the contraction ----------------
     f32x4 acc[2][2];                                     // [token block][head block]
@@ -435,8 +436,14 @@ mla_attn_pair_kernel(AttnParams p) {
     // scheduling barrier between them left the matrix unit idle longer)
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
-      const bf16x8 a0 = *(const bf16x8*)(sa + k * 64);
-      const bf16x8 a1 = *(const bf16x8*)(sa + 16 * TP + k * 64);
+      bf16x8 a0, a1;
+      if constexpr (CT == kFP8) {                        // codes widened in registers
+        a0 = fp8x8_to_bf16x8(*(const uint2*)(sa + k * 32));
+        a1 = fp8x8_to_bf16x8(*(const uint2*)(sa + 16 * TP + k * 32));
+      } else {
+        a0 = *(const bf16x8*)(sa + k * 64);
+        a1 = *(const bf16x8*)(sa + 16 * TP + k * 64);
+      }
       acc[0][0] = mfma_bf16_k32(a0, q[0][k], acc[0][0]);
       acc[0][1] = mfma_bf16_k32(a0, q[1][k], acc[0][1]);
       acc[1][0] = mfma_bf16_k32(a1, q[0][k], acc[1][0]);
@@ -527,14 +534,25 @@ mla_attn_pair_kernel(AttnParams p) {
     const uint32_t tr_addr = (uint32_t)(size_t)tb + tr_lane;
 #pragma unroll
     for (int n0 = 0; n0 < 16; n0 += 4) {
-      s16x4 lo[4], hi[4];
-      pv_read4<TP, 0>(tr_addr + n0 * 32, lo, hi);
+      bf16x8 a[4];
+      if constexpr (CT == kFP8) {
+        uint2 v[4];
+        lds_tr8_x4<0, 16, 32, 48>(tr_addr + n0 * 16, v[0], v[1], v[2], v[3]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[k] = fp8x8_to_bf16x8(v[k]);
+      } else {
+        s16x4 lo[4], hi[4];
+        pv_read4<TP, 0>(tr_addr + n0 * 32, lo, hi);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const s16x8 a8 = {lo[k][0], lo[k][1], lo[k][2], lo[k][3], hi[k][0], hi[k][1], hi[k][2], hi[k][3]};
+          a[k] = __builtin_bit_cast(bf16x8, a8);
+        }
+      }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const s16x8 a8 = {lo[k][0], lo[k][1], lo[k][2], lo[k][3], hi[k][0], hi[k][1], hi[k][2], hi[k][3]};
-        const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
-        o[0][n0 + k] = mfma_bf16_k32(a, pb[0], o[0][n0 + k]);
-        o[1][n0 + k] = mfma_bf16_k32(a, pb[1], o[1][n0 + k]);
+        o[0][n0 + k] = mfma_bf16_k32(a[k], pb[0], o[0][n0 + k]);
+        o[1][n0 + k] = mfma_bf16_k32(a[k], pb[1], o[1][n0 + k]);
       }
     }
 
