@@ -15,16 +15,20 @@ namespace mla {
 
 // One head-GEMM tile per workgroup, numbered (64-column block, head, batch
 // slice of 16*NBT rows) with the column block fastest. The absorb launch has
-// one more workgroup, the last, which builds the plan.
+// one more workgroup, the first (dispatched before the CUs fill up), which
+// builds the plan.
 template <int AT, int KD, int ND, int NBT, int KC>
 __global__ void __launch_bounds__(256)
 mla_headgemm_kernel(GemmParams p) {
   using G = HeadGemm<AT, KD, ND, NBT, KC>;
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
-  const int i = blockIdx.x;
-  if (p.seq_len && i == (int)gridDim.x - 1) {           // the extra plan workgroup
-    build_plan(p, (int64_t*)lds, (int)(G::W_BYTES / 8));
-    return;
+  int i = blockIdx.x;
+  if (p.seq_len) {                                       // workgroup 0 builds the plan
+    if (i == 0) {
+      build_plan(p, (int64_t*)lds, (int)(G::W_BYTES / 8));
+      return;
+    }
+    --i;
   }
   constexpr int NXB = ND / kNT;
   typename G::Regs rg;

@@ -68,12 +68,22 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
     if (lane == 0 && in_lds) lds[0] = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
       const int b = b0 + lane;
+      // the three per-sequence loads go out together (one asm block that
+      // waits at its end; left to itself the compiler waits for each load
+      // before issuing the next)
+      const int bc = b < B ? b : B - 1;
+      int Lr, cap;
+      int64_t row0;
+      asm volatile(
+          "global_load_dword %0, %3, off\n"
+          "global_load_dword %1, %4, off\n"
+          "global_load_dwordx2 %2, %5, off\n"
+          "s_waitcnt vmcnt(0)"
+          : "=&v"(Lr), "=&v"(cap), "=&v"(row0)
+          : "v"(p.seq_len + bc), "v"(p.seq_cap + bc), "v"(p.seq_start + bc)
+          : "memory");
       int L = 0;
-      if (b < B) {
-        const int Lr = p.seq_len[b];
-        const int cap = p.seq_cap[b];
-        L = Lr < 0 ? 0 : (Lr > cap ? cap : Lr);
-      }
+      if (b < B) L = Lr < 0 ? 0 : (Lr > cap ? cap : Lr);
       const int64_t n = (L + TL - 1) / TL;
       int64_t v = n;
 #pragma unroll
@@ -86,7 +96,7 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
       }
       if (b < B) {
         SeqInfo si;
-        si.row0 = p.seq_start[b];
+        si.row0 = row0;
         si.len = L;
         si.tile0 = (int32_t)(carry + v - n);
         si.tile1 = (int32_t)(carry + v);
@@ -105,9 +115,11 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
     }
     if (!in_lds && lane == 0) lds[0] = carry;            // NT for the other waves
   }
+  // the records are read back only by this workgroup's threads (and by later
+  // launches, which the kernel boundary orders), so workgroup scope suffices
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   const volatile int32_t* gtile0 = &p.seqinfo[0].tile0;
   // P_b for b < B (P_B = NT)
   auto prefix = [&](int b) -> int64_t {
@@ -124,11 +136,12 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
     }
     return lo;
   };
-  for (int64_t w = tid; w <= W; w += 256) p.starts[w] = (w * NT) / W;
+  const int nthr = (int)blockDim.x;
+  for (int64_t w = tid; w <= W; w += nthr) p.starts[w] = (w * NT) / W;
   if (NT == 0) {
-    for (int64_t w = tid; w < W; w += 256) p.wseq[w] = 0;
+    for (int64_t w = tid; w < W; w += nthr) p.wseq[w] = 0;
   }
-  for (int b = tid; b < B; b += 256) {
+  for (int b = tid; b < B; b += nthr) {
     const int64_t P0 = prefix(b), P1 = (b + 1 < B) ? prefix(b + 1) : NT;
     if (P1 > P0) {
       const int64_t wlo = ceil_div64(P0 * W, NT), whi = ceil_div64(P1 * W, NT);
@@ -145,10 +158,10 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
   if (!in_lds) {                                         // the records come back from memory
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
   // each worker's starting point
-  for (int64_t w = tid; w < W; w += 256) {
+  for (int64_t w = tid; w < W; w += nthr) {
     const int64_t r_lo = (w * NT) / W, r_hi = ((w + 1) * NT) / W;
     WorkerInfo wi;
     wi.r_hi = (int32_t)r_hi;
