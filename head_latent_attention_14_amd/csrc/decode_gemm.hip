@@ -524,10 +524,10 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
     if (e != hipSuccess) return e;
   }
   if (stage != 0 && stage != 3) return e;
-  // 3. merge the partials and apply W_UV: one fused launch (bf16) when the
-  //    sequences have few slots each (one merge round per row, on average)
-  //    and its workgroups fit the CUs at once, else the merge (into the q_lat
-  //    buffer, free once attention is done) and the projection
+  // 3. merge the partials and apply W_UV. bf16: one launch, per (64 output
+  //    columns, head, 16 rows) when the sequences have few slots each (one
+  //    merge round per row, on average) and its workgroups fit the CUs at
+  //    once, else per (head, row block). fp32: merge, then projection.
   const int64_t comb_wgs = (int64_t)(kDv / kNT) * a.H * ((a.B + 15) / 16);
   if (!f32 && plan.nslot <= 6 * (int64_t)a.B && comb_wgs <= kTargetCUs) {
     GemmParams c{};
@@ -545,9 +545,10 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
                        c);
     return hipGetLastError();
   }
-  if (!f32 && a.H % 8 == 0) {
+  if (!f32) {
     // many rows: merge + W_UV per (head, row block), the largest block that
-    // still gives every CU a workgroup (16 rows when none does)
+    // still gives every CU a workgroup (16 rows when none does); H is a
+    // multiple of 16, so the workgroups of one head share an XCD
     GemmParams c{};
     c.B = a.B;
     c.H = a.H;
@@ -569,6 +570,8 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
     }
     return hipGetLastError();
   }
+  // fp32: the merge (into the q_lat buffer, free once attention is done),
+  // then the projection
   GemmParams m{};
   m.B = a.B;
   m.H = a.H;
@@ -582,11 +585,7 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
   m.part_o = a.part_o;
   m.part_ml = a.part_ml;
   const int64_t pairs = (int64_t)a.B * a.H;
-  dim3 mgrid((unsigned)((pairs + 3) / 4));
-  if (f32)
-    hipLaunchKernelGGL(mla_merge_kernel<kF32>, mgrid, dim3(256), 0, s, m);
-  else
-    hipLaunchKernelGGL(mla_merge_kernel<kBF16>, mgrid, dim3(256), 0, s, m);
+  hipLaunchKernelGGL(mla_merge_kernel<kF32>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, m);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   GemmParams g{};
@@ -595,19 +594,7 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
   g.x = a.q_lat;
   g.w = a.w_uv;
   g.y = a.out;
-  if (f32) return launch_gemm_t<kF32, kDc, kDv, 1, 128>(g, s);
-  // 16, 32 or 64 batch rows per workgroup, whichever loads fewer bytes per CU:
-  // each workgroup reads a 64 KB weight slice and 16 KB of merged output per
-  // 16 rows, and every 256 workgroups share the CUs once more
-  auto per_cu = [&](int nbt) {
-    const int64_t wgs = (int64_t)(kDv / kNT) * a.H * ((a.B + 16 * nbt - 1) / (16 * nbt));
-    const int64_t rounds = (wgs + kTargetCUs - 1) / kTargetCUs;
-    return rounds * (64 + 16 * nbt);
-  };
-  const int64_t c1 = per_cu(1), c2 = per_cu(2), c4 = per_cu(4);
-  if (c4 < c2 && c4 < c1) return launch_gemm_t<kBF16, kDc, kDv, 4, kDc>(g, s);
-  return c2 < c1 ? launch_gemm_t<kBF16, kDc, kDv, 2, kDc>(g, s)
-                 : launch_gemm_t<kBF16, kDc, kDv, 1, kDc>(g, s);
+  return launch_gemm_t<kF32, kDc, kDv, 1, 128>(g, s);
 }
 
 }  // namespace mla
