@@ -134,6 +134,30 @@ def test_many_and_few_sequences(B):
     assert rel_l2(got, ro) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("B,H", [(22, 16), (500, 16), (6, 128)])
+def test_combine_row_blocks(B, H):
+    """Batches that reach the per-(head, row block) merge + W_UV launch with
+    16-row blocks ending in 6 rows (one wave per row), 32-row blocks ending in
+    20 rows (rows folded four at a time), and 6 rows of 128 heads. Every row of
+    the last block is checked, plus random ones, outputs and lse."""
+    rng = np.random.default_rng(B * 1000 + H)
+    lengths = rng.integers(1, 300, size=B)
+    base = W.WORKLOADS["v2lite_bf16" if H == 16 else "v2_bf16"]
+    p = W.make_problem(base, seed=B + H, B=B, lengths=lengths, H=H)
+    log(f"[combine blocks] B={B} H={H} T={p.T}")
+    dp = DeviceProblem(p)
+    o, lse = dp.step(poison=True)
+    last = list(range(max(0, B - 20), B))
+    pairs = {(b, int(h)) for b in last for h in rng.integers(H, size=2)}
+    pairs |= {(int(b), int(h)) for b, h in zip(rng.integers(B, size=16), rng.integers(H, size=16))}
+    pairs = sorted(pairs)
+    ro, rl = OracleView(p).decode(pairs)
+    got = np.stack([o[b, h] for b, h in pairs])
+    gl = np.array([lse[b, h] for b, h in pairs])
+    assert rel_l2(got, ro) <= TOL["bf16"]
+    assert np.abs(gl - rl).max() <= 50 * TOL["bf16"]
+
+
 def test_other_head_counts():
     for H in [32, 64]:
         p = W.make_problem(W.WORKLOADS["v2_bf16"], B=2, lengths=np.array([77, 300]), H=H)
