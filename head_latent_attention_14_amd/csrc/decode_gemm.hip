@@ -125,94 +125,6 @@ __device__ __forceinline__ float merge_row(const GemmParams& p, int b, int h, in
   return (lsum > 0.f) ? (mmax + __log2f(lsum)) * kLn2 : -INFINITY;
 }
 
-// Merge one (b, h) per wave into o_lat (the q_lat buffer) and lse.
-template <int AT>
-__global__ void __launch_bounds__(256)
-mla_merge_kernel(GemmParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int B = p.B, H = p.H;
-  if (pair >= (int64_t)B * H) return;
-  const int b = (int)(pair / H), h = (int)(pair - (int64_t)b * H);
-  float acc[8];
-  const float lse = merge_row<AT>(p, b, h, lane, acc);
-  if (p.lse && lane == 0) p.lse[pair] = lse;
-  char* dst = (char*)p.y + (pair * kDc + 8 * lane) * (AT == kF32 ? 4 : 2);
-  if constexpr (AT == kF32) {
-    *(f32x4*)dst = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    *(f32x4*)(dst + 16) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-  } else {
-    *(bf16x8*)dst = pack_bf16x8(acc);
-  }
-}
-
-// Merge and W_UV in one launch (bf16), for batches whose rows have few
-// partial slots: workgroup (64 output columns, head h, 16 batch rows) with
-// sixteen waves. Each wave merges one row (all its slot loads in one round)
-// while the weight slice is in flight, writes the merged row in bf16 to LDS
-// (the value the separate merge stores), and four waves then multiply. The
-// two column workgroups of a (head, rows) both merge the rows; the first
-// writes lse.
-__global__ void __launch_bounds__(1024)
-mla_combine_kernel(GemmParams p) {
-  using G = HeadGemm<kBF16, kDc, kDv, 1, kDc>;
-  constexpr int TPW = 1024;                            // threads
-  constexpr int WP = kDc * kNT * 2 / 16;               // 16-byte pieces of the weight slice
-  __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
-  char* w_lds = lds;
-  char* x_lds = lds + G::W_BYTES;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n0 = blockIdx.x * kNT, h = blockIdx.y, b0 = blockIdx.z * 16;
-  u32x4 wv[WP / TPW];
-#pragma unroll
-  for (int k = 0; k < WP / TPW; ++k) {
-    const int i = tid + TPW * k;
-    const int r = i / G::WPR, c = i - r * G::WPR;
-    wv[k] = *(const u32x4*)((const char*)p.w + (((int64_t)h * kDc + r) * kDv + n0) * 2 + c * 16);
-  }
-  {
-    const int b = b0 + wave;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (b < p.B) {
-      const float lse = merge_row<kBF16, 6>(p, b, h, lane, acc);
-      if (p.lse && blockIdx.x == 0 && lane == 0) p.lse[(int64_t)b * p.H + h] = lse;
-    }
-    *(bf16x8*)(x_lds + wave * G::XROW + 16 * lane) = pack_bf16x8(acc);
-  }
-#pragma unroll
-  for (int k = 0; k < WP / TPW; ++k) {
-    const int i = tid + TPW * k;
-    const int r = i / G::WPR, c = i - r * G::WPR;
-    *(u32x4*)(w_lds + r * G::WROW + c * 16) = wv[k];
-  }
-  __syncthreads();
-  if (wave >= 4) return;
-  const int l16 = lane & 15, g = lane >> 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < kDc; kk += 32) {
-    // A = W^T block: lane (n, g) gets W[kk + 8g + 0..7][16*wave + n]
-    const int rs = kk + 8 * g + (l16 >> 2);
-    const int cb = (16 * wave + 4 * (l16 & 3)) * 2;
-    const s16x4 lo = lds_read_tr16(w_lds, rs * G::WROW + cb);
-    const s16x4 hi = lds_read_tr16(w_lds, (rs + 4) * G::WROW + cb);
-    const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    const bf16x8 bv = lds_read_b128(x_lds, l16 * G::XROW + (kk + 8 * g) * 2);
-    acc = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a8), bv, acc);
-  }
-  // lane holds Y[b0 + l16][n0 + 16*wave + 4g + r]
-  const int b = b0 + l16;
-  if (b < p.B) {
-    const int n = n0 + 16 * wave + 4 * g;
-    uint2 v;
-    v.x = pack_bf16x2(acc[0], acc[1]);
-    v.y = pack_bf16x2(acc[2], acc[3]);
-    *(uint2*)((char*)p.y + (((int64_t)b * p.H + h) * kDv + n) * 2) = v;
-  }
-}
-
 // merge_slots over NR rows at once (bf16 partials): row j is sequence b[j]
 // with slot workers wf[j], wf[j]+step, ... up to wl[j]; each round takes RU
 // slots of every row, so all NR*RU slot loads of a round are in flight
@@ -294,6 +206,106 @@ __device__ __forceinline__ void merge_rows(const GemmParams& p, const int* b, co
         }
       }
     }
+  }
+}
+
+// Merge one (b, h) per wave into o_lat (the q_lat buffer) and lse.
+template <int AT>
+__global__ void __launch_bounds__(256)
+mla_merge_kernel(GemmParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int B = p.B, H = p.H;
+  if (pair >= (int64_t)B * H) return;
+  const int b = (int)(pair / H), h = (int)(pair - (int64_t)b * H);
+  float acc[8];
+  const float lse = merge_row<AT>(p, b, h, lane, acc);
+  if (p.lse && lane == 0) p.lse[pair] = lse;
+  char* dst = (char*)p.y + (pair * kDc + 8 * lane) * (AT == kF32 ? 4 : 2);
+  if constexpr (AT == kF32) {
+    *(f32x4*)dst = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4*)(dst + 16) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else {
+    *(bf16x8*)dst = pack_bf16x8(acc);
+  }
+}
+
+// Merge and W_UV in one launch (bf16), for batches whose rows have few
+// partial slots: workgroup (64 output columns, head h, 16 batch rows) with
+// sixteen waves. Each wave merges one row (all its slot loads in one round)
+// while the weight slice is in flight, writes the merged row in bf16 to LDS
+// (the value the separate merge stores), and four waves then multiply. The
+// two column workgroups of a (head, rows) both merge the rows; the first
+// writes lse.
+__global__ void __launch_bounds__(1024)
+mla_combine_kernel(GemmParams p) {
+  using G = HeadGemm<kBF16, kDc, kDv, 1, kDc>;
+  constexpr int TPW = 1024;                            // threads
+  constexpr int WP = kDc * kNT * 2 / 16;               // 16-byte pieces of the weight slice
+  __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+  char* w_lds = lds;
+  char* x_lds = lds + G::W_BYTES;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n0 = blockIdx.x * kNT, h = blockIdx.y, b0 = blockIdx.z * 16;
+  u32x4 wv[WP / TPW];
+#pragma unroll
+  for (int k = 0; k < WP / TPW; ++k) {
+    const int i = tid + TPW * k;
+    const int r = i / G::WPR, c = i - r * G::WPR;
+    wv[k] = *(const u32x4*)((const char*)p.w + (((int64_t)h * kDc + r) * kDv + n0) * 2 + c * 16);
+  }
+  {
+    const int b = b0 + wave;
+    float acc[1][8] = {{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
+    if (b < p.B) {
+      // one row, its slot bookkeeping in lanes (vector loads: sixteen waves
+      // of scalar loads per CU queue at the scalar cache)
+      const int bj[1] = {b};
+      const int64_t wf[1] = {ld_const(p.wfirst, b)};
+      const int64_t wl[1] = {ld_const(p.wlast, b)};
+      float mmax = -INFINITY, lsum = 0.f;
+      merge_rows<1, 8>(p, bj, wf, wl, h, lane, 1, acc, &mmax, &lsum);
+      if (wl[0] >= wf[0]) {
+        const float inv = 1.f / lsum;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[0][i] *= inv;
+      }
+      if (p.lse && blockIdx.x == 0 && lane == 0)
+        p.lse[(int64_t)b * p.H + h] = (lsum > 0.f) ? (mmax + __log2f(lsum)) * kLn2 : -INFINITY;
+    }
+    *(bf16x8*)(x_lds + wave * G::XROW + 16 * lane) = pack_bf16x8(acc[0]);
+  }
+#pragma unroll
+  for (int k = 0; k < WP / TPW; ++k) {
+    const int i = tid + TPW * k;
+    const int r = i / G::WPR, c = i - r * G::WPR;
+    *(u32x4*)(w_lds + r * G::WROW + c * 16) = wv[k];
+  }
+  __syncthreads();
+  if (wave >= 4) return;
+  const int l16 = lane & 15, g = lane >> 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < kDc; kk += 32) {
+    // A = W^T block: lane (n, g) gets W[kk + 8g + 0..7][16*wave + n]
+    const int rs = kk + 8 * g + (l16 >> 2);
+    const int cb = (16 * wave + 4 * (l16 & 3)) * 2;
+    const s16x4 lo = lds_read_tr16(w_lds, rs * G::WROW + cb);
+    const s16x4 hi = lds_read_tr16(w_lds, (rs + 4) * G::WROW + cb);
+    const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const bf16x8 bv = lds_read_b128(x_lds, l16 * G::XROW + (kk + 8 * g) * 2);
+    acc = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a8), bv, acc);
+  }
+  // lane holds Y[b0 + l16][n0 + 16*wave + 4g + r]
+  const int b = b0 + l16;
+  if (b < p.B) {
+    const int n = n0 + 16 * wave + 4 * g;
+    uint2 v;
+    v.x = pack_bf16x2(acc[0], acc[1]);
+    v.y = pack_bf16x2(acc[2], acc[3]);
+    *(uint2*)((char*)p.y + (((int64_t)b * p.H + h) * kDv + n) * 2) = v;
   }
 }
 
