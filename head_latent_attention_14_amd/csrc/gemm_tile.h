@@ -36,20 +36,28 @@ constexpr int kNT = 64;       // output columns per workgroup (one 16-wide block
 
 // The work plan, built by one extra workgroup of the absorb launch so the
 // attention and merge kernels need no divisions or searches. Sequence b has
-// n_b = ceil(len_b / tile) tiles (len clamped to [0, capacity]); P_b is the
-// prefix sum of n, NT = P_B, and the tiles of all sequences form one stream:
-//   seqinfo[b] = {first cache row, len_b, P_b, P_(b+1), next sequence with tiles}
-//   starts[w]  = floor(w * NT / W): worker w takes tiles [starts[w], starts[w+1])
-//   wseq[w]    = the sequence holding tile starts[w] (non-empty workers)
-//   wfirst[b], wlast[b] = first and last worker that touch sequence b
+// n_b = ceil(len_b / tile) tiles (len clamped to [0, capacity]). Starting a
+// sequence segment costs a worker about one tile's time (its queries come
+// in, a partial goes out), so a non-empty sequence counts kSegTiles more:
+// v_b = n_b + kSegTiles, or 0. P_b is the prefix sum of v, NT = P_B, and the
+// work of all sequences forms one stream in which sequence b holds
+// [P_b, P_(b+1)), its real tiles being the last n_b of them:
+//   seqinfo[b] = {first cache row, len_b, P_(b+1) - n_b, P_(b+1), next sequence with tiles}
+//   starts[w]  = floor(w * NT / W): worker w takes [starts[w], starts[w+1])
+//   wseq[w]    = the sequence holding starts[w] (non-empty workers)
+//   wfirst[b], wlast[b] = first and last worker that touch a real tile of b
 //                (wlast < wfirst for an empty sequence)
 // Splitting whole tiles keeps every split inside a sequence on a tile
-// boundary, so the only partial tile of a sequence is its last one.
+// boundary, so the only partial tile of a sequence is its last one. A worker
+// whose range holds only counted-but-empty units has no tiles and lies
+// outside every sequence's [wfirst, wlast].
 // floor(w NT / W) >= P exactly when w >= ceil(P W / NT), so sequence b holds
-// the starts of workers [ceil(P_b W/NT), ceil(P_(b+1) W/NT)), its first
-// worker is ceil((P_b + 1) W / NT) - 1 and its last ceil(P_(b+1) W / NT) - 1:
+// the starts of workers [ceil(P_b W/NT), ceil(P_(b+1) W/NT)), the worker
+// holding unit R is ceil((R + 1) W / NT) - 1, so b's first worker is that of
+// its first real tile R0 = P_(b+1) - n_b and its last ceil(P_(b+1) W / NT) - 1:
 // every entry is a closed form of the prefix sums, which stay in LDS (`lds`,
 // room for `lds_n` values) when they fit.
+constexpr int kSegTiles = 1;
 __device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
@@ -85,7 +93,7 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
       int L = 0;
       if (b < B) L = Lr < 0 ? 0 : (Lr > cap ? cap : Lr);
       const int64_t n = (L + TL - 1) / TL;
-      int64_t v = n;
+      int64_t v = n > 0 ? n + kSegTiles : 0;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int src = lane - off;
@@ -120,10 +128,17 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const volatile int32_t* gtile0 = &p.seqinfo[0].tile0;
-  // P_b for b < B (P_B = NT)
+  const volatile int32_t* gtile1 = &p.seqinfo[0].tile1;
+  const volatile int32_t* glen = &p.seqinfo[0].len;
+  constexpr int SI = sizeof(SeqInfo) / 4;
+  // P_b for b < B (P_B = NT): the end of the previous sequence's units
   auto prefix = [&](int b) -> int64_t {
-    return in_lds ? lds[b] : (int64_t)gtile0[(int64_t)b * (sizeof(SeqInfo) / 4)];
+    return in_lds ? lds[b] : (b == 0 ? 0 : (int64_t)gtile1[(int64_t)(b - 1) * SI]);
+  };
+  // real tiles of sequence b
+  auto ntiles = [&](int b) -> int64_t {
+    const int64_t len = in_lds ? llen[b] : (int64_t)glen[(int64_t)b * SI];
+    return (len + TL - 1) / TL;
   };
   const int64_t NT = in_lds ? lds[B] : lds[0];
   // the sequence holding tile t < NT: the largest b in [lo, B) with P_b <= t
@@ -146,7 +161,7 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
     if (P1 > P0) {
       const int64_t wlo = ceil_div64(P0 * W, NT), whi = ceil_div64(P1 * W, NT);
       for (int64_t w = wlo; w < whi; ++w) p.wseq[w] = b;
-      p.wfirst[b] = (int)(ceil_div64((P0 + 1) * W, NT) - 1);
+      p.wfirst[b] = (int)(ceil_div64((P1 - ntiles(b) + 1) * W, NT) - 1);
       p.wlast[b] = (int)(whi - 1);
     } else {
       p.wfirst[b] = 0;
@@ -166,20 +181,19 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
     WorkerInfo wi;
     wi.r_hi = (int32_t)r_hi;
     wi.pad = 0;
-    if (r_lo >= r_hi) {
-      wi.row0 = 0;
-      wi.b = -1;
-      wi.t = wi.t_end = 0;
-      wi.next = B;
-    } else {
+    wi.row0 = 0;
+    wi.b = -1;
+    wi.t = wi.t_end = 0;
+    wi.next = B;
+    if (r_lo < r_hi) {
       int b;
       int64_t t0, t1, len, row0;
       int nx;
       if (in_lds) {
         b = owner(0, r_lo);
-        t0 = lds[b];
         t1 = lds[b + 1];
         len = llen[b];
+        t0 = t1 - (len + TL - 1) / TL;                   // first real tile of b
         row0 = lrow[b];
         nx = (t1 < NT) ? owner(b + 1, t1) : B;
       } else {
@@ -191,12 +205,18 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
         row0 = si->row0;
         nx = si->next;
       }
-      const int64_t se = t1 < r_hi ? t1 : r_hi;
-      wi.b = b;
-      wi.t = (int32_t)((r_lo - t0) * TL);
-      wi.t_end = (int32_t)((se - t0) * TL < len ? (se - t0) * TL : len);
-      wi.row0 = row0 + wi.t;
-      wi.next = nx;
+      // a range that ends within b's counted-only units holds no tile (and
+      // cannot reach the next sequence); otherwise it starts at its first
+      // real tile of b
+      if (r_hi > t0) {
+        const int64_t first = r_lo > t0 ? r_lo : t0;
+        const int64_t se = t1 < r_hi ? t1 : r_hi;
+        wi.b = b;
+        wi.t = (int32_t)((first - t0) * TL);
+        wi.t_end = (int32_t)((se - t0) * TL < len ? (se - t0) * TL : len);
+        wi.row0 = row0 + wi.t;
+        wi.next = nx;
+      }
     }
     p.winfo[w] = wi;
   }

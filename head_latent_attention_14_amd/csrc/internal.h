@@ -31,13 +31,14 @@ hipError_t launch_append(int cache_type, const AppendArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- decode
 // Per-sequence record of the work plan (written by the absorb launch, read by
-// the attention kernels). Work is split in tiles: sequence b owns tiles
-// [tile0, tile1) of the stream of all sequences' tiles, ceil(len / tile) of
-// them, the last one possibly partial.
+// the attention kernels). Work is split in tiles: the sequences' tiles form
+// one stream in which each non-empty sequence also counts one unit for the
+// cost of starting it; sequence b's ceil(len / tile) real tiles, the last one
+// possibly partial, are [tile0, tile1) of that stream.
 struct SeqInfo {
   int64_t row0;     // cache row of the sequence's first token
   int32_t len;      // length clamped to [0, capacity]
-  int32_t tile0;    // first tile
+  int32_t tile0;    // first real tile
   int32_t tile1;    // one past the last tile
   int32_t next;     // next sequence that has tiles (B: none)
   int32_t pad[2];
