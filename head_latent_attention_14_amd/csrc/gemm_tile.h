@@ -30,6 +30,7 @@ struct GemmParams {
   int32_t H;
   int32_t workers;            // W of the attention launch
   int32_t tile;               // tokens per tile of the attention launch
+  int32_t seg_tiles;          // tiles of work counted for starting a sequence segment
 };
 
 constexpr int kNT = 64;       // output columns per workgroup (one 16-wide block per wave)
@@ -37,9 +38,9 @@ constexpr int kNT = 64;       // output columns per workgroup (one 16-wide block
 // The work plan, built by one extra workgroup of the absorb launch so the
 // attention and merge kernels need no divisions or searches. Sequence b has
 // n_b = ceil(len_b / tile) tiles (len clamped to [0, capacity]). Starting a
-// sequence segment costs a worker about one tile's time (its queries come
-// in, a partial goes out), so a non-empty sequence counts kSegTiles more:
-// v_b = n_b + kSegTiles, or 0. P_b is the prefix sum of v, NT = P_B, and the
+// sequence segment costs a worker about a tile's time or more (its queries
+// come in, a partial goes out), so a non-empty sequence counts seg_tiles
+// more (a property of the attention kernel): v_b = n_b + seg_tiles, or 0. P_b is the prefix sum of v, NT = P_B, and the
 // work of all sequences forms one stream in which sequence b holds
 // [P_b, P_(b+1)), its real tiles being the last n_b of them:
 //   seqinfo[b] = {first cache row, len_b, P_(b+1) - n_b, P_(b+1), next sequence with tiles}
@@ -57,7 +58,6 @@ constexpr int kNT = 64;       // output columns per workgroup (one 16-wide block
 // its first real tile R0 = P_(b+1) - n_b and its last ceil(P_(b+1) W / NT) - 1:
 // every entry is a closed form of the prefix sums, which stay in LDS (`lds`,
 // room for `lds_n` values) when they fit.
-constexpr int kSegTiles = 1;
 __device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
@@ -93,7 +93,7 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
       int L = 0;
       if (b < B) L = Lr < 0 ? 0 : (Lr > cap ? cap : Lr);
       const int64_t n = (L + TL - 1) / TL;
-      int64_t v = n > 0 ? n + kSegTiles : 0;
+      int64_t v = n > 0 ? n + p.seg_tiles : 0;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int src = lane - off;
@@ -370,6 +370,7 @@ inline GemmParams absorb_params(const DecodePlan& plan, const DecodeArgs& a) {
   g.starts = a.starts;
   g.seq_start = a.seq_start;
   g.tile = plan.tile;
+  g.seg_tiles = plan.seg_tiles;
   g.wseq = a.wseq;
   g.wfirst = a.wfirst;
   g.wlast = a.wlast;

@@ -68,6 +68,7 @@ struct DecodePlan {
   int ds;        // block kernel: value-dimension splits per head block
   int nstage;    // cache tiles in flight per workgroup (LDS ring depth)
   int tile;      // tokens per tile of the kernel (the unit of the work split)
+  int seg_tiles; // tiles of work the split counts for starting a sequence segment
   int workers;   // W: tile ranges of the stream of all sequences' tiles
   int head_groups;  // workgroups sharing one token range (H / heads per workgroup)
   int64_t nslot;    // partial-result slots: W + B
