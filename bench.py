@@ -5,7 +5,7 @@ A step is one pass of the whole hot path over one batch: mla_append of one
 new token per sequence, then mla_decode (absorb W_UK, attention over the
 latent cache, merge + W_UV) for every sequence. The append and the absorb
 stage go through mla_append_absorb (one launch: neither reads what the other
-writes), then mla_decode_attend and mla_decode_combine. The default workload is the
+writes), then mla_decode_attend_combine. The default workload is the
 DeepSeek-V2-Lite-shaped decode (B=64, H=16, L ~ U[1024, 4096], bf16 cache,
 d_model 2048). Inputs are synthetic and seeded; several replicas of the
 cache and weights are rotated so each step reads its cache from HBM, not
@@ -13,7 +13,10 @@ from the 256 MB Infinity Cache.
 
 Prints one JSON line. `value` is the step's algorithmic bytes (cache rows,
 weights, activations and outputs the method must move) per second, over a
-timed region of whole steps with events only at its ends. The attention
+timed region of whole steps with events only at its ends (the larger of the
+wall clock and the GPU events); untimed warmup steps come first, enough for
+the chip to reach its sustained clock. A second pass with an event between
+every two steps gives the per-step p10/p50/p90. The attention
 kernel's own duration (the roofline entry) is then measured as the same
 number of attention launches back to back on the launch stream, rotating over
 the replicas, between two HIP events. A second workload (the 128-head V2
@@ -71,8 +74,13 @@ def recorded_traffic(workload: str):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # timed steps: the wall clock around them carries a fixed cost (first
+    # launch, final synchronisation; about 90 us), which 300 steps amortise
+    ap.add_argument("--steps", type=int, default=300)
+    # untimed warmup: the 128-head step needs a few hundred steps (tens of ms)
+    # before the chip settles at its sustained clock (110.7 -> 94.7 us/step
+    # measured between 10 and 500 warmup steps)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="v2lite_bf16")
     ap.add_argument("--secondary", default="v2_bf16",
                     help="a second workload measured the same way and reported under "
@@ -164,7 +172,7 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
                      tok_seq=torch.from_numpy(p.tok_seq).to(dev),
                      tok_pos=torch.from_numpy(p.tok_pos).to(dev))
             # the append and the decode's absorb stage in one call (one launch
-            # where it applies), then attend and combine
+            # where it applies), then attend and combine in one more call
             r["app"] = mla.PreparedAppendAbsorb(r["cache"], r["h"], r["w_dkv"], r["w_kr"],
                                                 r["tok_seq"], r["tok_pos"], wl.rope_base,
                                                 r["seq_len"], r["q_nope"], r["q_pe"], r["w_uk"],
@@ -176,8 +184,7 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
         r = reps[i % R]
         if wl.append:
             r["app"]()
-            r["dec"].attend()
-            r["dec"].combine()
+            r["dec"].attend_combine()
         else:
             r["dec"]()
 
@@ -199,6 +206,20 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
     gpu_ms = start.elapsed_time(end) / steps
     ms = max(wall_ms, gpu_ms)
 
+    # the distribution over steps: another `steps` steps, an event between
+    # every two (outside the timed region above)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        evs[i].record(stream)
+        step(warmup + steps + i)
+    evs[steps].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps))
+
+    def pct(q):
+        return round(per[min(len(per) - 1, int(round(q * (len(per) - 1))))], 2)
+    step_pct = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}
+
     # the attention kernel's own duration: `steps` launches back to back on the
     # launch stream, rotating over the replicas (each absorbed first, so every
     # launch reads its cache from HBM), between two events
@@ -215,9 +236,20 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
     attn_ms = a0.elapsed_time(a1) / steps
     del reps
     torch.cuda.empty_cache()
-    return dict(wl=wl, p=p, T=p.T, B=B, H=H, R=R, ms=ms, step_bytes=step_bytes,
+    return dict(wl=wl, p=p, T=p.T, B=B, H=H, R=R, ms=ms, wall_ms=wall_ms, gpu_ms=gpu_ms,
+                step_pct=step_pct, step_bytes=step_bytes,
                 step_flops=step_flops, attn_bytes=ab["cache"], attn_flops=fl["attention"],
                 attn_ms=attn_ms)
+
+
+def gpu_info(torch):
+    """The device as the runtime reports it (name, compute units, clock)."""
+    pr = torch.cuda.get_device_properties(0)
+    info = {"name": pr.name, "compute_units": pr.multi_processor_count,
+            "arch": getattr(pr, "gcnArchName", None)}
+    clk = getattr(pr, "clock_rate", None)               # kHz where the build exposes it
+    info["max_clock_mhz"] = round(clk / 1e3) if clk else None
+    return info
 
 
 def main():
@@ -265,6 +297,9 @@ def main():
                    "B": m["B"], "H": m["H"], "T": m["T"], "d_c": 512, "d_r": 64,
                    "d_model": wl.d_model if wl.append else None, "replicas": m["R"]},
         "tflops": round(m["step_flops"] / (ms * 1e-3) / 1e12, 3),
+        "step_us_percentiles": m["step_pct"],
+        "step_us_host_gpu": [round(m["wall_ms"] * 1e3, 2), round(m["gpu_ms"] * 1e3, 2)],
+        "gpu": gpu_info(torch),
         "attended_tokens_per_s": round(m["T"] / (ms * 1e-3), 1),
         "step_bytes": int(m["step_bytes"]),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS,
@@ -281,6 +316,8 @@ def main():
             "workload": f"{sw.name}: MLA decode step, B={s['B']}, H={s['H']}, "
                         f"L~U[{sw.lo},{sw.hi}], {sw.cache} latent cache",
             "ms_per_step": round(s["ms"], 5),
+            "step_us_percentiles": s["step_pct"],
+            "step_us_host_gpu": [round(s["wall_ms"] * 1e3, 2), round(s["gpu_ms"] * 1e3, 2)],
             "value_GBps": round(s["step_bytes"] / (s["ms"] * 1e-3) / 1e9, 2),
             "tflops": round(s["step_flops"] / (s["ms"] * 1e-3) / 1e12, 3),
             "hbm_frac_step": round(s["step_bytes"] / (s["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -31,9 +31,11 @@ MLA_DTYPE_FP8_E4M3 = 2
 D_C, D_R, D_ROW, D_NOPE, D_V = 512, 64, 576, 128, 128
 
 EXPORTED = ["mla_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_absorb",
-            "mla_decode_attend", "mla_decode_combine", "mla_append_absorb", "mla_status_string",
+            "mla_decode_attend", "mla_decode_combine", "mla_decode_attend_combine",
+            "mla_append_absorb", "mla_status_string",
             "mla_abi_version"]
-DECODE_STAGES = ["mla_decode_absorb", "mla_decode_attend", "mla_decode_combine"]
+DECODE_STAGES = ["mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
+                 "mla_decode_attend_combine"]
 
 
 class mla_cache_t(ctypes.Structure):
@@ -63,7 +65,8 @@ def _load(path: str = LIB_PATH):
     lib.mla_decode_workspace_size.argtypes = [I32, I32, ctypes.c_int, ctypes.c_int,
                                               ctypes.POINTER(SZ)]
     lib.mla_decode_workspace_size.restype = ctypes.c_int
-    for name in ["mla_decode", "mla_decode_absorb", "mla_decode_attend", "mla_decode_combine"]:
+    for name in ["mla_decode", "mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
+                 "mla_decode_attend_combine"]:
         fn = getattr(lib, name)
         fn.argtypes = [C, P, P, P, P, P, ctypes.c_int, I32, F32, P, P, P, SZ, P]
         fn.restype = ctypes.c_int
@@ -240,6 +243,11 @@ def mla_decode_combine(*args, **kw) -> None:
     _decode_call("mla_decode_combine", *args, **kw)
 
 
+def mla_decode_attend_combine(*args, **kw) -> None:
+    """Stages 2 and 3 of mla_decode in one call (same arguments)."""
+    _decode_call("mla_decode_attend_combine", *args, **kw)
+
+
 class PreparedDecode:
     """mla_decode and its three stages with the arguments marshalled once.
 
@@ -276,6 +284,9 @@ class PreparedDecode:
 
     def combine(self) -> None:
         _check(lib.mla_decode_combine(*self._args), "mla_decode_combine")
+
+    def attend_combine(self) -> None:
+        _check(lib.mla_decode_attend_combine(*self._args), "mla_decode_attend_combine")
 
 
 class PreparedAppend:

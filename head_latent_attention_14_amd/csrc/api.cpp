@@ -252,6 +252,7 @@ MLA_DECODE_ENTRY(mla_decode, 0)
 MLA_DECODE_ENTRY(mla_decode_absorb, 1)
 MLA_DECODE_ENTRY(mla_decode_attend, 2)
 MLA_DECODE_ENTRY(mla_decode_combine, 3)
+MLA_DECODE_ENTRY(mla_decode_attend_combine, 4)
 
 mla_status_t mla_append_absorb(const mla_cache_t* cache, const void* h, int32_t n_tok,
                                int32_t d_model, const void* w_dkv, const void* w_kr,

@@ -531,11 +531,11 @@ hipError_t launch_decode(int ct, const DecodePlan& plan, const DecodeArgs& a, hi
     if (e != hipSuccess) return e;
   }
   // 2. attention over the latent rows -> split partials
-  if (stage == 0 || stage == 2) {
+  if (stage == 0 || stage == 2 || stage == 4) {
     e = launch_attn(ct, plan, a, s);
     if (e != hipSuccess) return e;
   }
-  if (stage != 0 && stage != 3) return e;
+  if (stage != 0 && stage != 3 && stage != 4) return e;
   // 3. merge the partials and apply W_UV. bf16: one launch, per (64 output
   //    columns, head, 16 rows) when the sequences have few slots each (one
   //    merge round per row, on average) and its workgroups fit the CUs at

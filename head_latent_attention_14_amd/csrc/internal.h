@@ -118,7 +118,7 @@ struct DecodeArgs {
   float* part_ml;
 };
 // stage: 1 = absorb (+ work plan), 2 = attention, 3 = merge + W_UV,
-// 0 = all three
+// 4 = attention then merge + W_UV, 0 = all three
 hipError_t launch_decode(int cache_type, const DecodePlan& plan, const DecodeArgs& a,
                          hipStream_t s, int stage);
 

@@ -195,6 +195,14 @@ mla_status_t mla_decode_combine(const mla_cache_t* cache, const int32_t* seq_len
                                 int32_t n_heads, float softmax_scale,
                                 void* out, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream);
+/* attend then combine in one call (stages 2 and 3): what completes a decode
+ * step after mla_decode_absorb or mla_append_absorb, with one host call. */
+mla_status_t mla_decode_attend_combine(const mla_cache_t* cache, const int32_t* seq_len,
+                                       const void* q_nope, const void* q_pe,
+                                       const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
+                                       int32_t n_heads, float softmax_scale,
+                                       void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * mla_append_absorb -- mla_append followed by mla_decode_absorb, in one launch
@@ -204,8 +212,8 @@ mla_status_t mla_decode_combine(const mla_cache_t* cache, const int32_t* seq_len
  * do not depend on each other. Arguments: mla_append's (cache, h ... rope_base)
  * then mla_decode's (seq_len ... stream), with the same meaning, ownership and
  * rules; both argument sets are validated before anything runs. Calling
- * mla_decode_attend and mla_decode_combine afterwards with the same decode
- * arguments and workspace completes the decode step: the result equals
+ * mla_decode_attend and mla_decode_combine (or mla_decode_attend_combine)
+ * afterwards with the same decode arguments and workspace completes the decode step: the result equals
  * mla_append then mla_decode. For callers that run a decode step right after
  * appending its token.
  */

@@ -25,6 +25,7 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"mla_append", "mla_decode_workspace_size", "mla_decode",
                           "mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
+                          "mla_decode_attend_combine",
                           "mla_append_absorb", "mla_status_string", "mla_abi_version"}
     for n in names:
         assert hasattr(lib, n), n

@@ -186,6 +186,14 @@ def test_prepared_calls_match_direct_calls():
     torch.cuda.synchronize()
     assert np.array_equal(dp.out.double().cpu().numpy(), o_direct)
     assert np.array_equal(dp.lse.double().cpu().numpy(), l_direct)
+    # stages 2 and 3 in one call
+    dp.out.zero_()
+    dp.lse.zero_()
+    pd.absorb()
+    pd.attend_combine()
+    torch.cuda.synchronize()
+    assert np.array_equal(dp.out.double().cpu().numpy(), o_direct)
+    assert np.array_equal(dp.lse.double().cpu().numpy(), l_direct)
 
 
 # Empty sequences between, before and after non-empty ones; lengths of 1, of a
