@@ -371,9 +371,10 @@ mla_attn_pair_kernel(AttnParams p) {
       }
     }
   };
-  load_q(c0.b);
-  wait_vmcnt<0>();
-
+  // the first tiles' copies, then the queries: the two arrive together (the
+  // compiler waits for the queries before their first use; the empty asm
+  // keeps it from hoisting the query loads above the copies, whose address
+  // arithmetic it would then make wait for them)
   Cursor lc = c0;
   bool lvalid = true;
   int issued = 0;
@@ -384,6 +385,11 @@ mla_attn_pair_kernel(AttnParams p) {
       ++issued;
       lvalid = advance<TILE>(lc, p, r_hi, lane);
     }
+  }
+  {
+    int b0 = c0.b;
+    asm volatile("" : "+s"(b0) :: "memory");
+    load_q(b0);
   }
 
   float m_run[2] = {-INFINITY, -INFINITY};   // running max per head block (log2 domain)
