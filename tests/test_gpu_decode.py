@@ -134,14 +134,16 @@ def test_many_and_few_sequences(B):
     assert rel_l2(got, ro) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("B,H", [(22, 16), (500, 16), (6, 128)])
-def test_combine_row_blocks(B, H):
+@pytest.mark.parametrize("B,H,maxlen", [(22, 16, 300), (500, 16, 300), (6, 128, 300), (300, 128, 40)])
+def test_combine_row_blocks(B, H, maxlen):
     """Batches that reach the per-(head, row block) merge + W_UV launch with
     16-row blocks ending in 6 rows (one wave per row), 32-row blocks ending in
-    20 rows (rows folded four at a time), and 6 rows of 128 heads. Every row of
-    the last block is checked, plus random ones, outputs and lse."""
+    20 rows (rows folded four at a time), 6 rows of 128 heads, and 300 short
+    sequences of 128 heads (the split counts several tiles per sequence start
+    there, so many workers' ranges hold no tile). Every row of the last block
+    is checked, plus random ones, outputs and lse."""
     rng = np.random.default_rng(B * 1000 + H)
-    lengths = rng.integers(1, 300, size=B)
+    lengths = rng.integers(1, maxlen, size=B)
     base = W.WORKLOADS["v2lite_bf16" if H == 16 else "v2_bf16"]
     p = W.make_problem(base, seed=B + H, B=B, lengths=lengths, H=H)
     log(f"[combine blocks] B={B} H={H} T={p.T}")
