@@ -1,8 +1,9 @@
 // MLA decode attention over the latent cache (split-K partials).
 //
-// One workgroup streams a contiguous range of cached tokens (a share of the
-// concatenation of all sequences, so every workgroup moves the same number of
-// bytes) through an LDS ring filled by asynchronous global->LDS copies. Every
+// One workgroup streams a contiguous range of the tiles of all sequences (a
+// share of their concatenation, each sequence start counted as some tiles of
+// work; see the work plan) through an LDS ring filled by asynchronous
+// global->LDS copies. Every
 // 32-token tile of 576-wide latent rows is read from HBM once and used from
 // LDS by all heads of the workgroup for both contractions (discosf explainer,
 // "long-context bottleneck": W_UK folds into the query and W_UV into the
@@ -10,8 +11,8 @@
 //   scores  S^T[t][h] = c_t . q_lat[h] + k_pe_t . q_pe[h]  (MFMA, A = tile rows)
 //   values  O^T[d][h] += sum_t c_t[d] p[t][h]              (MFMA, A = tile^T)
 // with an online softmax per head in between. When a range ends or crosses a
-// sequence boundary the unnormalised (m, l, o_lat) of that segment is written
-// to a partial slot; the merge kernel combines the slots of each sequence.
+// sequence boundary the segment's (m, l, o_lat / l) is written to a partial
+// slot; the merge + W_UV launch combines the slots of each sequence.
 #include <type_traits>
 
 #include "attn_tile.h"

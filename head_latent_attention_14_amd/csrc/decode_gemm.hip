@@ -233,8 +233,8 @@ mla_merge_kernel(GemmParams p) {
 // Merge and W_UV in one launch (bf16), for batches whose rows have few
 // partial slots: workgroup (64 output columns, head h, 16 batch rows) with
 // sixteen waves. Each wave merges one row (all its slot loads in one round)
-// while the weight slice is in flight, writes the merged row in bf16 to LDS
-// (the value the separate merge stores), and four waves then multiply. The
+// while the weight slice is in flight, writes the merged row in bf16 to LDS,
+// and four waves then multiply. The
 // two column workgroups of a (head, rows) both merge the rows; the first
 // writes lse.
 __global__ void __launch_bounds__(1024)
@@ -317,7 +317,7 @@ mla_combine_kernel(GemmParams p) {
 // waves merge: with 8 or more rows each wave merges whole rows; with fewer,
 // 8/R' waves share a row (R' = R rounded up to 1, 2 or 4), each folding every
 // (8/R')-th slot, and their states meet in LDS. The merged rows are stored in
-// LDS as bf16 (the value the separate merge writes); wave w then produces
+// LDS as bf16 (as the fused launch above does); wave w then produces
 // output columns 16w..16w+15 of all RB rows.
 template <int RB>
 __global__ void __launch_bounds__(512)
