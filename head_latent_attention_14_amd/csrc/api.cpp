@@ -10,6 +10,9 @@
 #include "../../include/libmla.h"
 #include "internal.h"
 
+#include <stdlib.h>
+#include <vector>
+
 namespace mla {
 
 static constexpr int kMaxHeads = 1024;
@@ -98,6 +101,56 @@ static mla_status_t check_cache(const mla_cache_t* c) {
   return MLA_OK;
 }
 
+// ---------------------------------------------------------------- MLA_DEBUG
+// With MLA_DEBUG=1 in the environment, the entry points also check the
+// device-resident contract before launching: every length in [1, capacity],
+// every appended token's sequence in [0, B) and position in [0, capacity),
+// every sequence's rows inside the cache. The arrays come to the host on the
+// caller's stream, which is synchronised (the only synchronisation the
+// library ever does); a violation returns MLA_ERR_INVALID_ARGUMENT and
+// nothing runs. Without it such values are clamped or skipped as documented.
+static bool debug_mode() {
+  const char* v = getenv("MLA_DEBUG");
+  return v && v[0] == '1' && v[1] == 0;
+}
+
+template <typename T>
+static bool to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
+  dst.resize(n);
+  if (n == 0) return true;
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s) != hipSuccess) return false;
+  return hipStreamSynchronize(s) == hipSuccess;
+}
+
+// the cache's rows and, when given, the lengths; MLA_ERR_HIP if a copy fails
+static mla_status_t debug_check_decode(const mla_cache_t* c, const int32_t* seq_len, hipStream_t s) {
+  std::vector<int64_t> start;
+  std::vector<int32_t> cap, len;
+  if (!to_host(start, c->seq_start, c->num_seqs, s) || !to_host(cap, c->seq_capacity, c->num_seqs, s))
+    return MLA_ERR_HIP;
+  if (seq_len && !to_host(len, seq_len, c->num_seqs, s)) return MLA_ERR_HIP;
+  for (int b = 0; b < c->num_seqs; ++b) {
+    if (start[b] < 0 || cap[b] < 0 || start[b] + cap[b] > c->total_rows) return MLA_ERR_INVALID_ARGUMENT;
+    if (seq_len && (len[b] < 1 || len[b] > cap[b])) return MLA_ERR_INVALID_ARGUMENT;
+  }
+  return MLA_OK;
+}
+
+static mla_status_t debug_check_append(const mla_cache_t* c, const int32_t* tok_seq,
+                                       const int32_t* tok_pos, int32_t n_tok, hipStream_t s) {
+  mla_status_t st = debug_check_decode(c, nullptr, s);
+  if (st != MLA_OK) return st;
+  std::vector<int32_t> cap, sq, ps;
+  if (!to_host(cap, c->seq_capacity, c->num_seqs, s) || !to_host(sq, tok_seq, n_tok, s) ||
+      !to_host(ps, tok_pos, n_tok, s))
+    return MLA_ERR_HIP;
+  for (int n = 0; n < n_tok; ++n) {
+    if (sq[n] < 0 || sq[n] >= c->num_seqs) return MLA_ERR_INVALID_ARGUMENT;
+    if (ps[n] < 0 || ps[n] >= cap[sq[n]]) return MLA_ERR_INVALID_ARGUMENT;
+  }
+  return MLA_OK;
+}
+
 extern "C" {
 
 int mla_abi_version(void) { return MLA_ABI_VERSION; }
@@ -156,6 +209,10 @@ mla_status_t mla_append(const mla_cache_t* cache, const void* h, int32_t n_tok, 
   const mla_status_t st = append_args(cache, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq,
                                       tok_pos, rope_base, a);
   if (st != MLA_OK || n_tok == 0) return st;
+  if (debug_mode()) {
+    const mla_status_t ds = debug_check_append(cache, tok_seq, tok_pos, n_tok, (hipStream_t)stream);
+    if (ds != MLA_OK) return ds;
+  }
   hipError_t e = launch_append(cache_type(cache->dtype), a, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -233,6 +290,10 @@ static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len
   const mla_status_t st = decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads,
                                       softmax_scale, out, lse, workspace, workspace_bytes, a, plan);
   if (st != MLA_OK) return st;
+  if (debug_mode()) {
+    const mla_status_t ds = debug_check_decode(cache, seq_len, (hipStream_t)stream);
+    if (ds != MLA_OK) return ds;
+  }
   hipError_t e = launch_decode(cache_type(cache->dtype), plan, a, (hipStream_t)stream, stage);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -270,6 +331,12 @@ mla_status_t mla_append_absorb(const mla_cache_t* cache, const void* h, int32_t 
   st = decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads, softmax_scale, out,
                    lse, workspace, workspace_bytes, da, plan);
   if (st != MLA_OK) return st;
+  if (debug_mode()) {
+    mla_status_t ds = n_tok > 0 ? debug_check_append(cache, tok_seq, tok_pos, n_tok, (hipStream_t)stream)
+                                : MLA_OK;
+    if (ds == MLA_OK) ds = debug_check_decode(cache, seq_len, (hipStream_t)stream);
+    if (ds != MLA_OK) return ds;
+  }
   const int ct = cache_type(cache->dtype);
   hipError_t e;
   if (n_tok > 0 && append_absorb_fits(ct, aa, da)) {

@@ -15,13 +15,22 @@
  *  - Pointers marked (device) are device memory on the current HIP device;
  *    pointers marked (host) are host memory. Every call only enqueues work on
  *    `stream` (a hipStream_t; NULL is the legacy default stream) and returns
- *    without synchronising. The library allocates no memory, keeps no state
- *    between calls, and may run concurrently on several streams when each
- *    call has its own workspace and outputs.
+ *    without synchronising (MLA_DEBUG below aside). The library allocates no
+ *    device memory, keeps no state between calls, and may run concurrently
+ *    on several streams when each call has its own workspace and outputs.
  *  - The caller owns every buffer. Inputs are only read; outputs and the
  *    workspace are overwritten.
  *  - Host-side validation happens before any HIP call. A call that returns
  *    an error enqueued nothing. MLA_ERR_HIP reports a launch failure.
+ *  - Device-resident values outside the contract (lengths outside
+ *    [1, capacity], appended tokens with a sequence outside [0, B) or a
+ *    position outside [0, capacity)) are clamped or skipped as each call
+ *    documents. With MLA_DEBUG=1 in the environment, mla_decode and its
+ *    stages, mla_append and mla_append_absorb first copy those arrays (and
+ *    seq_start/seq_capacity, whose rows must lie inside the cache) to the
+ *    host on `stream`, synchronise it, and return MLA_ERR_INVALID_ARGUMENT
+ *    without running anything if one is violated (MLA_ERR_HIP if a copy
+ *    fails). This is the only case in which a call synchronises.
  *  - All tensors are dense and row-major with the shapes given.
  */
 #ifndef LIBMLA_H
