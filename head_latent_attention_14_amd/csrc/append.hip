@@ -291,10 +291,22 @@ __device__ void append_bf16_block(const AppendArgs& a, int tb, int cg, AppendBf1
     const char* sb = stg + (c % NST) * STAGE;
     const char* pa = sb + l16 * RS + g * 16;
     const char* pb = pa + OPND;
+    // wave w takes k-steps 8w .. 8w+7
+    if (nks == KC / 32) {                              // full stage: all reads, then the MFMAs
+      bf16x8 av[8], bv[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {                      // wave w takes k-steps 8w .. 8w+7
-      const int ks = 8 * wave + u;
-      if (ks < nks) acc = mfma_bf16_k32(*(const bf16x8*)(pa + ks * 64), *(const bf16x8*)(pb + ks * 64), acc);
+      for (int u = 0; u < 8; ++u) {
+        av[u] = *(const bf16x8*)(pa + (8 * wave + u) * 64);
+        bv[u] = *(const bf16x8*)(pb + (8 * wave + u) * 64);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = mfma_bf16_k32(av[u], bv[u], acc);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ks = 8 * wave + u;
+        if (ks < nks) acc = mfma_bf16_k32(*(const bf16x8*)(pa + ks * 64), *(const bf16x8*)(pb + ks * 64), acc);
+      }
     }
     if (c + NST < nch) {
       __syncthreads();                                 // stage c consumed
@@ -333,12 +345,14 @@ mla_append_bf16_kernel(AppendArgs a) {
 
 // Append and the absorb launch of the following decode in one launch (bf16):
 // neither reads what the other writes (the absorb product and the work plan
-// read queries, weights and lengths, not cache rows), so workgroup i issues
-// the loads of absorb tile i, runs append block i while they are in flight,
-// then finishes the absorb tile in the same LDS. The last workgroup builds
-// the plan. Grid: max(append blocks, absorb tiles) + 1 workgroups.
+// read queries, weights and lengths, not cache rows). Workgroups [0, n_app)
+// run one append block each; the next n_absw run absorb tiles j and, when
+// it exists, j + n_absw (both tiles' loads go out first); the last one
+// builds the plan. An append block moves 128 KB through its CU, and a CU
+// issues its copies at a bounded rate, so the absorb tiles go to CUs of
+// their own rather than queueing their loads ahead of an append block's.
 __global__ void __launch_bounds__(256)
-mla_append_absorb_kernel(AppendArgs a, GemmParams g, int n_app, int n_abs) {
+mla_append_absorb_kernel(AppendArgs a, GemmParams g, int n_app, int n_absw, int n_abs) {
   using G = AbsorbBf16;
   __shared__ __attribute__((aligned(1024))) AppendBf16Lds L;
   static_assert(G::LDS_BYTES <= (int)sizeof(AppendBf16Lds::stg), "absorb tile fits the append stages");
@@ -347,38 +361,66 @@ mla_append_absorb_kernel(AppendArgs a, GemmParams g, int n_app, int n_abs) {
     build_plan(g, (int64_t*)L.stg, (int)(sizeof(L.stg) / 8));
     return;
   }
-  const int nxb = kDc / kNT;                             // absorb tiles per (head, batch slice)
-  const bool abs = wg < n_abs;
-  const int n0 = (wg % nxb) * kNT;
-  const int h = (wg / nxb) % g.H;
-  const int b0 = (wg / nxb / g.H) * G::BT;
-  typename G::Regs rg;
-  if (abs) G::load(g, n0, h, b0, rg);
   if (wg < n_app) {
     const int ntb = (a.n_tok + 15) / 16;
     append_bf16_block(a, wg % ntb, wg / ntb, L);
-    __syncthreads();                                     // append done with its stages
+    return;
   }
-  if (abs) G::run(g, n0, h, b0, rg, L.stg);
+  // absorb tile t: 64 columns from n0 of head h for batch rows from b0
+  const int nxb = kDc / kNT;                             // absorb tiles per (head, batch slice)
+  auto tile = [&](int t, int& n0, int& h, int& b0) {
+    n0 = (t % nxb) * kNT;
+    h = (t / nxb) % g.H;
+    b0 = (t / nxb / g.H) * G::BT;
+  };
+  const int t0 = wg - n_app, t1 = t0 + n_absw;
+  const bool two = t1 < n_abs;
+  int n0a, ha, b0a, n0b = 0, hb = 0, b0b = 0;
+  typename G::Regs ra, rb;
+  tile(t0, n0a, ha, b0a);
+  G::load(g, n0a, ha, b0a, ra);
+  if (two) {
+    tile(t1, n0b, hb, b0b);
+    G::load(g, n0b, hb, b0b, rb);
+  }
+  G::run(g, n0a, ha, b0a, ra, L.stg);
+  if (two) {
+    __syncthreads();                                     // the first tile's LDS reads are done
+    G::run(g, n0b, hb, b0b, rb, L.stg);
+  }
+}
+
+// The fused launch's workgroups: append blocks, absorb workgroups (one or
+// two tiles each) and the plan workgroup, all in one round of CUs (the
+// kernel's LDS allows one workgroup per CU); false when they do not fit.
+struct FusedGrid {
+  int n_app, n_absw, n_abs;
+};
+static bool fused_grid(const AppendArgs& a, const DecodeArgs& d, FusedGrid& f) {
+  const int64_t n_app = (int64_t)((a.n_tok + 15) / 16) * kNumGroups;
+  const int64_t n_abs = (int64_t)(kDc / kNT) * d.H * ((d.B + AbsorbBf16::BT - 1) / AbsorbBf16::BT);
+  const int64_t room = kTargetCUs - 1 - n_app;
+  if (room < 1 || n_abs > 2 * room) return false;
+  f.n_app = (int)n_app;
+  f.n_abs = (int)n_abs;
+  f.n_absw = (int)(n_abs < room ? n_abs : room);
+  return true;
 }
 
 hipError_t launch_append_absorb(const AppendArgs& a, const DecodePlan& plan, const DecodeArgs& d,
                                 hipStream_t s) {
-  const int n_app = ((a.n_tok + 15) / 16) * kNumGroups;
-  const int n_abs = (kDc / kNT) * d.H * ((d.B + AbsorbBf16::BT - 1) / AbsorbBf16::BT);
-  const int n = (n_app > n_abs ? n_app : n_abs) + 1;
-  hipLaunchKernelGGL(mla_append_absorb_kernel, dim3(n), dim3(256), 0, s, a, absorb_params(plan, d),
-                     n_app, n_abs);
+  FusedGrid f;
+  if (!fused_grid(a, d, f)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mla_append_absorb_kernel, dim3(f.n_app + f.n_absw + 1), dim3(256), 0, s, a,
+                     absorb_params(plan, d), f.n_app, f.n_absw, f.n_abs);
   return hipGetLastError();
 }
 
 // Whether the fused launch applies: bf16 cache and activations, and a grid
-// that fits the CUs in one round (its LDS allows one workgroup per CU).
+// that fits the CUs in one round.
 bool append_absorb_fits(int cache_type, const AppendArgs& a, const DecodeArgs& d) {
-  if (cache_type != kBF16) return false;
-  const int n_app = ((a.n_tok + 15) / 16) * kNumGroups;
-  const int n_abs = (kDc / kNT) * d.H * ((d.B + AbsorbBf16::BT - 1) / AbsorbBf16::BT);
-  return (n_app > n_abs ? n_app : n_abs) + 1 <= kTargetCUs;
+  FusedGrid f;
+  return cache_type == kBF16 && fused_grid(a, d, f);
 }
 
 hipError_t launch_append(int ct, const AppendArgs& a, hipStream_t s) {
