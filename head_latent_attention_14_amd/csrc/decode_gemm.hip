@@ -132,7 +132,8 @@ __device__ __forceinline__ float merge_row(const GemmParams& p, int b, int h, in
 // the weight 2^(m_s - M) l_s) runs in lane k = j*RU + u of the wave, and the
 // weights reach the data through readlane; the arithmetic and its order are
 // those of merge_slots. A row with no slot left in a round loads slot 0 (a
-// valid address) and ignores it.
+// valid address) and ignores it: every load is unconditional, so none waits
+// at a branch join.
 template <int NR, int RU>
 __device__ __forceinline__ void merge_rows(const GemmParams& p, const int* b, const int64_t* wf,
                                            const int64_t* wl, int h, int lane, int step,
@@ -167,10 +168,15 @@ __device__ __forceinline__ void merge_rows(const GemmParams& p, const int* b, co
     }
     const int64_t kw = kwf + w0 + (int64_t)ku * step;
     const bool kin = lane < NR * RU && kw <= kwl;
+    // all of a round's loads go out before any is used: a load under a
+    // branch (a short-circuit test) would be followed by a wait for every
+    // load before it
+    const int64_t kwc = kin ? kw : 0;
     const int64_t ks = kin ? (kw + kb) * H + h : (int64_t)h;
-    const bool kok = kin && p.starts[kin ? kw : 0] != p.starts[kin ? kw + 1 : 0];
+    const int64_t kst0 = p.starts[kwc], kst1 = p.starts[kwc + 1];
     const float km = p.part_ml[ks * 2];
     const float kl = p.part_ml[ks * 2 + 1];
+    const bool kok = kin & (kst0 != kst1);
     float ke = 0.f;                                    // this lane's slot weight
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
@@ -247,8 +253,14 @@ mla_combine_kernel(GemmParams p) {
   char* x_lds = lds + G::W_BYTES;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int n0 = blockIdx.x * kNT, h = blockIdx.y, b0 = blockIdx.z * 16;
+  const int bw = b0 + wave;                            // this wave's row
+  // the row's workers (scalar loads; unconditional, so nothing waits for
+  // them at a branch join), and the weight slice while the merge runs
+  const int bc = bw < p.B ? bw : p.B - 1;
+  const int64_t wf[1] = {ld_const(p.wfirst, bc)};
+  const int64_t wl[1] = {ld_const(p.wlast, bc)};
   u32x4 wv[WP / TPW];
 #pragma unroll
   for (int k = 0; k < WP / TPW; ++k) {
@@ -257,14 +269,11 @@ mla_combine_kernel(GemmParams p) {
     wv[k] = *(const u32x4*)((const char*)p.w + (((int64_t)h * kDc + r) * kDv + n0) * 2 + c * 16);
   }
   {
-    const int b = b0 + wave;
     float acc[1][8] = {{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
-    if (b < p.B) {
+    if (bw < p.B) {
       // one row, its slot bookkeeping in lanes (vector loads: sixteen waves
       // of scalar loads per CU queue at the scalar cache)
-      const int bj[1] = {b};
-      const int64_t wf[1] = {ld_const(p.wfirst, b)};
-      const int64_t wl[1] = {ld_const(p.wlast, b)};
+      const int bj[1] = {bw};
       float mmax = -INFINITY, lsum = 0.f;
       merge_rows<1, 8>(p, bj, wf, wl, h, lane, 1, acc, &mmax, &lsum);
       if (wl[0] >= wf[0]) {
@@ -273,7 +282,7 @@ mla_combine_kernel(GemmParams p) {
         for (int i = 0; i < 8; ++i) acc[0][i] *= inv;
       }
       if (p.lse && blockIdx.x == 0 && lane == 0)
-        p.lse[(int64_t)b * p.H + h] = (lsum > 0.f) ? (mmax + __log2f(lsum)) * kLn2 : -INFINITY;
+        p.lse[(int64_t)bw * p.H + h] = (lsum > 0.f) ? (mmax + __log2f(lsum)) * kLn2 : -INFINITY;
     }
     *(bf16x8*)(x_lds + wave * G::XROW + 16 * lane) = pack_bf16x8(acc[0]);
   }
