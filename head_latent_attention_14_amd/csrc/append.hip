@@ -193,15 +193,19 @@ struct AppendBf16Lds {
   static constexpr int STAGE = 2 * OPND;   // weight rows, then hidden rows
   static constexpr int NST = 2;
   char stg[NST * STAGE];
-  float red[4][16][17];                    // [wave][column][token]
+  float red[8][16][17];                    // [wave][column][token] (up to 8 waves)
   float rowt[16][17];                      // [token][column]
   float2 rot[16][8];                       // (cos, sin) per token and pair (RoPE groups)
   int64_t trow[16];
   int tpos[16];
 };
 
-// One (16 tokens, 16 columns) block: token block tb, column group cg.
+// One (16 tokens, 16 columns) block: token block tb, column group cg, run by
+// NW waves (4 or 8), which share the copies and the contraction's k-steps.
+template <int NW>
 __device__ void append_bf16_block(const AppendArgs& a, int tb, int cg, AppendBf16Lds& L) {
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  constexpr int KPW = 32 / NW;             // k-steps of a full stage per wave
   constexpr int KC = AppendBf16Lds::KC;
   constexpr int RS = AppendBf16Lds::RS;
   constexpr int OPND = AppendBf16Lds::OPND;
@@ -236,8 +240,8 @@ __device__ void append_bf16_block(const AppendArgs& a, int tb, int cg, AppendBf1
     const int k0 = c * KC;
     char* sb = stg + (c % NST) * STAGE;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int i = wave + 4 * u;
+    for (int u = 0; u < 64 / NW; ++u) {
+      const int i = wave + NW * u;
       const int op = i >> 5, r = (i >> 1) & 15, pc = i & 1;
       if (k0 + pc * 512 >= D) continue;
       const uint32_t voff = (uint32_t)(((r * D) + k0 + pc * 512) * 2 + lane * 16);
@@ -291,20 +295,20 @@ __device__ void append_bf16_block(const AppendArgs& a, int tb, int cg, AppendBf1
     const char* sb = stg + (c % NST) * STAGE;
     const char* pa = sb + l16 * RS + g * 16;
     const char* pb = pa + OPND;
-    // wave w takes k-steps 8w .. 8w+7
+    // wave w takes k-steps KPW*w .. KPW*w + KPW-1
     if (nks == KC / 32) {                              // full stage: all reads, then the MFMAs
-      bf16x8 av[8], bv[8];
+      bf16x8 av[KPW], bv[KPW];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        av[u] = *(const bf16x8*)(pa + (8 * wave + u) * 64);
-        bv[u] = *(const bf16x8*)(pb + (8 * wave + u) * 64);
+      for (int u = 0; u < KPW; ++u) {
+        av[u] = *(const bf16x8*)(pa + (KPW * wave + u) * 64);
+        bv[u] = *(const bf16x8*)(pb + (KPW * wave + u) * 64);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc = mfma_bf16_k32(av[u], bv[u], acc);
+      for (int u = 0; u < KPW; ++u) acc = mfma_bf16_k32(av[u], bv[u], acc);
     } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int ks = 8 * wave + u;
+      for (int u = 0; u < KPW; ++u) {
+        const int ks = KPW * wave + u;
         if (ks < nks) acc = mfma_bf16_k32(*(const bf16x8*)(pa + ks * 64), *(const bf16x8*)(pb + ks * 64), acc);
       }
     }
@@ -317,9 +321,12 @@ __device__ void append_bf16_block(const AppendArgs& a, int tb, int cg, AppendBf1
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][4 * g + r][l16] = acc[r];
   __syncthreads();
-  {
+  if (tid < 256) {
     const int cc = tid >> 4, t = tid & 15;
-    rowt[t][cc] = red[0][cc][t] + red[1][cc][t] + red[2][cc][t] + red[3][cc][t];
+    float v = red[0][cc][t];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += red[w][cc][t];
+    rowt[t][cc] = v;
   }
   __syncthreads();
   if (j0 >= kDc && tid < 128) {                        // RoPE: pair pr of token t
@@ -330,32 +337,35 @@ __device__ void append_bf16_block(const AppendArgs& a, int tb, int cg, AppendBf1
     rowt[t][2 * pr + 1] = x0 * cs.y + x1 * cs.x;
   }
   __syncthreads();
-  {
+  if (tid < 256) {
     const int t = tid >> 4, cc = tid & 15;
     if (tok0 + t < a.n_tok && trow[t] >= 0)
       ((uint16_t*)a.rows)[trow[t] * kDrow + j0 + cc] = f32_to_bf16_bits(rowt[t][cc]);
   }
 }
 
-__global__ void __launch_bounds__(256)
+template <int NW>
+__global__ void __launch_bounds__(64 * NW)
 mla_append_bf16_kernel(AppendArgs a) {
   __shared__ __attribute__((aligned(1024))) AppendBf16Lds L;
-  append_bf16_block(a, blockIdx.x, blockIdx.y, L);
+  append_bf16_block<NW>(a, blockIdx.x, blockIdx.y, L);
 }
 
 // Append and the absorb launch of the following decode in one launch (bf16):
 // neither reads what the other writes (the absorb product and the work plan
-// read queries, weights and lengths, not cache rows). Workgroups [0, n_app)
-// run one append block each; the next n_absw run absorb tiles j and, when
-// it exists, j + n_absw (both tiles' loads go out first); the last one
-// builds the plan. An append block moves 128 KB through its CU, and a CU
-// issues its copies at a bounded rate, so the absorb tiles go to CUs of
-// their own rather than queueing their loads ahead of an append block's.
-__global__ void __launch_bounds__(256)
+// read queries, weights and lengths, not cache rows). Workgroups of eight
+// waves: [0, n_app) run one append block each; the next n_absw run absorb
+// tiles j (waves 0-3) and, when it exists, j + n_absw (waves 4-7) side by
+// side in their own LDS; the last one builds the plan. An append block
+// moves 128 KB through its CU, and a wave issues its copies at a bounded
+// rate, so the absorb tiles go to CUs of their own rather than queueing
+// their loads ahead of an append block's.
+__global__ void __launch_bounds__(512)
 mla_append_absorb_kernel(AppendArgs a, GemmParams g, int n_app, int n_absw, int n_abs) {
   using G = AbsorbBf16;
   __shared__ __attribute__((aligned(1024))) AppendBf16Lds L;
-  static_assert(G::LDS_BYTES <= (int)sizeof(AppendBf16Lds::stg), "absorb tile fits the append stages");
+  static_assert(2 * G::LDS_BYTES <= (int)sizeof(AppendBf16Lds::stg), "two absorb tiles fit the append stages");
+  static_assert(G::kChunks == 1, "an absorb tile's run() takes one barrier");
   const int wg = blockIdx.x;
   if (wg == (int)gridDim.x - 1) {
     build_plan(g, (int64_t*)L.stg, (int)(sizeof(L.stg) / 8));
@@ -363,30 +373,22 @@ mla_append_absorb_kernel(AppendArgs a, GemmParams g, int n_app, int n_absw, int 
   }
   if (wg < n_app) {
     const int ntb = (a.n_tok + 15) / 16;
-    append_bf16_block(a, wg % ntb, wg / ntb, L);
+    append_bf16_block<8>(a, wg % ntb, wg / ntb, L);
     return;
   }
   // absorb tile t: 64 columns from n0 of head h for batch rows from b0
   const int nxb = kDc / kNT;                             // absorb tiles per (head, batch slice)
-  auto tile = [&](int t, int& n0, int& h, int& b0) {
-    n0 = (t % nxb) * kNT;
-    h = (t / nxb) % g.H;
-    b0 = (t / nxb / g.H) * G::BT;
-  };
-  const int t0 = wg - n_app, t1 = t0 + n_absw;
-  const bool two = t1 < n_abs;
-  int n0a, ha, b0a, n0b = 0, hb = 0, b0b = 0;
-  typename G::Regs ra, rb;
-  tile(t0, n0a, ha, b0a);
-  G::load(g, n0a, ha, b0a, ra);
-  if (two) {
-    tile(t1, n0b, hb, b0b);
-    G::load(g, n0b, hb, b0b, rb);
-  }
-  G::run(g, n0a, ha, b0a, ra, L.stg);
-  if (two) {
-    __syncthreads();                                     // the first tile's LDS reads are done
-    G::run(g, n0b, hb, b0b, rb, L.stg);
+  const int half = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8);
+  const int t = wg - n_app + half * n_absw;
+  if (t < n_abs) {
+    const int n0 = (t % nxb) * kNT;
+    const int h = (t / nxb) % g.H;
+    const int b0 = (t / nxb / g.H) * G::BT;
+    typename G::Regs rg;
+    G::load(g, n0, h, b0, rg);
+    G::run(g, n0, h, b0, rg, L.stg + half * G::LDS_BYTES);
+  } else {
+    __syncthreads();                                     // the other half's run() barrier
   }
 }
 
@@ -411,7 +413,7 @@ hipError_t launch_append_absorb(const AppendArgs& a, const DecodePlan& plan, con
                                 hipStream_t s) {
   FusedGrid f;
   if (!fused_grid(a, d, f)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mla_append_absorb_kernel, dim3(f.n_app + f.n_absw + 1), dim3(256), 0, s, a,
+  hipLaunchKernelGGL(mla_append_absorb_kernel, dim3(f.n_app + f.n_absw + 1), dim3(512), 0, s, a,
                      absorb_params(plan, d), f.n_app, f.n_absw, f.n_abs);
   return hipGetLastError();
 }
@@ -427,7 +429,7 @@ hipError_t launch_append(int ct, const AppendArgs& a, hipStream_t s) {
   dim3 grid((a.n_tok + 15) / 16, ct == kFP8 ? 1 : kNumGroups);
   switch (ct) {
     case kF32: hipLaunchKernelGGL(mla_append_kernel<kF32>, grid, dim3(256), 0, s, a); break;
-    case kBF16: hipLaunchKernelGGL(mla_append_bf16_kernel, grid, dim3(256), 0, s, a); break;
+    case kBF16: hipLaunchKernelGGL(mla_append_bf16_kernel<8>, grid, dim3(512), 0, s, a); break;
     case kFP8: hipLaunchKernelGGL(mla_append_kernel<kFP8>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }

@@ -227,7 +227,9 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
 // and y. The weight slice W[h][0:KD][n0:n0+64] is staged in LDS KC rows at a
 // time. load() issues the X tile and the first weight chunk into registers
 // (so a caller can put other work between the loads and their use); run()
-// stages them in LDS (`lds`, LDS_BYTES), computes and stores Y.
+// stages them in LDS (`lds`, LDS_BYTES), computes and stores Y. It runs on
+// 256 threads: threads 256k..256k+255 of a larger workgroup form a group of
+// their own (each with its own LDS), and run() takes 2*kChunks - 1 barriers.
 template <int AT, int KD, int ND, int NBT, int KC>
 struct HeadGemm {
   using E = typename std::conditional<AT == kF32, float, __bf16>::type;
@@ -241,6 +243,7 @@ struct HeadGemm {
   static constexpr int WPR = kNT * ES / 16;           // 16-byte pieces per weight row
   static constexpr int W_BYTES = KC * WROW;
   static constexpr int LDS_BYTES = KC * WROW + BT * XROW;
+  static constexpr int kChunks = KD / KC;             // weight chunks staged by run()
   static_assert(XP % 256 == 0 && WP % 256 == 0, "whole rounds of 16-byte pieces");
 
   struct Regs {
@@ -249,7 +252,7 @@ struct HeadGemm {
   };
 
   __device__ static void load_w(const GemmParams& p, int h, int n0, int k0, u32x4* v) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & 255;
 #pragma unroll
     for (int k = 0; k < WP / 256; ++k) {
       const int i = tid + 256 * k;
@@ -258,7 +261,7 @@ struct HeadGemm {
     }
   }
   __device__ static void store_w(char* w_lds, const u32x4* v) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & 255;
 #pragma unroll
     for (int k = 0; k < WP / 256; ++k) {
       const int i = tid + 256 * k;
@@ -267,7 +270,7 @@ struct HeadGemm {
     }
   }
   __device__ static void load(const GemmParams& p, int n0, int h, int b0, Regs& rg) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & 255;
 #pragma unroll
     for (int k = 0; k < XP / 256; ++k) {
       const int i = tid + 256 * k;
@@ -279,7 +282,7 @@ struct HeadGemm {
     load_w(p, h, n0, 0, rg.wv);
   }
   __device__ static void run(const GemmParams& p, int n0, int h, int b0, Regs& rg, char* lds) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & 255;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int l16 = lane & 15;
