@@ -13,8 +13,8 @@
 
 namespace mla {
 
-// One head-GEMM tile per workgroup, numbered (64-column block, head, batch
-// slice of 16*NBT rows) with the column block fastest. The absorb launch has
+// One head-GEMM tile per workgroup: 64 columns of one head for a batch slice
+// of 16*NBT rows (the numbering below groups tiles by XCD). The absorb launch has
 // one more workgroup, the first (dispatched before the CUs fill up), which
 // builds the plan.
 template <int AT, int KD, int ND, int NBT, int KC>
@@ -31,8 +31,15 @@ mla_headgemm_kernel(GemmParams p) {
     --i;
   }
   constexpr int NXB = ND / kNT;
+  // The column tiles of one (head, batch slice) read the same X rows, and
+  // the batch slices of one head the same weight slices. Workgroups are
+  // dispatched to the 8 XCDs in turn, each with its own L2: group (h, slice)
+  // j runs on the XCD of workgroups j % 8 (mod 8), so that L2 serves the
+  // repeats. A bijection as the group count H * slices is a multiple of 8.
+  const int slot = i / 8;
+  const int grp = i % 8 + 8 * (slot / NXB);
   typename G::Regs rg;
-  const int n0 = (i % NXB) * kNT, h = (i / NXB) % p.H, b0 = (i / NXB / p.H) * G::BT;
+  const int n0 = (slot % NXB) * kNT, h = grp % p.H, b0 = (grp / p.H) * G::BT;
   G::load(p, n0, h, b0, rg);
   G::run(p, n0, h, b0, rg, lds);
 }
