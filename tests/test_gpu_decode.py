@@ -287,6 +287,26 @@ def test_append_absorb_two_launch_path():
     assert np.array_equal(o, o_ref)
 
 
+def test_append_absorb_paired_absorb_tiles():
+    # 32 heads, 16 sequences: 36 append workgroups and 256 absorb tiles on
+    # 219 workgroups, 37 of which run a second tile beside the first; rows
+    # and outputs match append then decode bitwise, and the oracle
+    wl = W.WORKLOADS["v2lite_bf16"]
+    lengths = np.random.default_rng(32).integers(1, 700, size=16)
+    p = W.make_problem(wl, seed=32, B=16, lengths=lengths, H=32)
+    log(f"[append+absorb paired tiles] B=16 H=32 lengths={lengths.tolist()}")
+    a = DeviceProblem(p)
+    o_ref, _ = a.step(poison=True)
+    rows_ref = a.cache.rows.cpu().view(torch.int16).numpy().copy()
+    b = DeviceProblem(p)
+    o, _, rows = _fused_step(b)
+    assert np.array_equal(rows, rows_ref)
+    assert np.array_equal(o, o_ref)
+    pairs = [(0, 0), (7, 31), (15, 17)]
+    ro, _ = OracleView(p).decode(pairs)
+    assert rel_l2(np.stack([o[bb, hh] for bb, hh in pairs]), ro) <= TOL["bf16"]
+
+
 def test_combine_fused_launch_all_outputs():
     # 64 short sequences at 16 heads: few slots per sequence, so the merge and
     # W_UV run as one launch; every output and lse against the oracle, with
