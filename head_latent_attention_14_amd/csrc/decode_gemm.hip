@@ -247,9 +247,8 @@ mla_merge_kernel(GemmParams p) {
 // partial slots: workgroup (64 output columns, head h, 16 batch rows) with
 // sixteen waves. Each wave merges one row (all its slot loads in one round)
 // while the weight slice is in flight, writes the merged row in bf16 to LDS,
-// and four waves then multiply. The
-// two column workgroups of a (head, rows) both merge the rows; the first
-// writes lse.
+// and four waves then multiply. The two column workgroups of a (head, rows)
+// both merge the rows; the first writes lse.
 __global__ void __launch_bounds__(1024)
 mla_combine_kernel(GemmParams p) {
   using G = HeadGemm<kBF16, kDc, kDv, 1, kDc>;
