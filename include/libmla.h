@@ -222,9 +222,9 @@ mla_status_t mla_decode_attend_combine(const mla_cache_t* cache, const int32_t* 
  * then mla_decode's (seq_len ... stream), with the same meaning, ownership and
  * rules; both argument sets are validated before anything runs. Calling
  * mla_decode_attend and mla_decode_combine (or mla_decode_attend_combine)
- * afterwards with the same decode arguments and workspace completes the decode step: the result equals
- * mla_append then mla_decode. For callers that run a decode step right after
- * appending its token.
+ * afterwards with the same decode arguments and workspace completes the
+ * decode step: the result equals mla_append then mla_decode, bit for bit.
+ * For callers that run a decode step right after appending its token.
  */
 mla_status_t mla_append_absorb(const mla_cache_t* cache,
                                const void* h, int32_t n_tok, int32_t d_model,
