@@ -44,7 +44,7 @@ DecodePlan make_plan(int ct, int B, int H) {
   // what a segment start costs in tiles of work: queries in and a partial
   // out; the pair kernel moves 147 KB of queries and 128 KB of partial per
   // segment and drains its copy queue (measured best: 1 for the streaming
-  // kernel, 5 for the pair kernel, against 1..6)
+  // kernel against 0..6, 5 for the pair kernel against 1..6)
   p.seg_tiles = p.pair ? 5 : 1;
   int w = kTargetCUs / p.head_groups;
   w = w < 8 ? 8 : (w / 8) * 8;                 // a multiple of the 8 XCDs
