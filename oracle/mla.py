@@ -133,16 +133,6 @@ def quantize_rows(rows: np.ndarray, dtype: str) -> Tuple[np.ndarray, Optional[np
     raise ValueError(dtype)
 
 
-def widen_rows(rows, dtype: str, row_scale=None) -> np.ndarray:
-    """fp64 view of stored cache rows: f32/bf16 values widened, fp8 codes
-    decoded and multiplied by their row's scale."""
-    if dtype == "fp8":
-        codes = np.asarray(rows, dtype=np.uint8)
-        sc = np.asarray(row_scale, dtype=np.float64)
-        return e4m3_decode(codes) * sc[..., None]
-    return np.asarray(rows, dtype=np.float64)
-
-
 # ----------------------------------------------------------------------------
 # decode: unabsorbed textbook attention ([A], [B], R1, R2, R4, R5)
 # ----------------------------------------------------------------------------

@@ -64,3 +64,81 @@ def test_rows_beyond_length_are_not_read():
     o2, _ = OracleView(p).decode()
     p.rows.copy_(rows)
     assert np.array_equal(o1, o2)
+
+
+def _selection_problem(through: str):
+    """B sequences x H heads where every (b, h) has its own one-hot query
+    aimed at a distinct token t*(b, h) of its sequence, so that softmax puts
+    all but ~1e-26 of the weight on that token and o[b, h] must equal row
+    t*(b, h) of W_UV[h] (v = W_UV[h]^T c with c = e_t*): a query, W_UK or
+    W_UV taken from the wrong sequence or head lands on another token or
+    another head's weights.
+
+    through = "rope": the score is carried by q_pe . k_pe with k_pe_t = e_t;
+    through = "latent": by q_nope . (W_UK[h] c_t) with c_t = e_t and W_UK[h]
+    a head-specific permutation (row (j + 7h) % 128 picks latent dim j)."""
+    B, H, L = 3, 4, 12
+    rng = np.random.default_rng(11)
+    alpha = 60.0 / mla.softmax_scale()         # scaled winning score 60
+    tstar = np.array([[(5 * b + 3 * h + 1) % L for h in range(H)] for b in range(B)])
+    assert len({(b, int(tstar[b, h])) for b in range(B) for h in range(H)}) > B  # distinct targets
+    rows = np.zeros((B, L, 576))
+    for b in range(B):
+        for t in range(L):
+            if through == "rope":
+                rows[b, t, 512 + t] = 1.0
+                rows[b, t, :512] = rng.standard_normal(512)   # latent part carries no score
+            else:
+                rows[b, t, t] = 1.0
+    q_nope = np.zeros((B, H, 128))
+    q_pe = np.zeros((B, H, 64))
+    w_uk = np.zeros((H, 128, 512))
+    for h in range(H):
+        for j in range(512):
+            w_uk[h, (j + 7 * h) % 128, j] = 1.0 if through == "latent" else 0.0
+    for b in range(B):
+        for h in range(H):
+            t = int(tstar[b, h])
+            if through == "rope":
+                q_pe[b, h, t] = alpha
+            else:
+                q_nope[b, h, (t + 7 * h) % 128] = alpha
+    w_uv = rng.standard_normal((H, 512, 128)) / np.sqrt(512)
+    return B, H, L, rows, q_nope, q_pe, w_uk, w_uv, tstar
+
+
+def test_problem_decode_selects_each_sequence_and_head():
+    """Pins the per-(b, h) choice of q_nope, q_pe, W_UK and W_UV in the
+    problem-level decode (decode_problem / decode_sampled) against the
+    closed-form one-hot limit: o[b, h] = W_UV[h]^T c_t*, lse = the winning
+    score (+ ln(1 + (L-1) e^-60))."""
+    for through in ("rope", "latent"):
+        B, H, L, rows, q_nope, q_pe, w_uk, w_uv, tstar = _selection_problem(through)
+        o, lse = mla.decode_problem(lambda b: rows[b], q_nope, q_pe, w_uk, w_uv, B, H)
+        for b in range(B):
+            for h in range(H):
+                t = int(tstar[b, h])
+                want = rows[b, t, :512] @ w_uv[h]
+                assert np.allclose(o[b, h], want, rtol=0, atol=1e-13 * np.abs(want).max()), \
+                    (through, b, h)
+                assert abs(lse[b, h] - (60.0 + np.log1p((L - 1) * np.exp(-60.0)))) < 1e-12
+        # the sampled form picks the same pairs in any order
+        pairs = [(2, 1), (0, 3), (1, 2), (0, 0)]
+        os_, ls_ = mla.decode_sampled(lambda b: rows[b], q_nope, q_pe, w_uk, w_uv, pairs)
+        for n, (b, h) in enumerate(pairs):
+            assert np.array_equal(os_[n], o[b, h]) and ls_[n] == lse[b, h]
+
+
+def test_oracle_view_selects_sequence_rows():
+    """OracleView.rows64 hands decode the rows of the right sequence: each
+    sequence's rows are marked with its index, and L = 1 per head gives
+    W_UV[h]^T of that sequence's own row."""
+    p = W.make_problem(W.WORKLOADS["tiny_fp32"], B=3, lengths=np.array([1, 1, 1]), H=16)
+    for b in range(3):
+        p.rows[int(p.seq_start[b])] = float(b + 1)
+    v = OracleView(p)
+    o, _ = v.decode()
+    for b in range(3):
+        for h in (0, 15):
+            want = np.full(512, float(b + 1)) @ v.w_uv[h]
+            assert np.allclose(o[b, h], want, rtol=1e-13, atol=1e-13)
