@@ -1,35 +1,37 @@
 #!/usr/bin/env python3
-"""Benchmark of one MLA decode step on one MI355X.
+"""Benchmark of MLA decode steps on one MI355X.
 
-A step is one pass of the whole hot path over one batch: mla_append of one
-new token per sequence, then mla_decode (absorb W_UK, attention over the
-latent cache, merge + W_UV) for every sequence. The append and the absorb
-stage go through mla_append_absorb (one launch: neither reads what the other
-writes), then mla_decode_attend_combine. The default workload is the
-DeepSeek-V2-Lite-shaped decode (B=64, H=16, L ~ U[1024, 4096], bf16 cache,
-d_model 2048). Inputs are synthetic and seeded; several replicas of the
-cache and weights are rotated so each step reads its cache from HBM, not
-from the 256 MB Infinity Cache.
+A step is one pass of the whole hot path over one batch: for every sequence,
+absorb W_UK into the query, attend over the sequence's latent cache (split-K
+partials), merge the partials and apply W_UV; workloads that append (the
+DeepSeek-V2-Lite shape) first write one new latent row per sequence
+(mla_append_absorb, then mla_decode_attend_combine). Inputs are synthetic
+and seeded; several replicas of the cache and weights rotate so every step
+reads its cache from HBM, not from the 256 MB Infinity Cache.
 
-Prints one JSON line. `value` is the step's algorithmic bytes (cache rows,
-weights, activations and outputs the method must move) per second, over a
-timed region of whole steps with events only at its ends (the larger of the
-wall clock and the GPU events); untimed warmup steps come first, enough for
-the chip to reach its sustained clock. A second pass with an event between
-every two steps gives the per-step p10/p50/p90. The attention
-kernel's own duration (the roofline entry) is then measured as the same
-number of attention launches back to back on the launch stream, rotating over
-the replicas, between two HIP events. A second workload (the 128-head V2
-shape by default) is measured the same way and reported under "secondary",
-with its attention rate also against the bf16 MFMA peak.
+The headline workload is the DeepSeek-V2-shaped decode (B=32, H=128,
+L ~ U[2048, 8192], bf16 cache). The DeepSeek-V2-Lite step (B=64, H=16, with
+append), the 128K-token decode (B=4, H=128) and the fp8-cache decode (B=128,
+H=128) are measured the same way and reported under "workloads", each with
+its own roofline block; they run first, so the headline is timed with the
+chip at its sustained clock. For each workload: W untimed warmup steps, then
+exactly K timed steps with events only at the ends of the timed region
+(`ms_per_step` is the larger of the wall clock and the GPU events); a second
+pass with an event between every two steps gives p10/p50/p90. The attention
+kernel's own duration (the roofline entry) is K attention launches back to
+back on the launch stream, rotating over the replicas, between two HIP events.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -41,25 +43,27 @@ if ROOT not in sys.path:
 
 METRIC = "MLA decode latent-cache GB/s + TFLOP/s, % of MI355X roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA, MI355X
-KERNEL_SOURCES = ["head_latent_attention_14_amd/csrc/decode_attn.hip",
-                  "head_latent_attention_14_amd/csrc/decode_attn_stream.hip",
-                  "head_latent_attention_14_amd/csrc/attn_tile.h",
-                  "head_latent_attention_14_amd/csrc/common.h"]
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # dense, MI355X
+HEADLINE = "v2_bf16"
+OTHERS = ["v2lite_bf16", "long_bf16", "fp8_cache"]
+# every source that decides what the attention launch reads and writes: the
+# kernels, the work split (api.cpp, gemm_tile.h) and the shared headers
+KERNEL_SOURCES = sorted(glob.glob(os.path.join(ROOT, "head_latent_attention_14_amd", "csrc", "*")))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def recorded_traffic(workload: str):
     """HBM bytes per attention launch from the committed counter runs, if
-    they were taken on the current kernel source for this workload."""
+    they were taken on the current kernel sources for this workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -74,19 +78,15 @@ def recorded_traffic(workload: str):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    # timed steps: the wall clock around them carries a fixed cost (first
-    # launch, final synchronisation; about 90 us), which 300 steps amortise
-    ap.add_argument("--steps", type=int, default=300)
-    # untimed warmup: the 128-head step needs a few hundred steps (tens of ms)
-    # before the chip settles at its sustained clock (110.7 -> 94.7 us/step
-    # measured between 10 and 500 warmup steps)
-    ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--workload", default="v2lite_bf16")
-    ap.add_argument("--secondary", default="v2_bf16",
-                    help="a second workload measured the same way and reported under "
-                         "'secondary' (empty: none)")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE, help="the headline workload")
+    ap.add_argument("--others", default=",".join(OTHERS),
+                    help="comma-separated workloads measured first and reported under "
+                         "'workloads' (empty: none)")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 2x the MALL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
@@ -95,19 +95,25 @@ def parse():
     return ap.parse_args()
 
 
+def blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return f"{i.get('internal_api')} {i.get('version')}", i.get("num_threads")
+    except Exception:
+        pass
+    return None, None
+
+
 def cpu_baseline(p, seconds: float):
     """Time the fp64 oracle on whole sequences of the same problem until about
     `seconds` of CPU work; report its rate in the metric's unit."""
-    from oracle import mla as omla
     from oracle.problem import OracleView
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        blas_threads = None
+    blas, blas_threads = blas_info()
     view = OracleView(p)
     B, H = p.q_nope.shape[:2]
-    e_c = {"f32": 4, "bf16": 2, "fp8": 1}[p.wl.cache] + 0
+    e_c = {"f32": 4, "bf16": 2, "fp8": 1}[p.wl.cache]
     sf = 4 if p.wl.cache == "fp8" else 0
     e_a = {"f32": 4, "bf16": 2}[p.wl.act]
     t0 = time.perf_counter()
@@ -121,15 +127,72 @@ def cpu_baseline(p, seconds: float):
     el = time.perf_counter() - t0
     # the sample's share of the step's algorithmic bytes
     by = tokens * (576 * e_c + sf) + 2 * H * 128 * 512 * e_a * done / B + done * H * (192 + 128) * e_a
+    # the unabsorbed oracle's own fp64 work: K and V expansions plus scores and values
+    flops = tokens * H * (4 * 128 * 512 + 2 * (128 + 64) + 2 * 128)
     cores = len(os.sched_getaffinity(0))
     return {"value": by / el / 1e9, "unit": "GB/s", "cores": blas_threads or cores,
             "kind": "oracle",
             "sample": f"fp64 unabsorbed oracle, {done} sequence decodes over the {B} sequences "
                       f"(all {H} heads, {tokens} cached tokens, {el:.1f} s, "
-                      f"{cores} host cores visible)"}
+                      f"{cores} host cores visible)",
+            "blas": blas, "blas_threads": blas_threads,
+            "attended_tokens_per_s": round(tokens / el, 1),
+            "fp64_gflops": round(flops / el / 1e9, 2), "seconds": round(el, 2)}
 
 
-def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0):
+def gpu_clock_mhz():
+    """Current shader clock as the driver reports it (sysfs, else rocm-smi)."""
+    for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+        try:
+            for line in open(f):
+                if "*" in line:
+                    return float(line.split(":")[1].strip().rstrip("*").strip().lower()
+                                 .replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            pass
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+        for card in d.values():
+            for k, v in card.items():
+                if "sclk" in k.lower():
+                    return float(str(v).strip("()Mhz").replace("Mhz", ""))
+    except Exception:
+        pass
+    return None
+
+
+def gpu_info(torch):
+    """The device as the runtime reports it (name, compute units, clocks)."""
+    pr = torch.cuda.get_device_properties(0)
+    info = {"name": pr.name, "compute_units": pr.multi_processor_count,
+            "arch": getattr(pr, "gcnArchName", None)}
+    clk = getattr(pr, "clock_rate", None)               # kHz where the build exposes it
+    info["max_clock_mhz"] = round(clk / 1e3) if clk else None
+    return info
+
+
+def parity_sample(p, o, lse, n_seq: int = 2):
+    """rel-L2 and max-abs of the measured run's outputs against the oracle on
+    every head of `n_seq` sequences (the first and the longest)."""
+    from oracle.problem import OracleView
+    B, H = p.q_nope.shape[:2]
+    seqs = sorted({0, int(np.argmax(p.seq_len))})[:n_seq]
+    pairs = [(b, h) for b in seqs for h in range(H)]
+    ro, rl = OracleView(p).decode(pairs)
+    got = np.stack([o[b, h] for b, h in pairs])
+    gl = np.array([lse[b, h] for b, h in pairs])
+    err = float(np.linalg.norm(got - ro) / np.linalg.norm(ro))
+    bound = {"f32": 1e-5, "bf16": 2e-2, "fp8": 4e-2}[p.wl.cache]
+    return {"rel_l2": float(f"{err:.4g}"), "bound": bound, "ok": bool(err <= bound),
+            "max_abs": float(f"{np.abs(got - ro).max():.4g}"),
+            "lse_max_abs": float(f"{np.abs(gl - rl).max():.4g}"),
+            "sample": f"all {H} heads of sequences {seqs}"}
+
+
+def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0,
+            parity: bool = False):
     """Time `steps` decode steps of workload `name` (append when the workload
     has it, then absorb -> attend -> combine). Returns the measurements."""
     wl = W.WORKLOADS[name]
@@ -205,6 +268,7 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
     wall_ms = (t1 - t0) * 1e3 / steps
     gpu_ms = start.elapsed_time(end) / steps
     ms = max(wall_ms, gpu_ms)
+    clock = gpu_clock_mhz()
 
     # the distribution over steps: another `steps` steps, an event between
     # every two (outside the timed region above)
@@ -234,29 +298,50 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
     a1.record(stream)
     torch.cuda.synchronize()
     attn_ms = a0.elapsed_time(a1) / steps
+
+    par = None
+    if parity:
+        # the outputs of one full step of replica 0 against the oracle
+        step(0)
+        torch.cuda.synchronize()
+        r = reps[0]
+        par = parity_sample(p, r["out"].double().cpu().numpy(), r["lse"].double().cpu().numpy())
     del reps
     torch.cuda.empty_cache()
     return dict(wl=wl, p=p, T=p.T, B=B, H=H, R=R, ms=ms, wall_ms=wall_ms, gpu_ms=gpu_ms,
                 step_pct=step_pct, step_bytes=step_bytes,
                 step_flops=step_flops, attn_bytes=ab["cache"], attn_flops=fl["attention"],
-                attn_ms=attn_ms)
+                attn_ms=attn_ms, clock_mhz=clock, parity=par)
 
 
-def gpu_info(torch):
-    """The device as the runtime reports it (name, compute units, clock)."""
-    pr = torch.cuda.get_device_properties(0)
-    info = {"name": pr.name, "compute_units": pr.multi_processor_count,
-            "arch": getattr(pr, "gcnArchName", None)}
-    clk = getattr(pr, "clock_rate", None)               # kHz where the build exposes it
-    info["max_clock_mhz"] = round(clk / 1e3) if clk else None
-    return info
+def describe(wl, m) -> str:
+    return (f"{wl.name}: MLA decode step, {'append 1 token/seq + ' if wl.append else ''}"
+            f"decode, B={m['B']}, H={m['H']}, L~U[{wl.lo},{wl.hi}], {wl.cache} latent cache")
+
+
+def roofline(m, name: str) -> dict:
+    """The attention kernel against the HBM roofline (the binding bound at
+    every shape: its flop per cached byte is below the MFMA ridge), with its
+    matrix rate against the MFMA peak of the arithmetic it runs."""
+    wl = m["wl"]
+    gbs = m["attn_bytes"] / (m["attn_ms"] * 1e-3) / 1e9
+    tf = m["attn_flops"] / (m["attn_ms"] * 1e-3) / 1e12
+    mfma_dtype = "f32" if wl.cache == "f32" else "bf16"
+    return {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(name),
+            "kernel": "attention (mla_decode_attend)",
+            "kernel_avg_us": round(m["attn_ms"] * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(m["attn_bytes"]),
+            "tflops": round(tf, 2), "mfma_dtype": mfma_dtype,
+            "mfma_frac": round(tf / MFMA_PEAK_TFLOPS[mfma_dtype], 4)}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(every run here uses a single GPU; the design notes say how the path would "
+              "shard)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -273,11 +358,29 @@ def main():
     import workloads as W
 
     torch.cuda.set_device(0)
-    m = measure(mla, W, torch, args.workload, args.steps, args.warmup, args.replicas)
+    others = [w for w in args.others.split(",") if w and w != args.workload]
+    blocks = {}
+    for name in others:
+        s = measure(mla, W, torch, name, args.steps, args.warmup)
+        blocks[name] = {
+            "workload": describe(s["wl"], s),
+            "ms_per_step": round(s["ms"], 5),
+            "value": round(s["step_bytes"] / (s["ms"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "tflops": round(s["step_flops"] / (s["ms"] * 1e-3) / 1e12, 3),
+            "step_us_percentiles": s["step_pct"],
+            "step_us_host_gpu": [round(s["wall_ms"] * 1e3, 2), round(s["gpu_ms"] * 1e3, 2)],
+            "T": s["T"], "step_bytes": int(s["step_bytes"]), "clock_mhz": s["clock_mhz"],
+            "roofline": roofline(s, name),
+        }
+        print(f"# measured {name}: {s['ms'] * 1e3:.2f} us/step, attention "
+              f"{s['attn_ms'] * 1e3:.2f} us", file=sys.stderr, flush=True)
+
+    m = measure(mla, W, torch, args.workload, args.steps, args.warmup, args.replicas,
+                parity=not args.no_parity)
     wl, ms = m["wl"], m["ms"]
     value = m["step_bytes"] / (ms * 1e-3) / 1e9
-    attn_gbs = m["attn_bytes"] / (m["attn_ms"] * 1e-3) / 1e9
-    traffic = recorded_traffic(args.workload)
+    gi = gpu_info(torch)
+    gi["clock_mhz_after_timed_steps"] = m["clock_mhz"]
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -292,42 +395,19 @@ def main():
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-cache/bf16"}[wl.cache],
         "data": "synthetic (seeded normal draws; random-init weights of the DeepSeek-V2(-Lite) "
                 "MLA shapes)",
-        "config": {"workload": f"{wl.name}: MLA decode step, append {'1 token/seq + ' if wl.append else ''}"
-                               f"decode, B={m['B']}, H={m['H']}, L~U[{wl.lo},{wl.hi}], {wl.cache} latent cache",
+        "config": {"workload": describe(wl, m),
                    "B": m["B"], "H": m["H"], "T": m["T"], "d_c": 512, "d_r": 64,
                    "d_model": wl.d_model if wl.append else None, "replicas": m["R"]},
         "tflops": round(m["step_flops"] / (ms * 1e-3) / 1e12, 3),
         "step_us_percentiles": m["step_pct"],
         "step_us_host_gpu": [round(m["wall_ms"] * 1e3, 2), round(m["gpu_ms"] * 1e3, 2)],
-        "gpu": gpu_info(torch),
+        "gpu": gi,
         "attended_tokens_per_s": round(m["T"] / (ms * 1e-3), 1),
         "step_bytes": int(m["step_bytes"]),
-        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "attention (mla_decode_attend)",
-                     "kernel_avg_us": round(m["attn_ms"] * 1e3, 3),
-                     "algorithmic_bytes_per_launch": int(m["attn_bytes"])},
+        "roofline": roofline(m, args.workload),
+        "parity": m["parity"],
+        "workloads": blocks,
     }
-    if args.secondary and args.secondary != args.workload:
-        s = measure(mla, W, torch, args.secondary, args.steps, args.warmup)
-        sw = s["wl"]
-        s_attn = s["attn_bytes"] / (s["attn_ms"] * 1e-3) / 1e9
-        out["secondary"] = {
-            "workload": f"{sw.name}: MLA decode step, B={s['B']}, H={s['H']}, "
-                        f"L~U[{sw.lo},{sw.hi}], {sw.cache} latent cache",
-            "ms_per_step": round(s["ms"], 5),
-            "step_us_percentiles": s["step_pct"],
-            "step_us_host_gpu": [round(s["wall_ms"] * 1e3, 2), round(s["gpu_ms"] * 1e3, 2)],
-            "value_GBps": round(s["step_bytes"] / (s["ms"] * 1e-3) / 1e9, 2),
-            "tflops": round(s["step_flops"] / (s["ms"] * 1e-3) / 1e12, 3),
-            "hbm_frac_step": round(s["step_bytes"] / (s["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "attention_kernel_us": round(s["attn_ms"] * 1e3, 3),
-            "attention_GBps": round(s_attn, 2),
-            "attention_hbm_frac": round(s_attn / HBM_PEAK_GBS, 4),
-            "attention_tflops": round(s["attn_flops"] / (s["attn_ms"] * 1e-3) / 1e12, 2),
-            "attention_mfma_frac": round(s["attn_flops"] / (s["attn_ms"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
-            "attention_traffic": recorded_traffic(args.secondary),
-        }
     if not args.no_cpu_baseline:
         p = W.make_problem(wl)
         out["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)

@@ -122,6 +122,71 @@ def _stream(stream) -> int:
     return int(stream)
 
 
+_ACT_DTYPES = (torch.float32, torch.bfloat16)
+_CACHE_TORCH = {MLA_DTYPE_F32: torch.float32, MLA_DTYPE_BF16: torch.bfloat16}
+
+
+def _expect(t: Optional[torch.Tensor], name: str, shape, dtype, device) -> None:
+    """Raise unless `t` has exactly `shape`, `dtype` and `device`: the C side
+    trusts every extent it derives from the cache and the head count, so a
+    mismatched tensor would be read or written past its end on the device."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device} (the cache's device)")
+
+
+def _act_dtype(q_nope: torch.Tensor) -> torch.dtype:
+    if q_nope.dtype not in _ACT_DTYPES:
+        raise TypeError(f"activations must be float32 or bfloat16, not {q_nope.dtype}")
+    return q_nope.dtype
+
+
+def check_decode_args(cache: "LatentCache", seq_len, q_nope, q_pe, w_uk, w_uv, out, lse,
+                      workspace) -> int:
+    """Check every decode tensor against (B = cache.num_seqs, H = q_nope's
+    heads), the activation dtype (q_nope's), and the cache's device; returns H."""
+    cache.check()
+    dev = cache.rows.device
+    B = cache.num_seqs
+    if not isinstance(q_nope, torch.Tensor) or q_nope.dim() != 3:
+        raise ValueError("q_nope must be a [B, H, 128] tensor")
+    H = q_nope.shape[1]
+    act = _act_dtype(q_nope)
+    _expect(seq_len, "seq_len", (B,), torch.int32, dev)
+    _expect(q_nope, "q_nope", (B, H, D_NOPE), act, dev)
+    _expect(q_pe, "q_pe", (B, H, D_R), act, dev)
+    _expect(w_uk, "w_uk", (H, D_NOPE, D_C), act, dev)
+    _expect(w_uv, "w_uv", (H, D_C, D_V), act, dev)
+    _expect(out, "out", (B, H, D_V), act, dev)
+    if lse is not None:
+        _expect(lse, "lse", (B, H), torch.float32, dev)
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 \
+            or workspace.dim() != 1 or workspace.device != dev:
+        raise ValueError(f"workspace must be a 1-D uint8 tensor on {dev}")
+    return H
+
+
+def check_append_args(cache: "LatentCache", h, w_dkv, w_kr, tok_seq, tok_pos) -> None:
+    """Check the append tensors against h's [n_tok, d_model], the activation
+    dtype (h's) and the cache's device."""
+    cache.check()
+    dev = cache.rows.device
+    if not isinstance(h, torch.Tensor) or h.dim() != 2:
+        raise ValueError("h must be a [n_tok, d_model] tensor")
+    n_tok, d_model = h.shape
+    act = _act_dtype(h)
+    _expect(h, "h", (n_tok, d_model), act, dev)
+    _expect(w_dkv, "w_dkv", (D_C, d_model), act, dev)
+    _expect(w_kr, "w_kr", (D_R, d_model), act, dev)
+    _expect(tok_seq, "tok_seq", (n_tok,), torch.int32, dev)
+    _expect(tok_pos, "tok_pos", (n_tok,), torch.int32, dev)
+
+
 @dataclasses.dataclass
 class LatentCache:
     """Device tensors of a ragged latent cache (see mla_cache_t)."""
@@ -138,11 +203,23 @@ class LatentCache:
     def num_seqs(self) -> int:
         return self.seq_start.shape[0]
 
-    def struct(self) -> mla_cache_t:
-        if self.seq_start.dtype != torch.int64 or self.seq_capacity.dtype != torch.int32:
-            raise TypeError("seq_start must be int64 and seq_capacity int32")
+    def check(self) -> None:
+        """Shapes, dtypes and devices of the cache tensors."""
         if self.rows.dim() != 2 or self.rows.shape[1] != D_ROW:
             raise ValueError("rows must be [total_rows, 576]")
+        dev = self.rows.device
+        B = self.seq_start.shape[0] if self.seq_start.dim() == 1 else -1
+        if B < 1:
+            raise ValueError("seq_start must be a non-empty 1-D tensor")
+        _expect(self.seq_start, "seq_start", (B,), torch.int64, dev)
+        _expect(self.seq_capacity, "seq_capacity", (B,), torch.int32, dev)
+        if self.dtype == MLA_DTYPE_FP8_E4M3:
+            _expect(self.row_scale, "row_scale", (self.rows.shape[0],), torch.float32, dev)
+        elif self.row_scale is not None:
+            raise ValueError("row_scale is only for an fp8 cache")
+
+    def struct(self) -> mla_cache_t:
+        self.check()
         return mla_cache_t(self.dtype, D_C, D_R, self.num_seqs, self.rows.shape[0],
                            _ptr(self.rows), _ptr(self.row_scale), _ptr(self.seq_start),
                            _ptr(self.seq_capacity))
@@ -160,8 +237,7 @@ def mla_append(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: t
                tok_seq: torch.Tensor, tok_pos: torch.Tensor, rope_base: float,
                stream=None) -> None:
     """Write (W_DKV h) || RoPE(W_KR h, pos) into the cache (see libmla.h)."""
-    if tok_seq.dtype != torch.int32 or tok_pos.dtype != torch.int32:
-        raise TypeError("tok_seq and tok_pos must be int32")
+    check_append_args(cache, h, w_dkv, w_kr, tok_seq, tok_pos)
     n_tok, d_model = h.shape
     st = ctypes.byref(cache.struct())
     _check(lib.mla_append(st, _ptr(h), n_tok, d_model, _ptr(w_dkv), _ptr(w_kr),
@@ -176,12 +252,11 @@ def mla_append_absorb(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor,
                       softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
                       workspace: torch.Tensor, stream=None) -> None:
     """mla_append then mla_decode_absorb, in one launch where it applies (see libmla.h)."""
-    if tok_seq.dtype != torch.int32 or tok_pos.dtype != torch.int32 or seq_len.dtype != torch.int32:
-        raise TypeError("tok_seq, tok_pos and seq_len must be int32")
-    if lse is not None and lse.dtype != torch.float32:
-        raise TypeError("lse must be float32")
+    check_append_args(cache, h, w_dkv, w_kr, tok_seq, tok_pos)
+    H = check_decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, out, lse, workspace)
+    if h.dtype != q_nope.dtype:
+        raise TypeError("h and q_nope must share the activation dtype")
     n_tok, d_model = h.shape
-    B, H, _ = q_nope.shape
     st = ctypes.byref(cache.struct())
     _check(lib.mla_append_absorb(st, _ptr(h), n_tok, d_model, _ptr(w_dkv), _ptr(w_kr),
                                  _ptr(tok_seq), _ptr(tok_pos), float(rope_base), _ptr(seq_len),
@@ -207,11 +282,7 @@ def alloc_workspace(cache: LatentCache, n_heads: int, act_dtype: torch.dtype,
 
 def _decode_call(name, cache, seq_len, q_nope, q_pe, w_uk, w_uv, softmax_scale, out, lse,
                  workspace, stream=None):
-    if seq_len.dtype != torch.int32:
-        raise TypeError("seq_len must be int32")
-    if lse is not None and lse.dtype != torch.float32:
-        raise TypeError("lse must be float32")
-    B, H, _ = q_nope.shape
+    H = check_decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, out, lse, workspace)
     st = ctypes.byref(cache.struct())
     _check(getattr(lib, name)(st, _ptr(seq_len), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk),
                               _ptr(w_uv), dtype_code(q_nope.dtype), H, float(softmax_scale),
@@ -261,11 +332,7 @@ class PreparedDecode:
                  q_pe: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
                  softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
                  workspace: torch.Tensor, stream=None):
-        if seq_len.dtype != torch.int32:
-            raise TypeError("seq_len must be int32")
-        if lse is not None and lse.dtype != torch.float32:
-            raise TypeError("lse must be float32")
-        B, H, _ = q_nope.shape
+        H = check_decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, out, lse, workspace)
         self._keep = (cache, seq_len, q_nope, q_pe, w_uk, w_uv, out, lse, workspace)
         self._st = cache.struct()
         self._args = (ctypes.byref(self._st), _ptr(seq_len), _ptr(q_nope), _ptr(q_pe),
@@ -295,8 +362,7 @@ class PreparedAppend:
     def __init__(self, cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor,
                  w_kr: torch.Tensor, tok_seq: torch.Tensor, tok_pos: torch.Tensor,
                  rope_base: float, stream=None):
-        if tok_seq.dtype != torch.int32 or tok_pos.dtype != torch.int32:
-            raise TypeError("tok_seq and tok_pos must be int32")
+        check_append_args(cache, h, w_dkv, w_kr, tok_seq, tok_pos)
         n_tok, d_model = h.shape
         self._keep = (cache, h, w_dkv, w_kr, tok_seq, tok_pos)
         self._st = cache.struct()
@@ -319,13 +385,11 @@ class PreparedAppendAbsorb:
                  q_pe: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
                  softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
                  workspace: torch.Tensor, stream=None):
-        if (tok_seq.dtype != torch.int32 or tok_pos.dtype != torch.int32
-                or seq_len.dtype != torch.int32):
-            raise TypeError("tok_seq, tok_pos and seq_len must be int32")
-        if lse is not None and lse.dtype != torch.float32:
-            raise TypeError("lse must be float32")
+        check_append_args(cache, h, w_dkv, w_kr, tok_seq, tok_pos)
+        H = check_decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, out, lse, workspace)
+        if h.dtype != q_nope.dtype:
+            raise TypeError("h and q_nope must share the activation dtype")
         n_tok, d_model = h.shape
-        B, H, _ = q_nope.shape
         self._keep = (cache, h, w_dkv, w_kr, tok_seq, tok_pos, seq_len, q_nope, q_pe, w_uk, w_uv,
                       out, lse, workspace)
         self._st = cache.struct()

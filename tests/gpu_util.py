@@ -12,6 +12,10 @@ import workloads as W
 
 TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 4e-2}     # rel-L2 bounds on o[B,H,128]
 
+# Unit roundoff of the absorbed query q_lat = W_UK[h]^T q_nope as the kernels
+# hold it: fp32 for the f32 cache, bf16 (8 significant bits) otherwise.
+Q_LAT_U = {"f32": 2.0 ** -24, "bf16": 2.0 ** -8, "fp8": 2.0 ** -8}
+
 
 def log(msg: str):
     print(msg, flush=True)
@@ -71,3 +75,39 @@ def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64).ravel()
     b = np.asarray(b, np.float64).ravel()
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def lse_bounds(view, pairs, cache: str) -> np.ndarray:
+    """Per-(b, h) bound on |lse_gpu - lse_oracle|.
+
+    The kernels' dominant lse error is the rounding of q_lat (unit roundoff u,
+    Q_LAT_U) feeding every score: s_t moves by sigma * sum_i d_i q_i c_t,i with
+    |d_i| <= u, the d_i independent roundings, so its standard deviation is at
+    most sigma * u / sqrt(3) * sqrt(sum_i q_i^2 c_t,i^2). lse moves by a
+    softmax-weighted mean of those shifts, so 6 of those deviations at the
+    worst token bound it; 1e-4 (1 + |lse|) covers the fp32 accumulation, exp2
+    and log of the kernels (f32: 1e-5)."""
+    u = Q_LAT_U[cache]
+    sigma = 1.0 / math.sqrt(192.0)
+    out = np.empty(len(pairs))
+    sq, cur = None, None
+    for n, (b, h) in enumerate(pairs):
+        if b != cur:
+            sq, cur = view.rows64(b)[:, :512] ** 2, b
+        q_lat = view.w_uk[h].T @ view.q_nope[b, h]
+        dev = math.sqrt(float((sq @ (q_lat ** 2)).max())) if len(sq) else 0.0
+        out[n] = 6.0 * sigma * u / math.sqrt(3.0) * dev
+    return out
+
+
+def check_lse(got, ref, view, pairs, cache: str, what: str = "") -> float:
+    """Assert the lse bound on every listed pair; return the largest
+    |error| / bound."""
+    got = np.asarray(got, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    bound = lse_bounds(view, pairs, cache) + (1e-5 if cache == "f32" else 1e-4) * (1 + np.abs(ref))
+    err = np.abs(got - ref)
+    worst = float((err / bound).max()) if len(err) else 0.0
+    log(f"  lse max abs err {err.max() if len(err) else 0:.3e}, worst err/bound {worst:.3f} {what}")
+    assert np.all(err <= bound), (what, int(np.argmax(err / bound)), float(err.max()))
+    return worst

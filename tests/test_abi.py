@@ -175,3 +175,89 @@ def test_append_absorb_validation():
     assert _append_absorb(_cache(), ws=FAKE + 64) == E.MLA_ERR_INVALID_ARGUMENT
     need = mla.mla_decode_workspace_size(4, 16, E.MLA_DTYPE_BF16, E.MLA_DTYPE_BF16)
     assert _append_absorb(_cache(), ws_bytes=need - 1) == E.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
+# ---------------------------------------------------------------- binding checks
+# The binding checks every tensor against the cache's B, q_nope's H, the
+# activation dtype and the cache's device before any foreign call; these run
+# on CPU tensors (the checks fire before the "device tensors" check).
+import torch  # noqa: E402
+
+
+def _binding_problem(B=3, H=16, act=torch.bfloat16, cache_dt=torch.bfloat16, n_tok=2, dm=64):
+    rows = torch.zeros(50, 576, dtype=cache_dt)
+    cache = mla.LatentCache(rows=rows, seq_start=torch.arange(B, dtype=torch.int64) * 10,
+                            seq_capacity=torch.full((B,), 10, dtype=torch.int32),
+                            row_scale=torch.ones(50) if cache_dt == torch.uint8 else None)
+    d = dict(seq_len=torch.ones(B, dtype=torch.int32), q_nope=torch.zeros(B, H, 128, dtype=act),
+             q_pe=torch.zeros(B, H, 64, dtype=act), w_uk=torch.zeros(H, 128, 512, dtype=act),
+             w_uv=torch.zeros(H, 512, 128, dtype=act), out=torch.zeros(B, H, 128, dtype=act),
+             lse=torch.zeros(B, H), workspace=torch.zeros(256, dtype=torch.uint8))
+    a = dict(h=torch.zeros(n_tok, dm, dtype=act), w_dkv=torch.zeros(512, dm, dtype=act),
+             w_kr=torch.zeros(64, dm, dtype=act), tok_seq=torch.zeros(n_tok, dtype=torch.int32),
+             tok_pos=torch.zeros(n_tok, dtype=torch.int32))
+    return cache, d, a
+
+
+def test_binding_accepts_consistent_shapes_then_wants_device_tensors():
+    cache, d, a = _binding_problem()
+    assert mla.check_decode_args(cache, **d) == 16
+    mla.check_append_args(cache, **a)
+    with pytest.raises(ValueError, match="device tensors"):
+        mla.mla_decode(cache, softmax_scale=0.07, **d)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("q_nope", torch.zeros(2, 16, 128, dtype=torch.bfloat16)),     # fewer rows than num_seqs
+    ("q_pe", torch.zeros(3, 16, 32, dtype=torch.bfloat16)),
+    ("w_uk", torch.zeros(8, 128, 512, dtype=torch.bfloat16)),      # fewer heads than q_nope
+    ("w_uv", torch.zeros(16, 128, 512, dtype=torch.bfloat16)),     # transposed
+    ("out", torch.zeros(3, 16, 64, dtype=torch.bfloat16)),
+    ("lse", torch.zeros(3, 8)),
+    ("seq_len", torch.ones(4, dtype=torch.int32)),
+])
+def test_binding_rejects_shape_mismatch(name, bad):
+    cache, d, _ = _binding_problem()
+    d[name] = bad
+    with pytest.raises(ValueError, match=name):
+        mla.mla_decode(cache, softmax_scale=0.07, **d)
+    with pytest.raises(ValueError, match=name):
+        mla.PreparedDecode(cache, softmax_scale=0.07, **d)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("out", torch.zeros(3, 16, 128, dtype=torch.float32)),         # f32 out, bf16 activations
+    ("w_uk", torch.zeros(16, 128, 512, dtype=torch.float32)),
+    ("lse", torch.zeros(3, 16, dtype=torch.bfloat16)),
+    ("seq_len", torch.ones(3, dtype=torch.int64)),
+])
+def test_binding_rejects_dtype_mismatch(name, bad):
+    cache, d, _ = _binding_problem()
+    d[name] = bad
+    with pytest.raises(TypeError, match=name):
+        mla.mla_decode(cache, softmax_scale=0.07, **d)
+
+
+def test_binding_rejects_cache_and_append_mismatch():
+    cache, d, a = _binding_problem()
+    cache.seq_capacity = torch.full((2,), 10, dtype=torch.int32)
+    with pytest.raises(ValueError, match="seq_capacity"):
+        mla.mla_decode(cache, softmax_scale=0.07, **d)
+    cache, d, a = _binding_problem(cache_dt=torch.uint8)
+    cache.row_scale = torch.ones(49)
+    with pytest.raises(ValueError, match="row_scale"):
+        mla.mla_decode(cache, softmax_scale=0.07, **d)
+    cache, d, a = _binding_problem()
+    a["w_dkv"] = torch.zeros(512, 128, dtype=torch.bfloat16)     # d_model disagrees with h
+    with pytest.raises(ValueError, match="w_dkv"):
+        mla.mla_append(cache, rope_base=1e4, **a)
+    cache, d, a = _binding_problem()
+    a["tok_pos"] = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="tok_pos"):
+        mla.mla_append_absorb(cache, rope_base=1e4, softmax_scale=0.07, **a, **d)
+    cache, d, a = _binding_problem()
+    a["h"] = a["h"].float()
+    a["w_dkv"] = a["w_dkv"].float()
+    a["w_kr"] = a["w_kr"].float()
+    with pytest.raises(TypeError, match="activation dtype"):
+        mla.mla_append_absorb(cache, rope_base=1e4, softmax_scale=0.07, **a, **d)

@@ -205,3 +205,59 @@ def test_append_then_decode_end_to_end_full_size():
     pairs = [(b, h) for b in (0, 17, 40, 63) for h in range(16)]
     ro, _ = view.decode(pairs)
     assert rel_l2(np.stack([o[b, h] for b, h in pairs]), ro) <= 2e-2
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_append_bf16_large_positions(fused):
+    """The bf16 append kernels (mla_append's and the fused append + absorb
+    launch) form the RoPE angle in fp64, reduce it there and take sine and
+    cosine of the reduced angle in fp32: at positions up to 131071 the stored
+    rows still equal the oracle's exact rows rounded to bf16, except where the
+    exact value lies within the fp32 accumulation error of a rounding
+    midpoint (an unreduced fp32 angle is off by up to ~5e-3 rad there, far
+    outside that allowance)."""
+    mla = _mla()
+    rng = np.random.default_rng(131071)
+    dm = 512
+    positions = [0, 1, 4095, 4096, 32767, 65535, 100000, 131071] + \
+        [int(x) for x in rng.integers(0, 131072, size=8)]
+    n_tok = len(positions)
+    caps = [131072, 131072]
+    cache, starts = _cache("bf16", caps)
+    before = cache.rows.clone()
+    h = torch.from_numpy(rng.standard_normal((n_tok, dm)).astype(np.float32)).bfloat16()
+    wd = torch.from_numpy((rng.standard_normal((512, dm)) / math.sqrt(dm)).astype(np.float32)).bfloat16()
+    wk = torch.from_numpy((rng.standard_normal((64, dm)) / math.sqrt(dm)).astype(np.float32)).bfloat16()
+    seq = [i % 2 for i in range(n_tok)]
+    tseq = torch.tensor(seq, dtype=torch.int32).cuda()
+    tpos = torch.tensor(positions, dtype=torch.int32).cuda()
+    if fused:
+        B, H = 2, 16
+        seq_len = torch.tensor(caps, dtype=torch.int32).cuda()
+        q_nope = torch.randn(B, H, 128).bfloat16().cuda()
+        q_pe = torch.randn(B, H, 64).bfloat16().cuda()
+        w_uk = (torch.randn(H, 128, 512) / 23).bfloat16().cuda()
+        w_uv = (torch.randn(H, 512, 128) / 23).bfloat16().cuda()
+        out = torch.empty(B, H, 128, dtype=torch.bfloat16, device="cuda")
+        ws = mla.alloc_workspace(cache, H, torch.bfloat16)
+        mla.mla_append_absorb(cache, h.cuda(), wd.cuda(), wk.cuda(), tseq, tpos, 10000.0,
+                              seq_len, q_nope, q_pe, w_uk, w_uv, 1.0 / math.sqrt(192.0), out,
+                              None, ws)
+    else:
+        mla.mla_append(cache, h.cuda(), wd.cuda(), wk.cuda(), tseq, tpos, 10000.0)
+    torch.cuda.synchronize()
+    exact = omla.append_rows_exact(h.double().numpy(), wd.double().numpy(), wk.double().numpy(),
+                                   np.array(positions, dtype=np.float64), 10000.0)
+    stored, _, _ = omla.quantize_rows(exact, "bf16")
+    idx = [int(starts[s]) + p for s, p in zip(seq, positions)]
+    got = cache.rows[torch.tensor(idx, device="cuda")].cpu().double().numpy()
+    bound = _dot_bound(h.double().numpy(), wd.double().numpy(), wk.double().numpy(), positions,
+                       10000.0)
+    tie = _near_tie_bf16(exact, bound)
+    mism = (got != stored) & ~tie
+    log(f"  fused={fused}: {int((got != stored).sum())} of {got.size} differ, "
+        f"{int(tie.sum())} near ties, {int(mism.sum())} off-tie mismatches")
+    assert not mism.any()
+    changed = torch.nonzero(torch.any(before.view(torch.int16) != cache.rows.view(torch.int16),
+                                      dim=1)).flatten().cpu().tolist()
+    assert set(changed) <= set(idx)

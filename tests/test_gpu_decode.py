@@ -12,7 +12,7 @@ import torch
 
 import workloads as W
 from oracle.problem import OracleView
-from tests.gpu_util import TOL, DeviceProblem, log, rel_l2
+from tests.gpu_util import TOL, DeviceProblem, check_lse, log, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -35,48 +35,102 @@ def test_decode_small_all_outputs(name):
     log(f"[decode small] {name} lengths={p.seq_len.tolist()} H={p.wl.H}")
     dp = DeviceProblem(p)
     o, lse = dp.step(poison=True)
-    ro, rl = OracleView(p).decode()
+    view = OracleView(p)
+    ro, rl = view.decode()
     err = rel_l2(o, ro)
-    log(f"  rel-L2 {err:.3e} (bound {TOL[p.wl.cache]}), lse max abs {np.abs(lse - rl).max():.3e}")
+    log(f"  rel-L2 {err:.3e} (bound {TOL[p.wl.cache]}), max abs {np.abs(o - ro).max():.3e}")
     assert np.all(np.isfinite(o))
     assert err <= TOL[p.wl.cache]
-    assert np.abs(lse - rl).max() <= 50 * TOL[p.wl.cache]
+    B, H = p.q_nope.shape[:2]
+    check_lse(lse, rl, view, [(b, h) for b in range(B) for h in range(H)], p.wl.cache)
     # every sequence on its own meets the bound too
     for b in range(p.q_nope.shape[0]):
         assert rel_l2(o[b], ro[b]) <= TOL[p.wl.cache], b
 
 
+def _full_size_sequences(p, n_random):
+    """First, last, longest and shortest sequence (the longest is split over
+    the most workers), plus `n_random` others."""
+    B = len(p.seq_len)
+    pick = [0, B - 1, int(np.argmax(p.seq_len)), int(np.argmin(p.seq_len))]
+    rng = np.random.default_rng(100 + p.wl.index)
+    rest = [b for b in range(B) if b not in pick]
+    pick += [int(b) for b in rng.choice(rest, size=min(n_random, len(rest)), replace=False)] if rest else []
+    return sorted(set(pick))
+
+
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
-def test_decode_full_size_sampled(name):
+def test_decode_full_size_all_heads(name):
+    """At the benchmark's full size and launch configuration: every head of
+    at least eight sequences (for the 128K workload, whose four sequences
+    cost the oracle ~0.25 s per head each, every head of the first sequence
+    and 16 heads of each other one), each sequence's rel-L2 and
+    every lse checked, and the pooled rel-L2 and max-abs logged."""
     wl = W.WORKLOADS[name]
     p = W.make_problem(wl)
     log(f"[decode full] {name} B={wl.B} H={wl.H} T={p.T}")
     dp = DeviceProblem(p)
     o, lse = dp.step(poison=True)
-    rng = np.random.default_rng(100 + wl.index)
+    assert np.all(np.isfinite(o))
     B, H = wl.B, wl.H
-    n = 6 if name == "long_bf16" else 16
-    pairs = [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(n)]
-    pairs += [(0, 0), (B - 1, H - 1)]
+    if name == "long_bf16":
+        rng = np.random.default_rng(7)
+        pairs = [(0, h) for h in range(H)]
+        pairs += [(b, int(h)) for b in range(1, B) for h in rng.choice(H, 16, replace=False)]
+    else:
+        pairs = [(b, h) for b in _full_size_sequences(p, 4) for h in range(H)]
     pairs = sorted(set(pairs))
-    ro, rl = OracleView(p).decode(pairs)
+    view = OracleView(p)
+    ro, rl = view.decode(pairs)
     got = np.stack([o[b, h] for b, h in pairs])
     gl = np.array([lse[b, h] for b, h in pairs])
     err = rel_l2(got, ro)
-    log(f"  sampled {len(pairs)} pairs rel-L2 {err:.3e} lse max abs {np.abs(gl - rl).max():.3e}")
-    assert np.all(np.isfinite(o))
+    seqs = sorted({b for b, _ in pairs})
+    log(f"  {len(seqs)} sequences, {len(pairs)} (b, h): pooled rel-L2 {err:.3e} "
+        f"(bound {TOL[wl.cache]}), max abs {np.abs(got - ro).max():.3e}")
     assert err <= TOL[wl.cache]
-    assert np.abs(gl - rl).max() <= 50 * TOL[wl.cache]
+    for b in seqs:
+        idx = [i for i, (bb, _) in enumerate(pairs) if bb == b]
+        e_b = rel_l2(got[idx], ro[idx])
+        assert e_b <= TOL[wl.cache], (b, e_b)
+    check_lse(gl, rl, view, pairs, wl.cache)
 
 
-def test_decode_deterministic_and_repeatable():
-    p = _small("v2lite_bf16", lengths=[700, 5, 1300])
+@pytest.mark.parametrize("name,lengths", [("v2lite_bf16", [700, 5, 1300]),
+                                          ("v2_bf16", [3000, 5, 1300, 64]),
+                                          ("fp8_cache", [900, 33, 2000])])
+def test_decode_deterministic_and_repeatable(name, lengths):
+    # no floating-point atomics: two runs over poisoned outputs and workspace
+    # are bitwise equal, at 16 and at 128 heads (bf16 and fp8 caches)
+    p = _small(name, lengths=lengths)
     dp = DeviceProblem(p)
     dp.decode(poison=True)
     a = dp.out.clone()
     la = dp.lse.clone()
     dp.decode(poison=True)
     assert torch.equal(a, dp.out) and torch.equal(la, dp.lse)
+
+
+@pytest.mark.parametrize("name,lengths", [("v2lite_bf16", [700, 5, 1300]),
+                                          ("v2_bf16", [3000, 5, 1300, 64]),
+                                          ("v2_bf16", [40] * 300),
+                                          ("fp8_cache", [900, 33, 2000]),
+                                          ("tiny_fp32", [256, 3])])
+def test_decode_without_lse(name, lengths):
+    # lse = NULL takes its own branch in every merge kernel; out is bitwise
+    # the same as with lse requested
+    import head_latent_attention_14_amd as mla
+    p = _small(name, lengths=lengths)
+    dp = DeviceProblem(p)
+    dp.decode(poison=True)
+    torch.cuda.synchronize()
+    ref = dp.out.clone()
+    dp.out.fill_(float("nan"))
+    dp.ws.fill_(0xFF)
+    mla.mla_decode(dp.cache, dp.seq_len, dp.q_nope, dp.q_pe, dp.w_uk, dp.w_uv,
+                   1.0 / math.sqrt(192.0), dp.out, None, dp.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, dp.out)
 
 
 def test_nan_in_one_sequence_stays_there():
@@ -153,11 +207,12 @@ def test_combine_row_blocks(B, H, maxlen):
     pairs = {(b, int(h)) for b in last for h in rng.integers(H, size=2)}
     pairs |= {(int(b), int(h)) for b, h in zip(rng.integers(B, size=16), rng.integers(H, size=16))}
     pairs = sorted(pairs)
-    ro, rl = OracleView(p).decode(pairs)
+    view = OracleView(p)
+    ro, rl = view.decode(pairs)
     got = np.stack([o[b, h] for b, h in pairs])
     gl = np.array([lse[b, h] for b, h in pairs])
     assert rel_l2(got, ro) <= TOL["bf16"]
-    assert np.abs(gl - rl).max() <= 50 * TOL["bf16"]
+    check_lse(gl, rl, view, pairs, "bf16")
 
 
 def test_other_head_counts():
@@ -222,13 +277,15 @@ def test_empty_sequences_between_others(name, H):
     assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
     p2 = W.make_problem(wl, seed=5, B=len(GAPPY), lengths=make, H=H)
     p2.seq_len = np.array(GAPPY, dtype=np.int32)
-    ro, rl = OracleView(p2, apply_append=False).decode([(b, h) for b in full for h in range(H)])
+    view = OracleView(p2, apply_append=False)
+    pairs = [(b, h) for b in full for h in range(H)]
+    ro, rl = view.decode(pairs)
     got = np.stack([o[b, h] for b in full for h in range(H)])
     err = rel_l2(got, ro)
     log(f"  rel-L2 {err:.3e}")
     assert err <= TOL[wl.cache]
     gl = np.array([lse[b, h] for b in full for h in range(H)])
-    assert np.abs(gl - rl).max() <= 50 * TOL[wl.cache]
+    check_lse(gl, rl, view, pairs, wl.cache)
     # every non-empty sequence on its own meets the bound too
     for i, b in enumerate(full):
         assert rel_l2(got[i * H:(i + 1) * H], ro[i * H:(i + 1) * H]) <= TOL[wl.cache], b
@@ -326,11 +383,13 @@ def test_combine_fused_launch_all_outputs():
     p2 = W.make_problem(W.WORKLOADS["v2lite_bf16"], seed=64, B=64, lengths=lengths)
     p2.seq_len = lens.astype(np.int32)
     full = [b for b in range(64) if lens[b] > 0]
-    ro, rl = OracleView(p2, apply_append=False).decode([(b, h) for b in full for h in range(16)])
+    view = OracleView(p2, apply_append=False)
+    pairs = [(b, h) for b in full for h in range(16)]
+    ro, rl = view.decode(pairs)
     got = np.stack([o[b, h] for b in full for h in range(16)])
     assert rel_l2(got, ro) <= TOL["bf16"]
     gl = np.array([lse[b, h] for b in full for h in range(16)])
-    assert np.abs(gl - rl).max() <= 50 * TOL["bf16"]
+    check_lse(gl, rl, view, pairs, "bf16")
 
 
 @pytest.mark.parametrize("name", ["fp8_cache", "tiny_fp32"])
