@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["api.cpp", "append.hip", "decode_attn.hip", "decode_attn_stream.hip", "decode_gemm.hip"]
+SOURCES = ["api.cpp", "append.hip", "decode_attn.hip", "decode_attn_stream.hip", "decode_attn_h32.hip",
+           "decode_gemm.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -24,16 +25,19 @@ COMMON = [
     # no packed-fp32 VALU instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
-    # MFMA accumulators in ordinary VGPRs: the softmax rescale and the partial
-    # stores then touch them without AGPR<->VGPR copies every tile
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
+# MFMA accumulators in ordinary VGPRs: the softmax rescale and the partial
+# stores then touch them without AGPR<->VGPR copies every tile. Not for the
+# 128-head kernel, whose value accumulators fill the accumulation registers.
+PER_SOURCE = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] for src in SOURCES
+              if src not in ("api.cpp", "decode_attn_h32.hip")}
 
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *lang, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *lang, *COMMON, *PER_SOURCE.get(src, []), *extra, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -4,13 +4,13 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <hip/hip_runtime.h>
 
 #include "../../include/libmla.h"
 #include "internal.h"
 
-#include <stdlib.h>
 #include <vector>
 
 namespace mla {
@@ -20,9 +20,21 @@ static constexpr int kMaxSeqs = 1 << 20;
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// An environment switch read at planning time (experiments only).
+static bool getenv_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && v[0] == '1' && v[1] == 0;
+}
+
 DecodePlan make_plan(int ct, int B, int H) {
   DecodePlan p{};
-  if (ct != kF32 && H % 32 == 0) {
+  if (ct == kBF16 && H % 128 == 0 && getenv_flag("MLA_H32")) {
+    // 128-head groups over a bf16 cache: four waves of 32 heads, one per
+    // SIMD, a four-stage ring (opt-in while it is slower than the pair kernel)
+    p.h32 = true;
+    p.nstage = 4;
+    p.head_groups = H / 128;
+  } else if (ct != kF32 && H % 32 == 0) {
     // pair kernel: up to 128 heads (8 waves) per workgroup; the ring depth is
     // what fits in LDS beside the score-exchange buffer
     p.pair = true;
@@ -45,7 +57,7 @@ DecodePlan make_plan(int ct, int B, int H) {
   // out; the pair kernel moves 147 KB of queries and 128 KB of partial per
   // segment and drains its copy queue (measured best: 1 for the streaming
   // kernel against 0..6, 5 for the pair kernel against 1..6)
-  p.seg_tiles = p.pair ? 5 : 1;
+  p.seg_tiles = p.h32 ? 3 : (p.pair ? 5 : 1);
   int w = kTargetCUs / p.head_groups;
   w = w < 8 ? 8 : (w / 8) * 8;                 // a multiple of the 8 XCDs
   p.workers = w;

@@ -131,6 +131,24 @@ struct TileCopy {
     return (uint32_t)(r * RB + c * 16);
   }
 
+  // The same offset from the slot's row r = s / SPR written as the row of the
+  // wave's first slot (a wave-uniform division) plus one for the lanes past
+  // the next row boundary: two vector compares instead of a vector division.
+  __device__ __forceinline__ uint32_t off_rows(int k) const {
+    static_assert(SPR >= 64, "a wave's 64 slots cross at most one row boundary");
+    int ln = lane_;
+    asm volatile("" : "+v"(ln));
+    const int s0 = uniform(k * 64);
+    const int r0 = s0 / SPR;
+    const int thr = SPR * (r0 + 1) - s0;               // first lane of row r0 + 1
+    const int up = ln >= thr ? 1 : 0;
+    int r = r0 + up;
+    int c = ln + (s0 - SPR * r0) - SPR * up;
+    if (c >= RB / 16) c = RB / 16 - 1;
+    if (r >= TILE) r = TILE - 1;
+    return (uint32_t)(r * RB + c * 16);
+  }
+
   // One tile's copies, issued one at a time (so that a wave can spread them
   // over its compute instead of stalling on the memory pipeline at once).
   struct Pending {
@@ -149,6 +167,7 @@ struct TileCopy {
     q.sb = sb;
     return q;
   }
+  template <bool ROWS = false>
   __device__ __forceinline__ void copy(const Pending& q, int i) const {
     const int k = id(i);
     if (CT == kFP8 && k == NCH) {
@@ -156,7 +175,9 @@ struct TileCopy {
       buffer_copy4(q.srsrc, (uint32_t)(r * 4), q.sb + STAGE_DATA);
       return;
     }
-    uint32_t o = off(k);
+    uint32_t o;
+    if constexpr (ROWS) o = off_rows(k);
+    else o = off(k);
     if (q.nvalid < TILE) {
       const uint32_t r = o / RB;
       if (r >= (uint32_t)q.nvalid) o -= (r - (q.nvalid - 1)) * RB;
@@ -242,5 +263,7 @@ __device__ __forceinline__ float inv_or_zero(float l) { return l != 0.f ? 1.f / 
 
 // Launcher of the streaming kernel (decode_attn_stream.hip).
 hipError_t launch_attn_stream(const DecodePlan& plan, const AttnParams& prm, hipStream_t s);
+// Launcher of the 128-head kernel (decode_attn_h32.hip).
+hipError_t launch_attn_h32(const DecodePlan& plan, const AttnParams& prm, hipStream_t s);
 
 }  // namespace mla

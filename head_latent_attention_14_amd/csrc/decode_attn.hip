@@ -392,6 +392,10 @@ mla_attn_pair_kernel(AttnParams p) {
     asm volatile("" : "+s"(b0) :: "memory");
     load_q(b0);
   }
+  // the queries (and the first copies) land here: with a load of them still
+  // in flight at the loop, the compiler's wait counting would make every
+  // tile's score MFMAs wait for all copies issued before them
+  wait_vmcnt<0>();
 
   float m_run[2] = {-INFINITY, -INFINITY};   // running max per head block (log2 domain)
   float l_run[2] = {0.f, 0.f};               // this lane's share of the running sums
@@ -629,6 +633,7 @@ hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipS
   prm.scale_log2 = a.softmax_scale * kLog2e;
   const int W = plan.workers, G = plan.head_groups;
   if (plan.stream) return launch_attn_stream(plan, prm, s);
+  if (plan.h32) return launch_attn_h32(plan, prm, s);
 #define MLA_CASE(CT_, HB_, DS_, NS_)                                              \
   if (!plan.pair && ct == CT_ && plan.hb == HB_ && plan.ds == DS_ && plan.nstage == NS_) \
     return launch_attn_t<CT_, HB_, DS_, NS_>(prm, W, G, s);
