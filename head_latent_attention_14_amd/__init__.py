@@ -32,7 +32,7 @@ D_C, D_R, D_ROW, D_NOPE, D_V = 512, 64, 576, 128, 128
 
 EXPORTED = ["mla_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_absorb",
             "mla_decode_attend", "mla_decode_combine", "mla_decode_attend_combine",
-            "mla_append_absorb", "mla_status_string",
+            "mla_append_absorb", "mla_decode_noalloc", "mla_status_string",
             "mla_abi_version"]
 DECODE_STAGES = ["mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
                  "mla_decode_attend_combine"]
@@ -73,6 +73,8 @@ def _load(path: str = LIB_PATH):
     lib.mla_append_absorb.argtypes = [C, P, I32, I32, P, P, P, P, F32,
                                       P, P, P, P, P, ctypes.c_int, I32, F32, P, P, P, SZ, P]
     lib.mla_append_absorb.restype = ctypes.c_int
+    lib.mla_decode_noalloc.argtypes = [C, P, P, P, P, P, ctypes.c_int, I32, F32, P, P, P]
+    lib.mla_decode_noalloc.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -165,6 +167,8 @@ def check_decode_args(cache: "LatentCache", seq_len, q_nope, q_pe, w_uk, w_uv, o
     _expect(out, "out", (B, H, D_V), act, dev)
     if lse is not None:
         _expect(lse, "lse", (B, H), torch.float32, dev)
+    if workspace is None:
+        return H          # mla_decode_noalloc: the library's own array
     if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 \
             or workspace.dim() != 1 or workspace.device != dev:
         raise ValueError(f"workspace must be a 1-D uint8 tensor on {dev}")
@@ -297,6 +301,22 @@ def mla_decode(cache: LatentCache, seq_len: torch.Tensor, q_nope: torch.Tensor,
     """o[B,H,128] (and lse[B,H]) of MLA decode over the latent cache (see libmla.h)."""
     _decode_call("mla_decode", cache, seq_len, q_nope, q_pe, w_uk, w_uv, softmax_scale, out,
                  lse, workspace, stream)
+
+
+MLA_NOALLOC_WORKSPACE_BYTES = 64 << 20
+
+
+def mla_decode_noalloc(cache: LatentCache, seq_len: torch.Tensor, q_nope: torch.Tensor,
+                       q_pe: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                       softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
+                       stream=None) -> None:
+    """mla_decode with the library's per-device workspace (see libmla.h): for
+    callers that cannot allocate. Overlapping calls on one device race."""
+    H = check_decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, out, lse, None)
+    st = ctypes.byref(cache.struct())
+    _check(lib.mla_decode_noalloc(st, _ptr(seq_len), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk),
+                                  _ptr(w_uv), dtype_code(q_nope.dtype), H, float(softmax_scale),
+                                  _ptr(out), _ptr(lse), _stream(stream)), "mla_decode_noalloc")
 
 
 def mla_decode_absorb(*args, **kw) -> None:

@@ -11,6 +11,7 @@
 #include "../../include/libmla.h"
 #include "internal.h"
 
+#include <mutex>
 #include <vector>
 
 namespace mla {
@@ -358,6 +359,58 @@ mla_status_t mla_append_absorb(const mla_cache_t* cache, const void* h, int32_t 
     if (e == hipSuccess) e = launch_decode(ct, plan, da, (hipStream_t)stream, 1);
   }
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// mla_decode_noalloc: mla_decode with the workspace in a file-scope device
+// array instead of caller memory, for callers that cannot allocate.
+//
+// Each device the library runs on holds its own copy of `scratch` from module
+// load until the process ends. In host code `scratch` names only a host-side
+// stand-in: its device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and only that address is
+// handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_WORKSPACE_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's `scratch` (nullptr on failure).
+static void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+extern "C" {
+
+mla_status_t mla_decode_noalloc(const mla_cache_t* cache, const int32_t* seq_len,
+                                const void* q_nope, const void* q_pe, const void* w_uk,
+                                const void* w_uv, mla_dtype_t act_dtype, int32_t n_heads,
+                                float softmax_scale, void* out, float* lse, void* stream) {
+  // every host-side check, the workspace size included, before any HIP call:
+  // a fake non-null workspace stands in until the real address is known
+  DecodeArgs a;
+  DecodePlan plan;
+  mla_status_t st = decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads,
+                                softmax_scale, out, lse, (void*)(uintptr_t)256,
+                                MLA_NOALLOC_WORKSPACE_BYTES, a, plan);
+  if (st != MLA_OK) return st;
+  void* ws = scratch_address();
+  if (!ws) return MLA_ERR_HIP;
+  // the workspace needs no clearing: absorb writes everything the later
+  // stages read
+  return decode_impl(cache, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads, softmax_scale,
+                     out, lse, ws, MLA_NOALLOC_WORKSPACE_BYTES, stream, 0);
 }
 
 }  // extern "C"

@@ -16,8 +16,9 @@
  *    pointers marked (host) are host memory. Every call only enqueues work on
  *    `stream` (a hipStream_t; NULL is the legacy default stream) and returns
  *    without synchronising (MLA_DEBUG below aside). The library allocates no
- *    device memory, keeps no state between calls, and may run concurrently
- *    on several streams when each call has its own workspace and outputs.
+ *    device memory and keeps no state between calls (mla_decode_noalloc's
+ *    per-device array aside), and may run concurrently on several streams
+ *    when each call has its own workspace and outputs.
  *  - The caller owns every buffer. Inputs are only read; outputs and the
  *    workspace are overwritten.
  *  - Host-side validation happens before any HIP call. A call that returns
@@ -235,6 +236,29 @@ mla_status_t mla_append_absorb(const mla_cache_t* cache,
                                int32_t n_heads, float softmax_scale,
                                void* out, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_noalloc -- mla_decode without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops or harnesses that forbid hipMalloc). Same arguments, rules and result
+ * as mla_decode (bit for bit with the same inputs); the workspace is a
+ * library-owned device array of MLA_NOALLOC_WORKSPACE_BYTES per device,
+ * reserved when the library's device code loads on that device and held until
+ * the process ends. The call allocates nothing and needs no clearing of that
+ * array. It returns MLA_ERR_WORKSPACE_TOO_SMALL, having enqueued nothing,
+ * when mla_decode_workspace_size for (num_seqs, n_heads, dtypes) exceeds
+ * MLA_NOALLOC_WORKSPACE_BYTES (about 100 sequences at 128 heads over a bf16
+ * cache), and MLA_ERR_HIP if the array's device address cannot be found.
+ * All calls on one device share its array: calls that overlap in time on one
+ * device (different streams, or host threads, without ordering between them)
+ * race and give undefined results. Calls on one stream are ordered and safe.
+ */
+#define MLA_NOALLOC_WORKSPACE_BYTES (64u << 20)
+mla_status_t mla_decode_noalloc(const mla_cache_t* cache, const int32_t* seq_len,
+                                const void* q_nope, const void* q_pe,
+                                const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
+                                int32_t n_heads, float softmax_scale,
+                                void* out, float* lse, void* stream);
 
 /* Static English text for a status code (host). */
 const char* mla_status_string(mla_status_t status);

@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"mla_append", "mla_decode_workspace_size", "mla_decode",
                           "mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
                           "mla_decode_attend_combine",
-                          "mla_append_absorb", "mla_status_string", "mla_abi_version"}
+                          "mla_append_absorb", "mla_decode_noalloc", "mla_status_string",
+                          "mla_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert getattr(lib, n) is not None
@@ -261,3 +262,31 @@ def test_binding_rejects_cache_and_append_mismatch():
     a["w_kr"] = a["w_kr"].float()
     with pytest.raises(TypeError, match="activation dtype"):
         mla.mla_append_absorb(cache, rope_base=1e4, softmax_scale=0.07, **a, **d)
+
+
+def test_decode_noalloc_validation():
+    """mla_decode_noalloc checks its arguments like mla_decode, and a request
+    beyond its array, before any HIP call."""
+    E = mla
+    f = lib.mla_decode_noalloc
+    src = open(HEADER).read()
+    assert int(re.search(r"#define MLA_NOALLOC_WORKSPACE_BYTES \((\d+)u << (\d+)\)", src)
+               .expand(r"\1")) << 20 == mla.MLA_NOALLOC_WORKSPACE_BYTES
+
+    def call(c, H=16, act=E.MLA_DTYPE_BF16, null=None):
+        args = dict(seq_len=FAKE, q_nope=FAKE, q_pe=FAKE, w_uk=FAKE, w_uv=FAKE, out=FAKE)
+        if null:
+            args[null] = None
+        return f(ctypes.byref(c) if c is not None else None, args["seq_len"], args["q_nope"],
+                 args["q_pe"], args["w_uk"], args["w_uv"], act, H, 0.07, args["out"], None, None)
+
+    assert call(None) == E.MLA_ERR_INVALID_ARGUMENT
+    for null in ["seq_len", "q_nope", "q_pe", "w_uk", "w_uv", "out"]:
+        assert call(_cache(), null=null) == E.MLA_ERR_INVALID_ARGUMENT
+    assert call(_cache(d_c=256)) == E.MLA_ERR_INVALID_ARGUMENT
+    assert call(_cache(), H=24) == E.MLA_ERR_UNSUPPORTED
+    assert call(_cache(), act=E.MLA_DTYPE_F32) == E.MLA_ERR_UNSUPPORTED
+    big = _cache(dtype=E.MLA_DTYPE_FP8_E4M3, B=128, scale=FAKE)
+    need = mla.mla_decode_workspace_size(128, 128, E.MLA_DTYPE_FP8_E4M3, E.MLA_DTYPE_BF16)
+    assert need > mla.MLA_NOALLOC_WORKSPACE_BYTES
+    assert call(big, H=128) == E.MLA_ERR_WORKSPACE_TOO_SMALL
