@@ -67,6 +67,13 @@ __device__ __forceinline__ Cursor cursor_start(const AttnParams& p, int64_t w, i
   return c;
 }
 
+// The sequence of the worker's next segment after the current one (-1: none).
+__device__ __forceinline__ int next_segment_seq(const Cursor& c, const AttnParams& p, int64_t r_hi) {
+  if (c.nb >= p.B) return -1;
+  const int64_t t0 = __builtin_amdgcn_readlane(c.nx, 3);
+  return t0 < r_hi ? c.nb : -1;
+}
+
 // Move to the next tile of the worker's range; false when done.
 template <int TILE>
 __device__ __forceinline__ bool advance(Cursor& c, const AttnParams& p, int64_t r_hi, int lane) {

@@ -228,6 +228,17 @@ __device__ __forceinline__ void wait_tiles(int younger) {
     else wait_tiles<PER, KMAX - 1>(younger);
   }
 }
+// The same with EXTRA more operations issued after the younger copies (loads
+// and stores of a segment change) allowed to stay outstanding.
+template <int PER, int KMAX, int EXTRA>
+__device__ __forceinline__ void wait_tiles_extra(int younger) {
+  if constexpr (KMAX <= 0) {
+    wait_vmcnt<EXTRA>();
+  } else {
+    if (younger >= KMAX) wait_vmcnt<KMAX * PER + EXTRA>();
+    else wait_tiles_extra<PER, KMAX - 1, EXTRA>(younger);
+  }
+}
 
 // Workgroup barrier that does not wait for outstanding global loads: LDS
 // operations of this wave complete first (lgkmcnt(0)), vmcnt is left alone

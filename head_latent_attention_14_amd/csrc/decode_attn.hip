@@ -372,30 +372,31 @@ mla_attn_pair_kernel(AttnParams p) {
       }
     }
   };
-  // the first tiles' copies, then the queries: the two arrive together (the
-  // compiler waits for the queries before their first use; the empty asm
-  // keeps it from hoisting the query loads above the copies, whose address
-  // arithmetic it would then make wait for them)
+  // the first tile's copies, the queries, then the other prologue tiles'
+  // copies (the empty asm keeps the compiler from hoisting the query loads
+  // above the first copies, whose address arithmetic it would then make wait
+  // for them). A worker with fewer tiles than the prologue copies its first
+  // tile again into the unused stages, so that every path issues the same
+  // number of copies after the queries and one wait covers them: with a query
+  // load outstanding on some path into the loop, the compiler's wait counting
+  // would make every tile's score MFMAs wait for all copies issued before them
   Cursor lc = c0;
-  bool lvalid = true;
-  int issued = 0;
-#pragma unroll
-  for (int i = 0; i < NSTAGE - 1; ++i) {
-    if (lvalid) {
-      issue(lc, i);
-      ++issued;
-      lvalid = advance<TILE>(lc, p, r_hi, lane);
-    }
-  }
+  issue(lc, 0);
+  bool lvalid = advance<TILE>(lc, p, r_hi, lane);
   {
     int b0 = c0.b;
     asm volatile("" : "+s"(b0) :: "memory");
     load_q(b0);
   }
-  // the queries (and the first copies) land here: with a load of them still
-  // in flight at the loop, the compiler's wait counting would make every
-  // tile's score MFMAs wait for all copies issued before them
-  wait_vmcnt<0>();
+#pragma unroll
+  for (int i = 1; i < NSTAGE - 1; ++i) {
+    issue(lvalid ? lc : c0, i);
+    if (lvalid) lvalid = advance<TILE>(lc, p, r_hi, lane);
+  }
+  int issued = NSTAGE - 1;
+  // the queries and the first tile land here; later prologue tiles may stay
+  // in flight
+  wait_vmcnt<(NSTAGE - 2) * CPW>();
 
   float m_run[2] = {-INFINITY, -INFINITY};   // running max per head block (log2 domain)
   float l_run[2] = {0.f, 0.f};               // this lane's share of the running sums
@@ -419,10 +420,19 @@ mla_attn_pair_kernel(AttnParams p) {
                    : (uint32_t)((4 * g + (l16 >> 2)) * TP + 2 * 256 * half + 8 * (l16 & 3));
   char* xbuf = smem + NSTAGE * STAGE_BYTES;
 
+  // a segment change loads the next queries and then stores the partial
+  // (at least kStoreOps stores); the stores may stay in flight into the next
+  // tile
+  constexpr int kStoreOps = 32;
+  constexpr int kTileWait = (NSTAGE - 2) * CPW;
+  constexpr int kSegExtra = kStoreOps < 63 - kTileWait ? kStoreOps : 63 - kTileWait;
   Cursor cc = c0;
   int it = 0;
+  bool after_seg = false;
   while (true) {
-    wait_tiles<CPW, NSTAGE - 2>(issued - 1 - it);       // this wave's copies of tile `it` landed
+    // this wave's copies of tile `it` landed
+    if (after_seg) wait_tiles_extra<CPW, NSTAGE - 2, kSegExtra>(issued - 1 - it);
+    else wait_tiles<CPW, NSTAGE - 2>(issued - 1 - it);
     barrier_lds();                                       // tile visible; stage it-1 and xbuf free
     // the next tile's copies go out after this wave's score MFMAs are issued
     const bool do_copy = lvalid;
@@ -570,6 +580,11 @@ mla_attn_pair_kernel(AttnParams p) {
     // ---------------- segment end: write the partial ----------------
     const bool seg_end = (cc.t + TILE >= cc.t_end);
     if (seg_end) {
+      // the next segment's queries go out before the partial's stores, so
+      // that the wait for them below leaves the stores in flight
+      const int nseq = next_segment_seq(cc, p, r_hi);
+      if (nseq >= 0) load_q(nseq);
+      __builtin_amdgcn_sched_barrier(0);
       const int64_t slot = w + cc.b;
       const int ln = opaque(lane);
 #pragma unroll
@@ -589,12 +604,12 @@ mla_attn_pair_kernel(AttnParams p) {
 #pragma unroll
         for (int nb = 0; nb < 16; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      // the queries have landed (at least kStoreOps stores follow them);
+      // the stores may stay in flight
+      wait_vmcnt<kStoreOps>();
     }
     if (!advance<TILE>(cc, p, r_hi, lane)) break;
-    if (seg_end) {
-      load_q(cc.b);
-      wait_vmcnt<0>();
-    }
+    after_seg = seg_end;
     ++it;
   }
 }
