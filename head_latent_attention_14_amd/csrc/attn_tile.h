@@ -199,25 +199,22 @@ struct TileCopy {
     const int64_t left = c.t_end - c.t;
     const int nvalid = left < TILE ? (int)left : TILE;
     const auto rsrc = make_rsrc(rows + c.row0 * RB, (uint32_t)(TILE * RB));
+    // exactly one copy instruction per i on every path, so that wait counts
+    // the compiler derives for later loads hold on all of them
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int k = id(i);
-      if (NCOPY != NCH && k >= NCH) continue;
-      uint32_t o = off(k);
-      if (nvalid < TILE) {
-        const uint32_t r = o / RB;
-        if (r >= (uint32_t)nvalid) o -= (r - (nvalid - 1)) * RB;
-      }
-      buffer_copy16(rsrc, o, sb + k * 1024);
-    }
-    if constexpr (CT == kFP8) {
-#pragma unroll
-      for (int i = 0; i < CPW; ++i) {
-        if (id(i) == NCH) {
-          const auto srsrc = make_rsrc(row_scale + c.row0, (uint32_t)(TILE * 4));
-          const int r = (lane & (TILE - 1)) < nvalid ? (lane & (TILE - 1)) : nvalid - 1;
-          buffer_copy4(srsrc, (uint32_t)(r * 4), sb + STAGE_DATA);
+      if (CT == kFP8 && k == NCH) {
+        const auto srsrc = make_rsrc(row_scale + c.row0, (uint32_t)(TILE * 4));
+        const int r = (lane & (TILE - 1)) < nvalid ? (lane & (TILE - 1)) : nvalid - 1;
+        buffer_copy4(srsrc, (uint32_t)(r * 4), sb + STAGE_DATA);
+      } else {
+        uint32_t o = off(k);
+        if (nvalid < TILE) {
+          const uint32_t r = o / RB;
+          if (r >= (uint32_t)nvalid) o -= (r - (nvalid - 1)) * RB;
         }
+        buffer_copy16(rsrc, o, sb + k * 1024);
       }
     }
   }

@@ -158,6 +158,48 @@ __device__ __forceinline__ void lds_tr8_x4(uint32_t addr, uint2& r0, uint2& r1, 
       : "memory");
 }
 
+// 16- and 8-byte LDS reads at compile-time offsets from one per-lane
+// address, completed inside the asm block. For reads the compiler must not see: a
+// visible LDS read after asynchronous global->LDS copies can make it wait for
+// every copy in flight.
+template <int O0, int O1>
+__device__ __forceinline__ void lds_read_b128_x2(uint32_t addr, u32x4& r0, u32x4& r1) {
+  asm volatile(
+      "ds_read_b128 %0, %2 offset:%3\n"
+      "ds_read_b128 %1, %2 offset:%4\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(addr), "i"(O0), "i"(O1)
+      : "memory");
+}
+template <int O0, int O1>
+__device__ __forceinline__ void lds_read_b64_x2(uint32_t addr, uint2& r0, uint2& r1) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 a, b;
+  asm volatile(
+      "ds_read_b64 %0, %2 offset:%3\n"
+      "ds_read_b64 %1, %2 offset:%4\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b)
+      : "v"(addr), "i"(O0), "i"(O1)
+      : "memory");
+  r0 = uint2{a[0], a[1]};
+  r1 = uint2{b[0], b[1]};
+}
+template <int O0, int O1, int O2, int O3>
+__device__ __forceinline__ void lds_read_b128_x4(uint32_t addr, u32x4& r0, u32x4& r1, u32x4& r2,
+                                                 u32x4& r3) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%5\n"
+      "ds_read_b128 %1, %4 offset:%6\n"
+      "ds_read_b128 %2, %4 offset:%7\n"
+      "ds_read_b128 %3, %4 offset:%8\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(addr), "i"(O0), "i"(O1), "i"(O2), "i"(O3)
+      : "memory");
+}
+
 // Eight e4m3fn codes (bytes 0..7 of v) as eight bf16 values, in order; every
 // e4m3fn value is exact in bf16 and the unit scale leaves it unchanged.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint2 v) {

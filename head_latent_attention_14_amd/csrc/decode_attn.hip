@@ -355,22 +355,42 @@ mla_attn_pair_kernel(AttnParams p) {
     cp.issue(p.rows, p.row_scale, c, smem + stage * STAGE_BYTES, lane);
   };
 
-  // query fragments (B operand of the score MFMA): head block hb, k-step 9*half + j
+  // query fragments (B operand of the score MFMA): head block hb, k-step j of
+  // this wave's half of the row (elements 288*half ..). bf16: lane group g
+  // holds elements 32j + 8g .. +7 of the half. fp8: k-steps 2m and 2m+1
+  // (m < 4) hold elements 64m + 16g .. +7 and 64m + 16g + 8 .. +15, so that
+  // one 16-byte read of the codes feeds both; k-step 8 is 256 + 8g .. +7.
+  // The contraction runs over the same elements either way.
+  auto q_elem = [&](int j, int gg) {
+    if (CT == kFP8 && j < 8) return 288 * half + 64 * (j >> 1) + 16 * gg + 8 * (j & 1);
+    return 288 * half + 32 * j + 8 * gg;
+  };
   bf16x8 q[2][9];
   auto load_q = [&](int b) {
     const int ln = opaque(lane);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int64_t base = (int64_t)b * H + hp + 16 * hb + (ln & 15);
-      const __bf16* ql = (const __bf16*)p.q_lat + base * kDc + 8 * (ln >> 4);
-      const __bf16* qp = (const __bf16*)p.q_pe + base * kDr + 8 * (ln >> 4);
+      const __bf16* ql = (const __bf16*)p.q_lat + base * kDc;
+      const __bf16* qp = (const __bf16*)p.q_pe + base * kDr;
 #pragma unroll
       for (int j = 0; j < 9; ++j) {
-        const int ks = 9 * half + j;                     // k-steps 16, 17 are the RoPE part
-        const __bf16* src = ks < 16 ? ql + 32 * ks : qp + 32 * (ks - 16);
+        const int e = q_elem(j, ln >> 4);                // elements 512.. are the RoPE part
+        const __bf16* src = e < kDc ? ql + e : qp + (e - kDc);
         q[hb][j] = *(const bf16x8*)src;
       }
     }
+  };
+  // After a wait that covers the query loads: an empty asm that reads and
+  // rewrites every query register, so that no path the compiler cannot rule
+  // out (it does not correlate the branches that issue copies and loads)
+  // leaves a query load outstanding in its wait counting; otherwise every
+  // tile's score MFMAs would wait for all copies issued before them.
+  auto settle_q = [&]() {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int j = 0; j < 9; ++j) asm volatile("" : "+v"(q[hb][j]));
   };
   // the first tile's copies, the queries, then the other prologue tiles'
   // copies (the empty asm keeps the compiler from hoisting the query loads
@@ -397,6 +417,7 @@ mla_attn_pair_kernel(AttnParams p) {
   // the queries and the first tile land here; later prologue tiles may stay
   // in flight
   wait_vmcnt<(NSTAGE - 2) * CPW>();
+  settle_q();
 
   float m_run[2] = {-INFINITY, -INFINITY};   // running max per head block (log2 domain)
   float l_run[2] = {0.f, 0.f};               // this lane's share of the running sums
@@ -407,7 +428,8 @@ mla_attn_pair_kernel(AttnParams p) {
     for (int nb = 0; nb < 16; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // score A operand: tile row l16 (+16 for the second token block), k-step 9*half
-  const uint32_t s_base = (uint32_t)(l16 * TP + g * 8 * EB + half * 9 * 32 * EB);
+  const uint32_t s_base = (CT == kFP8) ? (uint32_t)(l16 * TP + half * 288)
+                                       : (uint32_t)(l16 * TP + g * 8 * EB + half * 9 * 32 * EB);
   // transposing value reads. bf16: source lane (g, l16) points at row
   // 4g + l16/4, dims 256*half + 4*(l16%4) .. +3. fp8: source lane (g, l16)
   // points at row T(g, l16/2), dims 256*half + 8*(l16%2) .. +7, with
@@ -455,12 +477,30 @@ mla_attn_pair_kernel(AttnParams p) {
     // one batch of nine k-steps: the compiler places the 18 operand reads
     // among the 36 MFMAs as registers allow (measured: batches of two with a
     // scheduling barrier between them left the matrix unit idle longer)
+    // fp8: 16-byte reads of the codes, two k-steps each (the last k-step an
+    // 8-byte read), in small asm batches the compiler does not see (a visible
+    // LDS read here would make it wait for every copy in flight), widened in
+    // registers
+    u32x4 c8[2][4];
+    const uint32_t a16 = (uint32_t)(size_t)sa + 16 * g;
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
       bf16x8 a0, a1;
       if constexpr (CT == kFP8) {                        // codes widened in registers
-        a0 = fp8x8_to_bf16x8(*(const uint2*)(sa + k * 32));
-        a1 = fp8x8_to_bf16x8(*(const uint2*)(sa + 16 * TP + k * 32));
+        uint2 u0, u1;
+        if (k < 8) {
+          if (k == 0) lds_read_b128_x2<0, 16 * TP>(a16, c8[0][0], c8[1][0]);
+          if (k == 2) lds_read_b128_x2<64, 16 * TP + 64>(a16, c8[0][1], c8[1][1]);
+          if (k == 4) lds_read_b128_x2<128, 16 * TP + 128>(a16, c8[0][2], c8[1][2]);
+          if (k == 6) lds_read_b128_x2<192, 16 * TP + 192>(a16, c8[0][3], c8[1][3]);
+          const u32x4 v0 = c8[0][k >> 1], v1 = c8[1][k >> 1];
+          u0 = (k & 1) ? uint2{v0[2], v0[3]} : uint2{v0[0], v0[1]};
+          u1 = (k & 1) ? uint2{v1[2], v1[3]} : uint2{v1[0], v1[1]};
+        } else {
+          lds_read_b64_x2<0, 16 * TP>((uint32_t)(size_t)sa + 256 + 8 * g, u0, u1);
+        }
+        a0 = fp8x8_to_bf16x8(u0);
+        a1 = fp8x8_to_bf16x8(u1);
       } else {
         a0 = *(const bf16x8*)(sa + k * 64);
         a1 = *(const bf16x8*)(sa + 16 * TP + k * 64);
@@ -486,13 +526,19 @@ mla_attn_pair_kernel(AttnParams p) {
     for (int i = 0; i < 4; ++i) acc[i >> 1][i & 1] += *(const f32x4*)(xp + i * 1024);
 
     // ---------------- online softmax per head block ----------------
+    // fp8 row scales of tokens 4g.. and 16 + 4g.. (1 otherwise)
+    u32x4 scl8[2];
+    if constexpr (CT == kFP8)
+      lds_read_b128_x2<0, 64>((uint32_t)(size_t)(stage + STAGE_DATA) + 16 * g, scl8[0], scl8[1]);
     float tsc[8];                                        // fp8 row scales (1 otherwise)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if constexpr (CT == kFP8) {
-        const float* scl = (const float*)(stage + STAGE_DATA);
-        tsc[r] = scl[4 * g + r];
-        tsc[4 + r] = scl[16 + 4 * g + r];
+        // (the element goes through a plain variable: a bit cast of a vector
+        // element expression read the vector's first element here)
+        const unsigned int w0 = scl8[0][r], w1 = scl8[1][r];
+        tsc[r] = __builtin_bit_cast(float, w0);
+        tsc[4 + r] = __builtin_bit_cast(float, w1);
       } else {
         tsc[r] = 1.f;
         tsc[4 + r] = 1.f;
@@ -607,6 +653,7 @@ mla_attn_pair_kernel(AttnParams p) {
       // the queries have landed (at least kStoreOps stores follow them);
       // the stores may stay in flight
       wait_vmcnt<kStoreOps>();
+      settle_q();
     }
     if (!advance<TILE>(cc, p, r_hi, lane)) break;
     after_seg = seg_end;
