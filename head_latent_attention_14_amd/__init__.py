@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla.so")
+# MLA_LIBRARY names another build of the same library (the host-sanitized
+# one the ABI tests use); the in-tree build otherwise
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(_HERE, "libmla.so")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARGUMENT = 1

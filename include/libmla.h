@@ -51,19 +51,24 @@ extern "C" {
 #define MLA_D_NOPE 128       /* per-head non-RoPE query/key width */
 #define MLA_D_V 128          /* per-head value width */
 
-typedef enum {
+/* Status codes and dtype codes are plain 32-bit integers (the named values
+ * below), so that any value a caller passes, valid or not, is well defined
+ * to receive and is rejected by validation rather than being undefined. */
+typedef int32_t mla_status_t;
+enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size or shape */
   MLA_ERR_UNSUPPORTED = 2,        /* valid but unsupported dtype combination / head count */
   MLA_ERR_WORKSPACE_TOO_SMALL = 3,
   MLA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
-} mla_status_t;
+};
 
-typedef enum {
+typedef int32_t mla_dtype_t;
+enum {
   MLA_DTYPE_F32 = 0,
   MLA_DTYPE_BF16 = 1,
   MLA_DTYPE_FP8_E4M3 = 2          /* OCP e4m3fn codes (max 448, no infinities) */
-} mla_dtype_t;
+};
 
 /*
  * Ragged per-sequence latent cache (the MLA cache of one layer). The struct
@@ -260,7 +265,8 @@ mla_status_t mla_decode_noalloc(const mla_cache_t* cache, const int32_t* seq_len
                                 int32_t n_heads, float softmax_scale,
                                 void* out, float* lse, void* stream);
 
-/* Static English text for a status code (host). */
+/* Static English text for a status code (host); "unknown status" for any
+ * other value. */
 const char* mla_status_string(mla_status_t status);
 
 /* MLA_ABI_VERSION of the loaded library. */
