@@ -17,7 +17,9 @@ What it computes, and where the pages say so:
     up-projection recovers K/V from the latent). The absorbed form the method
     uses reaches the same result by associativity (same section: W_UK folds
     into the query side, W_UV into the output side);
-  * append: c_KV = W_DKV h and k_pe = RoPE(W_KR h), stored in the cache dtype.
+  * append: c_KV = W_DKV h and k_pe = RoPE(W_KR h), stored in the cache dtype;
+    RoPE optionally with YaRN frequencies (discosf explainer, "decoupled RoPE
+    and YaRN" section, with the formula of the published YaRN method).
 
 Readings where the pages are silent are listed in the package's modules next
 to the code that takes them.
@@ -25,7 +27,7 @@ to the code that takes them.
 from .numerics import (round_bf16, round_f32, e4m3_decode, e4m3_encode,
                        E4M3_MAX, e4m3_value_table)
 from .mla import (D_C, D_R, D_ROW, D_NOPE, D_V, softmax_scale, rope_inv_freq,
-                  rope_rotate, append_rows_exact, quantize_rows,
+                  yarn_inv_freq, yarn_softmax_factor, rope_rotate, append_rows_exact, quantize_rows,
                   decode_head, decode_problem, decode_sampled, attention_weights,
                   mla_cache_elements_per_token, mha_cache_elements_per_token,
                   gqa_equivalent_groups, cache_bytes)

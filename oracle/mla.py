@@ -30,6 +30,16 @@ Readings taken where the pages are silent (each listed in the design notes):
   R7  fp8 cache: e4m3fn codes with one fp32 scale per token,
       scale = fp32(max|row| / 448) (1 for an all-zero row),
       code = round-to-nearest-even, saturating, of row / scale.
+  R8  YaRN on the decoupled key [B gives scale 40, alpha 1, beta 32 and a
+      160K target, but no formula]: the frequencies follow the published
+      YaRN method ("NTK-by-parts" interpolation): for pair i with
+      theta_i = base^(-2i/64) and wavelength 2*pi/theta_i, r_i = L / wavelength
+      is the number of rotations over the original context L; the ramp
+      gamma = clip((r_i - alpha) / (beta - alpha), 0, 1) mixes the
+      interpolated and the original frequency,
+      theta'_i = (1 - gamma) * theta_i / s + gamma * theta_i;
+      L = target / s = 160K / 40 = 4096. The method's attention temperature
+      multiplies the softmax scale by (0.1 ln s + 1)^2 (s > 1; 1 otherwise).
 """
 from __future__ import annotations
 
@@ -84,12 +94,38 @@ def rope_inv_freq(base: float, d_r: int = D_R) -> np.ndarray:
     return np.power(np.float64(base), -2.0 * i / d_r)
 
 
-def rope_rotate(k: np.ndarray, pos, base: float) -> np.ndarray:
+def yarn_inv_freq(base: float, scale: float, alpha: float, beta: float, orig_context: int,
+                  d_r: int = D_R) -> np.ndarray:
+    """YaRN frequencies theta'_i of the RoPE pairs, fp64 (R8): the number of
+    rotations r_i of pair i over the original context decides between the
+    original frequency (r_i >= beta: many rotations, kept), the frequency
+    divided by the scale (r_i <= alpha: less than about one rotation,
+    interpolated) and a linear mix of the two in between."""
+    theta = rope_inv_freq(base, d_r)
+    wavelength = 2.0 * np.pi / theta
+    r = float(orig_context) / wavelength
+    gamma = np.clip((r - alpha) / (beta - alpha), 0.0, 1.0)
+    return (1.0 - gamma) * theta / scale + gamma * theta
+
+
+def yarn_softmax_factor(scale: float) -> float:
+    """Factor on the softmax scale from YaRN's attention temperature:
+    sqrt(1/t) = 0.1 ln s + 1 scales both query and key, so the logits gain
+    (0.1 ln s + 1)^2 (R8); 1 for s <= 1."""
+    if scale <= 1.0:
+        return 1.0
+    m = 0.1 * np.log(np.float64(scale)) + 1.0
+    return float(m * m)
+
+
+def rope_rotate(k: np.ndarray, pos, base: float, inv_freq: Optional[np.ndarray] = None) -> np.ndarray:
     """Rotate each interleaved pair (k[2i], k[2i+1]) of the last axis by
-    pos * theta_i. `k` is [..., 64], `pos` broadcasts against k[..., 0]."""
+    pos * theta_i. `k` is [..., 64], `pos` broadcasts against k[..., 0];
+    `inv_freq` replaces the plain frequencies (YaRN, R8)."""
     k = np.asarray(k, dtype=np.float64)
     pos = np.asarray(pos, dtype=np.float64)[..., None]
-    phi = pos * rope_inv_freq(base, k.shape[-1])     # [..., 32], fp64 angles
+    theta = rope_inv_freq(base, k.shape[-1]) if inv_freq is None else np.asarray(inv_freq, np.float64)
+    phi = pos * theta                                # [..., 32], fp64 angles
     c, s = np.cos(phi), np.sin(phi)
     even, odd = k[..., 0::2], k[..., 1::2]
     out = np.empty_like(k)
@@ -102,13 +138,13 @@ def rope_rotate(k: np.ndarray, pos, base: float) -> np.ndarray:
 # append ([A] compression, [B] RoPE key, R6, R7)
 # ----------------------------------------------------------------------------
 def append_rows_exact(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray,
-                      pos: np.ndarray, base: float) -> np.ndarray:
+                      pos: np.ndarray, base: float, inv_freq: Optional[np.ndarray] = None) -> np.ndarray:
     """Latent rows before storage rounding, fp64 [n_tok, 576]:
-    row = (W_DKV h) || RoPE(W_KR h, pos)."""
+    row = (W_DKV h) || RoPE(W_KR h, pos) (with `inv_freq`: YaRN, R8)."""
     h = np.asarray(h, dtype=np.float64)
     c = h @ np.asarray(w_dkv, dtype=np.float64).T          # [n_tok, 512]
     k = h @ np.asarray(w_kr, dtype=np.float64).T           # [n_tok, 64]
-    return np.concatenate([c, rope_rotate(k, pos, base)], axis=1)
+    return np.concatenate([c, rope_rotate(k, pos, base, inv_freq)], axis=1)
 
 
 def quantize_rows(rows: np.ndarray, dtype: str) -> Tuple[np.ndarray, Optional[np.ndarray], np.ndarray]:
