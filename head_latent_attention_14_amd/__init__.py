@@ -34,7 +34,8 @@ D_C, D_R, D_ROW, D_NOPE, D_V = 512, 64, 576, 128, 128
 
 EXPORTED = ["mla_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_absorb",
             "mla_decode_attend", "mla_decode_combine", "mla_decode_attend_combine",
-            "mla_append_absorb", "mla_decode_noalloc", "mla_status_string",
+            "mla_append_absorb", "mla_decode_noalloc", "mla_append_yarn",
+            "mla_yarn_softmax_factor", "mla_status_string",
             "mla_abi_version"]
 DECODE_STAGES = ["mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
                  "mla_decode_attend_combine"]
@@ -51,6 +52,16 @@ class mla_cache_t(ctypes.Structure):
         ("row_scale", ctypes.c_void_p),
         ("seq_start", ctypes.c_void_p),
         ("seq_capacity", ctypes.c_void_p),
+    ]
+
+
+class mla_yarn_t(ctypes.Structure):
+    _fields_ = [
+        ("base", ctypes.c_float),
+        ("scale", ctypes.c_float),
+        ("alpha", ctypes.c_float),
+        ("beta", ctypes.c_float),
+        ("orig_context", ctypes.c_int32),
     ]
 
 
@@ -77,6 +88,11 @@ def _load(path: str = LIB_PATH):
     lib.mla_append_absorb.restype = ctypes.c_int
     lib.mla_decode_noalloc.argtypes = [C, P, P, P, P, P, ctypes.c_int, I32, F32, P, P, P]
     lib.mla_decode_noalloc.restype = ctypes.c_int
+    lib.mla_append_yarn.argtypes = [C, P, I32, I32, P, P, ctypes.c_int, P, P,
+                                    ctypes.POINTER(mla_yarn_t), P]
+    lib.mla_append_yarn.restype = ctypes.c_int
+    lib.mla_yarn_softmax_factor.argtypes = [F32]
+    lib.mla_yarn_softmax_factor.restype = F32
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -249,6 +265,26 @@ def mla_append(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: t
     _check(lib.mla_append(st, _ptr(h), n_tok, d_model, _ptr(w_dkv), _ptr(w_kr),
                           dtype_code(h.dtype), _ptr(tok_seq), _ptr(tok_pos),
                           float(rope_base), _stream(stream)), "mla_append")
+
+
+def mla_append_yarn(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor,
+                    tok_seq: torch.Tensor, tok_pos: torch.Tensor, base: float = 10000.0,
+                    scale: float = 40.0, alpha: float = 1.0, beta: float = 32.0,
+                    orig_context: int = 4096, stream=None) -> None:
+    """mla_append with the RoPE key at YaRN frequencies (see libmla.h); the
+    defaults are DeepSeek-V2's."""
+    check_append_args(cache, h, w_dkv, w_kr, tok_seq, tok_pos)
+    n_tok, d_model = h.shape
+    st = ctypes.byref(cache.struct())
+    rope = mla_yarn_t(float(base), float(scale), float(alpha), float(beta), int(orig_context))
+    _check(lib.mla_append_yarn(st, _ptr(h), n_tok, d_model, _ptr(w_dkv), _ptr(w_kr),
+                               dtype_code(h.dtype), _ptr(tok_seq), _ptr(tok_pos),
+                               ctypes.byref(rope), _stream(stream)), "mla_append_yarn")
+
+
+def mla_yarn_softmax_factor(scale: float) -> float:
+    """(0.1 ln scale + 1)^2 for scale > 1, else 1 (see libmla.h)."""
+    return float(lib.mla_yarn_softmax_factor(float(scale)))
 
 
 def mla_append_absorb(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor,

@@ -183,10 +183,37 @@ const char* mla_status_string(mla_status_t s) {
 
 // Validate mla_append's arguments and fill `a` (n_tok == 0 is valid and
 // leaves nothing to launch).
+// YaRN frequencies of the RoPE pairs (the published YaRN method's
+// "NTK-by-parts" interpolation, with the constants the discosf explainer's
+// "decoupled RoPE and YaRN" section gives): pair i turns
+// orig_context * theta_i / (2 pi) times over the original context; pairs with
+// at most `alpha` turns run `scale` times slower, pairs with at least `beta`
+// keep theta_i, and a linear ramp in the number of turns mixes the two in
+// between. fp64, like the plain table.
+static void yarn_table(const mla_yarn_t& y, double* inv_freq) {
+  const double two_pi = 6.283185307179586;
+  for (int i = 0; i < MLA_D_R / 2; ++i) {
+    const double theta = pow((double)y.base, -2.0 * i / (double)MLA_D_R);
+    const double turns = (double)y.orig_context * theta / two_pi;
+    double g = (turns - (double)y.alpha) / ((double)y.beta - (double)y.alpha);
+    g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+    inv_freq[i] = (1.0 - g) * theta / (double)y.scale + g * theta;
+  }
+}
+
+static bool valid_yarn(const mla_yarn_t* y) {
+  if (!y) return false;
+  auto fin = [](float v) { return isfinite(v) != 0; };
+  return fin(y->base) && y->base > 0.f && fin(y->scale) && y->scale >= 1.f && fin(y->alpha) &&
+         y->alpha >= 0.f && fin(y->beta) && y->beta > y->alpha && y->orig_context >= 1;
+}
+
+// `yarn` NULL: plain RoPE with `rope_base`; else YaRN frequencies (its base).
 static mla_status_t append_args(const mla_cache_t* cache, const void* h, int32_t n_tok,
                                 int32_t d_model, const void* w_dkv, const void* w_kr,
                                 mla_dtype_t act_dtype, const int32_t* tok_seq,
-                                const int32_t* tok_pos, float rope_base, AppendArgs& a) {
+                                const int32_t* tok_pos, float rope_base, AppendArgs& a,
+                                const mla_yarn_t* yarn = nullptr) {
   mla_status_t st = check_cache(cache);
   if (st != MLA_OK) return st;
   if (!valid_dtype(act_dtype)) return MLA_ERR_INVALID_ARGUMENT;
@@ -207,8 +234,12 @@ static mla_status_t append_args(const mla_cache_t* cache, const void* h, int32_t
   a.tok_pos = tok_pos;
   a.n_tok = n_tok;
   a.d_model = d_model;
-  for (int i = 0; i < MLA_D_R / 2; ++i)
-    a.inv_freq[i] = pow((double)rope_base, -2.0 * i / (double)MLA_D_R);
+  if (yarn) {
+    yarn_table(*yarn, a.inv_freq);
+  } else {
+    for (int i = 0; i < MLA_D_R / 2; ++i)
+      a.inv_freq[i] = pow((double)rope_base, -2.0 * i / (double)MLA_D_R);
+  }
   return MLA_OK;
 }
 
@@ -228,6 +259,29 @@ mla_status_t mla_append(const mla_cache_t* cache, const void* h, int32_t n_tok, 
   }
   hipError_t e = launch_append(cache_type(cache->dtype), a, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_append_yarn(const mla_cache_t* cache, const void* h, int32_t n_tok,
+                             int32_t d_model, const void* w_dkv, const void* w_kr,
+                             mla_dtype_t act_dtype, const int32_t* tok_seq,
+                             const int32_t* tok_pos, const mla_yarn_t* rope, void* stream) {
+  if (!valid_yarn(rope)) return MLA_ERR_INVALID_ARGUMENT;
+  AppendArgs a;
+  const mla_status_t st = append_args(cache, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq,
+                                      tok_pos, rope->base, a, rope);
+  if (st != MLA_OK || n_tok == 0) return st;
+  if (debug_mode()) {
+    const mla_status_t ds = debug_check_append(cache, tok_seq, tok_pos, n_tok, (hipStream_t)stream);
+    if (ds != MLA_OK) return ds;
+  }
+  hipError_t e = launch_append(cache_type(cache->dtype), a, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+float mla_yarn_softmax_factor(float scale) {
+  if (!(scale > 1.f) || !isfinite(scale)) return 1.f;
+  const double m = 0.1 * log((double)scale) + 1.0;
+  return (float)(m * m);
 }
 
 mla_status_t mla_decode_workspace_size(int32_t num_seqs, int32_t n_heads, mla_dtype_t cache_dtype,

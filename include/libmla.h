@@ -130,6 +130,43 @@ mla_status_t mla_append(const mla_cache_t* cache,
                         float rope_base, void* stream);
 
 /*
+ * YaRN parameters of the decoupled RoPE key (discosf explainer, "decoupled
+ * RoPE and YaRN" section: YaRN with scale 40, alpha 1, beta 32 extends the
+ * context to 160K; the formula is the published YaRN method's). For pair i,
+ * theta_i = base^(-2i/64) turns orig_context * theta_i / (2 pi) times over the
+ * original context; with gamma = clamp((turns - alpha) / (beta - alpha), 0, 1)
+ * the pair rotates at theta'_i = (1 - gamma) * theta_i / scale + gamma * theta_i
+ * (computed in fp64 on the host). DeepSeek-V2's values: base 10000, scale 40,
+ * alpha 1, beta 32, orig_context 4096 (160K / 40).
+ */
+typedef struct {
+  float base;                    /* > 0 */
+  float scale;                   /* >= 1 (1 gives plain RoPE) */
+  float alpha;                   /* >= 0 */
+  float beta;                    /* > alpha */
+  int32_t orig_context;          /* >= 1 */
+} mla_yarn_t;
+
+/*
+ * mla_append_yarn -- mla_append with the RoPE key rotated at the YaRN
+ * frequencies theta'_i of `rope` (host) instead of base^(-2i/64); everything
+ * else (arguments, storage, rules) as mla_append. A NULL or out-of-range
+ * `rope` returns MLA_ERR_INVALID_ARGUMENT.
+ */
+mla_status_t mla_append_yarn(const mla_cache_t* cache,
+                             const void* h, int32_t n_tok, int32_t d_model,
+                             const void* w_dkv, const void* w_kr, mla_dtype_t act_dtype,
+                             const int32_t* tok_seq, const int32_t* tok_pos,
+                             const mla_yarn_t* rope, void* stream);
+
+/*
+ * mla_yarn_softmax_factor -- the factor YaRN's attention temperature puts on
+ * the softmax scale: (0.1 ln scale + 1)^2 for scale > 1, else 1. A decode over
+ * rows appended with mla_append_yarn passes softmax_scale times this factor.
+ */
+float mla_yarn_softmax_factor(float scale);
+
+/*
  * mla_decode_workspace_size -- bytes of device workspace mla_decode needs for
  * `num_seqs` sequences and `n_heads` heads with the given dtypes. The result
  * does not depend on the sequence lengths. Writes *bytes (host).

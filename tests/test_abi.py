@@ -18,7 +18,7 @@ FAKE = 0x100000      # a non-null address; never dereferenced on the error paths
 
 def _declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:mla_status_t|const char\*|int)\s+(mla_\w+)\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:mla_status_t|const char\*|int|float)\s+(mla_\w+)\(", src, re.M)))
 
 
 def test_exports_every_declared_symbol():
@@ -26,8 +26,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"mla_append", "mla_decode_workspace_size", "mla_decode",
                           "mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
                           "mla_decode_attend_combine",
-                          "mla_append_absorb", "mla_decode_noalloc", "mla_status_string",
-                          "mla_abi_version"}
+                          "mla_append_absorb", "mla_decode_noalloc", "mla_append_yarn",
+                          "mla_yarn_softmax_factor", "mla_status_string", "mla_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert getattr(lib, n) is not None
@@ -290,3 +290,31 @@ def test_decode_noalloc_validation():
     need = mla.mla_decode_workspace_size(128, 128, E.MLA_DTYPE_FP8_E4M3, E.MLA_DTYPE_BF16)
     assert need > mla.MLA_NOALLOC_WORKSPACE_BYTES
     assert call(big, H=128) == E.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_append_yarn_validation_and_softmax_factor():
+    E = mla
+    c = _cache()
+
+    def call(rope, n_tok=4, null=None):
+        args = dict(h=FAKE, w_dkv=FAKE, w_kr=FAKE, tok_seq=FAKE, tok_pos=FAKE)
+        if null:
+            args[null] = None
+        r = ctypes.byref(rope) if rope is not None else None
+        return lib.mla_append_yarn(ctypes.byref(c), args["h"], n_tok, 128, args["w_dkv"], args["w_kr"],
+                                   E.MLA_DTYPE_BF16, args["tok_seq"], args["tok_pos"], r, None)
+
+    good = dict(base=10000.0, scale=40.0, alpha=1.0, beta=32.0, orig_context=4096)
+    assert call(None) == E.MLA_ERR_INVALID_ARGUMENT
+    for k, v in [("base", 0.0), ("base", float("nan")), ("scale", 0.5), ("scale", float("inf")),
+                 ("alpha", -1.0), ("beta", 1.0), ("orig_context", 0)]:
+        assert call(mla.mla_yarn_t(**dict(good, **{k: v}))) == E.MLA_ERR_INVALID_ARGUMENT, k
+    assert call(mla.mla_yarn_t(**good), null="h") == E.MLA_ERR_INVALID_ARGUMENT
+    assert call(mla.mla_yarn_t(**good), n_tok=-1) == E.MLA_ERR_INVALID_ARGUMENT
+    # n_tok == 0 is a valid no-op that touches nothing
+    assert call(mla.mla_yarn_t(**good), n_tok=0) == E.MLA_OK
+    import math
+    assert mla.mla_yarn_softmax_factor(1.0) == 1.0
+    assert mla.mla_yarn_softmax_factor(0.25) == 1.0
+    assert mla.mla_yarn_softmax_factor(float("nan")) == 1.0
+    assert abs(mla.mla_yarn_softmax_factor(math.exp(10.0)) - 4.0) < 1e-6

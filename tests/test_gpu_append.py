@@ -261,3 +261,90 @@ def test_append_bf16_large_positions(fused):
     changed = torch.nonzero(torch.any(before.view(torch.int16) != cache.rows.view(torch.int16),
                                       dim=1)).flatten().cpu().tolist()
     assert set(changed) <= set(idx)
+
+
+# ---------------------------------------------------------------- YaRN
+YARN = dict(base=10000.0, scale=40.0, alpha=1.0, beta=32.0, orig_context=4096)
+
+
+def _append_yarn(cache, h, wd, wk, seq, pos):
+    mla = _mla()
+    mla.mla_append_yarn(cache, h.cuda(), wd.cuda(), wk.cuda(),
+                        torch.tensor(seq, dtype=torch.int32).cuda(),
+                        torch.tensor(pos, dtype=torch.int32).cuda(), **YARN)
+    torch.cuda.synchronize()
+
+
+def _yarn_freq():
+    return omla.yarn_inv_freq(YARN["base"], YARN["scale"], YARN["alpha"], YARN["beta"],
+                              YARN["orig_context"])
+
+
+def test_yarn_rope_indexing_exact_unit_probe():
+    """With unit inputs pair i of the stored key is at angle pos * theta'_i
+    (the YaRN frequency: kept, slowed 40x, or mixed), within 1e-6 rad of the
+    fp64 value, at positions up to 131071, in an fp32 cache."""
+    dm = 64
+    positions = [0, 1, 3, 4095, 4096, 40000, 100000, 131071]
+    n = len(positions)
+    cache, starts = _cache("f32", [131072, 9])
+    before = cache.rows.clone()
+    h = torch.zeros(n, dm)
+    h[:, 0] = 1.0
+    wd = torch.zeros(512, dm)
+    wd[3, 0] = 1.0
+    wk = torch.zeros(64, dm)
+    wk[0::2, 0] = 1.0
+    _append_yarn(cache, h, wd, wk, [0] * n, positions)
+    rows = cache.rows.cpu().double().numpy()
+    inv = _yarn_freq()
+    plain = omla.rope_inv_freq(YARN["base"])
+    assert np.any(inv != plain)                    # the probe does see a different table
+    worst = 0.0
+    for p in positions:
+        r = rows[int(starts[0]) + p]
+        assert r[3] == 1.0 and np.count_nonzero(r[:512]) == 1
+        for i in range(32):
+            ang = math.atan2(r[512 + 2 * i + 1], r[512 + 2 * i])
+            want = math.remainder(p * float(inv[i]), 2 * math.pi)
+            d = abs(math.remainder(ang - want, 2 * math.pi))
+            worst = max(worst, d)
+            assert d < 1e-6, (p, i, ang, want)
+    log(f"  YaRN: worst RoPE angle error {worst:.2e} rad")
+    changed = np.nonzero(np.any(_bits(before) != _bits(cache.rows), axis=1))[0]
+    assert sorted(changed.tolist()) == sorted(int(starts[0]) + p for p in positions)
+
+
+@pytest.mark.parametrize("n_tok", [7, 64])
+def test_append_yarn_bf16_values(n_tok):
+    """bf16 rows written with YaRN frequencies equal the oracle's rounding of
+    the exact rows (off the rounding midpoints), at positions up to 131071."""
+    rng = np.random.default_rng(50 + n_tok)
+    dm = 2048
+    caps = [131072, 257]
+    cache, starts = _cache("bf16", caps)
+    before = cache.rows.clone()
+    h = torch.from_numpy(rng.standard_normal((n_tok, dm)).astype(np.float32)).bfloat16()
+    wd = torch.from_numpy((rng.standard_normal((512, dm)) / math.sqrt(dm)).astype(np.float32)).bfloat16()
+    wk = torch.from_numpy((rng.standard_normal((64, dm)) / math.sqrt(dm)).astype(np.float32)).bfloat16()
+    seq = [i % 2 for i in range(n_tok)]
+    # distinct slots per sequence, the last slot of each among them
+    picks = {s: list(rng.choice(caps[s] - 1, size=seq.count(s) - 1, replace=False)) + [caps[s] - 1]
+             for s in (0, 1)}
+    pos = [int(picks[s].pop()) for s in seq]
+    _append_yarn(cache, h, wd, wk, seq, pos)
+    exact = omla.append_rows_exact(h.double().numpy(), wd.double().numpy(), wk.double().numpy(),
+                                   np.array(pos, dtype=np.float64), YARN["base"], _yarn_freq())
+    stored, _, _ = omla.quantize_rows(exact, "bf16")
+    rows = cache.rows.cpu().double().numpy()
+    got = np.stack([rows[int(starts[s]) + p] for s, p in zip(seq, pos)])
+    bound = _dot_bound(h.double().numpy(), wd.double().numpy(), wk.double().numpy(), pos,
+                       YARN["base"])
+    tie = _near_tie_bf16(exact, bound)
+    mism = (got != stored) & ~tie
+    log(f"  YaRN bf16 n_tok={n_tok}: {int((got != stored).sum())} of {got.size} differ, "
+        f"{int(tie.sum())} near ties, {int(mism.sum())} off-tie mismatches")
+    assert not mism.any()
+    assert np.all(np.abs(got - exact) <= np.ldexp(1.0, np.frexp(exact)[1] - 8) + bound)
+    changed = np.nonzero(np.any(_bits(before) != _bits(cache.rows), axis=1))[0]
+    assert set(changed.tolist()) <= {int(starts[s]) + p for s, p in zip(seq, pos)}
