@@ -27,7 +27,7 @@ to the code that takes them.
 from .numerics import (round_bf16, round_f32, e4m3_decode, e4m3_encode,
                        E4M3_MAX, e4m3_value_table)
 from .mla import (D_C, D_R, D_ROW, D_NOPE, D_V, softmax_scale, rope_inv_freq,
-                  yarn_inv_freq, yarn_softmax_factor, rope_rotate, append_rows_exact, quantize_rows,
+                  yarn_inv_freq, yarn_softmax_factor, rope_rotate, paged_rows, append_rows_exact, quantize_rows,
                   decode_head, decode_problem, decode_sampled, attention_weights,
                   mla_cache_elements_per_token, mha_cache_elements_per_token,
                   gqa_equivalent_groups, cache_bytes)

@@ -40,6 +40,14 @@ Readings taken where the pages are silent (each listed in the design notes):
       theta'_i = (1 - gamma) * theta_i / s + gamma * theta_i;
       L = target / s = 160K / 40 = 4096. The method's attention temperature
       multiplies the softmax scale by (0.1 ln s + 1)^2 (s > 1; 1 otherwise).
+  R9  paged cache [the deployment guides name vLLM's PagedAttention and
+      continuous batching as the serving engine's features (mlqm.cn guide,
+      sections 3.2 "software environment" and 8.2 "deployment optimisation"),
+      without a layout]: the cache is a pool of pages of P rows (P a multiple
+      of the 32-token tile); sequence b's token t lives in row
+      block_table[b][t // P] * P + t % P; rows are stored as in the contiguous
+      cache, so attention over a paged cache equals attention over the
+      sequence's rows gathered in token order.
 """
 from __future__ import annotations
 
@@ -145,6 +153,15 @@ def append_rows_exact(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray,
     c = h @ np.asarray(w_dkv, dtype=np.float64).T          # [n_tok, 512]
     k = h @ np.asarray(w_kr, dtype=np.float64).T           # [n_tok, 64]
     return np.concatenate([c, rope_rotate(k, pos, base, inv_freq)], axis=1)
+
+
+def paged_rows(rows: np.ndarray, block_table: np.ndarray, page_tokens: int, b: int,
+               length: int) -> np.ndarray:
+    """Sequence b's first `length` rows of a paged cache, in token order (R9):
+    token t is row block_table[b][t // P] * P + t % P of `rows`."""
+    t = np.arange(length)
+    idx = np.asarray(block_table)[b, t // page_tokens].astype(np.int64) * page_tokens + t % page_tokens
+    return np.asarray(rows)[idx]
 
 
 def quantize_rows(rows: np.ndarray, dtype: str) -> Tuple[np.ndarray, Optional[np.ndarray], np.ndarray]:
