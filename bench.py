@@ -299,6 +299,31 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
     torch.cuda.synchronize()
     attn_ms = a0.elapsed_time(a1) / steps
 
+    # append alone, plain RoPE and YaRN (the same kernel with another
+    # frequency table; launch-bound at these sizes, so µs only)
+    append_us = None
+    if wl.append:
+        r = reps[0]
+        seq_t, pos_t = r["tok_seq"], r["tok_pos"]
+        calls = {
+            "rope": lambda: mla.mla_append(r["cache"], r["h"], r["w_dkv"], r["w_kr"], seq_t, pos_t,
+                                           wl.rope_base, stream),
+            "yarn": lambda: mla.mla_append_yarn(r["cache"], r["h"], r["w_dkv"], r["w_kr"], seq_t,
+                                                pos_t, base=wl.rope_base, stream=stream),
+        }
+        append_us = {}
+        for k, fn in calls.items():
+            fn()
+            torch.cuda.synchronize()
+            b0 = torch.cuda.Event(enable_timing=True)
+            b1 = torch.cuda.Event(enable_timing=True)
+            b0.record(stream)
+            for _ in range(20):
+                fn()
+            b1.record(stream)
+            torch.cuda.synchronize()
+            append_us[k] = round(b0.elapsed_time(b1) / 20 * 1e3, 2)
+
     par = None
     if parity:
         # the outputs of one full step of replica 0 against the oracle
@@ -311,7 +336,7 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
     return dict(wl=wl, p=p, T=p.T, B=B, H=H, R=R, ms=ms, wall_ms=wall_ms, gpu_ms=gpu_ms,
                 step_pct=step_pct, step_bytes=step_bytes,
                 step_flops=step_flops, attn_bytes=ab["cache"], attn_flops=fl["attention"],
-                attn_ms=attn_ms, clock_mhz=clock, parity=par)
+                attn_ms=attn_ms, clock_mhz=clock, parity=par, append_us=append_us)
 
 
 def describe(wl, m) -> str:
@@ -372,6 +397,8 @@ def main():
             "T": s["T"], "step_bytes": int(s["step_bytes"]), "clock_mhz": s["clock_mhz"],
             "roofline": roofline(s, name),
         }
+        if s["append_us"]:
+            blocks[name]["append_us"] = s["append_us"]
         print(f"# measured {name}: {s['ms'] * 1e3:.2f} us/step, attention "
               f"{s['attn_ms'] * 1e3:.2f} us", file=sys.stderr, flush=True)
 

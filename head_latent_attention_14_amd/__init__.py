@@ -35,7 +35,8 @@ D_C, D_R, D_ROW, D_NOPE, D_V = 512, 64, 576, 128, 128
 EXPORTED = ["mla_append", "mla_decode_workspace_size", "mla_decode", "mla_decode_absorb",
             "mla_decode_attend", "mla_decode_combine", "mla_decode_attend_combine",
             "mla_append_absorb", "mla_decode_noalloc", "mla_append_yarn",
-            "mla_yarn_softmax_factor", "mla_status_string",
+            "mla_yarn_softmax_factor", "mla_append_paged", "mla_decode_paged",
+            "mla_status_string",
             "mla_abi_version"]
 DECODE_STAGES = ["mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
                  "mla_decode_attend_combine"]
@@ -52,6 +53,21 @@ class mla_cache_t(ctypes.Structure):
         ("row_scale", ctypes.c_void_p),
         ("seq_start", ctypes.c_void_p),
         ("seq_capacity", ctypes.c_void_p),
+    ]
+
+
+class mla_paged_cache_t(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("d_c", ctypes.c_int32),
+        ("d_r", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("page_tokens", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("total_pages", ctypes.c_int64),
+        ("rows", ctypes.c_void_p),
+        ("row_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
     ]
 
 
@@ -93,6 +109,11 @@ def _load(path: str = LIB_PATH):
     lib.mla_append_yarn.restype = ctypes.c_int
     lib.mla_yarn_softmax_factor.argtypes = [F32]
     lib.mla_yarn_softmax_factor.restype = F32
+    PC = ctypes.POINTER(mla_paged_cache_t)
+    lib.mla_append_paged.argtypes = [PC, P, I32, I32, P, P, ctypes.c_int, P, P, F32, P]
+    lib.mla_append_paged.restype = ctypes.c_int
+    lib.mla_decode_paged.argtypes = [PC, P, P, P, P, P, ctypes.c_int, I32, F32, P, P, P, SZ, P]
+    lib.mla_decode_paged.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -245,6 +266,71 @@ class LatentCache:
         return mla_cache_t(self.dtype, D_C, D_R, self.num_seqs, self.rows.shape[0],
                            _ptr(self.rows), _ptr(self.row_scale), _ptr(self.seq_start),
                            _ptr(self.seq_capacity))
+
+
+@dataclasses.dataclass
+class PagedLatentCache:
+    """Device tensors of a paged latent cache (see mla_paged_cache_t): token t
+    of sequence b is row block_table[b, t // page_tokens] * page_tokens +
+    t % page_tokens of `rows`."""
+    rows: torch.Tensor                 # [total_pages * page_tokens, 576] f32 | bf16 | uint8 codes
+    block_table: torch.Tensor          # [B, max_pages] int32
+    page_tokens: int
+    row_scale: Optional[torch.Tensor] = None   # [total_pages * page_tokens] f32 (fp8 only)
+
+    @property
+    def dtype(self) -> int:
+        return dtype_code(self.rows.dtype)
+
+    @property
+    def num_seqs(self) -> int:
+        return self.block_table.shape[0]
+
+    def check(self) -> None:
+        """Shapes, dtypes and devices of the cache tensors."""
+        if self.rows.dim() != 2 or self.rows.shape[1] != D_ROW:
+            raise ValueError("rows must be [total_pages * page_tokens, 576]")
+        if self.page_tokens < 32 or self.page_tokens % 32 or self.rows.shape[0] % self.page_tokens:
+            raise ValueError("page_tokens must be a multiple of 32 dividing the row count")
+        dev = self.rows.device
+        if self.block_table.dim() != 2 or self.block_table.shape[0] < 1:
+            raise ValueError("block_table must be a [B, max_pages] tensor")
+        _expect(self.block_table, "block_table", tuple(self.block_table.shape), torch.int32, dev)
+        if self.dtype == MLA_DTYPE_FP8_E4M3:
+            _expect(self.row_scale, "row_scale", (self.rows.shape[0],), torch.float32, dev)
+        elif self.row_scale is not None:
+            raise ValueError("row_scale is only for an fp8 cache")
+
+    def struct(self) -> mla_paged_cache_t:
+        self.check()
+        return mla_paged_cache_t(self.dtype, D_C, D_R, self.num_seqs, int(self.page_tokens),
+                                 self.block_table.shape[1], self.rows.shape[0] // self.page_tokens,
+                                 _ptr(self.rows), _ptr(self.row_scale), _ptr(self.block_table))
+
+
+def mla_append_paged(cache: PagedLatentCache, h: torch.Tensor, w_dkv: torch.Tensor,
+                     w_kr: torch.Tensor, tok_seq: torch.Tensor, tok_pos: torch.Tensor,
+                     rope_base: float, stream=None) -> None:
+    """mla_append into a paged cache (see libmla.h)."""
+    check_append_args(cache, h, w_dkv, w_kr, tok_seq, tok_pos)
+    n_tok, d_model = h.shape
+    st = ctypes.byref(cache.struct())
+    _check(lib.mla_append_paged(st, _ptr(h), n_tok, d_model, _ptr(w_dkv), _ptr(w_kr),
+                                dtype_code(h.dtype), _ptr(tok_seq), _ptr(tok_pos),
+                                float(rope_base), _stream(stream)), "mla_append_paged")
+
+
+def mla_decode_paged(cache: PagedLatentCache, seq_len: torch.Tensor, q_nope: torch.Tensor,
+                     q_pe: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                     softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
+                     workspace: torch.Tensor, stream=None) -> None:
+    """mla_decode over a paged cache (see libmla.h)."""
+    H = check_decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, out, lse, workspace)
+    st = ctypes.byref(cache.struct())
+    _check(lib.mla_decode_paged(st, _ptr(seq_len), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk),
+                                _ptr(w_uv), dtype_code(q_nope.dtype), H, float(softmax_scale),
+                                _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                _stream(stream)), "mla_decode_paged")
 
 
 def mla_abi_version() -> int:

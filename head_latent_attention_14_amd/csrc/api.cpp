@@ -103,14 +103,68 @@ static int cache_type(int dtype) {
   return dtype == MLA_DTYPE_F32 ? kF32 : (dtype == MLA_DTYPE_BF16 ? kBF16 : kFP8);
 }
 
-static mla_status_t check_cache(const mla_cache_t* c) {
+// The cache as the launchers see it: contiguous per-sequence row ranges
+// (seq_start, seq_cap) or a page pool with a block table.
+struct CacheView {
+  int32_t dtype;
+  int32_t num_seqs;
+  void* rows;
+  float* row_scale;
+  const int64_t* seq_start;      // contiguous
+  const int32_t* seq_cap;        // contiguous
+  int64_t total_rows;
+  const int32_t* block_table;    // paged ([B][max_pages]), else null
+  int32_t page_tokens;
+  int32_t max_pages;
+  int64_t total_pages;
+};
+
+static mla_status_t check_common(int32_t dtype, int32_t d_c, int32_t d_r, int32_t num_seqs,
+                                 const void* rows, const float* row_scale) {
+  if (!valid_dtype(dtype)) return MLA_ERR_INVALID_ARGUMENT;
+  if (d_c != MLA_D_C || d_r != MLA_D_R) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_seqs < 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_seqs > kMaxSeqs) return MLA_ERR_UNSUPPORTED;
+  if (!rows) return MLA_ERR_INVALID_ARGUMENT;
+  if (dtype == MLA_DTYPE_FP8_E4M3 && !row_scale) return MLA_ERR_INVALID_ARGUMENT;
+  return MLA_OK;
+}
+
+static mla_status_t view_of(const mla_cache_t* c, CacheView& v) {
   if (!c) return MLA_ERR_INVALID_ARGUMENT;
-  if (!valid_dtype(c->dtype)) return MLA_ERR_INVALID_ARGUMENT;
-  if (c->d_c != MLA_D_C || c->d_r != MLA_D_R) return MLA_ERR_INVALID_ARGUMENT;
-  if (c->num_seqs < 1 || c->total_rows < 1) return MLA_ERR_INVALID_ARGUMENT;
-  if (c->num_seqs > kMaxSeqs) return MLA_ERR_UNSUPPORTED;
-  if (!c->rows || !c->seq_start || !c->seq_capacity) return MLA_ERR_INVALID_ARGUMENT;
-  if (c->dtype == MLA_DTYPE_FP8_E4M3 && !c->row_scale) return MLA_ERR_INVALID_ARGUMENT;
+  const mla_status_t st = check_common(c->dtype, c->d_c, c->d_r, c->num_seqs, c->rows, c->row_scale);
+  if (st != MLA_OK) return st;
+  if (c->total_rows < 1 || !c->seq_start || !c->seq_capacity) return MLA_ERR_INVALID_ARGUMENT;
+  v = CacheView{};
+  v.dtype = c->dtype;
+  v.num_seqs = c->num_seqs;
+  v.rows = c->rows;
+  v.row_scale = c->row_scale;
+  v.seq_start = c->seq_start;
+  v.seq_cap = c->seq_capacity;
+  v.total_rows = c->total_rows;
+  return MLA_OK;
+}
+
+static mla_status_t view_of(const mla_paged_cache_t* c, CacheView& v) {
+  if (!c) return MLA_ERR_INVALID_ARGUMENT;
+  const mla_status_t st = check_common(c->dtype, c->d_c, c->d_r, c->num_seqs, c->rows, c->row_scale);
+  if (st != MLA_OK) return st;
+  if (!c->block_table || c->max_pages < 1 || c->total_pages < 1) return MLA_ERR_INVALID_ARGUMENT;
+  if (c->page_tokens < 32 || c->page_tokens % 32 != 0) return MLA_ERR_INVALID_ARGUMENT;
+  // positions and lengths are int32: a sequence's capacity must fit
+  if ((int64_t)c->max_pages * c->page_tokens > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if (c->total_pages > INT64_MAX / c->page_tokens) return MLA_ERR_INVALID_ARGUMENT;
+  v = CacheView{};
+  v.dtype = c->dtype;
+  v.num_seqs = c->num_seqs;
+  v.rows = c->rows;
+  v.row_scale = c->row_scale;
+  v.total_rows = c->total_pages * c->page_tokens;
+  v.block_table = c->block_table;
+  v.page_tokens = c->page_tokens;
+  v.max_pages = c->max_pages;
+  v.total_pages = c->total_pages;
   return MLA_OK;
 }
 
@@ -135,30 +189,53 @@ static bool to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) 
   return hipStreamSynchronize(s) == hipSuccess;
 }
 
-// the cache's rows and, when given, the lengths; MLA_ERR_HIP if a copy fails
-static mla_status_t debug_check_decode(const mla_cache_t* c, const int32_t* seq_len, hipStream_t s) {
-  std::vector<int64_t> start;
-  std::vector<int32_t> cap, len;
-  if (!to_host(start, c->seq_start, c->num_seqs, s) || !to_host(cap, c->seq_capacity, c->num_seqs, s))
-    return MLA_ERR_HIP;
-  if (seq_len && !to_host(len, seq_len, c->num_seqs, s)) return MLA_ERR_HIP;
-  for (int b = 0; b < c->num_seqs; ++b) {
-    if (start[b] < 0 || cap[b] < 0 || start[b] + cap[b] > c->total_rows) return MLA_ERR_INVALID_ARGUMENT;
-    if (seq_len && (len[b] < 1 || len[b] > cap[b])) return MLA_ERR_INVALID_ARGUMENT;
+// Each sequence's capacity (and, contiguous, its rows inside the cache;
+// paged, every table entry a call can use inside the pool: all of them when
+// `len` is null, else those of the first ceil(len / P) blocks).
+static mla_status_t debug_capacity(const CacheView& c, const std::vector<int32_t>* len,
+                                   std::vector<int32_t>& cap, hipStream_t s) {
+  const int B = c.num_seqs;
+  if (c.block_table) {
+    std::vector<int32_t> tab;
+    if (!to_host(tab, c.block_table, (size_t)B * c.max_pages, s)) return MLA_ERR_HIP;
+    cap.assign(B, c.max_pages * c.page_tokens);
+    for (int b = 0; b < B; ++b) {
+      const int64_t used = len ? ((int64_t)(*len)[b] + c.page_tokens - 1) / c.page_tokens : c.max_pages;
+      for (int64_t j = 0; j < used && j < c.max_pages; ++j) {
+        const int32_t pg = tab[(size_t)b * c.max_pages + j];
+        if (pg < 0 || pg >= c.total_pages) return MLA_ERR_INVALID_ARGUMENT;
+      }
+    }
+    return MLA_OK;
   }
+  std::vector<int64_t> start;
+  if (!to_host(start, c.seq_start, B, s) || !to_host(cap, c.seq_cap, B, s)) return MLA_ERR_HIP;
+  for (int b = 0; b < B; ++b)
+    if (start[b] < 0 || cap[b] < 0 || start[b] + cap[b] > c.total_rows) return MLA_ERR_INVALID_ARGUMENT;
   return MLA_OK;
 }
 
-static mla_status_t debug_check_append(const mla_cache_t* c, const int32_t* tok_seq,
-                                       const int32_t* tok_pos, int32_t n_tok, hipStream_t s) {
-  mla_status_t st = debug_check_decode(c, nullptr, s);
+// the cache's rows and the lengths; MLA_ERR_HIP if a copy fails
+static mla_status_t debug_check_decode(const CacheView& c, const int32_t* seq_len, hipStream_t s) {
+  std::vector<int32_t> cap, len;
+  if (!to_host(len, seq_len, c.num_seqs, s)) return MLA_ERR_HIP;
+  for (int b = 0; b < c.num_seqs; ++b)
+    if (len[b] < 1) return MLA_ERR_INVALID_ARGUMENT;
+  const mla_status_t st = debug_capacity(c, &len, cap, s);
   if (st != MLA_OK) return st;
+  for (int b = 0; b < c.num_seqs; ++b)
+    if (len[b] > cap[b]) return MLA_ERR_INVALID_ARGUMENT;
+  return MLA_OK;
+}
+
+static mla_status_t debug_check_append(const CacheView& c, const int32_t* tok_seq,
+                                       const int32_t* tok_pos, int32_t n_tok, hipStream_t s) {
   std::vector<int32_t> cap, sq, ps;
-  if (!to_host(cap, c->seq_capacity, c->num_seqs, s) || !to_host(sq, tok_seq, n_tok, s) ||
-      !to_host(ps, tok_pos, n_tok, s))
-    return MLA_ERR_HIP;
+  mla_status_t st = debug_capacity(c, nullptr, cap, s);
+  if (st != MLA_OK) return st;
+  if (!to_host(sq, tok_seq, n_tok, s) || !to_host(ps, tok_pos, n_tok, s)) return MLA_ERR_HIP;
   for (int n = 0; n < n_tok; ++n) {
-    if (sq[n] < 0 || sq[n] >= c->num_seqs) return MLA_ERR_INVALID_ARGUMENT;
+    if (sq[n] < 0 || sq[n] >= c.num_seqs) return MLA_ERR_INVALID_ARGUMENT;
     if (ps[n] < 0 || ps[n] >= cap[sq[n]]) return MLA_ERR_INVALID_ARGUMENT;
   }
   return MLA_OK;
@@ -181,8 +258,6 @@ const char* mla_status_string(mla_status_t s) {
 
 }  // extern "C"
 
-// Validate mla_append's arguments and fill `a` (n_tok == 0 is valid and
-// leaves nothing to launch).
 // YaRN frequencies of the RoPE pairs (the published YaRN method's
 // "NTK-by-parts" interpolation, with the constants the discosf explainer's
 // "decoupled RoPE and YaRN" section gives): pair i turns
@@ -208,25 +283,29 @@ static bool valid_yarn(const mla_yarn_t* y) {
          y->alpha >= 0.f && fin(y->beta) && y->beta > y->alpha && y->orig_context >= 1;
 }
 
-// `yarn` NULL: plain RoPE with `rope_base`; else YaRN frequencies (its base).
-static mla_status_t append_args(const mla_cache_t* cache, const void* h, int32_t n_tok,
+// Validate mla_append's arguments and fill `a` (n_tok == 0 is valid and
+// leaves nothing to launch). `yarn` NULL: plain RoPE with `rope_base`; else
+// YaRN frequencies (its base).
+static mla_status_t append_args(const CacheView& cache, const void* h, int32_t n_tok,
                                 int32_t d_model, const void* w_dkv, const void* w_kr,
                                 mla_dtype_t act_dtype, const int32_t* tok_seq,
                                 const int32_t* tok_pos, float rope_base, AppendArgs& a,
                                 const mla_yarn_t* yarn = nullptr) {
-  mla_status_t st = check_cache(cache);
-  if (st != MLA_OK) return st;
   if (!valid_dtype(act_dtype)) return MLA_ERR_INVALID_ARGUMENT;
   if (n_tok < 0 || d_model <= 0 || d_model % 64 != 0) return MLA_ERR_INVALID_ARGUMENT;
   if (!(rope_base > 0.f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARGUMENT;
-  if (!supported_pair(cache->dtype, act_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (!supported_pair(cache.dtype, act_dtype)) return MLA_ERR_UNSUPPORTED;
   if (n_tok > 0 && (!h || !w_dkv || !w_kr || !tok_seq || !tok_pos)) return MLA_ERR_INVALID_ARGUMENT;
   a = AppendArgs{};
-  a.rows = cache->rows;
-  a.row_scale = cache->row_scale;
-  a.seq_start = cache->seq_start;
-  a.seq_cap = cache->seq_capacity;
-  a.num_seqs = cache->num_seqs;
+  a.rows = cache.rows;
+  a.row_scale = cache.row_scale;
+  a.seq_start = cache.seq_start;
+  a.seq_cap = cache.seq_cap;
+  a.num_seqs = cache.num_seqs;
+  a.block_table = cache.block_table;
+  a.page_tokens = cache.page_tokens;
+  a.max_pages = cache.max_pages;
+  a.total_pages = cache.total_pages;
   a.h = h;
   a.w_dkv = w_dkv;
   a.w_kr = w_kr;
@@ -243,39 +322,58 @@ static mla_status_t append_args(const mla_cache_t* cache, const void* h, int32_t
   return MLA_OK;
 }
 
+// append through any cache view (YaRN table when `yarn` is given)
+static mla_status_t append_impl(const CacheView& cv, const void* h, int32_t n_tok,
+                                int32_t d_model, const void* w_dkv, const void* w_kr,
+                                mla_dtype_t act_dtype, const int32_t* tok_seq,
+                                const int32_t* tok_pos, float rope_base, const mla_yarn_t* yarn,
+                                void* stream) {
+  AppendArgs a;
+  const mla_status_t st = append_args(cv, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq,
+                                      tok_pos, rope_base, a, yarn);
+  if (st != MLA_OK || n_tok == 0) return st;
+  if (debug_mode()) {
+    const mla_status_t ds = debug_check_append(cv, tok_seq, tok_pos, n_tok, (hipStream_t)stream);
+    if (ds != MLA_OK) return ds;
+  }
+  hipError_t e = launch_append(cache_type(cv.dtype), a, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 extern "C" {
 
 mla_status_t mla_append(const mla_cache_t* cache, const void* h, int32_t n_tok, int32_t d_model,
                         const void* w_dkv, const void* w_kr, mla_dtype_t act_dtype,
                         const int32_t* tok_seq, const int32_t* tok_pos, float rope_base,
                         void* stream) {
-  AppendArgs a;
-  const mla_status_t st = append_args(cache, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq,
-                                      tok_pos, rope_base, a);
-  if (st != MLA_OK || n_tok == 0) return st;
-  if (debug_mode()) {
-    const mla_status_t ds = debug_check_append(cache, tok_seq, tok_pos, n_tok, (hipStream_t)stream);
-    if (ds != MLA_OK) return ds;
-  }
-  hipError_t e = launch_append(cache_type(cache->dtype), a, (hipStream_t)stream);
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  CacheView cv;
+  const mla_status_t st = view_of(cache, cv);
+  if (st != MLA_OK) return st;
+  return append_impl(cv, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq, tok_pos, rope_base,
+                     nullptr, stream);
 }
 
 mla_status_t mla_append_yarn(const mla_cache_t* cache, const void* h, int32_t n_tok,
                              int32_t d_model, const void* w_dkv, const void* w_kr,
                              mla_dtype_t act_dtype, const int32_t* tok_seq,
                              const int32_t* tok_pos, const mla_yarn_t* rope, void* stream) {
+  CacheView cv;
+  const mla_status_t st = view_of(cache, cv);
+  if (st != MLA_OK) return st;
   if (!valid_yarn(rope)) return MLA_ERR_INVALID_ARGUMENT;
-  AppendArgs a;
-  const mla_status_t st = append_args(cache, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq,
-                                      tok_pos, rope->base, a, rope);
-  if (st != MLA_OK || n_tok == 0) return st;
-  if (debug_mode()) {
-    const mla_status_t ds = debug_check_append(cache, tok_seq, tok_pos, n_tok, (hipStream_t)stream);
-    if (ds != MLA_OK) return ds;
-  }
-  hipError_t e = launch_append(cache_type(cache->dtype), a, (hipStream_t)stream);
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return append_impl(cv, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq, tok_pos, rope->base,
+                     rope, stream);
+}
+
+mla_status_t mla_append_paged(const mla_paged_cache_t* cache, const void* h, int32_t n_tok,
+                              int32_t d_model, const void* w_dkv, const void* w_kr,
+                              mla_dtype_t act_dtype, const int32_t* tok_seq,
+                              const int32_t* tok_pos, float rope_base, void* stream) {
+  CacheView cv;
+  const mla_status_t st = view_of(cache, cv);
+  if (st != MLA_OK) return st;
+  return append_impl(cv, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq, tok_pos, rope_base,
+                     nullptr, stream);
 }
 
 float mla_yarn_softmax_factor(float scale) {
@@ -298,32 +396,34 @@ mla_status_t mla_decode_workspace_size(int32_t num_seqs, int32_t n_heads, mla_dt
 }  // extern "C"
 
 // Validate mla_decode's arguments and fill `a` and the launch plan.
-static mla_status_t decode_args(const mla_cache_t* cache, const int32_t* seq_len,
+static mla_status_t decode_args(const CacheView& cache, const int32_t* seq_len,
                                 const void* q_nope, const void* q_pe, const void* w_uk,
                                 const void* w_uv, mla_dtype_t act_dtype, int32_t n_heads,
                                 float softmax_scale, void* out, float* lse, void* workspace,
                                 size_t workspace_bytes, DecodeArgs& a, DecodePlan& plan) {
-  mla_status_t st = check_cache(cache);
-  if (st != MLA_OK) return st;
   if (!valid_dtype(act_dtype)) return MLA_ERR_INVALID_ARGUMENT;
   if (!seq_len || !q_nope || !q_pe || !w_uk || !w_uv || !out || !workspace)
     return MLA_ERR_INVALID_ARGUMENT;
   if (n_heads < 1) return MLA_ERR_INVALID_ARGUMENT;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARGUMENT;
   if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_INVALID_ARGUMENT;
-  if (!supported_pair(cache->dtype, act_dtype)) return MLA_ERR_UNSUPPORTED;
+  if (!supported_pair(cache.dtype, act_dtype)) return MLA_ERR_UNSUPPORTED;
   if (n_heads % 16 != 0 || n_heads > kMaxHeads) return MLA_ERR_UNSUPPORTED;
-  const int ct = cache_type(cache->dtype);
-  const int B = cache->num_seqs;
+  const int ct = cache_type(cache.dtype);
+  const int B = cache.num_seqs;
   const WorkspaceLayout wl = workspace_layout(ct, B, n_heads);
   if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
   char* ws = (char*)workspace;
   a = DecodeArgs{};
-  a.rows = cache->rows;
-  a.row_scale = cache->row_scale;
-  a.seq_start = cache->seq_start;
-  a.seq_cap = cache->seq_capacity;
+  a.rows = cache.rows;
+  a.row_scale = cache.row_scale;
+  a.seq_start = cache.seq_start;
+  a.seq_cap = cache.seq_cap;
+  a.block_table = cache.block_table;
+  a.page_tokens = cache.page_tokens;
+  a.max_pages = cache.max_pages;
+  a.total_pages = cache.total_pages;
   a.seq_len = seq_len;
   a.B = B;
   a.H = n_heads;
@@ -347,22 +447,34 @@ static mla_status_t decode_args(const mla_cache_t* cache, const int32_t* seq_len
   return MLA_OK;
 }
 
+static mla_status_t decode_view(const CacheView& cv, const int32_t* seq_len, const void* q_nope,
+                                const void* q_pe, const void* w_uk, const void* w_uv,
+                                mla_dtype_t act_dtype, int32_t n_heads, float softmax_scale,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream, int stage) {
+  DecodeArgs a;
+  DecodePlan plan;
+  const mla_status_t st = decode_args(cv, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads,
+                                      softmax_scale, out, lse, workspace, workspace_bytes, a, plan);
+  if (st != MLA_OK) return st;
+  if (debug_mode()) {
+    const mla_status_t ds = debug_check_decode(cv, seq_len, (hipStream_t)stream);
+    if (ds != MLA_OK) return ds;
+  }
+  hipError_t e = launch_decode(cache_type(cv.dtype), plan, a, (hipStream_t)stream, stage);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 static mla_status_t decode_impl(const mla_cache_t* cache, const int32_t* seq_len,
                                 const void* q_nope, const void* q_pe, const void* w_uk,
                                 const void* w_uv, mla_dtype_t act_dtype, int32_t n_heads,
                                 float softmax_scale, void* out, float* lse, void* workspace,
                                 size_t workspace_bytes, void* stream, int stage) {
-  DecodeArgs a;
-  DecodePlan plan;
-  const mla_status_t st = decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads,
-                                      softmax_scale, out, lse, workspace, workspace_bytes, a, plan);
+  CacheView cv;
+  const mla_status_t st = view_of(cache, cv);
   if (st != MLA_OK) return st;
-  if (debug_mode()) {
-    const mla_status_t ds = debug_check_decode(cache, seq_len, (hipStream_t)stream);
-    if (ds != MLA_OK) return ds;
-  }
-  hipError_t e = launch_decode(cache_type(cache->dtype), plan, a, (hipStream_t)stream, stage);
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return decode_view(cv, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads, softmax_scale, out,
+                     lse, workspace, workspace_bytes, stream, stage);
 }
 
 #define MLA_DECODE_ENTRY(NAME, STAGE)                                                        \
@@ -382,6 +494,18 @@ MLA_DECODE_ENTRY(mla_decode_attend, 2)
 MLA_DECODE_ENTRY(mla_decode_combine, 3)
 MLA_DECODE_ENTRY(mla_decode_attend_combine, 4)
 
+mla_status_t mla_decode_paged(const mla_paged_cache_t* cache, const int32_t* seq_len,
+                              const void* q_nope, const void* q_pe, const void* w_uk,
+                              const void* w_uv, mla_dtype_t act_dtype, int32_t n_heads,
+                              float softmax_scale, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  CacheView cv;
+  const mla_status_t st = view_of(cache, cv);
+  if (st != MLA_OK) return st;
+  return decode_view(cv, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads, softmax_scale, out,
+                     lse, workspace, workspace_bytes, stream, 0);
+}
+
 mla_status_t mla_append_absorb(const mla_cache_t* cache, const void* h, int32_t n_tok,
                                int32_t d_model, const void* w_dkv, const void* w_kr,
                                const int32_t* tok_seq, const int32_t* tok_pos, float rope_base,
@@ -389,22 +513,24 @@ mla_status_t mla_append_absorb(const mla_cache_t* cache, const void* h, int32_t 
                                const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
                                int32_t n_heads, float softmax_scale, void* out, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream) {
+  CacheView cv;
+  mla_status_t st = view_of(cache, cv);
+  if (st != MLA_OK) return st;
   AppendArgs aa;
-  mla_status_t st = append_args(cache, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq, tok_pos,
-                                rope_base, aa);
+  st = append_args(cv, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq, tok_pos, rope_base, aa);
   if (st != MLA_OK) return st;
   DecodeArgs da;
   DecodePlan plan;
-  st = decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads, softmax_scale, out,
+  st = decode_args(cv, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads, softmax_scale, out,
                    lse, workspace, workspace_bytes, da, plan);
   if (st != MLA_OK) return st;
   if (debug_mode()) {
-    mla_status_t ds = n_tok > 0 ? debug_check_append(cache, tok_seq, tok_pos, n_tok, (hipStream_t)stream)
+    mla_status_t ds = n_tok > 0 ? debug_check_append(cv, tok_seq, tok_pos, n_tok, (hipStream_t)stream)
                                 : MLA_OK;
-    if (ds == MLA_OK) ds = debug_check_decode(cache, seq_len, (hipStream_t)stream);
+    if (ds == MLA_OK) ds = debug_check_decode(cv, seq_len, (hipStream_t)stream);
     if (ds != MLA_OK) return ds;
   }
-  const int ct = cache_type(cache->dtype);
+  const int ct = cache_type(cv.dtype);
   hipError_t e;
   if (n_tok > 0 && append_absorb_fits(ct, aa, da)) {
     e = launch_append_absorb(aa, plan, da, (hipStream_t)stream);
@@ -453,9 +579,12 @@ mla_status_t mla_decode_noalloc(const mla_cache_t* cache, const int32_t* seq_len
                                 float softmax_scale, void* out, float* lse, void* stream) {
   // every host-side check, the workspace size included, before any HIP call:
   // a fake non-null workspace stands in until the real address is known
+  CacheView cv;
+  mla_status_t st = view_of(cache, cv);
+  if (st != MLA_OK) return st;
   DecodeArgs a;
   DecodePlan plan;
-  mla_status_t st = decode_args(cache, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads,
+  st = decode_args(cv, seq_len, q_nope, q_pe, w_uk, w_uv, act_dtype, n_heads,
                                 softmax_scale, out, lse, (void*)(uintptr_t)256,
                                 MLA_NOALLOC_WORKSPACE_BYTES, a, plan);
   if (st != MLA_OK) return st;

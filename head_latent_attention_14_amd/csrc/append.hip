@@ -53,6 +53,22 @@ mla_append_kernel(AppendArgs a) {
       sq[t] = ld_const(a.tok_seq, tok);
       ps[t] = ld_const(a.tok_pos, tok);
     }
+    if (a.block_table) {
+      // paged: the row from the block table; a position past the table or a
+      // table entry outside the page pool skips the token
+      if (lane == 0) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          bool ok = sq[t] >= 0 && sq[t] < a.num_seqs;
+          const int64_t r = ok ? paged_row(a.block_table, a.max_pages, a.page_tokens, a.total_pages,
+                                           sq[t], ps[t], ok)
+                               : 0;
+          trow[t] = ok ? r : -1;
+          tpos[t] = ps[t];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int sc = (sq[t] >= 0 && sq[t] < a.num_seqs) ? sq[t] : 0;
@@ -259,11 +275,17 @@ __device__ void append_bf16_block(const AppendArgs& a, int tb, int cg, AppendBf1
     const int sq = a.tok_seq[t];
     const int ps = a.tok_pos[t];
     const int sc = (sq >= 0 && sq < a.num_seqs) ? sq : 0;
-    const int cap = a.seq_cap[sc];
-    const int64_t st = a.seq_start[sc];
     if (g == 0) {
-      const bool ok = sq >= 0 && sq < a.num_seqs && ps >= 0 && ps < cap;
-      trow[l16] = ok ? st + ps : -1;
+      bool ok = sq >= 0 && sq < a.num_seqs;
+      int64_t r = 0;
+      if (a.block_table) {                 // paged: the row from the block table
+        if (ok) r = paged_row(a.block_table, a.max_pages, a.page_tokens, a.total_pages, sq, ps, ok);
+      } else {
+        const int cap = a.seq_cap[sc];
+        ok = ok && ps >= 0 && ps < cap;
+        r = a.seq_start[sc] + ps;
+      }
+      trow[l16] = ok ? r : -1;
       tpos[l16] = ps;
     }
     if (j0 >= kDc) {

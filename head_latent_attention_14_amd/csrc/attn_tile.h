@@ -20,6 +20,14 @@ struct AttnParams {
   int32_t B;
   int32_t H;
   float scale_log2;          // softmax_scale * log2(e)
+  // paged cache (block_table non-null): a tile never spans two pages
+  // (page_tokens is a multiple of the tile); the cursor looks up the next
+  // page when it crosses into it
+  const int32_t* block_table;  // [B][max_pages]
+  int32_t max_pages;
+  int32_t page_tokens;
+  int32_t page_tiles;          // page_tokens / tile
+  int64_t total_pages;
 };
 
 // Per cache dtype: bytes of a stored row, bytes of a padded LDS row, and
@@ -44,15 +52,26 @@ struct Cursor {
   int64_t row0;     // cache row of token t
   int nb;           // next sequence with tiles (B: none)
   int nx;           // this lane's word of seqinfo[nb]
+  int page;         // paged cache: block of token t in the sequence's table
+  int page_left;    // paged cache: tiles of that page from t on
 };
+
+// Paged cache: the row of the first token of block `page` of sequence b (an
+// entry outside the pool reads page 0 of it: a wrong page, never outside it).
+__device__ __forceinline__ int64_t page_row0(const AttnParams& p, int b, int page) {
+  const int64_t pg = ld_const(p.block_table, (int64_t)b * p.max_pages + page);
+  return (pg >= 0 && pg < p.total_pages ? pg : 0) * p.page_tokens;
+}
 
 __device__ __forceinline__ int seqinfo_word(const SeqInfo* si, int b, int lane) {
   return ((const int*)(si + b))[lane & 7];
 }
 
 // The first tile of worker w (c.b < 0: the worker has none); r_hi receives
-// one past its last tile.
-template <int TILE>
+// one past its last tile. PAGED: the cache is a page pool (AttnParams'
+// block table); a compile-time switch, so that the contiguous kernels carry
+// none of the page bookkeeping.
+template <int TILE, bool PAGED>
 __device__ __forceinline__ Cursor cursor_start(const AttnParams& p, int64_t w, int lane,
                                                int64_t& r_hi) {
   const WorkerInfo* wi = p.winfo + w;
@@ -64,6 +83,13 @@ __device__ __forceinline__ Cursor cursor_start(const AttnParams& p, int64_t w, i
   c.nb = ld_const(&wi->next, 0);
   r_hi = ld_const(&wi->r_hi, 0);
   c.nx = (c.b >= 0 && c.nb < p.B) ? seqinfo_word(p.seqinfo, c.nb, opaque(lane)) : 0;
+  c.page = 0;
+  c.page_left = 0;
+  if (PAGED && c.b >= 0) {
+    const int t = (int)c.t;
+    c.page = t / p.page_tokens;
+    c.page_left = p.page_tiles - (t - c.page * p.page_tokens) / TILE;
+  }
   return c;
 }
 
@@ -75,11 +101,20 @@ __device__ __forceinline__ int next_segment_seq(const Cursor& c, const AttnParam
 }
 
 // Move to the next tile of the worker's range; false when done.
-template <int TILE>
+template <int TILE, bool PAGED>
 __device__ __forceinline__ bool advance(Cursor& c, const AttnParams& p, int64_t r_hi, int lane) {
   c.t += TILE;
   c.row0 += TILE;
-  if (c.t < c.t_end) return true;
+  if (c.t < c.t_end) {
+    if constexpr (PAGED) {
+      if (--c.page_left == 0) {                        // into the next page
+        ++c.page;
+        c.page_left = p.page_tiles;
+        c.row0 = page_row0(p, c.b, c.page);
+      }
+    }
+    return true;
+  }
   if (c.nb >= p.B) return false;
   const int64_t t0 = __builtin_amdgcn_readlane(c.nx, 3);
   if (t0 >= r_hi) return false;
@@ -93,6 +128,10 @@ __device__ __forceinline__ bool advance(Cursor& c, const AttnParams& p, int64_t 
                      (uint32_t)__builtin_amdgcn_readlane(c.nx, 0));
   c.nb = __builtin_amdgcn_readlane(c.nx, 5);
   if (c.nb < p.B) c.nx = seqinfo_word(p.seqinfo, c.nb, opaque(lane));
+  if constexpr (PAGED) {                                // the plan's row0 is page 0's
+    c.page = 0;
+    c.page_left = p.page_tiles;
+  }
   return true;
 }
 
@@ -114,23 +153,23 @@ struct TileCopy {
   static constexpr int CPW = (NCOPY + NW - 1) / NW;
   static_assert(NCOPY > NW, "a repeated copy needs an earlier copy of the same wave");
 
-  int wave_, lane_;
+  int wave_;
 
-  __device__ __forceinline__ void init(int wave, int lane) {
-    wave_ = wave;
-    lane_ = lane;
+  __device__ __forceinline__ void init(int wave, int /*lane*/) { wave_ = wave; }
+  // this lane's index, recomputed at each use (two VALU operations) rather
+  // than held in a register through the tile loop
+  __device__ __forceinline__ static int lane_id() {
+    return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   }
   // wave-uniform copy index of this wave's i-th copy (a 1 KB block of the stage)
   __device__ __forceinline__ int id(int i) const {
     const int k = wave_ + i * NW;
     return k >= NCOPY ? k - NW : k;                      // repeat this wave's previous copy
   }
-  // this lane's byte offset in a full tile for copy k (the lane index passes
-  // through an empty asm so the offsets are recomputed at every issue rather
-  // than hoisted out of the tile loop into registers)
+  // this lane's byte offset in a full tile for copy k (recomputed at every
+  // issue rather than hoisted out of the tile loop into registers)
   __device__ __forceinline__ uint32_t off(int k) const {
-    int ln = lane_;
-    asm volatile("" : "+v"(ln));
+    const int ln = lane_id();
     const int s = k * 64 + ln;
     int r = s / SPR, c = s - (s / SPR) * SPR;
     if (c >= RB / 16) c = RB / 16 - 1;
@@ -143,8 +182,7 @@ struct TileCopy {
   // the next row boundary: two vector compares instead of a vector division.
   __device__ __forceinline__ uint32_t off_rows(int k) const {
     static_assert(SPR >= 64, "a wave's 64 slots cross at most one row boundary");
-    int ln = lane_;
-    asm volatile("" : "+v"(ln));
+    const int ln = lane_id();
     const int s0 = uniform(k * 64);
     const int r0 = s0 / SPR;
     const int thr = SPR * (r0 + 1) - s0;               // first lane of row r0 + 1
@@ -178,7 +216,8 @@ struct TileCopy {
   __device__ __forceinline__ void copy(const Pending& q, int i) const {
     const int k = id(i);
     if (CT == kFP8 && k == NCH) {
-      const int r = (lane_ & (TILE - 1)) < q.nvalid ? (lane_ & (TILE - 1)) : q.nvalid - 1;
+      const int ln = lane_id() & (TILE - 1);
+      const int r = ln < q.nvalid ? ln : q.nvalid - 1;
       buffer_copy4(q.srsrc, (uint32_t)(r * 4), q.sb + STAGE_DATA);
       return;
     }

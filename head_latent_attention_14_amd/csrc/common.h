@@ -251,6 +251,18 @@ __device__ __forceinline__ void buffer_copy4(__amdgpu_buffer_rsrc_t r, uint32_t 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 4, voff, 0, 0, 0);
 }
 
+// Cache row of token `pos` of sequence `seq` in a paged cache:
+// block_table[seq][pos / P] * P + pos % P. `valid` is false (and the row 0)
+// when pos is past the table or the table's entry lies outside the page pool.
+__device__ __forceinline__ int64_t paged_row(const int32_t* table, int max_pages, int P,
+                                             int64_t total_pages, int seq, int pos, bool& valid) {
+  const int j = pos / P;
+  valid = pos >= 0 && j < max_pages;
+  const int64_t page = valid ? (int64_t)table[(int64_t)seq * max_pages + j] : 0;
+  valid = valid && page >= 0 && page < total_pages;
+  return valid ? page * P + (pos - j * P) : 0;
+}
+
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 template <int N>

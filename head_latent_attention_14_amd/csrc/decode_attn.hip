@@ -19,7 +19,7 @@
 
 namespace mla {
 
-template <int CT, int HB, int DS, int NSTAGE>
+template <int CT, int HB, int DS, int NSTAGE, bool PAGED>
 __global__ void __launch_bounds__(64 * HB * DS)
 mla_attn_kernel(AttnParams p) {
   constexpr int NW = HB * DS;
@@ -54,7 +54,7 @@ mla_attn_kernel(AttnParams p) {
   const int h = (blockIdx.y * HB + hb) * 16 + l16;       // head of this lane
   const int64_t w = blockIdx.x;
   int64_t r_hi;
-  const Cursor c0 = cursor_start<TILE>(p, w, lane, r_hi);
+  const Cursor c0 = cursor_start<TILE, PAGED>(p, w, lane, r_hi);
   if (c0.b < 0) return;                                  // whole workgroup
 
   TileCopy<CT, NW> cp;
@@ -102,7 +102,7 @@ mla_attn_kernel(AttnParams p) {
     if (lvalid) {
       issue(lc, i);
       ++issued;
-      lvalid = advance<TILE>(lc, p, r_hi, lane);
+      lvalid = advance<TILE, PAGED>(lc, p, r_hi, lane);
     }
   }
 
@@ -137,7 +137,7 @@ mla_attn_kernel(AttnParams p) {
       else
         pend = cp.prepare(p.rows, p.row_scale, lc, smem + (issued % NSTAGE) * STAGE_BYTES);
       ++issued;
-      lvalid = advance<TILE>(lc, p, r_hi, lane);
+      lvalid = advance<TILE, PAGED>(lc, p, r_hi, lane);
     }
     const char* stage = smem + (it % NSTAGE) * STAGE_BYTES;
     const int64_t left = cc.t_end - cc.t;
@@ -300,7 +300,7 @@ mla_attn_kernel(AttnParams p) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (!advance<TILE>(cc, p, r_hi, lane)) break;
+    if (!advance<TILE, PAGED>(cc, p, r_hi, lane)) break;
     if (seg_end) {
       load_q(cc.b);
       wait_vmcnt<0>();
@@ -318,7 +318,7 @@ mla_attn_kernel(AttnParams p) {
 // 72 for the query half and 128 for the output half, so NP pairs (up to 128
 // heads) run as 2*NP waves of one workgroup, two waves per SIMD at NP = 4,
 // and each tile is fetched from HBM once for all of them.
-template <int CT, int NP, int NSTAGE>
+template <int CT, int NP, int NSTAGE, bool PAGED>
 __global__ void __launch_bounds__(128 * NP)
 mla_attn_pair_kernel(AttnParams p) {
   static_assert(CT == kBF16 || CT == kFP8, "pair kernel: bf16 or fp8 cache");
@@ -346,7 +346,7 @@ mla_attn_pair_kernel(AttnParams p) {
   const int hp = (blockIdx.y * NP + (wave >> 1)) * 32;  // first head of the pair
   const int64_t w = blockIdx.x;
   int64_t r_hi;
-  const Cursor c0 = cursor_start<TILE>(p, w, lane, r_hi);
+  const Cursor c0 = cursor_start<TILE, PAGED>(p, w, lane, r_hi);
   if (c0.b < 0) return;                                  // whole workgroup
 
   TileCopy<CT, NW> cp;
@@ -402,7 +402,7 @@ mla_attn_pair_kernel(AttnParams p) {
   // would make every tile's score MFMAs wait for all copies issued before them
   Cursor lc = c0;
   issue(lc, 0);
-  bool lvalid = advance<TILE>(lc, p, r_hi, lane);
+  bool lvalid = advance<TILE, PAGED>(lc, p, r_hi, lane);
   {
     int b0 = c0.b;
     asm volatile("" : "+s"(b0) :: "memory");
@@ -411,7 +411,7 @@ mla_attn_pair_kernel(AttnParams p) {
 #pragma unroll
   for (int i = 1; i < NSTAGE - 1; ++i) {
     issue(lvalid ? lc : c0, i);
-    if (lvalid) lvalid = advance<TILE>(lc, p, r_hi, lane);
+    if (lvalid) lvalid = advance<TILE, PAGED>(lc, p, r_hi, lane);
   }
   int issued = NSTAGE - 1;
   // the queries and the first tile land here; later prologue tiles may stay
@@ -462,7 +462,7 @@ mla_attn_pair_kernel(AttnParams p) {
     if (do_copy) {
       pend = cp.prepare(p.rows, p.row_scale, lc, smem + (issued % NSTAGE) * STAGE_BYTES);
       ++issued;
-      lvalid = advance<TILE>(lc, p, r_hi, lane);
+      lvalid = advance<TILE, PAGED>(lc, p, r_hi, lane);
     }
     const char* stage = smem + (it % NSTAGE) * STAGE_BYTES;
     const int64_t left = cc.t_end - cc.t;
@@ -655,7 +655,7 @@ mla_attn_pair_kernel(AttnParams p) {
       wait_vmcnt<kStoreOps>();
       settle_q();
     }
-    if (!advance<TILE>(cc, p, r_hi, lane)) break;
+    if (!advance<TILE, PAGED>(cc, p, r_hi, lane)) break;
     after_seg = seg_end;
     ++it;
   }
@@ -667,7 +667,10 @@ static hipError_t launch_pair_t(const AttnParams& prm, int workers, int head_gro
                                 hipStream_t s) {
   dim3 grid(workers, head_groups);
   dim3 block(128 * NP);
-  hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE>), grid, block, 0, s, prm);
+  if (prm.block_table)
+    hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE, true>), grid, block, 0, s, prm);
+  else
+    hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE, false>), grid, block, 0, s, prm);
   return hipGetLastError();
 }
 
@@ -676,7 +679,10 @@ static hipError_t launch_attn_t(const AttnParams& prm, int workers, int head_gro
                                 hipStream_t s) {
   dim3 grid(workers, head_groups);
   dim3 block(64 * HB * DS);
-  hipLaunchKernelGGL((mla_attn_kernel<CT, HB, DS, NSTAGE>), grid, block, 0, s, prm);
+  if (prm.block_table)
+    hipLaunchKernelGGL((mla_attn_kernel<CT, HB, DS, NSTAGE, true>), grid, block, 0, s, prm);
+  else
+    hipLaunchKernelGGL((mla_attn_kernel<CT, HB, DS, NSTAGE, false>), grid, block, 0, s, prm);
   return hipGetLastError();
 }
 
@@ -693,6 +699,11 @@ hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipS
   prm.B = a.B;
   prm.H = a.H;
   prm.scale_log2 = a.softmax_scale * kLog2e;
+  prm.block_table = a.block_table;
+  prm.max_pages = a.max_pages;
+  prm.page_tokens = a.page_tokens;
+  prm.page_tiles = a.block_table ? a.page_tokens / plan.tile : 0;
+  prm.total_pages = a.total_pages;
   const int W = plan.workers, G = plan.head_groups;
   if (plan.stream) return launch_attn_stream(plan, prm, s);
   if (plan.h32) return launch_attn_h32(plan, prm, s);

@@ -157,7 +157,7 @@ __device__ __forceinline__ void scale_acc4(f32x16& o, int c, float alpha, bool f
       : [al] "v"(alpha));
 }
 
-template <int CT, int NW, int NSTAGE, int NACC>
+template <int CT, int NW, int NSTAGE, int NACC, bool PAGED>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_attn_h32_kernel(AttnParams p) {
   static_assert(CT == kBF16, "bf16 cache");
@@ -178,7 +178,7 @@ mla_attn_h32_kernel(AttnParams p) {
   const int hw = (blockIdx.y * NW + wave) * 32;          // this wave's first head
   const int64_t w = blockIdx.x;
   int64_t r_hi;
-  const Cursor c0 = cursor_start<TILE>(p, w, lane, r_hi);
+  const Cursor c0 = cursor_start<TILE, PAGED>(p, w, lane, r_hi);
   if (c0.b < 0) return;                                  // whole workgroup
 
   TC cp;
@@ -209,7 +209,7 @@ mla_attn_h32_kernel(AttnParams p) {
     if (lvalid) {
       cp.issue(p.rows, p.row_scale, lc, smem + i * STAGE_BYTES, lane);
       ++issued;
-      lvalid = advance<TILE>(lc, p, r_hi, lane);
+      lvalid = advance<TILE, PAGED>(lc, p, r_hi, lane);
     }
   }
   {
@@ -242,7 +242,7 @@ mla_attn_h32_kernel(AttnParams p) {
     if (do_copy) {
       pend = cp.prepare(p.rows, p.row_scale, lc, smem + (issued % NSTAGE) * STAGE_BYTES);
       ++issued;
-      lvalid = advance<TILE>(lc, p, r_hi, lane);
+      lvalid = advance<TILE, PAGED>(lc, p, r_hi, lane);
     }
     const uint32_t tb = (uint32_t)(size_t)(smem + (it % NSTAGE) * STAGE_BYTES);
     const int64_t left = cc.t_end - cc.t;
@@ -397,7 +397,7 @@ mla_attn_h32_kernel(AttnParams p) {
       l_run = 0.f;
       fresh = true;
     }
-    if (!advance<TILE>(cc, p, r_hi, lane)) break;
+    if (!advance<TILE, PAGED>(cc, p, r_hi, lane)) break;
     if (seg_end) {
       load_q(cc.b);
       wait_vmcnt<0>();
@@ -409,7 +409,10 @@ mla_attn_h32_kernel(AttnParams p) {
 hipError_t launch_attn_h32(const DecodePlan& plan, const AttnParams& prm, hipStream_t s) {
   dim3 grid(plan.workers, plan.head_groups);
   if (plan.nstage == 4) {
-    hipLaunchKernelGGL((mla_attn_h32_kernel<kBF16, 4, 4, 2>), grid, dim3(256), 0, s, prm);
+    if (prm.block_table)
+      hipLaunchKernelGGL((mla_attn_h32_kernel<kBF16, 4, 4, 2, true>), grid, dim3(256), 0, s, prm);
+    else
+      hipLaunchKernelGGL((mla_attn_h32_kernel<kBF16, 4, 4, 2, false>), grid, dim3(256), 0, s, prm);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

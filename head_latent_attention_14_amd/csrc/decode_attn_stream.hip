@@ -29,7 +29,7 @@
 
 namespace mla {
 
-template <int NSTAGE>
+template <int NSTAGE, bool PAGED>
 __global__ void __launch_bounds__(320)
 mla_attn_stream_kernel(AttnParams p) {
   constexpr int CT = kBF16;
@@ -70,7 +70,7 @@ mla_attn_stream_kernel(AttnParams p) {
   const int B = p.B;
   const int64_t w = blockIdx.x;
   int64_t r_hi;
-  const Cursor c0 = cursor_start<TILE>(p, w, lane, r_hi);
+  const Cursor c0 = cursor_start<TILE, PAGED>(p, w, lane, r_hi);
   if (c0.b < 0) return;                                  // whole workgroup
 
   char* qlds = smem + NSTAGE * STAGE_BYTES;             // two query buffers (segment parity)
@@ -166,7 +166,7 @@ mla_attn_stream_kernel(AttnParams p) {
       const int b = lc.b;
       const bool seg_end = (lc.t + TILE >= lc.t_end);
       ++issued;
-      lvalid = advance<TILE>(lc, p, r_hi, lane);
+      lvalid = advance<TILE, PAGED>(lc, p, r_hi, lane);
       if (lane == 0) meta[stage] = TileMeta{b, k.nvalid, seg_end ? 1 : 0, lvalid ? 1 : 0, lc.b};
       return (seg_end ? 1 : 0) | (lvalid ? 2 : 0) | (lc.b << 2);
     };
@@ -372,7 +372,10 @@ mla_attn_stream_kernel(AttnParams p) {
 hipError_t launch_attn_stream(const DecodePlan& plan, const AttnParams& prm, hipStream_t s) {
   if (plan.nstage != 3) return hipErrorInvalidValue;
   dim3 grid(plan.workers, plan.head_groups);
-  hipLaunchKernelGGL(mla_attn_stream_kernel<3>, grid, dim3(320), 0, s, prm);
+  if (prm.block_table)
+    hipLaunchKernelGGL((mla_attn_stream_kernel<3, true>), grid, dim3(320), 0, s, prm);
+  else
+    hipLaunchKernelGGL((mla_attn_stream_kernel<3, false>), grid, dim3(320), 0, s, prm);
   return hipGetLastError();
 }
 

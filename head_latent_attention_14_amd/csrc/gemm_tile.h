@@ -26,6 +26,10 @@ struct GemmParams {
   const int32_t* seq_len;     // absorb: [B]
   const int32_t* seq_cap;     // absorb: [B]
   const int64_t* seq_start;   // absorb: [B]
+  const int32_t* block_table; // absorb, paged cache: [B][max_pages] (null: contiguous)
+  int32_t page_tokens;
+  int32_t max_pages;
+  int64_t total_pages;
   int32_t B;
   int32_t H;
   int32_t workers;            // W of the attention launch
@@ -82,14 +86,24 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
       const int bc = b < B ? b : B - 1;
       int Lr, cap;
       int64_t row0;
-      asm volatile(
-          "global_load_dword %0, %3, off\n"
-          "global_load_dword %1, %4, off\n"
-          "global_load_dwordx2 %2, %5, off\n"
-          "s_waitcnt vmcnt(0)"
-          : "=&v"(Lr), "=&v"(cap), "=&v"(row0)
-          : "v"(p.seq_len + bc), "v"(p.seq_cap + bc), "v"(p.seq_start + bc)
-          : "memory");
+      if (p.block_table) {
+        // paged: the capacity is the table's, the first row that of page 0
+        // (an entry outside the pool reads page 0: attention then reads a
+        // wrong page, never outside the pool)
+        Lr = p.seq_len[bc];
+        cap = p.max_pages * p.page_tokens;
+        bool ok;
+        row0 = paged_row(p.block_table, p.max_pages, p.page_tokens, p.total_pages, bc, 0, ok);
+      } else {
+        asm volatile(
+            "global_load_dword %0, %3, off\n"
+            "global_load_dword %1, %4, off\n"
+            "global_load_dwordx2 %2, %5, off\n"
+            "s_waitcnt vmcnt(0)"
+            : "=&v"(Lr), "=&v"(cap), "=&v"(row0)
+            : "v"(p.seq_len + bc), "v"(p.seq_cap + bc), "v"(p.seq_start + bc)
+            : "memory");
+      }
       int L = 0;
       if (b < B) L = Lr < 0 ? 0 : (Lr > cap ? cap : Lr);
       const int64_t n = (L + TL - 1) / TL;
@@ -214,7 +228,12 @@ __device__ void build_plan(const GemmParams& p, int64_t* lds, int lds_n) {
         wi.b = b;
         wi.t = (int32_t)((first - t0) * TL);
         wi.t_end = (int32_t)((se - t0) * TL < len ? (se - t0) * TL : len);
-        wi.row0 = row0 + wi.t;
+        if (p.block_table) {
+          bool ok;
+          wi.row0 = paged_row(p.block_table, p.max_pages, p.page_tokens, p.total_pages, b, wi.t, ok);
+        } else {
+          wi.row0 = row0 + wi.t;
+        }
         wi.next = nx;
       }
     }
@@ -379,6 +398,10 @@ inline GemmParams absorb_params(const DecodePlan& plan, const DecodeArgs& a) {
   g.wlast = a.wlast;
   g.seq_len = a.seq_len;
   g.seq_cap = a.seq_cap;
+  g.block_table = a.block_table;
+  g.page_tokens = a.page_tokens;
+  g.max_pages = a.max_pages;
+  g.total_pages = a.total_pages;
   g.x = a.q_nope;
   g.w = a.w_uk;
   g.y = a.q_lat;

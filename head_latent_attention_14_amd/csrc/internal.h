@@ -26,6 +26,13 @@ struct AppendArgs {
   int32_t n_tok;
   int32_t d_model;
   double inv_freq[32];        // rope_base^(-2i/64), fp64
+  // paged cache (block_table non-null): token t of sequence b is row
+  // block_table[b][t / page_tokens] * page_tokens + t % page_tokens;
+  // seq_start and seq_cap are unused
+  const int32_t* block_table; // [B][max_pages]
+  int32_t page_tokens;
+  int32_t max_pages;
+  int64_t total_pages;
 };
 hipError_t launch_append(int cache_type, const AppendArgs& a, hipStream_t s);
 
@@ -97,6 +104,11 @@ struct DecodeArgs {
   const int64_t* seq_start;
   const int32_t* seq_cap;
   const int32_t* seq_len;
+  // paged cache (block_table non-null; seq_start/seq_cap unused), as in AppendArgs
+  const int32_t* block_table;
+  int32_t page_tokens;
+  int32_t max_pages;
+  int64_t total_pages;
   int32_t B;
   int32_t H;
   // activations / weights (bf16 or f32)

@@ -93,6 +93,34 @@ typedef struct {
 } mla_cache_t;
 
 /*
+ * Paged latent cache: the same rows in a pool of pages of `page_tokens` rows
+ * each, found through a per-sequence block table (the layout behind the
+ * PagedAttention of the serving engines the mlqm.cn deployment guide names,
+ * sections 3.2 "software environment" and 8.2 "deployment optimisation").
+ * Token t (0 <= t < max_pages * page_tokens) of sequence b is row
+ *   block_table[b][t / page_tokens] * page_tokens + t % page_tokens
+ * of `rows`; rows and row scales are stored as in mla_cache_t. page_tokens is
+ * a positive multiple of 32 (a 32-token tile never spans two pages). Entries
+ * a call uses (blocks below ceil(len / page_tokens) for decode, the block of
+ * each appended position for append) must lie in [0, total_pages): decode
+ * reads page 0 instead of an entry outside the pool, append skips such a
+ * token, and MLA_DEBUG=1 reports either as MLA_ERR_INVALID_ARGUMENT. Pages of
+ * different sequences must not overlap where rows are written.
+ */
+typedef struct {
+  mla_dtype_t dtype;             /* element type of rows: F32, BF16 or FP8_E4M3 */
+  int32_t d_c;                   /* must be 512 */
+  int32_t d_r;                   /* must be 64 */
+  int32_t num_seqs;              /* B >= 1 */
+  int32_t page_tokens;           /* rows per page: a positive multiple of 32 */
+  int32_t max_pages;             /* block-table columns (pages per sequence) >= 1 */
+  int64_t total_pages;           /* pages in `rows` >= 1 */
+  void* rows;                    /* (device) [total_pages * page_tokens][576] */
+  float* row_scale;              /* (device) [total_pages * page_tokens] for FP8_E4M3, else NULL */
+  const int32_t* block_table;    /* (device) [B][max_pages] page of each block */
+} mla_paged_cache_t;
+
+/*
  * mla_append -- compress hidden states into latent cache rows.
  *
  * For each token n (discosf explainer, "long-context bottleneck" and
@@ -214,10 +242,32 @@ mla_status_t mla_decode(const mla_cache_t* cache, const int32_t* seq_len,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_append_paged / mla_decode_paged -- mla_append and mla_decode over a
+ * paged cache: same arguments, rules and results, with each sequence's
+ * capacity max_pages * page_tokens and its rows found through the block
+ * table. mla_decode_paged takes the workspace of mla_decode_workspace_size and
+ * equals mla_decode over the same rows laid out contiguously, bit for bit.
+ */
+mla_status_t mla_append_paged(const mla_paged_cache_t* cache,
+                              const void* h, int32_t n_tok, int32_t d_model,
+                              const void* w_dkv, const void* w_kr, mla_dtype_t act_dtype,
+                              const int32_t* tok_seq, const int32_t* tok_pos,
+                              float rope_base, void* stream);
+mla_status_t mla_decode_paged(const mla_paged_cache_t* cache, const int32_t* seq_len,
+                              const void* q_nope, const void* q_pe,
+                              const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
+                              int32_t n_heads, float softmax_scale,
+                              void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The three stages mla_decode runs, exposed so a caller can time or
  * interleave them. Same arguments and rules as mla_decode; calling
  * absorb, attend and combine in this order on one stream with the same
- * workspace equals one mla_decode call. The workspace carries the
+ * workspace equals one mla_decode call. attend and combine trust the work
+ * plan absorb left in the workspace: calling them on a workspace that absorb
+ * (or mla_append_absorb) has not prepared with the same cache, lengths and
+ * head count is undefined, and can read and write outside the buffers. The workspace carries the
  * intermediate results between the stages:
  *   absorb  -- q_lat = W_UK[h]^T q_nope for every (b, h), and the work plan
  *              (tile counts of the clamped lengths, each worker's tile range)

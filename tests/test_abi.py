@@ -27,7 +27,8 @@ def test_exports_every_declared_symbol():
                           "mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
                           "mla_decode_attend_combine",
                           "mla_append_absorb", "mla_decode_noalloc", "mla_append_yarn",
-                          "mla_yarn_softmax_factor", "mla_status_string", "mla_abi_version"}
+                          "mla_yarn_softmax_factor", "mla_append_paged", "mla_decode_paged",
+                          "mla_status_string", "mla_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert getattr(lib, n) is not None
@@ -318,3 +319,56 @@ def test_append_yarn_validation_and_softmax_factor():
     assert mla.mla_yarn_softmax_factor(0.25) == 1.0
     assert mla.mla_yarn_softmax_factor(float("nan")) == 1.0
     assert abs(mla.mla_yarn_softmax_factor(math.exp(10.0)) - 4.0) < 1e-6
+
+
+def _paged(dtype=mla.MLA_DTYPE_BF16, B=4, P=64, max_pages=8, total_pages=20, table=FAKE,
+           scale=None, d_c=512):
+    return mla.mla_paged_cache_t(dtype, d_c, 64, B, P, max_pages, total_pages, FAKE, scale, table)
+
+
+def test_paged_validation():
+    """Paged entry points check the pool, the page size and the table before
+    any HIP call."""
+    E = mla
+
+    def dec(c, H=16, act=E.MLA_DTYPE_BF16, ws_bytes=1 << 40):
+        return lib.mla_decode_paged(ctypes.byref(c) if c is not None else None, FAKE, FAKE, FAKE,
+                                    FAKE, FAKE, act, H, 0.07, FAKE, None, FAKE, ws_bytes, None)
+
+    def app(c, n_tok=4):
+        return lib.mla_append_paged(ctypes.byref(c) if c is not None else None, FAKE, n_tok, 128,
+                                    FAKE, FAKE, E.MLA_DTYPE_BF16, FAKE, FAKE, 10000.0, None)
+
+    for f in (dec, app):
+        assert f(None) == E.MLA_ERR_INVALID_ARGUMENT
+        assert f(_paged(P=48)) == E.MLA_ERR_INVALID_ARGUMENT        # not a multiple of 32
+        assert f(_paged(P=0)) == E.MLA_ERR_INVALID_ARGUMENT
+        assert f(_paged(max_pages=0)) == E.MLA_ERR_INVALID_ARGUMENT
+        assert f(_paged(total_pages=0)) == E.MLA_ERR_INVALID_ARGUMENT
+        assert f(_paged(table=None)) == E.MLA_ERR_INVALID_ARGUMENT
+        assert f(_paged(B=0)) == E.MLA_ERR_INVALID_ARGUMENT
+        assert f(_paged(d_c=256)) == E.MLA_ERR_INVALID_ARGUMENT
+        assert f(_paged(dtype=E.MLA_DTYPE_FP8_E4M3)) == E.MLA_ERR_INVALID_ARGUMENT  # no row_scale
+        # capacities must fit int32 positions
+        assert f(_paged(P=1 << 16, max_pages=1 << 16)) == E.MLA_ERR_UNSUPPORTED
+    assert dec(_paged(), H=24) == E.MLA_ERR_UNSUPPORTED
+    need = mla.mla_decode_workspace_size(4, 16, E.MLA_DTYPE_BF16, E.MLA_DTYPE_BF16)
+    assert dec(_paged(), ws_bytes=need - 1) == E.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert app(_paged(), n_tok=0) == E.MLA_OK                      # a no-op
+
+
+def test_paged_binding_checks_shapes():
+    torch = pytest.importorskip("torch")
+    pc = mla.PagedLatentCache(rows=torch.zeros(128, 576, dtype=torch.bfloat16),
+                              block_table=torch.zeros(2, 2, dtype=torch.int32), page_tokens=64)
+    assert pc.num_seqs == 2 and pc.dtype == mla.MLA_DTYPE_BF16
+    pc.check()
+    with pytest.raises((ValueError, TypeError)):
+        mla.PagedLatentCache(rows=torch.zeros(100, 576, dtype=torch.bfloat16),
+                             block_table=torch.zeros(2, 2, dtype=torch.int32), page_tokens=64).check()
+    with pytest.raises((ValueError, TypeError)):
+        mla.PagedLatentCache(rows=torch.zeros(128, 576, dtype=torch.bfloat16),
+                             block_table=torch.zeros(2, 2, dtype=torch.int64), page_tokens=64).check()
+    with pytest.raises((ValueError, TypeError)):
+        mla.PagedLatentCache(rows=torch.zeros(128, 576, dtype=torch.uint8),
+                             block_table=torch.zeros(2, 2, dtype=torch.int32), page_tokens=64).check()
