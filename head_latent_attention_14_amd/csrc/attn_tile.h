@@ -27,7 +27,7 @@ struct AttnParams {
   int32_t max_pages;
   int32_t page_tokens;
   int32_t page_tiles;          // page_tokens / tile
-  int64_t total_pages;
+  uint32_t page_limit;         // min(pool pages, 2^31): a valid entry is below it
 };
 
 // Per cache dtype: bytes of a stored row, bytes of a padded LDS row, and
@@ -41,30 +41,56 @@ template <> struct Tr<kF32> { static constexpr int kRowBytes = 2304, kPad = 2320
 constexpr int kConvPad = 1168;   // padded bf16 row of the widened fp8 tile
 constexpr float kSlack = 8.f;    // lazy-rescale slack of the running max (log2 units)
 
+__device__ __forceinline__ int seqinfo_word(const SeqInfo* si, int b, int lane) {
+  return ((const int*)(si + b))[lane & 7];
+}
+
 // A worker's position in its tile range: the tile at token t of sequence b.
-// The record of the next sequence with tiles is loaded one segment ahead
-// (lane l holds its 32-bit word l % 8), so moving into it needs no memory
-// access on the way.
+// The record of the next sequence with tiles is loaded one segment ahead, so
+// moving into it needs no memory access on the way. The contiguous kernels
+// hold it spread over the lanes (lane l holds its 32-bit word l % 8: one
+// VGPR); the paged kernels hold it in scalar registers, loaded with scalar
+// loads: there the register allocator moves the record between registers in
+// the tile loop, and a move of a VGPR whose vector load may still be pending
+// waits for every tile copy in flight, while a scalar load is counted apart
+// from the copies.
 struct Cursor {
   int b;            // sequence
   int64_t t;        // first token of the tile, local to the sequence
   int64_t t_end;    // end of this worker's segment of the sequence (local)
   int64_t row0;     // cache row of token t
   int nb;           // next sequence with tiles (B: none)
-  int nx;           // this lane's word of seqinfo[nb]
+  int nx;           // contiguous kernels: this lane's word of seqinfo[nb]
+  int nw[6];        // paged kernels: words 0..5 of seqinfo[nb]
   int page;         // paged cache: block of token t in the sequence's table
   int page_left;    // paged cache: tiles of that page from t on
 };
 
-// Paged cache: the row of the first token of block `page` of sequence b (an
-// entry outside the pool reads page 0 of it: a wrong page, never outside it).
-__device__ __forceinline__ int64_t page_row0(const AttnParams& p, int b, int page) {
-  const int64_t pg = ld_const(p.block_table, (int64_t)b * p.max_pages + page);
-  return (pg >= 0 && pg < p.total_pages ? pg : 0) * p.page_tokens;
+// Load the record of sequence c.nb (which must be below B) into the cursor.
+template <bool PAGED>
+__device__ __forceinline__ void load_next(Cursor& c, const AttnParams& p, int lane) {
+  if constexpr (PAGED) {
+    const int* rec = (const int*)(p.seqinfo + c.nb);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) c.nw[k] = ld_const(rec, k);
+  } else {
+    c.nx = seqinfo_word(p.seqinfo, c.nb, opaque(lane));
+  }
+}
+// Word k of the loaded record (wave-uniform).
+template <bool PAGED>
+__device__ __forceinline__ int next_word(const Cursor& c, int k) {
+  if constexpr (PAGED) return c.nw[k];
+  else return __builtin_amdgcn_readlane(c.nx, k);
 }
 
-__device__ __forceinline__ int seqinfo_word(const SeqInfo* si, int b, int lane) {
-  return ((const int*)(si + b))[lane & 7];
+// Paged cache: the row of the first token of block `page` of sequence b (an
+// entry outside the pool reads page 0 of it: a wrong page, never outside it).
+// One unsigned 32-bit compare tests both bounds (a negative entry is 2^31 or
+// more as unsigned), so the test stays on the scalar unit.
+__device__ __forceinline__ int64_t page_row0(const AttnParams& p, int b, int page) {
+  const int32_t pg = ld_const(p.block_table, (int64_t)b * p.max_pages + page);
+  return (int64_t)((uint32_t)pg < p.page_limit ? pg : 0) * p.page_tokens;
 }
 
 // The first tile of worker w (c.b < 0: the worker has none); r_hi receives
@@ -82,7 +108,10 @@ __device__ __forceinline__ Cursor cursor_start(const AttnParams& p, int64_t w, i
   c.row0 = ld_const(&wi->row0, 0);
   c.nb = ld_const(&wi->next, 0);
   r_hi = ld_const(&wi->r_hi, 0);
-  c.nx = (c.b >= 0 && c.nb < p.B) ? seqinfo_word(p.seqinfo, c.nb, opaque(lane)) : 0;
+  c.nx = 0;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) c.nw[k] = 0;
+  if (c.b >= 0 && c.nb < p.B) load_next<PAGED>(c, p, lane);
   c.page = 0;
   c.page_left = 0;
   if (PAGED && c.b >= 0) {
@@ -94,9 +123,10 @@ __device__ __forceinline__ Cursor cursor_start(const AttnParams& p, int64_t w, i
 }
 
 // The sequence of the worker's next segment after the current one (-1: none).
+template <bool PAGED>
 __device__ __forceinline__ int next_segment_seq(const Cursor& c, const AttnParams& p, int64_t r_hi) {
   if (c.nb >= p.B) return -1;
-  const int64_t t0 = __builtin_amdgcn_readlane(c.nx, 3);
+  const int64_t t0 = next_word<PAGED>(c, 3);
   return t0 < r_hi ? c.nb : -1;
 }
 
@@ -116,18 +146,18 @@ __device__ __forceinline__ bool advance(Cursor& c, const AttnParams& p, int64_t 
     return true;
   }
   if (c.nb >= p.B) return false;
-  const int64_t t0 = __builtin_amdgcn_readlane(c.nx, 3);
+  const int64_t t0 = next_word<PAGED>(c, 3);
   if (t0 >= r_hi) return false;
-  const int64_t t1 = __builtin_amdgcn_readlane(c.nx, 4);
-  const int64_t len = __builtin_amdgcn_readlane(c.nx, 2);
+  const int64_t t1 = next_word<PAGED>(c, 4);
+  const int64_t len = next_word<PAGED>(c, 2);
   const int64_t se = t1 < r_hi ? t1 : r_hi;
   c.b = c.nb;
   c.t = 0;
   c.t_end = (se - t0) * TILE < len ? (se - t0) * TILE : len;
-  c.row0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(c.nx, 1) << 32) |
-                     (uint32_t)__builtin_amdgcn_readlane(c.nx, 0));
-  c.nb = __builtin_amdgcn_readlane(c.nx, 5);
-  if (c.nb < p.B) c.nx = seqinfo_word(p.seqinfo, c.nb, opaque(lane));
+  c.row0 = (int64_t)(((uint64_t)(uint32_t)next_word<PAGED>(c, 1) << 32) |
+                     (uint32_t)next_word<PAGED>(c, 0));
+  c.nb = next_word<PAGED>(c, 5);
+  if (c.nb < p.B) load_next<PAGED>(c, p, lane);
   if constexpr (PAGED) {                                // the plan's row0 is page 0's
     c.page = 0;
     c.page_left = p.page_tiles;

@@ -628,7 +628,7 @@ mla_attn_pair_kernel(AttnParams p) {
     if (seg_end) {
       // the next segment's queries go out before the partial's stores, so
       // that the wait for them below leaves the stores in flight
-      const int nseq = next_segment_seq(cc, p, r_hi);
+      const int nseq = next_segment_seq<PAGED>(cc, p, r_hi);
       if (nseq >= 0) load_q(nseq);
       __builtin_amdgcn_sched_barrier(0);
       const int64_t slot = w + cc.b;
@@ -703,7 +703,7 @@ hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipS
   prm.max_pages = a.max_pages;
   prm.page_tokens = a.page_tokens;
   prm.page_tiles = a.block_table ? a.page_tokens / plan.tile : 0;
-  prm.total_pages = a.total_pages;
+  prm.page_limit = (uint32_t)(a.total_pages < (int64_t)1 << 31 ? a.total_pages : (int64_t)1 << 31);
   const int W = plan.workers, G = plan.head_groups;
   if (plan.stream) return launch_attn_stream(plan, prm, s);
   if (plan.h32) return launch_attn_h32(plan, prm, s);
