@@ -42,6 +42,7 @@ DecodePlan make_plan(int ct, int B, int H) {
     p.np = (H % 128 == 0) ? 4 : (H % 64 == 0) ? 2 : 1;
     p.nstage = (ct == kFP8 || p.np == 1) ? 4 : 3;
     p.head_groups = H / (32 * p.np);
+    p.f8 = ct == kFP8 && getenv_flag("MLA_FP8_MFMA");
   } else if (ct == kBF16) {
     // 16-head blocks over a bf16 cache: the streaming kernel
     p.stream = true;

@@ -33,6 +33,20 @@ __device__ __forceinline__ f32x4 mfma_bf16_k32(const bf16x8& a, const bf16x8& b,
 __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// e4m3fn x e4m3fn, K = 128 (v_mfma_scale_f32_16x16x128_f8f6f4 with both block
+// scales 2^0): lane l supplies 32 codes of row / column l%16; A and B take the
+// same K order, so any assignment of elements to (l/16, byte) that A and B
+// share contracts over the same elements.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma_fp8_k128(const i32x8& a, const i32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// e4m3fn x e4m3fn, K = 32 (v_mfma_f32_16x16x32_fp8_fp8): 8 codes per lane.
+__device__ __forceinline__ f32x4 mfma_fp8_k32(uint2 a, uint2 b, const f32x4& c) {
+  const long la = (long)(((uint64_t)a.y << 32) | a.x);
+  const long lb = (long)(((uint64_t)b.y << 32) | b.x);
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(la, lb, c, 0, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // conversions
@@ -78,6 +92,14 @@ __device__ __forceinline__ uint32_t f32x4_to_fp8x4_sat(float a, float b, float c
   b = __builtin_fminf(__builtin_fmaxf(b, -448.f), 448.f);
   c = __builtin_fminf(__builtin_fmaxf(c, -448.f), 448.f);
   d = __builtin_fminf(__builtin_fmaxf(d, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// fp32 -> e4m3fn codes, round to nearest even, for values known to lie within
+// +-448 (no clamp).
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;

@@ -318,10 +318,23 @@ mla_attn_kernel(AttnParams p) {
 // 72 for the query half and 128 for the output half, so NP pairs (up to 128
 // heads) run as 2*NP waves of one workgroup, two waves per SIMD at NP = 4,
 // and each tile is fetched from HBM once for all of them.
-template <int CT, int NP, int NSTAGE, bool PAGED>
+//
+// F8 (fp8 cache): the value contraction on fp8 MFMA (K = 32 tokens, the
+// tile's codes straight from the transposing reads). The value weights
+// p * scale_t become e4m3 codes, the one extra rounding of this variant
+// (about 2% relative error in the output): they are multiplied by 2^G, G the
+// segment's exponent that keeps scale_t * 2^G <= 2^kF8Lift for every row
+// seen (lowered, with a power-of-two rescale of o, when a tile has a larger
+// scale), and the lazy max keeps a slack of 2^(8 - kF8Lift), so that every
+// weight is at most 256 and the largest near 2^kF8Lift or more, away from the
+// format's subnormals; the output is divided by 2^G at the end.
+template <int CT, int NP, int NSTAGE, bool PAGED, bool F8>
 __global__ void __launch_bounds__(128 * NP)
 mla_attn_pair_kernel(AttnParams p) {
   static_assert(CT == kBF16 || CT == kFP8, "pair kernel: bf16 or fp8 cache");
+  static_assert(!F8 || CT == kFP8, "fp8 MFMA needs the fp8 cache");
+  constexpr int kF8Lift = 4;
+  constexpr float kSlackP = F8 ? (float)(8 - kF8Lift) : kSlack;
   constexpr int NW = 2 * NP;
   constexpr int TILE = 32;
   constexpr int RP = Tr<CT>::kPad;
@@ -441,6 +454,10 @@ mla_attn_pair_kernel(AttnParams p) {
       (CT == kFP8) ? (uint32_t)(((tq < 4 ? 4 * g + tq : 16 + 4 * g + tq - 4)) * TP + 256 * half + 8 * (l16 & 1))
                    : (uint32_t)((4 * g + (l16 >> 2)) * TP + 2 * 256 * half + 8 * (l16 & 3));
   char* xbuf = smem + NSTAGE * STAGE_BYTES;
+  // F8: exponent G of the value weights (a large start: the first tile of a
+  // segment lowers it)
+  constexpr int kGStart = 127;
+  int gexp = kGStart;
 
   // a segment change loads the next queries and then stores the partial
   // (at least kStoreOps stores); the stores may stay in flight into the next
@@ -566,22 +583,45 @@ mla_attn_pair_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 1; i < 8; ++i) t = __builtin_fmaxf(t, sc[hb][i]);
       tmax[hb] = max_over_groups(t);
-      grow = grow || (tmax[hb] > m_run[hb] + kSlack);
+      grow = grow || (tmax[hb] > m_run[hb] + kSlackP);
+    }
+    // F8: a tile whose largest row scale exceeds 2^(kF8Lift - G) lowers G
+    // (o follows)
+    float gshift = 1.f;
+    if constexpr (F8) {
+      float tm = tsc[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) tm = __builtin_fmaxf(tm, tsc[i]);
+      tm = max_over_groups(tm);                          // all 32 rows of the tile
+      // tm < 2^e (e = frexp exponent), so tm * 2^(kF8Lift - e) < 2^kF8Lift
+      const int gneed = kF8Lift - uniform(__builtin_amdgcn_frexp_expf(tm));
+      if (gneed < gexp) {
+        gshift = __builtin_amdgcn_ldexpf(1.f, gneed - gexp);
+        gexp = gneed;
+      }
     }
     // lazy rescale: the reference max moves only when a score exceeds it by
     // more than 2^kSlack (o and l always share the reference)
-    if (__any(grow)) {
+    if (__any(grow) || (F8 && gshift != 1.f)) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const float m_new = __builtin_fmaxf(m_run[hb], tmax[hb]);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[hb] - m_new);
+        float alpha = __builtin_amdgcn_exp2f(m_run[hb] - m_new);
+        if (F8 && m_new == m_run[hb]) alpha = 1.f;       // (also when both are -inf)
         l_run[hb] *= alpha;
+        const float ao = F8 ? alpha * gshift : alpha;
 #pragma unroll
-        for (int nb = 0; nb < 16; ++nb) o[hb][nb] *= alpha;
+        for (int nb = 0; nb < 16; ++nb) o[hb][nb] *= ao;
         m_run[hb] = m_new;
       }
     }
     bf16x8 pb[2];
+    uint2 p8[2];                                         // F8: e4m3 codes of the value weights
+    if constexpr (F8) {
+      const float g2 = __builtin_amdgcn_ldexpf(1.f, gexp);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tsc[i] *= g2;          // below 2^kF8Lift
+    }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const float m_use = (m_run[hb] == -INFINITY) ? 0.f : m_run[hb];
@@ -594,13 +634,27 @@ mla_attn_pair_kernel(AttnParams p) {
         pv[i] = e * tsc[i];                              // fp8: value scale folded into P
       }
       l_run[hb] += psum;
-      pb[hb] = pack_bf16x8(pv);
+      if constexpr (F8)
+        p8[hb] = uint2{f32x4_to_fp8x4(pv[0], pv[1], pv[2], pv[3]),
+                       f32x4_to_fp8x4(pv[4], pv[5], pv[6], pv[7])};
+      else
+        pb[hb] = pack_bf16x8(pv);
     }
 
     // ---------------- values: O^T += tile^T P^T, this wave's 256 dims ----------------
     const uint32_t tr_addr = (uint32_t)(size_t)tb + tr_lane;
 #pragma unroll
     for (int n0 = 0; n0 < 16; n0 += 4) {
+      if constexpr (F8) {                                // codes straight into fp8 MFMA
+        uint2 v[4];
+        lds_tr8_x4<0, 16, 32, 48>(tr_addr + n0 * 16, v[0], v[1], v[2], v[3]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          o[0][n0 + k] = mfma_fp8_k32(v[k], p8[0], o[0][n0 + k]);
+          o[1][n0 + k] = mfma_fp8_k32(v[k], p8[1], o[1][n0 + k]);
+        }
+        continue;
+      }
       bf16x8 a[4];
       if constexpr (CT == kFP8) {
         uint2 v[4];
@@ -637,7 +691,8 @@ mla_attn_pair_kernel(AttnParams p) {
       for (int hb = 0; hb < 2; ++hb) {
         const float lsum = sum_over_groups(l_run[hb]);
         const int h = hp + 16 * hb + (ln & 15);
-        const float inv = inv_or_zero(lsum);
+        float inv = inv_or_zero(lsum);
+        if constexpr (F8) inv *= __builtin_amdgcn_ldexpf(1.f, -gexp);
         const int64_t po = (slot * H + h) * kDc + 256 * half + 4 * (ln >> 4);
 #pragma unroll
         for (int nb = 0; nb < 16; ++nb) store_part4<CT>(p.part_o, po + nb * 16, o[hb][nb], inv);
@@ -654,6 +709,7 @@ mla_attn_pair_kernel(AttnParams p) {
       // the stores may stay in flight
       wait_vmcnt<kStoreOps>();
       settle_q();
+      gexp = kGStart;
     }
     if (!advance<TILE, PAGED>(cc, p, r_hi, lane)) break;
     after_seg = seg_end;
@@ -662,15 +718,25 @@ mla_attn_pair_kernel(AttnParams p) {
 }
 
 // ------------------------------------------------------------------ launch
+template <int CT, int NP, int NSTAGE, bool F8>
+static void launch_pair_f(const AttnParams& prm, dim3 grid, dim3 block, hipStream_t s) {
+  if (prm.block_table)
+    hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE, true, F8>), grid, block, 0, s, prm);
+  else
+    hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE, false, F8>), grid, block, 0, s, prm);
+}
 template <int CT, int NP, int NSTAGE>
-static hipError_t launch_pair_t(const AttnParams& prm, int workers, int head_groups,
+static hipError_t launch_pair_t(const AttnParams& prm, bool f8, int workers, int head_groups,
                                 hipStream_t s) {
   dim3 grid(workers, head_groups);
   dim3 block(128 * NP);
-  if (prm.block_table)
-    hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE, true>), grid, block, 0, s, prm);
-  else
-    hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE, false>), grid, block, 0, s, prm);
+  if constexpr (CT == kFP8) {
+    if (f8) launch_pair_f<CT, NP, NSTAGE, true>(prm, grid, block, s);
+    else launch_pair_f<CT, NP, NSTAGE, false>(prm, grid, block, s);
+  } else {
+    (void)f8;
+    launch_pair_f<CT, NP, NSTAGE, false>(prm, grid, block, s);
+  }
   return hipGetLastError();
 }
 
@@ -712,7 +778,7 @@ hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipS
     return launch_attn_t<CT_, HB_, DS_, NS_>(prm, W, G, s);
 #define MLA_PAIR(CT_, NP_, NS_)                                                   \
   if (plan.pair && ct == CT_ && plan.np == NP_ && plan.nstage == NS_)             \
-    return launch_pair_t<CT_, NP_, NS_>(prm, W, G, s);
+    return launch_pair_t<CT_, NP_, NS_>(prm, plan.f8, W, G, s);
   MLA_CASE(kF32, 1, 4, 2)
   MLA_CASE(kBF16, 1, 4, 4)
   MLA_CASE(kFP8, 1, 4, 4)

@@ -71,6 +71,7 @@ struct DecodePlan {
   bool pair;     // pair kernel (two waves per 32 heads) instead of the block kernel
   bool stream;   // streaming kernel (one copy wave + four compute waves per 16 heads)
   bool h32;      // 128-head kernel (four waves of 32 heads, one per SIMD)
+  bool f8;       // pair kernel over an fp8 cache: fp8 MFMA for both contractions
   int np;        // pair kernel: 32-head pairs per workgroup
   int hb;        // block kernel: 16-head blocks per workgroup
   int ds;        // block kernel: value-dimension splits per head block

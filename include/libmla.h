@@ -32,6 +32,12 @@
  *    host on `stream`, synchronise it, and return MLA_ERR_INVALID_ARGUMENT
  *    without running anything if one is violated (MLA_ERR_HIP if a copy
  *    fails). This is the only case in which a call synchronises.
+ *  - Kernel choice switches read from the environment at each decode call:
+ *    MLA_FP8_MFMA=1 runs the value contraction over an fp8 cache (32 heads
+ *    or more) on fp8 MFMA with e4m3 value weights (output error about 2e-2
+ *    relative instead of about 3e-3); MLA_H32=1 selects the 128-head
+ *    one-wave-per-SIMD kernel for a bf16 cache. Results stay within the
+ *    decode tolerances either way.
  *  - All tensors are dense and row-major with the shapes given.
  */
 #ifndef LIBMLA_H
