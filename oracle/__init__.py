@@ -17,6 +17,9 @@ What it computes, and where the pages say so:
     up-projection recovers K/V from the latent). The absorbed form the method
     uses reaches the same result by associativity (same section: W_UK folds
     into the query side, W_UV into the output side);
+  * prefill (many queries per sequence): the same attention per query token
+    over the rows up to its own position (causal); the pages report prompt
+    throughput beside generation (DeepSeek-V2 reading card, "Evidence");
   * append: c_KV = W_DKV h and k_pe = RoPE(W_KR h), stored in the cache dtype;
     RoPE optionally with YaRN frequencies (discosf explainer, "decoupled RoPE
     and YaRN" section, with the formula of the published YaRN method).
@@ -29,6 +32,7 @@ from .numerics import (round_bf16, round_f32, e4m3_decode, e4m3_encode,
 from .mla import (D_C, D_R, D_ROW, D_NOPE, D_V, softmax_scale, rope_inv_freq,
                   yarn_inv_freq, yarn_softmax_factor, rope_rotate, paged_rows, append_rows_exact, quantize_rows,
                   decode_head, decode_problem, decode_sampled, attention_weights,
+                  prefill_head, prefill_positions, prefill_problem,
                   mla_cache_elements_per_token, mha_cache_elements_per_token,
                   gqa_equivalent_groups, cache_bytes)
 

@@ -48,6 +48,14 @@ Readings taken where the pages are silent (each listed in the design notes):
       block_table[b][t // P] * P + t % P; rows are stored as in the contiguous
       cache, so attention over a paged cache equals attention over the
       sequence's rows gathered in token order.
+  R10 prefill / multi-query attention [the pages measure prompt processing
+      beside generation -- over 100K prompt tokens/s on one 8-GPU node
+      (DeepSeek-V2 reading card, "Evidence"; discosf explainer, throughput
+      paragraph) -- but give no prefill formula]: the queries of sequence b
+      are its last n_b positions, whose rows are already in the cache; the
+      query at 0-based position p attends rows 0..p of its sequence (causal)
+      with the decode score, softmax and output (R1, R2, R5); n_b = L_b is a
+      whole-prompt prefill, n_b < L_b a chunk after a cached prefix.
 """
 from __future__ import annotations
 
@@ -249,3 +257,59 @@ def decode_problem(rows64_of_seq, q_nope, q_pe, w_uk, w_uv, B: int, H: int):
     pairs = [(b, h) for b in range(B) for h in range(H)]
     o, lse = decode_sampled(rows64_of_seq, q_nope, q_pe, w_uk, w_uv, pairs)
     return o.reshape(B, H, D_V), lse.reshape(B, H)
+
+
+# ----------------------------------------------------------------------------
+# prefill: causal multi-query attention (R10 with R1, R2, R5)
+# ----------------------------------------------------------------------------
+def prefill_head(C: np.ndarray, R: np.ndarray, q_nope: np.ndarray, q_pe: np.ndarray,
+                 w_uk: np.ndarray, w_uv: np.ndarray, pos: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """o [n, 128] and lse [n] for n queries of one (sequence, head).
+
+    C [L, 512] and R [L, 64] are the sequence's rows, q_nope [n, 128] and
+    q_pe [n, 64] the queries, pos [n] their 0-based positions (< L). As in
+    decode, K = C W_UK^T and V = C W_UV are expanded explicitly; query i's
+    scores over rows t > pos[i] are excluded (weight 0)."""
+    C = np.asarray(C, np.float64)
+    R = np.asarray(R, np.float64)
+    pos = np.asarray(pos, np.int64)
+    L = C.shape[0]
+    if len(pos) and (pos.min() < 0 or pos.max() >= L):
+        raise ValueError("query position outside the sequence")
+    K = C @ np.asarray(w_uk, np.float64).T          # K[t, i] = sum_j W_UK[i, j] C[t, j]
+    V = C @ np.asarray(w_uv, np.float64)            # V[t, i] = sum_j C[t, j] W_UV[j, i]
+    s = softmax_scale() * (np.asarray(q_nope, np.float64) @ K.T + np.asarray(q_pe, np.float64) @ R.T)
+    s[np.arange(L)[None, :] > pos[:, None]] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    return (e / z) @ V, (m + np.log(z))[:, 0]
+
+
+def prefill_positions(seq_len: int, n_q: int) -> np.ndarray:
+    """Positions of a sequence's n_q queries: its last n_q slots (R10)."""
+    if not 0 <= n_q <= seq_len:
+        raise ValueError("a sequence has at most seq_len queries")
+    return np.arange(seq_len - n_q, seq_len, dtype=np.int64)
+
+
+def prefill_problem(rows64_of_seq, seq_len, q_start, q_nope, q_pe, w_uk, w_uv,
+                    heads: Optional[Sequence[int]] = None):
+    """o [n_q, H, 128] and lse [n_q, H] (heads not listed stay 0 / -inf).
+
+    Query rows q_start[b] .. q_start[b+1]-1 belong to sequence b."""
+    n_q, H = q_nope.shape[0], q_nope.shape[1]
+    heads = range(H) if heads is None else heads
+    out = np.zeros((n_q, H, D_V))
+    lse = np.full((n_q, H), -np.inf)
+    for b in range(len(seq_len)):
+        q0, q1 = int(q_start[b]), int(q_start[b + 1])
+        if q1 == q0:
+            continue
+        rows = rows64_of_seq(b)
+        pos = prefill_positions(int(seq_len[b]), q1 - q0)
+        for h in heads:
+            out[q0:q1, h], lse[q0:q1, h] = prefill_head(rows[:, :D_C], rows[:, D_C:],
+                                                        q_nope[q0:q1, h], q_pe[q0:q1, h],
+                                                        w_uk[h], w_uv[h], pos)
+    return out, lse

@@ -68,3 +68,28 @@ class OracleView:
                                       self.w_uv, B, H)
         return mla.decode_sampled(self.rows64, self.q_nope, self.q_pe, self.w_uk,
                                   self.w_uv, pairs)
+
+
+class PrefillOracleView:
+    """fp64 view of a `workloads.PrefillProblem` (no append step)."""
+
+    def __init__(self, p):
+        self.p = p
+        self.dtype = p.wl.cache
+        self.q_nope = _np64(p.q_nope)
+        self.q_pe = _np64(p.q_pe)
+        self.w_uk = _np64(p.w_uk)
+        self.w_uv = _np64(p.w_uv)
+
+    def rows64(self, b: int) -> np.ndarray:
+        p = self.p
+        s, L = int(p.seq_start[b]), int(p.seq_len[b])
+        sl = p.rows[s:s + L]
+        if self.dtype == "fp8":
+            return e4m3_decode(sl.numpy()) * p.row_scale[s:s + L].to(torch.float64).numpy()[:, None]
+        return sl.to(torch.float64).numpy()
+
+    def prefill(self, heads=None):
+        """(o [n_q, H, 128], lse [n_q, H]); heads not in `heads` stay 0 / -inf."""
+        return mla.prefill_problem(self.rows64, self.p.seq_len, self.p.q_start, self.q_nope,
+                                   self.q_pe, self.w_uk, self.w_uv, heads)

@@ -17,7 +17,7 @@ distributions that are not available; uniform length draws stand in for them.
 from __future__ import annotations
 
 import dataclasses
-from typing import Optional
+from typing import Optional, Sequence
 
 import numpy as np
 import torch
@@ -196,3 +196,118 @@ def algorithmic_flops(p: Problem) -> dict:
     attn = 2 * H * (D_ROW + D_C) * p.T
     absorb = 4 * B * H * D_NOPE * D_C
     return {"attention": attn, "absorb_project": absorb, "total": attn + absorb}
+
+
+# ----------------------------------------------------------------------------
+# prefill / multi-query problems: the last n_b positions of each sequence are
+# queries (n_b = L_b: a whole prompt; n_b < L_b: a chunk after a cached prefix)
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    index: int             # RNG seed
+    B: int
+    H: int
+    lo: int                # sequence length drawn uniformly in [lo, hi]
+    hi: int
+    cache: str             # "bf16" | "fp8"
+    chunk: int = 0         # 0: every position is a query; else n_b = min(chunk, L_b)
+
+
+PREFILL_WORKLOADS = {
+    w.name: w for w in [
+        # DeepSeek-V2 attention shape (128 heads), four prompts of 2K-4K tokens
+        PrefillWorkload("prefill_bf16", 10, B=4, H=128, lo=2048, hi=4096, cache="bf16"),
+        # a 512-token chunk after a cached prefix, fp8 cache
+        PrefillWorkload("prefill_chunk_fp8", 11, B=8, H=128, lo=1024, hi=6144, cache="fp8",
+                        chunk=512),
+    ]
+}
+
+
+@dataclasses.dataclass
+class PrefillProblem:
+    """One synthetic prefill problem (host tensors)."""
+    wl: PrefillWorkload
+    seq_len: np.ndarray          # [B] int32
+    seq_start: np.ndarray        # [B] int64
+    seq_capacity: np.ndarray     # [B] int32
+    total_rows: int
+    rows: torch.Tensor           # [total_rows, 576] bf16 | uint8 codes
+    row_scale: Optional[torch.Tensor]
+    q_start: np.ndarray          # [B + 1] int32: queries of b are rows q_start[b]..q_start[b+1]-1
+    q_nope: torch.Tensor         # [n_q, H, 128] bf16
+    q_pe: torch.Tensor           # [n_q, H, 64] bf16
+    w_uk: torch.Tensor           # [H, 128, 512] bf16
+    w_uv: torch.Tensor           # [H, 512, 128] bf16
+
+    @property
+    def n_q(self) -> int:
+        return int(self.q_start[-1])
+
+    @property
+    def T(self) -> int:
+        return int(self.seq_len.astype(np.int64).sum())
+
+
+def make_prefill_problem(wl: PrefillWorkload, seed: Optional[int] = None, *,
+                         lengths: Optional[Sequence[int]] = None,
+                         n_queries: Optional[Sequence[int]] = None,
+                         H: Optional[int] = None, canary: int = CANARY_ROWS) -> PrefillProblem:
+    """Draw a prefill problem. Draw order (fixed): lengths, cache rows (fp8:
+    then one uniform per row for the scale), q_nope, q_pe, W_UK, W_UV."""
+    rng = np.random.Generator(np.random.PCG64(wl.index if seed is None else seed))
+    H = wl.H if H is None else H
+    if lengths is None:
+        seq_len = rng.integers(wl.lo, wl.hi, size=wl.B, endpoint=True).astype(np.int32)
+    else:
+        seq_len = np.asarray(lengths, dtype=np.int32).copy()
+    B = len(seq_len)
+    if n_queries is None:
+        nq = seq_len.copy() if wl.chunk == 0 else np.minimum(seq_len, wl.chunk).astype(np.int32)
+    else:
+        nq = np.asarray(n_queries, dtype=np.int32).copy()
+        assert nq.shape == (B,) and np.all((nq >= 0) & (nq <= seq_len))
+    q_start = np.zeros(B + 1, dtype=np.int32)
+    q_start[1:] = np.cumsum(nq)
+    cap = seq_len.astype(np.int64) + canary
+    seq_start = np.zeros(B, dtype=np.int64)
+    if B > 1:
+        seq_start[1:] = np.cumsum(cap)[:-1]
+    total_rows = int(cap.sum())
+    z = _normal(rng, (total_rows, D_ROW))
+    row_scale = None
+    if wl.cache == "fp8":
+        rows = fp8_codes_from_normal(z)
+        u = rng.uniform(-0.5, 0.5, size=total_rows)
+        row_scale = torch.from_numpy((np.exp(u) / FP8_SPREAD).astype(np.float32))
+    else:
+        rows = _to(z, wl.cache)
+    del z
+    n_q = int(q_start[-1])
+    w_std = 1.0 / np.sqrt(D_C)
+    q_nope = _to(_normal(rng, (n_q, H, D_NOPE)), "bf16")
+    q_pe = _to(_normal(rng, (n_q, H, D_R)), "bf16")
+    w_uk = _to(_normal(rng, (H, D_NOPE, D_C), w_std), "bf16")
+    w_uv = _to(_normal(rng, (H, D_C, D_V), w_std), "bf16")
+    return PrefillProblem(wl=wl, seq_len=seq_len, seq_start=seq_start,
+                          seq_capacity=cap.astype(np.int32), total_rows=total_rows, rows=rows,
+                          row_scale=row_scale, q_start=q_start, q_nope=q_nope, q_pe=q_pe,
+                          w_uk=w_uk, w_uv=w_uv)
+
+
+def prefill_flops(p: PrefillProblem) -> dict:
+    """Matrix work of a prefill step: the up-projection of every cached row
+    to per-head K (128) and V (128) from its 512-wide latent, and the causal
+    attention (score over 128 + 64 dims, values over 128) counted over the
+    (query, row) pairs a query may see."""
+    H = p.q_nope.shape[1]
+    kv = 2.0 * p.T * D_C * (D_NOPE + D_V) * H
+    pairs = 0
+    for b in range(len(p.seq_len)):
+        L = int(p.seq_len[b])
+        n = int(p.q_start[b + 1] - p.q_start[b])
+        pos = np.arange(L - n, L, dtype=np.int64)
+        pairs += int((pos + 1).sum())
+    attn = 2.0 * pairs * H * (D_NOPE + D_R + D_V)
+    return {"kv": kv, "attn": attn, "total": kv + attn, "pairs": pairs}
