@@ -36,7 +36,7 @@ EXPORTED = ["mla_append", "mla_decode_workspace_size", "mla_decode", "mla_decode
             "mla_decode_attend", "mla_decode_combine", "mla_decode_attend_combine",
             "mla_append_absorb", "mla_decode_noalloc", "mla_append_yarn",
             "mla_yarn_softmax_factor", "mla_append_paged", "mla_decode_paged",
-            "mla_status_string",
+            "mla_prefill_workspace_size", "mla_prefill", "mla_status_string",
             "mla_abi_version"]
 DECODE_STAGES = ["mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
                  "mla_decode_attend_combine"]
@@ -114,6 +114,11 @@ def _load(path: str = LIB_PATH):
     lib.mla_append_paged.restype = ctypes.c_int
     lib.mla_decode_paged.argtypes = [PC, P, P, P, P, P, ctypes.c_int, I32, F32, P, P, P, SZ, P]
     lib.mla_decode_paged.restype = ctypes.c_int
+    lib.mla_prefill_workspace_size.argtypes = [I32, I32, I64, I64, ctypes.POINTER(SZ)]
+    lib.mla_prefill_workspace_size.restype = ctypes.c_int
+    lib.mla_prefill.argtypes = [C, P, P, I64, I64, P, P, P, P, ctypes.c_int, I32, F32, P, P,
+                                P, SZ, P]
+    lib.mla_prefill.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -545,3 +550,50 @@ class PreparedAppendAbsorb:
 
     def __call__(self) -> None:
         _check(lib.mla_append_absorb(*self._args), "mla_append_absorb")
+
+
+# ---------------------------------------------------------------- prefill
+def mla_prefill_workspace_size(num_seqs: int, n_heads: int, n_q: int, max_kv_rows: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.mla_prefill_workspace_size(num_seqs, n_heads, n_q, max_kv_rows, ctypes.byref(n)),
+           "mla_prefill_workspace_size")
+    return n.value
+
+
+def alloc_prefill_workspace(cache: LatentCache, n_heads: int, n_q: int, max_kv_rows: int,
+                            device=None) -> torch.Tensor:
+    n = mla_prefill_workspace_size(cache.num_seqs, n_heads, n_q, max_kv_rows)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device or cache.rows.device)
+
+
+def mla_prefill(cache: LatentCache, seq_len: torch.Tensor, q_start: torch.Tensor,
+                max_kv_rows: int, q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk: torch.Tensor,
+                w_uv: torch.Tensor, softmax_scale: float, out: torch.Tensor,
+                lse: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
+    """Causal multi-query attention: query rows q_start[b]..q_start[b+1]-1 are
+    sequence b's last positions (see libmla.h)."""
+    cache.check()
+    dev = cache.rows.device
+    B = cache.num_seqs
+    if not isinstance(q_nope, torch.Tensor) or q_nope.dim() != 3:
+        raise ValueError("q_nope must be a [n_q, H, 128] tensor")
+    n_q, H = q_nope.shape[0], q_nope.shape[1]
+    if q_nope.dtype != torch.bfloat16:
+        raise TypeError("prefill activations must be bfloat16")
+    _expect(seq_len, "seq_len", (B,), torch.int32, dev)
+    _expect(q_start, "q_start", (B + 1,), torch.int32, dev)
+    _expect(q_nope, "q_nope", (n_q, H, D_NOPE), torch.bfloat16, dev)
+    _expect(q_pe, "q_pe", (n_q, H, D_R), torch.bfloat16, dev)
+    _expect(w_uk, "w_uk", (H, D_NOPE, D_C), torch.bfloat16, dev)
+    _expect(w_uv, "w_uv", (H, D_C, D_V), torch.bfloat16, dev)
+    _expect(out, "out", (n_q, H, D_V), torch.bfloat16, dev)
+    if lse is not None:
+        _expect(lse, "lse", (n_q, H), torch.float32, dev)
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 \
+            or workspace.dim() != 1 or workspace.device != dev:
+        raise ValueError(f"workspace must be a 1-D uint8 tensor on {dev}")
+    st = ctypes.byref(cache.struct())
+    _check(lib.mla_prefill(st, _ptr(seq_len), _ptr(q_start), n_q, int(max_kv_rows), _ptr(q_nope),
+                           _ptr(q_pe), _ptr(w_uk), _ptr(w_uv), MLA_DTYPE_BF16, H,
+                           float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                           workspace.numel(), _stream(stream)), "mla_prefill")

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
 SOURCES = ["api.cpp", "append.hip", "decode_attn.hip", "decode_attn_stream.hip", "decode_attn_h32.hip",
-           "decode_gemm.hip"]
+           "decode_gemm.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -85,6 +85,21 @@ WorkspaceLayout workspace_layout(int ct, int B, int H) {
   return l;
 }
 
+PrefillLayout prefill_layout(int B, int H, int64_t max_kv_rows) {
+  PrefillLayout l{};
+  l.kv_rows = (int64_t)kPfRows * ((max_kv_rows + kPfRows - 1) / kPfRows + B);
+  size_t off = 0;
+  l.kv_row0 = off;  off = align256(off + sizeof(int64_t) * ((size_t)B + 1));
+  l.qb_start = off; off = align256(off + sizeof(int32_t) * ((size_t)B + 1));
+  l.lenc = off;     off = align256(off + sizeof(int32_t) * (size_t)B);
+  l.nq = off;       off = align256(off + sizeof(int32_t) * (size_t)B);
+  l.kn = off;       off = align256(off + (size_t)H * l.kv_rows * 128 * 2);
+  l.kpe = off;      off = align256(off + (size_t)l.kv_rows * MLA_D_R * 2);
+  l.v = off;        off = align256(off + (size_t)H * l.kv_rows * 128 * 2);
+  l.total = off;
+  return l;
+}
+
 }  // namespace mla
 
 using namespace mla;
@@ -539,6 +554,115 @@ mla_status_t mla_append_absorb(const mla_cache_t* cache, const void* h, int32_t 
     e = n_tok > 0 ? launch_append(ct, aa, (hipStream_t)stream) : hipSuccess;
     if (e == hipSuccess) e = launch_decode(ct, plan, da, (hipStream_t)stream, 1);
   }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- prefill
+// Largest workspace row bound and query count the launches can index.
+static constexpr int64_t kMaxPrefillRows = (int64_t)1 << 31;
+
+static mla_status_t prefill_shape(int32_t num_seqs, int32_t n_heads, int64_t n_q,
+                                  int64_t max_kv_rows) {
+  if (num_seqs < 1 || n_heads < 1 || n_q < 0 || max_kv_rows < 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (num_seqs > kMaxSeqs || n_heads > kMaxHeads) return MLA_ERR_UNSUPPORTED;
+  if (n_q > INT32_MAX || max_kv_rows > kMaxPrefillRows) return MLA_ERR_UNSUPPORTED;
+  // attention grid: heads x (query blocks + sequences), rounded to 8
+  const int64_t items = (int64_t)n_heads * ((n_q + kPfQ - 1) / kPfQ + num_seqs);
+  if (items + 8 > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+extern "C" {
+
+mla_status_t mla_prefill_workspace_size(int32_t num_seqs, int32_t n_heads, int64_t n_q,
+                                        int64_t max_kv_rows, size_t* bytes) {
+  if (!bytes) return MLA_ERR_INVALID_ARGUMENT;
+  const mla_status_t st = prefill_shape(num_seqs, n_heads, n_q, max_kv_rows);
+  if (st != MLA_OK) return st;
+  *bytes = prefill_layout(num_seqs, n_heads, max_kv_rows).total;
+  return MLA_OK;
+}
+
+}  // extern "C"
+
+// MLA_DEBUG: lengths in [0, capacity], q_start non-decreasing from 0 to n_q,
+// every sequence's queries at most its length, the padded rows within the
+// bound, rows inside the cache
+static mla_status_t debug_check_prefill(const CacheView& c, const int32_t* seq_len,
+                                        const int32_t* q_start, int64_t n_q, int64_t max_kv_rows,
+                                        hipStream_t s) {
+  std::vector<int32_t> cap, len, qs;
+  const mla_status_t st = debug_capacity(c, nullptr, cap, s);
+  if (st != MLA_OK) return st;
+  if (!to_host(len, seq_len, c.num_seqs, s) || !to_host(qs, q_start, (size_t)c.num_seqs + 1, s))
+    return MLA_ERR_HIP;
+  if (qs[0] != 0 || qs[c.num_seqs] != n_q) return MLA_ERR_INVALID_ARGUMENT;
+  int64_t rows = 0;
+  for (int b = 0; b < c.num_seqs; ++b) {
+    if (len[b] < 0 || len[b] > cap[b]) return MLA_ERR_INVALID_ARGUMENT;
+    if (qs[b + 1] < qs[b] || qs[b + 1] - qs[b] > len[b]) return MLA_ERR_INVALID_ARGUMENT;
+    rows += len[b];
+  }
+  if (rows > max_kv_rows) return MLA_ERR_INVALID_ARGUMENT;
+  return MLA_OK;
+}
+
+extern "C" {
+
+mla_status_t mla_prefill(const mla_cache_t* cache, const int32_t* seq_len, const int32_t* q_start,
+                         int64_t n_q, int64_t max_kv_rows, const void* q_nope, const void* q_pe,
+                         const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
+                         int32_t n_heads, float softmax_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  CacheView cv;
+  mla_status_t st = view_of(cache, cv);
+  if (st != MLA_OK) return st;
+  if (!valid_dtype(act_dtype)) return MLA_ERR_INVALID_ARGUMENT;
+  st = prefill_shape(cv.num_seqs, n_heads, n_q, max_kv_rows);
+  if (st != MLA_OK) return st;
+  if (!seq_len || !q_start || !q_nope || !q_pe || !w_uk || !w_uv || !out || !workspace)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (act_dtype != MLA_DTYPE_BF16 ||
+      (cv.dtype != MLA_DTYPE_BF16 && cv.dtype != MLA_DTYPE_FP8_E4M3))
+    return MLA_ERR_UNSUPPORTED;
+  const PrefillLayout wl = prefill_layout(cv.num_seqs, n_heads, max_kv_rows);
+  if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (debug_mode()) {
+    const mla_status_t ds = debug_check_prefill(cv, seq_len, q_start, n_q, max_kv_rows,
+                                                (hipStream_t)stream);
+    if (ds != MLA_OK) return ds;
+  }
+  char* ws = (char*)workspace;
+  PrefillArgs a{};
+  a.rows = cv.rows;
+  a.row_scale = cv.row_scale;
+  a.seq_start = cv.seq_start;
+  a.seq_cap = cv.seq_cap;
+  a.seq_len = seq_len;
+  a.q_start = q_start;
+  a.n_q = n_q;
+  a.kv_rows = wl.kv_rows;
+  a.B = cv.num_seqs;
+  a.H = n_heads;
+  a.q_nope = q_nope;
+  a.q_pe = q_pe;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.out = out;
+  a.lse = lse;
+  a.softmax_scale = softmax_scale;
+  a.kv_row0 = (int64_t*)(ws + wl.kv_row0);
+  a.qb_start = (int32_t*)(ws + wl.qb_start);
+  a.lenc = (int32_t*)(ws + wl.lenc);
+  a.nq = (int32_t*)(ws + wl.nq);
+  a.kn = ws + wl.kn;
+  a.kpe = ws + wl.kpe;
+  a.v = ws + wl.v;
+  const hipError_t e = launch_prefill(cache_type(cv.dtype), a, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

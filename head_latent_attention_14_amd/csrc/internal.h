@@ -142,4 +142,55 @@ bool append_absorb_fits(int cache_type, const AppendArgs& a, const DecodeArgs& d
 hipError_t launch_append_absorb(const AppendArgs& a, const DecodePlan& plan, const DecodeArgs& d,
                                 hipStream_t s);
 
+// ---------------------------------------------------------------- prefill
+// Causal multi-query attention: the queries of sequence b are its last n_b
+// positions. Three launches: a one-workgroup plan (prefix sums), the
+// up-projection of every cached row to per-head K (128, plus the shared
+// 64-wide RoPE key) and V (128), and the attention over query blocks.
+constexpr int kPfRows = 128;      // cached rows per up-projection workgroup (and K/V padding)
+constexpr int kPfQ = 256;         // queries per attention workgroup (8 waves of 32)
+constexpr int kPfKV = 64;         // cached rows per attention step
+
+struct PrefillLayout {
+  int64_t kv_rows;   // rows of the K/V buffers: kPfRows * (ceil(max_kv_rows / kPfRows) + B)
+  size_t kv_row0;    // int64 [B+1] first packed K/V row of each sequence (multiples of kPfRows)
+  size_t qb_start;   // int32 [B+1] first query block of each sequence
+  size_t lenc;       // int32 [B] length clamped to [0, capacity] (0: not served)
+  size_t nq;         // int32 [B] queries of each sequence (clamped to [0, length])
+  size_t kn;         // bf16 [H][kv_rows][128] K without the RoPE part
+  size_t kpe;        // bf16 [kv_rows][64] the RoPE key (shared by the heads)
+  size_t v;          // bf16 [H][kv_rows][128]
+  size_t total;
+};
+PrefillLayout prefill_layout(int B, int H, int64_t max_kv_rows);
+
+struct PrefillArgs {
+  const void* rows;           // contiguous cache storage
+  const float* row_scale;     // fp8 only
+  const int64_t* seq_start;   // [B]
+  const int32_t* seq_cap;     // [B]
+  const int32_t* seq_len;     // [B]
+  const int32_t* q_start;     // [B+1]
+  int64_t n_q;
+  int64_t kv_rows;            // PrefillLayout::kv_rows
+  int32_t B;
+  int32_t H;
+  const void* q_nope;         // [n_q][H][128] bf16
+  const void* q_pe;           // [n_q][H][64] bf16
+  const void* w_uk;           // [H][128][512] bf16
+  const void* w_uv;           // [H][512][128] bf16
+  void* out;                  // [n_q][H][128] bf16
+  float* lse;                 // [n_q][H] or null
+  float softmax_scale;
+  // workspace views
+  int64_t* kv_row0;
+  int32_t* qb_start;
+  int32_t* lenc;
+  int32_t* nq;
+  void* kn;
+  void* kpe;
+  void* v;
+};
+hipError_t launch_prefill(int cache_type, const PrefillArgs& a, hipStream_t s);
+
 }  // namespace mla

@@ -1,0 +1,536 @@
+// MLA prefill / multi-query attention over the latent cache: the queries of
+// sequence b are its last n_b positions, and the query at position p attends
+// rows 0..p of b (causal). The pages report prompt processing beside
+// generation (DeepSeek-V2 reading card, "Evidence": over 100K prompt tokens/s
+// on one 8-GPU node) without a prefill formula; the score, softmax and output
+// are decode's.
+//
+// With many queries per sequence the unabsorbed form is the cheaper one: a
+// (query, row) pair then costs 128 + 64 multiply-adds for the score and 128
+// for the value per head, against 576 + 512 over the latent, and the
+// up-projection K = W_UK c, V = W_UV^T c is paid once per row (discosf
+// explainer, "long-context bottleneck": the latent is up-projected to K/V at
+// attention time). Three launches:
+//   plan   one workgroup: per-sequence prefix sums of the padded K/V rows and
+//          of the query blocks;
+//   kv     per (head, 128 cached rows): K[h] (128 dims) and V[h] (128 dims) as
+//          bf16 into the workspace, on bf16 MFMA; head 0 also copies the shared
+//          RoPE key (fp8 caches: codes widened exactly, scales applied to the
+//          fp32 products);
+//   attn   per (head, 256 queries): 8 waves of 32 queries stream 64-row K/V
+//          blocks through a two-stage LDS ring (asynchronous global->LDS
+//          copies), S^T = K Q^T and O^T += V^T P^T on 16x16x32 bf16 MFMA with
+//          an online softmax, the causal mask on the diagonal blocks only.
+#include <type_traits>
+
+#include "attn_tile.h"
+
+namespace mla {
+
+// ------------------------------------------------------------------ plan
+__global__ void __launch_bounds__(256) mla_prefill_plan_kernel(PrefillArgs a) {
+  __shared__ int64_t s_kv[256];
+  __shared__ int32_t s_qb[256];
+  const int tid = threadIdx.x;
+  int64_t carry_kv = 0;
+  int32_t carry_qb = 0;
+  for (int base = 0; base < a.B; base += 256) {
+    const int b = base + tid;
+    int len = 0, n = 0;
+    int64_t kvr = 0;
+    int32_t qb = 0;
+    if (b < a.B) {
+      const int cap = a.seq_cap[b] > 0 ? a.seq_cap[b] : 0;
+      len = a.seq_len[b];
+      len = len < 0 ? 0 : (len > cap ? cap : len);
+      int64_t q0 = a.q_start[b], q1 = a.q_start[b + 1];
+      q0 = q0 < 0 ? 0 : (q0 > a.n_q ? a.n_q : q0);
+      q1 = q1 < q0 ? q0 : (q1 > a.n_q ? a.n_q : q1);
+      n = (int)(q1 - q0);
+      kvr = (int64_t)((len + kPfRows - 1) / kPfRows) * kPfRows;
+      qb = (n + kPfQ - 1) / kPfQ;
+    }
+    s_kv[tid] = kvr;
+    s_qb[tid] = qb;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {                // inclusive scans
+      const int64_t xk = tid >= d ? s_kv[tid - d] : 0;
+      const int32_t xq = tid >= d ? s_qb[tid - d] : 0;
+      __syncthreads();
+      s_kv[tid] += xk;
+      s_qb[tid] += xq;
+      __syncthreads();
+    }
+    if (b < a.B) {
+      int64_t r0 = carry_kv + s_kv[tid] - kvr;
+      // a sequence whose rows would pass the K/V buffers is not served
+      // (its queries get o = 0, lse = -inf): the caller's row bound was short
+      if (r0 + kvr > a.kv_rows) len = 0;
+      a.kv_row0[b] = r0;
+      a.qb_start[b] = carry_qb + s_qb[tid] - qb;
+      a.lenc[b] = len;
+      a.nq[b] = n;
+    }
+    carry_kv += s_kv[255];
+    carry_qb += s_qb[255];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.kv_row0[a.B] = carry_kv;
+    a.qb_start[a.B] = carry_qb;
+  }
+}
+
+// Largest b in [0, B) with arr[b] <= x (arr non-decreasing, arr[0] <= x),
+// through scalar loads.
+template <typename T>
+__device__ __forceinline__ int search_seq(const T* arr, int B, int64_t x) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)ld_const(arr, mid) <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------------ kv
+// One workgroup per (head h = blockIdx.x, 128 packed rows = blockIdx.y).
+// D^T = W X^T with A = the weight rows (output dims, 16 per block) and B =
+// the latent rows (16 per block), so a lane ends with four consecutive
+// output dims of one row (one 8-byte store). Wave w computes output dims
+// 64w .. 64w + 63 of [K (0..127) | V (128..255)] for all 128 rows. The
+// latent is contracted in 8 chunks of 64, each staged in LDS (latent rows,
+// W_UK rows, W_UV rows) from registers loaded one chunk ahead.
+template <int CT>
+__global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
+  constexpr int KC = 64;
+  constexpr int XP = KC * 2 + 16;                      // LDS pitch of a latent row chunk (bf16)
+  constexpr int WKP = KC * 2 + 16;                     // W_UK row chunk
+  constexpr int WVP = 128 * 2 + 16;                    // W_UV row (one latent dim)
+  constexpr int X_BYTES = kPfRows * XP;
+  constexpr int WK_BYTES = 128 * WKP;
+  constexpr int WV_BYTES = KC * WVP;
+  __shared__ __attribute__((aligned(16))) char lds[X_BYTES + WK_BYTES + WV_BYTES];
+  __shared__ float s_scale[kPfRows];
+  char* xs = lds;
+  char* wk = lds + X_BYTES;
+  char* wv = wk + WK_BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int h = blockIdx.x;
+  const int H = a.H;
+  const int64_t r0 = (int64_t)blockIdx.y * kPfRows;
+  if (r0 >= ld_const(a.kv_row0, a.B)) return;
+  const int b = search_seq(a.kv_row0, a.B, r0);
+  const int L = ld_const(a.lenc, b);
+  const int t0 = (int)(r0 - ld_const(a.kv_row0, b));
+  const int64_t crow0 = ld_const(a.seq_start, b) + t0;   // cache row of packed row r0
+  constexpr int RB = (CT == kFP8) ? kDrow : kDrow * 2;   // bytes of a cache row
+  const char* rows = (const char*)a.rows;
+
+  if constexpr (CT == kFP8) {
+    if (tid < kPfRows) s_scale[tid] = (t0 + tid < L) ? a.row_scale[crow0 + tid] : 0.f;
+  }
+
+  // ---- global loads of one chunk into registers ----
+  constexpr int NX = (CT == kFP8) ? 2 : 4;             // 16-byte pieces of latent per thread
+  struct Chunk {
+    u32x4 x[NX];
+    u32x4 k[4];
+    u32x4 v[4];
+  };
+  auto load = [&](int k0, Chunk& c) {
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+      const int i = tid + 256 * j;
+      const int r = (CT == kFP8) ? (i >> 2) : (i >> 3);
+      const int p = (CT == kFP8) ? (i & 3) : (i & 7);
+      c.x[j] = u32x4{0u, 0u, 0u, 0u};
+      if (t0 + r < L)
+        c.x[j] = *(const u32x4*)(rows + (crow0 + r) * RB + (CT == kFP8 ? k0 : 2 * k0) + 16 * p);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid + 256 * j;
+      const int n = i >> 3, p = i & 7;                 // W_UK[h][n][k0 + 8p ..]
+      c.k[j] = *(const u32x4*)((const char*)a.w_uk + (((int64_t)h * 128 + n) * kDc + k0) * 2 + 16 * p);
+      const int kk = i >> 4, q = i & 15;               // W_UV[h][k0 + kk][8q ..]
+      c.v[j] = *(const u32x4*)((const char*)a.w_uv + (((int64_t)h * kDc + k0 + kk) * 128) * 2 + 16 * q);
+    }
+  };
+  auto store = [&](const Chunk& c) {
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+      const int i = tid + 256 * j;
+      if constexpr (CT == kFP8) {                      // 16 codes -> 16 exact bf16 values
+        const int r = i >> 2, p = i & 3;
+        const u32x4 u = c.x[j];
+        const uint2 e0 = fp8x4_to_bf16x4(u[0]), e1 = fp8x4_to_bf16x4(u[1]);
+        const uint2 e2 = fp8x4_to_bf16x4(u[2]), e3 = fp8x4_to_bf16x4(u[3]);
+        *(u32x4*)(xs + r * XP + 32 * p) = u32x4{e0.x, e0.y, e1.x, e1.y};
+        *(u32x4*)(xs + r * XP + 32 * p + 16) = u32x4{e2.x, e2.y, e3.x, e3.y};
+      } else {
+        const int r = i >> 3, p = i & 7;
+        *(u32x4*)(xs + r * XP + 16 * p) = c.x[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid + 256 * j;
+      *(u32x4*)(wk + (i >> 3) * WKP + 16 * (i & 7)) = c.k[j];
+      *(u32x4*)(wv + (i >> 4) * WVP + 16 * (i & 15)) = c.v[j];
+    }
+  };
+
+  f32x4 acc[4][8];                                     // [output block][row block]
+#pragma unroll
+  for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) acc[ob][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bool is_k = wave < 2;
+  const int nbase = 64 * (wave & 1);                   // first output dim of the wave in K or V
+  Chunk cur;
+  load(0, cur);
+  for (int k0 = 0; k0 < kDc; k0 += KC) {
+    __syncthreads();                                   // previous chunk consumed
+    store(cur);
+    __syncthreads();
+    if (k0 + KC < kDc) load(k0 + KC, cur);             // next chunk in flight during the MFMAs
+#pragma unroll
+    for (int kk = 0; kk < KC; kk += 32) {
+      bf16x8 w8[4];
+#pragma unroll
+      for (int ob = 0; ob < 4; ++ob) {
+        if (is_k) {                                    // lane (n, g): W_UK[h][n][kk + 8g ..]
+          w8[ob] = *(const bf16x8*)(wk + (nbase + 16 * ob + l16) * WKP + (kk + 8 * g) * 2);
+        } else {                                       // lane (n, g): W_UV[h][kk + 8g + 0..7][n]
+          const int rs = kk + 8 * g + (l16 >> 2);
+          const int cb = (nbase + 16 * ob + 4 * (l16 & 3)) * 2;
+          const s16x4 lo = lds_read_tr16(wv, rs * WVP + cb);
+          const s16x4 hi = lds_read_tr16(wv, (rs + 4) * WVP + cb);
+          const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          w8[ob] = __builtin_bit_cast(bf16x8, a8);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < 8; ++rb) {
+        const bf16x8 x8 = *(const bf16x8*)(xs + (16 * rb + l16) * XP + (kk + 8 * g) * 2);
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob) acc[ob][rb] = mfma_bf16_k32(w8[ob], x8, acc[ob][rb]);
+      }
+    }
+  }
+
+  // ---- epilogue: lane holds D^T[dim 16 ob + 4g + r][row 16 rb + l16]; rows
+  // past the sequence are written as zeros ----
+  char* dst_base = (char*)(is_k ? a.kn : a.v) + ((int64_t)h * a.kv_rows + r0) * 128 * 2;
+#pragma unroll
+  for (int rb = 0; rb < 8; ++rb) {
+    const int r = 16 * rb + l16;
+    float sc = (t0 + r < L) ? 1.f : 0.f;
+    if constexpr (CT == kFP8) sc = s_scale[r];        // 0 past the sequence
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob) {
+      const f32x4 x = acc[ob][rb] * sc;
+      uint2 u;
+      u.x = pack_bf16x2(x[0], x[1]);
+      u.y = pack_bf16x2(x[2], x[3]);
+      *(uint2*)(dst_base + ((int64_t)r * 128 + nbase + 16 * ob + 4 * g) * 2) = u;
+    }
+  }
+
+  // ---- head 0: the shared RoPE key of the 128 rows (bf16; fp8 codes times
+  // the row scale, rounded once) ----
+  if (h == 0) {
+    char* kpe = (char*)a.kpe + r0 * kDr * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid + 256 * j;                     // 8-element piece i of the 128 x 64 block
+      const int r = i >> 3, p = i & 7;
+      u32x4 out = u32x4{0u, 0u, 0u, 0u};
+      if (t0 + r < L) {
+        if constexpr (CT == kFP8) {
+          const uint2 c = *(const uint2*)(rows + (crow0 + r) * RB + kDc + 8 * p);
+          const float sc = s_scale[r];
+          float f[8];
+#pragma unroll
+          for (int w2 = 0; w2 < 2; ++w2) {
+            const uint32_t word = w2 ? c.y : c.x;
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+            const float v0 = lo[0], v1 = lo[1], v2 = hi[0], v3 = hi[1];
+            f[4 * w2 + 0] = v0 * sc;
+            f[4 * w2 + 1] = v1 * sc;
+            f[4 * w2 + 2] = v2 * sc;
+            f[4 * w2 + 3] = v3 * sc;
+          }
+          out = u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+        } else {
+          out = *(const u32x4*)(rows + (crow0 + r) * RB + kDc * 2 + 16 * p);
+        }
+      }
+      *(u32x4*)(kpe + (r * kDr + 8 * p) * 2) = out;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ attention
+// One workgroup per (head, block of 256 queries of one sequence). Work items
+// are ordered by (head, sequence, query block, later blocks first) and dealt
+// to the 8 XCDs in contiguous ranges, so the workgroups that read one
+// (sequence, head)'s K/V run on one XCD close together and share its L2.
+// LDS stages hold 64 K rows (128 + 64 dims, pitch 400 B: 16 rows of a
+// 16-byte operand read start on distinct bank groups) and 64 V rows (pitch
+// 272 B); stage slot s of a copy is K row s / 25, chunk s % 25 (chunks
+// 0..15 from K[h], 16..23 from the RoPE key, 24 a repeat of 23) or V row
+// s / 17, chunk s % 17 (16 a repeat of 15).
+constexpr int kPfKP = 400;                             // K row pitch in LDS
+constexpr int kPfVP = 272;                             // V row pitch in LDS
+constexpr int kPfKSlots = kPfKP / 16;                  // 25
+constexpr int kPfVSlots = kPfVP / 16;                  // 17
+constexpr int kPfKCopies = kPfKV * kPfKSlots / 64;     // 25 one-kilobyte copies
+constexpr int kPfVCopies = kPfKV * kPfVSlots / 64;     // 17
+constexpr int kPfStage = (kPfKCopies + kPfVCopies) * 1024;
+
+__global__ void __launch_bounds__(512) mla_prefill_attn_kernel(PrefillArgs a) {
+  static_assert(kPfKV * kPfKSlots % 64 == 0 && kPfKV * kPfVSlots % 64 == 0, "whole copies");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kPfStage];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int H = a.H;
+  const int B = a.B;
+
+  // ---- work item ----
+  const int per = gridDim.x / 8;
+  const int64_t k = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  const int QB = ld_const(a.qb_start, B);
+  if (QB == 0 || k >= (int64_t)H * QB) return;
+  const int h = (int)(k / QB);
+  const int qbg = (int)(k - (int64_t)h * QB);
+  const int b = search_seq(a.qb_start, B, qbg);
+  const int qb0 = ld_const(a.qb_start, b);
+  const int nqb = ld_const(a.qb_start, b + 1) - qb0;
+  const int j = nqb - 1 - (qbg - qb0);                 // later blocks (longer rows) first
+  const int L = ld_const(a.lenc, b);
+  const int n = ld_const(a.nq, b);
+  int64_t qrow0 = ld_const(a.q_start, b);
+  qrow0 = qrow0 < 0 ? 0 : (qrow0 > a.n_q ? a.n_q : qrow0);
+  const int64_t kv0_row = ld_const(a.kv_row0, b);
+  // positions: query i of the sequence sits at L - n + i
+  const int i_blk = j * kPfQ;                          // first query of the block
+  const int i_last = (i_blk + kPfQ < n ? i_blk + kPfQ : n) - 1;
+  const int p_last = L - n + i_last;                   // the block's last position
+  const int nblk = p_last >= 0 ? (p_last + kPfKV) / kPfKV : 0;
+  const int i_w = i_blk + 32 * wave;                   // this wave's first query
+  const int p_w0 = L - n + i_w;                        // its first position
+
+  // ---- queries: B operand of the score MFMA, lane (query l16, k-run 8g) ----
+  bf16x8 q[2][6];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    int i = i_w + 16 * qb + l16;
+    i = i < n ? i : n - 1;                             // rows past the sequence's queries: any valid one
+    const int64_t qr = qrow0 + i;
+    const __bf16* qn = (const __bf16*)a.q_nope + (qr * H + h) * kDnope;
+    const __bf16* qp = (const __bf16*)a.q_pe + (qr * H + h) * kDr;
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk)
+      q[qb][kk] = kk < 4 ? *(const bf16x8*)(qn + 32 * kk + 8 * g) : *(const bf16x8*)(qp + 32 * (kk - 4) + 8 * g);
+  }
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) asm volatile("" : "+v"(q[qb][kk]));
+
+  // ---- copies of K/V block `blk` into stage `st`: copy c of the 42 goes to
+  // wave c % 8 ----
+  const char* kn = (const char*)a.kn + (int64_t)h * a.kv_rows * 256;
+  const char* vv = (const char*)a.v + (int64_t)h * a.kv_rows * 256;
+  const char* kpe = (const char*)a.kpe;
+  auto issue = [&](int blk, int st) {
+    const int64_t row0 = kv0_row + (int64_t)blk * kPfKV;
+    char* stage = smem + st * kPfStage;
+#pragma unroll
+    for (int c0 = 0; c0 < kPfKCopies + kPfVCopies; c0 += 8) {
+      const int c = c0 + wave;
+      if (c >= kPfKCopies + kPfVCopies) continue;
+      const int ln = TileCopy<kBF16, 1>::lane_id();
+      const char* src;
+      if (c < kPfKCopies) {
+        const int s = 64 * c + ln;
+        const int r = s / kPfKSlots;
+        int ch = s - r * kPfKSlots;
+        ch = ch < 24 ? ch : 23;
+        src = ch < 16 ? kn + ((row0 + r) * 128 + 8 * ch) * 2 : kpe + ((row0 + r) * kDr + 8 * (ch - 16)) * 2;
+      } else {
+        const int s = 64 * (c - kPfKCopies) + ln;
+        const int r = s / kPfVSlots;
+        int ch = s - r * kPfVSlots;
+        ch = ch < 16 ? ch : 15;
+        src = vv + ((row0 + r) * 128 + 8 * ch) * 2;
+      }
+      async_copy16(src, stage + c * 1024);
+    }
+  };
+
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  f32x4 o[8][2];                                       // O^T: dims 16 db + 4g + r, query l16 of block qb
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db][0] = o[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sl2 = a.softmax_scale * kLog2e;
+  const uint32_t k_lane = (uint32_t)(l16 * kPfKP + 16 * g);
+  const uint32_t v_lane = (uint32_t)((4 * g + (l16 >> 2)) * kPfVP + 8 * (l16 & 3));
+
+  if (nblk > 0) issue(0, 0);
+  for (int blk = 0; blk < nblk; ++blk) {
+    wait_vmcnt<0>();
+    barrier_lds();                                     // block blk visible; the other stage free
+    if (blk + 1 < nblk) issue(blk + 1, (blk + 1) & 1);
+    const int kv0 = blk * kPfKV;
+    if (kv0 > p_w0 + 31) continue;                     // every query of this wave is earlier
+    const char* stage = smem + (blk & 1) * kPfStage;
+    const uint32_t ks = (uint32_t)(size_t)stage + k_lane;
+    const uint32_t vs = (uint32_t)(size_t)(stage + kPfKCopies * 1024) + v_lane;
+
+    // scores S^T[row 16 kb + 4g + r][query 16 qb + l16]
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc[kb][0] = acc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) {
+      u32x4 r4[4];
+      if (kk == 0) lds_read_b128_x4<0, 16 * kPfKP, 32 * kPfKP, 48 * kPfKP>(ks, r4[0], r4[1], r4[2], r4[3]);
+      if (kk == 1) lds_read_b128_x4<64, 16 * kPfKP + 64, 32 * kPfKP + 64, 48 * kPfKP + 64>(ks, r4[0], r4[1], r4[2], r4[3]);
+      if (kk == 2) lds_read_b128_x4<128, 16 * kPfKP + 128, 32 * kPfKP + 128, 48 * kPfKP + 128>(ks, r4[0], r4[1], r4[2], r4[3]);
+      if (kk == 3) lds_read_b128_x4<192, 16 * kPfKP + 192, 32 * kPfKP + 192, 48 * kPfKP + 192>(ks, r4[0], r4[1], r4[2], r4[3]);
+      if (kk == 4) lds_read_b128_x4<256, 16 * kPfKP + 256, 32 * kPfKP + 256, 48 * kPfKP + 256>(ks, r4[0], r4[1], r4[2], r4[3]);
+      if (kk == 5) lds_read_b128_x4<320, 16 * kPfKP + 320, 32 * kPfKP + 320, 48 * kPfKP + 320>(ks, r4[0], r4[1], r4[2], r4[3]);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 a8 = __builtin_bit_cast(bf16x8, r4[kb]);
+        acc[kb][0] = mfma_bf16_k32(a8, q[0][kk], acc[kb][0]);
+        acc[kb][1] = mfma_bf16_k32(a8, q[1][kk], acc[kb][1]);
+      }
+    }
+
+    // online softmax per query (log2 domain, lazy rescale as in decode)
+    const bool diag = kv0 + kPfKV - 1 > p_w0;           // some row is past some query's position
+    bf16x8 pb[2][2];                                   // [query block][k-step of 32 rows]
+    float sc[2][16];
+    bool grow = false;
+    float tmax[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int pq = p_w0 + 16 * qb + l16;             // this lane's query position
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = acc[kb][qb][r] * sl2;
+          if (diag && kv0 + 16 * kb + 4 * g + r > pq) x = -INFINITY;
+          sc[qb][4 * kb + r] = x;
+        }
+      float t = sc[qb][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) t = __builtin_fmaxf(t, sc[qb][i]);
+      tmax[qb] = max_over_groups(t);
+      grow = grow || (tmax[qb] > m_run[qb] + kSlack);
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m_new = __builtin_fmaxf(m_run[qb], tmax[qb]);
+        float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        if (m_new == m_run[qb]) alpha = 1.f;           // (also when both are -inf)
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
+        m_run[qb] = m_new;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+      float pv[16];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(sc[qb][i] - m_use);
+        psum += pv[i];
+      }
+      l_run[qb] += psum;
+      pb[qb][0] = pack_bf16x8(pv);                     // rows 4g.. (block 0) and 16 + 4g.. (block 1)
+      pb[qb][1] = pack_bf16x8(pv + 8);                 // rows 32 + 4g.. and 48 + 4g..
+    }
+
+    // values: O^T[dim][query] += V^T P^T over two k-steps of 32 rows
+#pragma unroll
+    for (int kstep = 0; kstep < 2; ++kstep) {
+#pragma unroll
+      for (int d0 = 0; d0 < 8; d0 += 4) {
+        s16x4 lo[4], hi[4];
+        if (kstep == 0 && d0 == 0) pv_read4<kPfVP, 0>(vs, lo, hi);
+        if (kstep == 0 && d0 == 4) pv_read4<kPfVP, 4>(vs, lo, hi);
+        if (kstep == 1 && d0 == 0) pv_read4<kPfVP, 0>(vs + 32 * kPfVP, lo, hi);
+        if (kstep == 1 && d0 == 4) pv_read4<kPfVP, 4>(vs + 32 * kPfVP, lo, hi);
+#pragma unroll
+        for (int kd = 0; kd < 4; ++kd) {
+          const s16x8 a8 = {lo[kd][0], lo[kd][1], lo[kd][2], lo[kd][3], hi[kd][0], hi[kd][1], hi[kd][2], hi[kd][3]};
+          const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+          o[d0 + kd][0] = mfma_bf16_k32(av, pb[0][kstep], o[d0 + kd][0]);
+          o[d0 + kd][1] = mfma_bf16_k32(av, pb[1][kstep], o[d0 + kd][1]);
+        }
+      }
+    }
+  }
+
+  // ---- outputs of the wave's valid queries ----
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lsum = sum_over_groups(l_run[qb]);
+    const int i = i_w + 16 * qb + l16;
+    if (i >= n || i < 0) continue;
+    const int64_t qr = qrow0 + i;
+    const float inv = inv_or_zero(lsum);
+    char* dst = (char*)a.out + ((qr * H + h) * kDv + 4 * g) * 2;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const f32x4 x = o[db][qb] * inv;
+      uint2 u;
+      u.x = pack_bf16x2(x[0], x[1]);
+      u.y = pack_bf16x2(x[2], x[3]);
+      *(uint2*)(dst + 32 * db) = u;
+    }
+    if (a.lse && g == 0)
+      a.lse[qr * H + h] = lsum > 0.f ? (m_run[qb] + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------ launch
+hipError_t launch_prefill(int ct, const PrefillArgs& a, hipStream_t s) {
+  if (a.B == 0 || a.n_q == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_prefill_plan_kernel, dim3(1), dim3(256), 0, s, a);
+  const int64_t tiles = a.kv_rows / kPfRows;
+  if (ct == kFP8)
+    hipLaunchKernelGGL(mla_prefill_kv_kernel<kFP8>, dim3(a.H, (unsigned)tiles), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(mla_prefill_kv_kernel<kBF16>, dim3(a.H, (unsigned)tiles), dim3(256), 0, s, a);
+  const int64_t items = (int64_t)a.H * ((a.n_q + kPfQ - 1) / kPfQ + a.B);
+  const int64_t grid = (items + 7) / 8 * 8;
+  hipLaunchKernelGGL(mla_prefill_attn_kernel, dim3((unsigned)grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -358,6 +358,52 @@ mla_status_t mla_decode_noalloc(const mla_cache_t* cache, const int32_t* seq_len
                                 int32_t n_heads, float softmax_scale,
                                 void* out, float* lse, void* stream);
 
+/*
+ * mla_prefill -- causal multi-query (prefill) attention over the latent cache.
+ * The pages report prompt processing beside generation (DeepSeek-V2 reading
+ * card, "Evidence": over 100K prompt tokens/s on one 8-GPU node) but give no
+ * prefill formula; this call takes the plain reading. The queries of
+ * sequence b are query rows q_start[b] .. q_start[b+1]-1, its LAST
+ * n_b = q_start[b+1] - q_start[b] positions: query row q_start[b] + i sits at
+ * position p = seq_len[b] - n_b + i and attends cache rows 0..p of b (their
+ * rows must already be in the cache, e.g. from mla_append). Score, softmax
+ * and output are mla_decode's for a sequence of length p + 1 (discosf
+ * explainer, "long-context bottleneck"): o = sum_t softmax_t(s) (W_UV[h]^T c_t),
+ * s_t = softmax_scale * (q_nope . W_UK[h] c_t + q_pe . k_pe,t); it is computed
+ * in the unabsorbed form (each cached row up-projected once to per-head K and
+ * V, rounded to bf16 in the workspace).
+ *   cache          contiguous cache, BF16 or FP8_E4M3 (F32: MLA_ERR_UNSUPPORTED).
+ *   seq_len        device int32 [num_seqs], in [0, capacity].
+ *   q_start        device int32 [num_seqs + 1], non-decreasing from 0 to n_q,
+ *                  with n_b <= seq_len[b].
+ *   n_q            query rows (0: nothing runs).
+ *   max_kv_rows    host bound >= sum of seq_len; sizes the workspace.
+ *   q_nope, q_pe   device BF16 [n_q][n_heads][128], [n_q][n_heads][64].
+ *   w_uk, w_uv     device BF16 [n_heads][128][512], [n_heads][512][128].
+ *   act_dtype      MLA_DTYPE_BF16 (others: MLA_ERR_UNSUPPORTED).
+ *   n_heads        1..1024, any count.
+ *   out            device BF16 [n_q][n_heads][128]; lse device F32
+ *                  [n_q][n_heads] (natural log) or NULL.
+ *   workspace      device, 256-byte aligned, at least
+ *                  mla_prefill_workspace_size(num_seqs, n_heads, n_q,
+ *                  max_kv_rows) bytes (about 64 KB per cached row at 128
+ *                  heads); caller-owned, overwritten.
+ * Contract values on the device are clamped: lengths into [0, capacity],
+ * q_start into [0, n_q]; a query whose position would be negative gets o = 0
+ * and lse = -inf, and so do the queries of every sequence from the first
+ * whose rows pass max_kv_rows. MLA_DEBUG=1 reports those cases as
+ * MLA_ERR_INVALID_ARGUMENT. Errors: MLA_ERR_INVALID_ARGUMENT (null pointer,
+ * bad count or scale, misaligned workspace), MLA_ERR_UNSUPPORTED (dtypes,
+ * sizes past the limits), MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP.
+ */
+mla_status_t mla_prefill_workspace_size(int32_t num_seqs, int32_t n_heads, int64_t n_q,
+                                        int64_t max_kv_rows, size_t* bytes);
+mla_status_t mla_prefill(const mla_cache_t* cache, const int32_t* seq_len, const int32_t* q_start,
+                         int64_t n_q, int64_t max_kv_rows, const void* q_nope, const void* q_pe,
+                         const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
+                         int32_t n_heads, float softmax_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static English text for a status code (host); "unknown status" for any
  * other value. */
 const char* mla_status_string(mla_status_t status);

@@ -28,6 +28,7 @@ def test_exports_every_declared_symbol():
                           "mla_decode_attend_combine",
                           "mla_append_absorb", "mla_decode_noalloc", "mla_append_yarn",
                           "mla_yarn_softmax_factor", "mla_append_paged", "mla_decode_paged",
+                          "mla_prefill_workspace_size", "mla_prefill",
                           "mla_status_string", "mla_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -372,3 +373,75 @@ def test_paged_binding_checks_shapes():
     with pytest.raises((ValueError, TypeError)):
         mla.PagedLatentCache(rows=torch.zeros(128, 576, dtype=torch.uint8),
                              block_table=torch.zeros(2, 2, dtype=torch.int32), page_tokens=64).check()
+
+
+def test_prefill_validation():
+    """mla_prefill checks the cache, counts, dtypes, pointers and workspace
+    before any HIP call."""
+    E = mla
+
+    def pf(c, n_q=64, kv=1000, H=16, act=E.MLA_DTYPE_BF16, scale=0.07, ws=FAKE,
+           ws_bytes=1 << 40, null=None):
+        args = dict(seq_len=FAKE, q_start=FAKE, q_nope=FAKE, q_pe=FAKE, w_uk=FAKE, w_uv=FAKE,
+                    out=FAKE)
+        if null:
+            args[null] = None
+        return lib.mla_prefill(ctypes.byref(c) if c is not None else None, args["seq_len"],
+                               args["q_start"], n_q, kv, args["q_nope"], args["q_pe"],
+                               args["w_uk"], args["w_uv"], act, H, scale, args["out"], None, ws,
+                               ws_bytes, None)
+
+    assert pf(None) == E.MLA_ERR_INVALID_ARGUMENT
+    for null in ["seq_len", "q_start", "q_nope", "q_pe", "w_uk", "w_uv", "out"]:
+        assert pf(_cache(), null=null) == E.MLA_ERR_INVALID_ARGUMENT, null
+    assert pf(_cache(), ws=None) == E.MLA_ERR_INVALID_ARGUMENT
+    assert pf(_cache(), ws=FAKE + 64) == E.MLA_ERR_INVALID_ARGUMENT
+    assert pf(_cache(), H=0) == E.MLA_ERR_INVALID_ARGUMENT
+    assert pf(_cache(), H=2000) == E.MLA_ERR_UNSUPPORTED
+    assert pf(_cache(), n_q=-1) == E.MLA_ERR_INVALID_ARGUMENT
+    assert pf(_cache(), kv=-1) == E.MLA_ERR_INVALID_ARGUMENT
+    assert pf(_cache(), scale=0.0) == E.MLA_ERR_INVALID_ARGUMENT
+    assert pf(_cache(), scale=float("inf")) == E.MLA_ERR_INVALID_ARGUMENT
+    # f32 caches and non-bf16 activations are not supported
+    assert pf(_cache(dtype=E.MLA_DTYPE_F32)) == E.MLA_ERR_UNSUPPORTED
+    assert pf(_cache(), act=E.MLA_DTYPE_F32) == E.MLA_ERR_UNSUPPORTED
+    assert pf(_cache(), act=9) == E.MLA_ERR_INVALID_ARGUMENT
+    # any head count; the workspace grows with heads and rows
+    n1 = mla.mla_prefill_workspace_size(4, 1, 64, 1000)
+    n3 = mla.mla_prefill_workspace_size(4, 3, 64, 1000)
+    n3b = mla.mla_prefill_workspace_size(4, 3, 64, 5000)
+    assert 0 < n1 < n3 < n3b and n1 % 256 == 0
+    assert pf(_cache(), H=3, ws_bytes=n3 - 1) == E.MLA_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(mla.MlaError):
+        mla.mla_prefill_workspace_size(0, 16, 64, 1000)
+    assert lib.mla_prefill_workspace_size(4, 16, 64, 1000, None) == E.MLA_ERR_INVALID_ARGUMENT
+    # sizes past what the launches index
+    assert lib.mla_prefill_workspace_size(4, 16, 1 << 40, 1000, ctypes.byref(ctypes.c_size_t())) \
+        == E.MLA_ERR_UNSUPPORTED
+
+
+def test_prefill_binding_checks_shapes():
+    torch = pytest.importorskip("torch")
+    cache = mla.LatentCache(rows=torch.zeros(64, 576, dtype=torch.bfloat16),
+                            seq_start=torch.tensor([0, 32], dtype=torch.int64),
+                            seq_capacity=torch.tensor([32, 32], dtype=torch.int32))
+    H, n_q = 2, 5
+    ok = dict(seq_len=torch.zeros(2, dtype=torch.int32), q_start=torch.zeros(3, dtype=torch.int32),
+              q_nope=torch.zeros(n_q, H, 128, dtype=torch.bfloat16),
+              q_pe=torch.zeros(n_q, H, 64, dtype=torch.bfloat16),
+              w_uk=torch.zeros(H, 128, 512, dtype=torch.bfloat16),
+              w_uv=torch.zeros(H, 512, 128, dtype=torch.bfloat16),
+              out=torch.zeros(n_q, H, 128, dtype=torch.bfloat16))
+
+    def call(**over):
+        a = dict(ok, **over)
+        mla.mla_prefill(cache, a["seq_len"], a["q_start"], 64, a["q_nope"], a["q_pe"], a["w_uk"],
+                        a["w_uv"], 0.07, a["out"], None, torch.zeros(256, dtype=torch.uint8))
+
+    for bad in [dict(q_start=torch.zeros(2, dtype=torch.int32)),
+                dict(q_pe=torch.zeros(n_q, H, 32, dtype=torch.bfloat16)),
+                dict(out=torch.zeros(n_q, H, 128, dtype=torch.float32)),
+                dict(q_nope=torch.zeros(n_q, H, 128, dtype=torch.float32)),
+                dict(w_uv=torch.zeros(H, 128, 512, dtype=torch.bfloat16))]:
+        with pytest.raises((ValueError, TypeError)):
+            call(**bad)
