@@ -93,8 +93,7 @@ PrefillLayout prefill_layout(int B, int H, int64_t max_kv_rows) {
   l.qb_start = off; off = align256(off + sizeof(int32_t) * ((size_t)B + 1));
   l.lenc = off;     off = align256(off + sizeof(int32_t) * (size_t)B);
   l.nq = off;       off = align256(off + sizeof(int32_t) * (size_t)B);
-  l.kn = off;       off = align256(off + (size_t)H * l.kv_rows * 128 * 2);
-  l.kpe = off;      off = align256(off + (size_t)l.kv_rows * MLA_D_R * 2);
+  l.k = off;        off = align256(off + (size_t)H * l.kv_rows * (128 + MLA_D_R) * 2);
   l.v = off;        off = align256(off + (size_t)H * l.kv_rows * 128 * 2);
   l.total = off;
   return l;
@@ -659,8 +658,7 @@ mla_status_t mla_prefill(const mla_cache_t* cache, const int32_t* seq_len, const
   a.qb_start = (int32_t*)(ws + wl.qb_start);
   a.lenc = (int32_t*)(ws + wl.lenc);
   a.nq = (int32_t*)(ws + wl.nq);
-  a.kn = ws + wl.kn;
-  a.kpe = ws + wl.kpe;
+  a.k = ws + wl.k;
   a.v = ws + wl.v;
   const hipError_t e = launch_prefill(cache_type(cv.dtype), a, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;

@@ -222,6 +222,59 @@ __device__ __forceinline__ void lds_read_b128_x4(uint32_t addr, u32x4& r0, u32x4
       : "memory");
 }
 
+// Eight 16-byte LDS reads at compile-time offsets from one per-lane address,
+// completed inside the asm block (as lds_read_b128_x4).
+template <int O0, int O1, int O2, int O3, int O4, int O5, int O6, int O7>
+__device__ __forceinline__ void lds_read_b128_x8(uint32_t addr, u32x4* r) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%9\n"
+      "ds_read_b128 %1, %8 offset:%10\n"
+      "ds_read_b128 %2, %8 offset:%11\n"
+      "ds_read_b128 %3, %8 offset:%12\n"
+      "ds_read_b128 %4, %8 offset:%13\n"
+      "ds_read_b128 %5, %8 offset:%14\n"
+      "ds_read_b128 %6, %8 offset:%15\n"
+      "ds_read_b128 %7, %8 offset:%16\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(addr), "i"(O0), "i"(O1), "i"(O2), "i"(O3), "i"(O4), "i"(O5), "i"(O6), "i"(O7)
+      : "memory");
+}
+
+// Sixteen transposing reads (ds_read_b64_tr_b16) at offsets O(i) = A + B*(i/2)
+// + C*(i%2) from one per-lane address, completed inside the asm block: r[2j]
+// at A + B*j, r[2j+1] at A + B*j + C.
+template <int A, int B, int C>
+__device__ __forceinline__ void lds_tr16_x16(uint32_t addr, s16x4* r) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%17\n"
+      "ds_read_b64_tr_b16 %1, %16 offset:%18\n"
+      "ds_read_b64_tr_b16 %2, %16 offset:%19\n"
+      "ds_read_b64_tr_b16 %3, %16 offset:%20\n"
+      "ds_read_b64_tr_b16 %4, %16 offset:%21\n"
+      "ds_read_b64_tr_b16 %5, %16 offset:%22\n"
+      "ds_read_b64_tr_b16 %6, %16 offset:%23\n"
+      "ds_read_b64_tr_b16 %7, %16 offset:%24\n"
+      "ds_read_b64_tr_b16 %8, %16 offset:%25\n"
+      "ds_read_b64_tr_b16 %9, %16 offset:%26\n"
+      "ds_read_b64_tr_b16 %10, %16 offset:%27\n"
+      "ds_read_b64_tr_b16 %11, %16 offset:%28\n"
+      "ds_read_b64_tr_b16 %12, %16 offset:%29\n"
+      "ds_read_b64_tr_b16 %13, %16 offset:%30\n"
+      "ds_read_b64_tr_b16 %14, %16 offset:%31\n"
+      "ds_read_b64_tr_b16 %15, %16 offset:%32\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(addr), "i"(A), "i"(A + C), "i"(A + B), "i"(A + B + C), "i"(A + 2 * B),
+        "i"(A + 2 * B + C), "i"(A + 3 * B), "i"(A + 3 * B + C), "i"(A + 4 * B),
+        "i"(A + 4 * B + C), "i"(A + 5 * B), "i"(A + 5 * B + C), "i"(A + 6 * B),
+        "i"(A + 6 * B + C), "i"(A + 7 * B), "i"(A + 7 * B + C)
+      : "memory");
+}
+
 // Eight e4m3fn codes (bytes 0..7 of v) as eight bf16 values, in order; every
 // e4m3fn value is exact in bf16 and the unit scale leaves it unchanged.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint2 v) {

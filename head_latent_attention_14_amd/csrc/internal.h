@@ -145,8 +145,8 @@ hipError_t launch_append_absorb(const AppendArgs& a, const DecodePlan& plan, con
 // ---------------------------------------------------------------- prefill
 // Causal multi-query attention: the queries of sequence b are its last n_b
 // positions. Three launches: a one-workgroup plan (prefix sums), the
-// up-projection of every cached row to per-head K (128, plus the shared
-// 64-wide RoPE key) and V (128), and the attention over query blocks.
+// up-projection of every cached row to per-head K (128, followed by a copy of
+// the row's 64-wide RoPE key) and V (128), and the attention over query blocks.
 constexpr int kPfRows = 128;      // cached rows per up-projection workgroup (and K/V padding)
 constexpr int kPfQ = 256;         // queries per attention workgroup (8 waves of 32)
 constexpr int kPfKV = 64;         // cached rows per attention step
@@ -157,8 +157,7 @@ struct PrefillLayout {
   size_t qb_start;   // int32 [B+1] first query block of each sequence
   size_t lenc;       // int32 [B] length clamped to [0, capacity] (0: not served)
   size_t nq;         // int32 [B] queries of each sequence (clamped to [0, length])
-  size_t kn;         // bf16 [H][kv_rows][128] K without the RoPE part
-  size_t kpe;        // bf16 [kv_rows][64] the RoPE key (shared by the heads)
+  size_t k;          // bf16 [H][kv_rows][192] K: 128 up-projected dims, then the RoPE key
   size_t v;          // bf16 [H][kv_rows][128]
   size_t total;
 };
@@ -187,8 +186,7 @@ struct PrefillArgs {
   int32_t* qb_start;
   int32_t* lenc;
   int32_t* nq;
-  void* kn;
-  void* kpe;
+  void* k;
   void* v;
 };
 hipError_t launch_prefill(int cache_type, const PrefillArgs& a, hipStream_t s);

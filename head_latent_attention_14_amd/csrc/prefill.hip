@@ -13,10 +13,10 @@
 // attention time). Three launches:
 //   plan   one workgroup: per-sequence prefix sums of the padded K/V rows and
 //          of the query blocks;
-//   kv     per (head, 128 cached rows): K[h] (128 dims) and V[h] (128 dims) as
-//          bf16 into the workspace, on bf16 MFMA; head 0 also copies the shared
-//          RoPE key (fp8 caches: codes widened exactly, scales applied to the
-//          fp32 products);
+//   kv     per (head, 128 cached rows): K[h] (128 dims, then a copy of the
+//          row's RoPE key, so that a K row is one 384-byte run) and V[h] (128
+//          dims) as bf16 into the workspace, on bf16 MFMA (fp8 caches: codes
+//          widened exactly, scales applied to the fp32 products);
 //   attn   per (head, 256 queries): 8 waves of 32 queries stream 64-row K/V
 //          blocks through a two-stage LDS ring (asynchronous global->LDS
 //          copies), S^T = K Q^T and O^T += V^T P^T on 16x16x32 bf16 MFMA with
@@ -229,7 +229,9 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
 
   // ---- epilogue: lane holds D^T[dim 16 ob + 4g + r][row 16 rb + l16]; rows
   // past the sequence are written as zeros ----
-  char* dst_base = (char*)(is_k ? a.kn : a.v) + ((int64_t)h * a.kv_rows + r0) * 128 * 2;
+  constexpr int KW = 128 + kDr;                        // K row width (elements)
+  const int dst_w = is_k ? KW : 128;
+  char* dst_base = (char*)(is_k ? a.k : a.v) + ((int64_t)h * a.kv_rows + r0) * dst_w * 2;
 #pragma unroll
   for (int rb = 0; rb < 8; ++rb) {
     const int r = 16 * rb + l16;
@@ -241,14 +243,14 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
       uint2 u;
       u.x = pack_bf16x2(x[0], x[1]);
       u.y = pack_bf16x2(x[2], x[3]);
-      *(uint2*)(dst_base + ((int64_t)r * 128 + nbase + 16 * ob + 4 * g) * 2) = u;
+      *(uint2*)(dst_base + ((int64_t)r * dst_w + nbase + 16 * ob + 4 * g) * 2) = u;
     }
   }
 
-  // ---- head 0: the shared RoPE key of the 128 rows (bf16; fp8 codes times
-  // the row scale, rounded once) ----
-  if (h == 0) {
-    char* kpe = (char*)a.kpe + r0 * kDr * 2;
+  // ---- the RoPE key of the 128 rows after K[h]'s 128 dims (bf16; fp8 codes
+  // times the row scale, rounded once) ----
+  {
+    char* kpe = (char*)a.k + ((int64_t)h * a.kv_rows + r0) * KW * 2 + 128 * 2;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = tid + 256 * j;                     // 8-element piece i of the 128 x 64 block
@@ -276,7 +278,7 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
           out = *(const u32x4*)(rows + (crow0 + r) * RB + kDc * 2 + 16 * p);
         }
       }
-      *(u32x4*)(kpe + (r * kDr + 8 * p) * 2) = out;
+      *(u32x4*)(kpe + (r * KW + 8 * p) * 2) = out;
     }
   }
 }
@@ -298,10 +300,12 @@ constexpr int kPfVSlots = kPfVP / 16;                  // 17
 constexpr int kPfKCopies = kPfKV * kPfKSlots / 64;     // 25 one-kilobyte copies
 constexpr int kPfVCopies = kPfKV * kPfVSlots / 64;     // 17
 constexpr int kPfStage = (kPfKCopies + kPfVCopies) * 1024;
+constexpr int kPfStages = 3;                           // LDS ring depth (129 KB)
 
 __global__ void __launch_bounds__(512) mla_prefill_attn_kernel(PrefillArgs a) {
   static_assert(kPfKV * kPfKSlots % 64 == 0 && kPfKV * kPfVSlots % 64 == 0, "whole copies");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kPfStage];
+  constexpr int NS = kPfStages;
+  __shared__ __attribute__((aligned(1024))) char smem[NS * kPfStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -354,33 +358,37 @@ __global__ void __launch_bounds__(512) mla_prefill_attn_kernel(PrefillArgs a) {
     for (int kk = 0; kk < 6; ++kk) asm volatile("" : "+v"(q[qb][kk]));
 
   // ---- copies of K/V block `blk` into stage `st`: copy c of the 42 goes to
-  // wave c % 8 ----
-  const char* kn = (const char*)a.kn + (int64_t)h * a.kv_rows * 256;
-  const char* vv = (const char*)a.v + (int64_t)h * a.kv_rows * 256;
-  const char* kpe = (const char*)a.kpe;
+  // wave c % 8; a lane's byte offset in the block's K rows (384 B) or V rows
+  // (256 B) is fixed per copy, so it is computed once ----
+  constexpr int kCopies = kPfKCopies + kPfVCopies;
+  constexpr int kMaxPer = (kCopies + 7) / 8;
+  uint32_t coff[kMaxPer];
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int c = wave + 8 * i;
+    const int ln = lane;
+    if (c < kPfKCopies) {
+      const int sl = 64 * c + ln, r = sl / kPfKSlots;
+      const int ch = sl - r * kPfKSlots;
+      coff[i] = (uint32_t)(r * 384 + 16 * (ch < 23 ? ch : 23));
+    } else {
+      const int sl = 64 * (c - kPfKCopies) + ln, r = sl / kPfVSlots;
+      const int ch = sl - r * kPfVSlots;
+      coff[i] = (uint32_t)(r * 256 + 16 * (ch < 15 ? ch : 15));
+    }
+  }
+  const char* kbase = (const char*)a.k + (int64_t)h * a.kv_rows * 384;
+  const char* vbase = (const char*)a.v + (int64_t)h * a.kv_rows * 256;
   auto issue = [&](int blk, int st) {
     const int64_t row0 = kv0_row + (int64_t)blk * kPfKV;
+    const auto rk = make_rsrc(kbase + row0 * 384, kPfKV * 384);
+    const auto rv = make_rsrc(vbase + row0 * 256, kPfKV * 256);
     char* stage = smem + st * kPfStage;
 #pragma unroll
-    for (int c0 = 0; c0 < kPfKCopies + kPfVCopies; c0 += 8) {
-      const int c = c0 + wave;
-      if (c >= kPfKCopies + kPfVCopies) continue;
-      const int ln = TileCopy<kBF16, 1>::lane_id();
-      const char* src;
-      if (c < kPfKCopies) {
-        const int s = 64 * c + ln;
-        const int r = s / kPfKSlots;
-        int ch = s - r * kPfKSlots;
-        ch = ch < 24 ? ch : 23;
-        src = ch < 16 ? kn + ((row0 + r) * 128 + 8 * ch) * 2 : kpe + ((row0 + r) * kDr + 8 * (ch - 16)) * 2;
-      } else {
-        const int s = 64 * (c - kPfKCopies) + ln;
-        const int r = s / kPfVSlots;
-        int ch = s - r * kPfVSlots;
-        ch = ch < 16 ? ch : 15;
-        src = vv + ((row0 + r) * 128 + 8 * ch) * 2;
-      }
-      async_copy16(src, stage + c * 1024);
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int c = wave + 8 * i;
+      if (c < kPfKCopies) buffer_copy16(rk, coff[i], stage + c * 1024);
+      else if (c < kCopies) buffer_copy16(rv, coff[i], stage + c * 1024);
     }
   };
 
@@ -393,14 +401,20 @@ __global__ void __launch_bounds__(512) mla_prefill_attn_kernel(PrefillArgs a) {
   const uint32_t k_lane = (uint32_t)(l16 * kPfKP + 16 * g);
   const uint32_t v_lane = (uint32_t)((4 * g + (l16 >> 2)) * kPfVP + 8 * (l16 & 3));
 
-  if (nblk > 0) issue(0, 0);
+  // this wave's copies per block: copies wave, wave + 8, ... of the 42
+  const bool six = wave < kCopies % 8;                 // (kCopies + 7) / 8 copies, else one fewer
+  for (int i = 0; i < NS - 1 && i < nblk; ++i) issue(i, i);
   for (int blk = 0; blk < nblk; ++blk) {
-    wait_vmcnt<0>();
-    barrier_lds();                                     // block blk visible; the other stage free
-    if (blk + 1 < nblk) issue(blk + 1, (blk + 1) & 1);
+    // block blk's copies have landed: the ones of blocks blk+1 .. blk+NS-2
+    // already issued may stay in flight
+    const int younger = (nblk - 1 - blk < NS - 2) ? nblk - 1 - blk : NS - 2;
+    if (six) wait_tiles<(kCopies + 7) / 8, NS - 2>(younger);
+    else wait_tiles<kCopies / 8, NS - 2>(younger);
+    barrier_lds();                                     // block blk visible; stage (blk - 1) % NS free
+    if (blk + NS - 1 < nblk) issue(blk + NS - 1, (blk + NS - 1) % NS);
     const int kv0 = blk * kPfKV;
     if (kv0 > p_w0 + 31) continue;                     // every query of this wave is earlier
-    const char* stage = smem + (blk & 1) * kPfStage;
+    const char* stage = smem + (blk % NS) * kPfStage;
     const uint32_t ks = (uint32_t)(size_t)stage + k_lane;
     const uint32_t vs = (uint32_t)(size_t)(stage + kPfKCopies * 1024) + v_lane;
 
@@ -408,21 +422,22 @@ __global__ void __launch_bounds__(512) mla_prefill_attn_kernel(PrefillArgs a) {
     f32x4 acc[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) acc[kb][0] = acc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // two k-steps (eight 16-byte reads) per wait
 #pragma unroll
-    for (int kk = 0; kk < 6; ++kk) {
-      u32x4 r4[4];
-      if (kk == 0) lds_read_b128_x4<0, 16 * kPfKP, 32 * kPfKP, 48 * kPfKP>(ks, r4[0], r4[1], r4[2], r4[3]);
-      if (kk == 1) lds_read_b128_x4<64, 16 * kPfKP + 64, 32 * kPfKP + 64, 48 * kPfKP + 64>(ks, r4[0], r4[1], r4[2], r4[3]);
-      if (kk == 2) lds_read_b128_x4<128, 16 * kPfKP + 128, 32 * kPfKP + 128, 48 * kPfKP + 128>(ks, r4[0], r4[1], r4[2], r4[3]);
-      if (kk == 3) lds_read_b128_x4<192, 16 * kPfKP + 192, 32 * kPfKP + 192, 48 * kPfKP + 192>(ks, r4[0], r4[1], r4[2], r4[3]);
-      if (kk == 4) lds_read_b128_x4<256, 16 * kPfKP + 256, 32 * kPfKP + 256, 48 * kPfKP + 256>(ks, r4[0], r4[1], r4[2], r4[3]);
-      if (kk == 5) lds_read_b128_x4<320, 16 * kPfKP + 320, 32 * kPfKP + 320, 48 * kPfKP + 320>(ks, r4[0], r4[1], r4[2], r4[3]);
+    for (int k2 = 0; k2 < 3; ++k2) {
+      u32x4 r8[8];
+      constexpr int R = 16 * kPfKP;
+      if (k2 == 0) lds_read_b128_x8<0, R, 2 * R, 3 * R, 64, R + 64, 2 * R + 64, 3 * R + 64>(ks, r8);
+      if (k2 == 1) lds_read_b128_x8<128, R + 128, 2 * R + 128, 3 * R + 128, 192, R + 192, 2 * R + 192, 3 * R + 192>(ks, r8);
+      if (k2 == 2) lds_read_b128_x8<256, R + 256, 2 * R + 256, 3 * R + 256, 320, R + 320, 2 * R + 320, 3 * R + 320>(ks, r8);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 a8 = __builtin_bit_cast(bf16x8, r4[kb]);
-        acc[kb][0] = mfma_bf16_k32(a8, q[0][kk], acc[kb][0]);
-        acc[kb][1] = mfma_bf16_k32(a8, q[1][kk], acc[kb][1]);
-      }
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 a8 = __builtin_bit_cast(bf16x8, r8[4 * h2 + kb]);
+          acc[kb][0] = mfma_bf16_k32(a8, q[0][2 * k2 + h2], acc[kb][0]);
+          acc[kb][1] = mfma_bf16_k32(a8, q[1][2 * k2 + h2], acc[kb][1]);
+        }
     }
 
     // online softmax per query (log2 domain, lazy rescale as in decode)
@@ -433,19 +448,27 @@ __global__ void __launch_bounds__(512) mla_prefill_attn_kernel(PrefillArgs a) {
     float tmax[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int pq = p_w0 + 16 * qb + l16;             // this lane's query position
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = acc[kb][qb][r] * sl2;
-          if (diag && kv0 + 16 * kb + 4 * g + r > pq) x = -INFINITY;
-          sc[qb][4 * kb + r] = x;
-        }
+        for (int r = 0; r < 4; ++r) sc[qb][4 * kb + r] = acc[kb][qb][r];   // unscaled: the scale enters the exponent
+    }
+    if (diag) {                                        // (a uniform branch: only diagonal blocks mask)
+      const int lim = p_w0 + l16 - kv0 - 4 * g;        // row 16 kb + r is visible to query 16 qb + l16
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)                   //   when 16 kb + r <= lim + 16 qb
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kb + r > lim + 16 * qb) sc[qb][4 * kb + r] = -INFINITY;
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
       float t = sc[qb][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) t = __builtin_fmaxf(t, sc[qb][i]);
-      tmax[qb] = max_over_groups(t);
+      tmax[qb] = max_over_groups(t) * sl2;             // (sl2 > 0: the max commutes)
       grow = grow || (tmax[qb] > m_run[qb] + kSlack);
     }
     if (__any(grow)) {
@@ -467,7 +490,7 @@ __global__ void __launch_bounds__(512) mla_prefill_attn_kernel(PrefillArgs a) {
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(sc[qb][i] - m_use);
+        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][i], sl2, -m_use));
         psum += pv[i];
       }
       l_run[qb] += psum;
@@ -475,23 +498,20 @@ __global__ void __launch_bounds__(512) mla_prefill_attn_kernel(PrefillArgs a) {
       pb[qb][1] = pack_bf16x8(pv + 8);                 // rows 32 + 4g.. and 48 + 4g..
     }
 
-    // values: O^T[dim][query] += V^T P^T over two k-steps of 32 rows
+    // values: O^T[dim][query] += V^T P^T over two k-steps of 32 rows, all
+    // eight dim blocks' operands (sixteen transposing reads) per wait
 #pragma unroll
     for (int kstep = 0; kstep < 2; ++kstep) {
+      s16x4 rr[16];                                    // [2 db]: rows 0..15, [2 db + 1]: rows 16..31
+      if (kstep == 0) lds_tr16_x16<0, 32, 16 * kPfVP>(vs, rr);
+      else lds_tr16_x16<32 * kPfVP, 32, 16 * kPfVP>(vs, rr);
 #pragma unroll
-      for (int d0 = 0; d0 < 8; d0 += 4) {
-        s16x4 lo[4], hi[4];
-        if (kstep == 0 && d0 == 0) pv_read4<kPfVP, 0>(vs, lo, hi);
-        if (kstep == 0 && d0 == 4) pv_read4<kPfVP, 4>(vs, lo, hi);
-        if (kstep == 1 && d0 == 0) pv_read4<kPfVP, 0>(vs + 32 * kPfVP, lo, hi);
-        if (kstep == 1 && d0 == 4) pv_read4<kPfVP, 4>(vs + 32 * kPfVP, lo, hi);
-#pragma unroll
-        for (int kd = 0; kd < 4; ++kd) {
-          const s16x8 a8 = {lo[kd][0], lo[kd][1], lo[kd][2], lo[kd][3], hi[kd][0], hi[kd][1], hi[kd][2], hi[kd][3]};
-          const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
-          o[d0 + kd][0] = mfma_bf16_k32(av, pb[0][kstep], o[d0 + kd][0]);
-          o[d0 + kd][1] = mfma_bf16_k32(av, pb[1][kstep], o[d0 + kd][1]);
-        }
+      for (int db = 0; db < 8; ++db) {
+        const s16x4 lo = rr[2 * db], hi = rr[2 * db + 1];
+        const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+        o[db][0] = mfma_bf16_k32(av, pb[0][kstep], o[db][0]);
+        o[db][1] = mfma_bf16_k32(av, pb[1][kstep], o[db][1]);
       }
     }
   }
