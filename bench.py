@@ -9,6 +9,12 @@ DeepSeek-V2-Lite shape) first write one new latent row per sequence
 and seeded; several replicas of the cache and weights rotate so every step
 reads its cache from HBM, not from the 256 MB Infinity Cache.
 
+Prefill (causal multi-query attention, mla_prefill) is measured on its own
+workloads after the decode ones and reported under "prefill": prompt tokens/s
+and the matrix TFLOP/s of a whole call (up-projection of every cached row to
+per-head K/V, plus attention over the (query, row) pairs a query may see)
+against the bf16 MFMA peak, with a sampled parity check against the oracle.
+
 The headline workload is the DeepSeek-V2-shaped decode (B=32, H=128,
 L ~ U[2048, 8192], bf16 cache). The DeepSeek-V2-Lite step (B=64, H=16, with
 append), the 128K-token decode (B=4, H=128) and the fp8-cache decode (B=128,
@@ -46,6 +52,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # dense, MI355X
 HEADLINE = "v2_bf16"
 OTHERS = ["v2lite_bf16", "long_bf16", "fp8_cache"]
+PREFILLS = ["prefill_bf16", "prefill_chunk_fp8"]
 # every source that decides what the attention launch reads and writes: the
 # kernels, the work split (api.cpp, gemm_tile.h) and the shared headers
 KERNEL_SOURCES = sorted(glob.glob(os.path.join(ROOT, "head_latent_attention_14_amd", "csrc", "*")))
@@ -84,6 +91,8 @@ def parse():
     ap.add_argument("--others", default=",".join(OTHERS),
                     help="comma-separated workloads measured first and reported under "
                          "'workloads' (empty: none)")
+    ap.add_argument("--prefill", default=",".join(PREFILLS),
+                    help="comma-separated prefill workloads reported under 'prefill' (empty: none)")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 2x the MALL")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed steps for this long before the warm-up (clock ramp)")
@@ -351,6 +360,68 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
                 attn_ms=attn_ms, clock_mhz=clock, parity=par, append_us=append_us)
 
 
+def measure_prefill(mla, W, torch, name: str, steps: int, warmup: int) -> dict:
+    """One mla_prefill call per step over a seeded prefill problem (inputs in
+    HBM); steps timed between two events, plus a sampled parity check."""
+    wl = W.PREFILL_WORKLOADS[name]
+    p = W.make_prefill_problem(wl)
+    dev = torch.device("cuda")
+    scale = p.row_scale.to(dev) if p.row_scale is not None else None
+    cache = mla.LatentCache(rows=p.rows.to(dev), seq_start=torch.from_numpy(p.seq_start).to(dev),
+                            seq_capacity=torch.from_numpy(p.seq_capacity).to(dev), row_scale=scale)
+    seq_len = torch.from_numpy(p.seq_len).to(dev)
+    q_start = torch.from_numpy(p.q_start).to(dev)
+    q_nope, q_pe = p.q_nope.to(dev), p.q_pe.to(dev)
+    w_uk, w_uv = p.w_uk.to(dev), p.w_uv.to(dev)
+    n_q, H = p.q_nope.shape[:2]
+    out = torch.empty(n_q, H, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(n_q, H, dtype=torch.float32, device=dev)
+    ws = mla.alloc_prefill_workspace(cache, H, n_q, p.T)
+    sm = 1.0 / math.sqrt(192.0)
+
+    def call():
+        mla.mla_prefill(cache, seq_len, q_start, p.T, q_nope, q_pe, w_uk, w_uv, sm, out, lse, ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ms = max(e0.elapsed_time(e1) / steps, wall)
+    fl = W.prefill_flops(p)
+    # parity: every query of the last sequence, heads 0 and H-1
+    from oracle.problem import PrefillOracleView
+    b = len(p.seq_len) - 1
+    q0, q1 = int(p.q_start[b]), int(p.q_start[b + 1])
+    heads = [0, H - 1]
+    ro, _ = PrefillOracleView(p).prefill(heads)
+    got = out[q0:q1].double().cpu().numpy()[:, heads]
+    ref = ro[q0:q1][:, heads]
+    err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    tfl = fl["total"] / (ms * 1e-3) / 1e12
+    return {
+        "workload": (f"{name}: causal multi-query prefill, B={len(p.seq_len)}, H={H}, "
+                     f"L~U[{wl.lo},{wl.hi}], "
+                     + ("every position a query" if wl.chunk == 0 else f"last {wl.chunk} positions queries")
+                     + f", {wl.cache} cache"),
+        "ms_per_call": round(ms, 4),
+        "prompt_tokens_per_s": round(n_q / (ms * 1e-3), 1),
+        "n_q": n_q, "T": p.T,
+        "tflops": round(tfl, 2),
+        "mfma_dtype": "bf16",
+        "mfma_frac": round(tfl / MFMA_PEAK_TFLOPS["bf16"], 4),
+        "matrix_flops": {"kv_up_projection": fl["kv"], "attention": fl["attn"]},
+        "parity": {"rel_l2": err, "bound": 2e-2 if wl.cache == "bf16" else 4e-2,
+                   "sample": f"every query of sequence {b}, heads {heads}"},
+    }
+
+
 def describe(wl, m) -> str:
     return (f"{wl.name}: MLA decode step, {'append 1 token/seq + ' if wl.append else ''}"
             f"decode, B={m['B']}, H={m['H']}, L~U[{wl.lo},{wl.hi}], {wl.cache} latent cache")
@@ -414,6 +485,12 @@ def main():
         print(f"# measured {name}: {s['ms'] * 1e3:.2f} us/step, attention "
               f"{s['attn_ms'] * 1e3:.2f} us", file=sys.stderr, flush=True)
 
+    prefill = {}
+    for name in [w for w in args.prefill.split(",") if w]:
+        prefill[name] = measure_prefill(mla, W, torch, name, args.steps, args.warmup)
+        print(f"# measured {name}: {prefill[name]['ms_per_call'] * 1e3:.1f} us/call",
+              file=sys.stderr, flush=True)
+
     m = measure(mla, W, torch, args.workload, args.steps, args.warmup, args.replicas,
                 parity=not args.no_parity, settle_ms=args.settle_ms)
     wl, ms = m["wl"], m["ms"]
@@ -447,6 +524,7 @@ def main():
         "roofline": roofline(m, args.workload),
         "parity": m["parity"],
         "workloads": blocks,
+        "prefill": prefill,
     }
     if not args.no_cpu_baseline:
         p = W.make_problem(wl)

@@ -95,7 +95,8 @@ __device__ __forceinline__ int search_seq(const T* arr, int B, int64_t x) {
 }
 
 // ------------------------------------------------------------------ kv
-// One workgroup per (head h = blockIdx.x, 128 packed rows = blockIdx.y).
+// One workgroup per (128 packed rows = blockIdx.x, head h = blockIdx.y): the
+// row tiles of one head run next to each other and share its weights in L2.
 // D^T = W X^T with A = the weight rows (output dims, 16 per block) and B =
 // the latent rows (16 per block), so a lane ends with four consecutive
 // output dims of one row (one 8-byte store). Wave w computes output dims
@@ -122,9 +123,9 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
   const int wave = uniform(tid >> 6);
   const int l16 = lane & 15;
   const int g = lane >> 4;
-  const int h = blockIdx.x;
+  const int h = blockIdx.y;
   const int H = a.H;
-  const int64_t r0 = (int64_t)blockIdx.y * kPfRows;
+  const int64_t r0 = (int64_t)blockIdx.x * kPfRows;
   if (r0 >= ld_const(a.kv_row0, a.B)) return;
   const int b = search_seq(a.kv_row0, a.B, r0);
   const int L = ld_const(a.lenc, b);
@@ -544,9 +545,9 @@ hipError_t launch_prefill(int ct, const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(mla_prefill_plan_kernel, dim3(1), dim3(256), 0, s, a);
   const int64_t tiles = a.kv_rows / kPfRows;
   if (ct == kFP8)
-    hipLaunchKernelGGL(mla_prefill_kv_kernel<kFP8>, dim3(a.H, (unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mla_prefill_kv_kernel<kFP8>, dim3((unsigned)tiles, a.H), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(mla_prefill_kv_kernel<kBF16>, dim3(a.H, (unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mla_prefill_kv_kernel<kBF16>, dim3((unsigned)tiles, a.H), dim3(256), 0, s, a);
   const int64_t items = (int64_t)a.H * ((a.n_q + kPfQ - 1) / kPfQ + a.B);
   const int64_t grid = (items + 7) / 8 * 8;
   hipLaunchKernelGGL(mla_prefill_attn_kernel, dim3((unsigned)grid), dim3(512), 0, s, a);
