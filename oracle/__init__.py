@@ -28,9 +28,11 @@ Readings where the pages are silent are listed in the package's modules next
 to the code that takes them.
 """
 from .numerics import (round_bf16, round_f32, e4m3_decode, e4m3_encode,
-                       E4M3_MAX, e4m3_value_table)
+                       E4M3_MAX, e4m3_value_table, e2m3_decode, e2m3_encode, e2m3_value_table,
+                       E2M3_MAX, MX_BLOCK, mx_block_exponent, pack6, unpack6)
 from .mla import (D_C, D_R, D_ROW, D_NOPE, D_V, softmax_scale, rope_inv_freq,
                   yarn_inv_freq, yarn_softmax_factor, rope_rotate, paged_rows, append_rows_exact, quantize_rows,
+                  fp6_rows,
                   decode_head, decode_problem, decode_sampled, attention_weights,
                   prefill_head, prefill_positions, prefill_problem,
                   mla_cache_elements_per_token, mha_cache_elements_per_token,

@@ -48,6 +48,15 @@ Readings taken where the pages are silent (each listed in the design notes):
       block_table[b][t // P] * P + t % P; rows are stored as in the contiguous
       cache, so attention over a paged cache equals attention over the
       sequence's rows gathered in token order.
+  R11 the ~6-bit cache [reading card, "Method adaptation": elements quantised
+      to about 6 bits on average; no format named]: OCP microscaling FP6 --
+      e2m3 elements (sign, 2-bit exponent with bias 1, 3-bit mantissa, largest
+      7.5) in blocks of 32 consecutive elements of a row, each block with one
+      e8m0 scale 2^X, X = floor(log2(max|block|)) - 2 (so the block's largest
+      element lies in [4, 8) before rounding), elements rounded to nearest
+      even with saturation at 7.5; 18 blocks per 576-wide row, 6.25 bits per
+      element. Codes are packed little-endian: element i of a row takes bits
+      6i .. 6i+5 of its 432-byte bit string.
   R10 prefill / multi-query attention [the pages measure prompt processing
       beside generation -- over 100K prompt tokens/s on one 8-GPU node
       (DeepSeek-V2 reading card, "Evidence"; discosf explainer, throughput
@@ -63,7 +72,8 @@ from typing import Iterable, Optional, Sequence, Tuple
 
 import numpy as np
 
-from .numerics import round_bf16, round_f32, e4m3_decode, e4m3_encode, E4M3_MAX
+from .numerics import (round_bf16, round_f32, e4m3_decode, e4m3_encode, E4M3_MAX,
+                       e2m3_decode, e2m3_encode, mx_block_exponent, pack6, unpack6, MX_BLOCK)
 
 D_C = 512
 D_R = 64
@@ -191,7 +201,25 @@ def quantize_rows(rows: np.ndarray, dtype: str) -> Tuple[np.ndarray, Optional[np
         codes = e4m3_encode(rows / scale[:, None])
         deq = e4m3_decode(codes) * scale[:, None]
         return codes, scale, deq
+    if dtype == "fp6":
+        # R11: blocks of 32 along the row, one shared power-of-two exponent each
+        n = rows.shape[0]
+        blk = rows.reshape(n, -1, MX_BLOCK)
+        x = mx_block_exponent(np.max(np.abs(blk), axis=2))          # [n, 18]
+        codes = e2m3_encode(blk / np.ldexp(1.0, x)[..., None])         # exact scaling
+        deq = (e2m3_decode(codes) * np.ldexp(1.0, x)[..., None]).reshape(n, -1)
+        return pack6(codes.reshape(n, -1)), (x + 127).astype(np.uint8), deq
     raise ValueError(dtype)
+
+
+def fp6_rows(packed: np.ndarray, scale_codes: np.ndarray) -> np.ndarray:
+    """fp64 values of fp6 cache rows (R11): e2m3 codes unpacked from the
+    row's bit string, times 2^(scale code - 127) of their block of 32."""
+    codes = unpack6(packed)
+    n = codes.shape[0]
+    blk = e2m3_decode(codes).reshape(n, -1, MX_BLOCK)
+    x = np.asarray(scale_codes, dtype=np.int64) - 127
+    return (blk * np.ldexp(1.0, x)[..., None]).reshape(n, -1)
 
 
 # ----------------------------------------------------------------------------

@@ -52,6 +52,8 @@ class OracleView:
             codes = sl.numpy()
             sc = p.row_scale[s:s + L].to(torch.float64).numpy()
             out = e4m3_decode(codes) * sc[:, None]
+        elif self.dtype == "fp6":
+            out = mla.fp6_rows(sl.numpy(), p.row_scale[s:s + L].numpy())
         else:
             out = sl.to(torch.float64).numpy()
         for r, v in self.appended.items():

@@ -56,8 +56,13 @@ WORKLOADS = {
         Workload("v2_bf16", 2, B=32, H=128, lo=2048, hi=8192, cache="bf16", act="bf16"),
         Workload("long_bf16", 3, B=4, H=128, lo=131072, hi=131072, cache="bf16", act="bf16"),
         Workload("fp8_cache", 4, B=128, H=128, lo=512, hi=4096, cache="fp8", act="bf16"),
+        # the ~6-bit cache: e2m3 codes in blocks of 32 with one e8m0 scale each
+        Workload("fp6_cache", 5, B=128, H=128, lo=512, hi=4096, cache="fp6", act="bf16"),
     ]
 }
+# bytes of a stored row (and of its scale record) per cache format
+ROW_BYTES = {"f32": 2304, "bf16": 1152, "fp8": 576, "fp6": 432}
+FP6_SCALES_PER_ROW = 18
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
@@ -138,15 +143,22 @@ def make_problem(wl: Workload, seed: Optional[int] = None, *, B: Optional[int] =
         seq_start[1:] = np.cumsum(cap)[:-1]
     total_rows = int(cap.sum())
 
-    z = _normal(rng, (total_rows, D_ROW))
     row_scale = None
-    if wl.cache == "fp8":
-        rows = fp8_codes_from_normal(z)
-        u = rng.uniform(-0.5, 0.5, size=total_rows)
-        row_scale = torch.from_numpy((np.exp(u) / FP8_SPREAD).astype(np.float32))
+    if wl.cache == "fp6":
+        # any byte string is a valid packed row of 6-bit codes; block scale
+        # codes 120..127 (2^-7 .. 1)
+        rows = torch.from_numpy(rng.integers(0, 256, size=(total_rows, ROW_BYTES["fp6"]), dtype=np.uint8))
+        row_scale = torch.from_numpy(rng.integers(120, 128, size=(total_rows, FP6_SCALES_PER_ROW),
+                                                  dtype=np.uint8))
     else:
-        rows = _to(z, wl.cache)
-    del z
+        z = _normal(rng, (total_rows, D_ROW))
+        if wl.cache == "fp8":
+            rows = fp8_codes_from_normal(z)
+            u = rng.uniform(-0.5, 0.5, size=total_rows)
+            row_scale = torch.from_numpy((np.exp(u) / FP8_SPREAD).astype(np.float32))
+        else:
+            rows = _to(z, wl.cache)
+        del z
 
     act = wl.act
     w_std = 1.0 / np.sqrt(D_C)   # fan_in of both up-projections is d_c = 512
@@ -180,10 +192,10 @@ def canary_mask(p: Problem) -> np.ndarray:
 
 def algorithmic_bytes(p: Problem) -> dict:
     """Bytes the decode must move (cache rows + scales, both weights, q, out)."""
-    e_c = {"f32": 4, "bf16": 2, "fp8": 1}[p.wl.cache]
     e_a = {"f32": 4, "bf16": 2}[p.wl.act]
     B, H = p.q_nope.shape[0], p.q_nope.shape[1]
-    cache = p.T * (D_ROW * e_c + (4 if p.wl.cache == "fp8" else 0))
+    scale_bytes = {"fp8": 4, "fp6": FP6_SCALES_PER_ROW}.get(p.wl.cache, 0)
+    cache = p.T * (ROW_BYTES[p.wl.cache] + scale_bytes)
     weights = 2 * H * D_NOPE * D_C * e_a
     q = B * H * (D_NOPE + D_R) * e_a
     out = B * H * D_V * e_a
