@@ -54,9 +54,10 @@ Readings taken where the pages are silent (each listed in the design notes):
       7.5) in blocks of 32 consecutive elements of a row, each block with one
       e8m0 scale 2^X, X = floor(log2(max|block|)) - 2 (so the block's largest
       element lies in [4, 8) before rounding), elements rounded to nearest
-      even with saturation at 7.5; 18 blocks per 576-wide row, 6.25 bits per
-      element. Codes are packed little-endian: element i of a row takes bits
-      6i .. 6i+5 of its 432-byte bit string.
+      even with saturation at 7.5; 18 blocks per 576-wide row. A stored row is
+      464 bytes: the codes packed little-endian (element i takes bits
+      6i .. 6i+5 of bytes 0..431), the 18 scale codes (bytes 432..449), zero
+      padding to a multiple of 16 bytes (6.44 bits per element).
   R10 prefill / multi-query attention [the pages measure prompt processing
       beside generation -- over 100K prompt tokens/s on one 8-GPU node
       (DeepSeek-V2 reading card, "Evidence"; discosf explainer, throughput
@@ -208,17 +209,26 @@ def quantize_rows(rows: np.ndarray, dtype: str) -> Tuple[np.ndarray, Optional[np
         x = mx_block_exponent(np.max(np.abs(blk), axis=2))          # [n, 18]
         codes = e2m3_encode(blk / np.ldexp(1.0, x)[..., None])         # exact scaling
         deq = (e2m3_decode(codes) * np.ldexp(1.0, x)[..., None]).reshape(n, -1)
-        return pack6(codes.reshape(n, -1)), (x + 127).astype(np.uint8), deq
+        stored = np.zeros((n, FP6_ROW_BYTES), dtype=np.uint8)
+        stored[:, :FP6_CODE_BYTES] = pack6(codes.reshape(n, -1))
+        stored[:, FP6_CODE_BYTES:FP6_CODE_BYTES + D_ROW // MX_BLOCK] = x + 127
+        return stored, None, deq
     raise ValueError(dtype)
 
 
-def fp6_rows(packed: np.ndarray, scale_codes: np.ndarray) -> np.ndarray:
-    """fp64 values of fp6 cache rows (R11): e2m3 codes unpacked from the
-    row's bit string, times 2^(scale code - 127) of their block of 32."""
-    codes = unpack6(packed)
+FP6_CODE_BYTES = 432          # 576 six-bit codes
+FP6_ROW_BYTES = 464           # codes, 18 scale codes, padding
+
+
+def fp6_rows(stored: np.ndarray) -> np.ndarray:
+    """fp64 values of stored fp6 cache rows [n, 464] (R11): e2m3 codes
+    unpacked from bytes 0..431, each times 2^(code - 127) of its block's
+    scale byte (bytes 432..449)."""
+    stored = np.asarray(stored, dtype=np.uint8)
+    codes = unpack6(stored[:, :FP6_CODE_BYTES])
     n = codes.shape[0]
     blk = e2m3_decode(codes).reshape(n, -1, MX_BLOCK)
-    x = np.asarray(scale_codes, dtype=np.int64) - 127
+    x = stored[:, FP6_CODE_BYTES:FP6_CODE_BYTES + D_ROW // MX_BLOCK].astype(np.int64) - 127
     return (blk * np.ldexp(1.0, x)[..., None]).reshape(n, -1)
 
 

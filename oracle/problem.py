@@ -53,7 +53,7 @@ class OracleView:
             sc = p.row_scale[s:s + L].to(torch.float64).numpy()
             out = e4m3_decode(codes) * sc[:, None]
         elif self.dtype == "fp6":
-            out = mla.fp6_rows(sl.numpy(), p.row_scale[s:s + L].numpy())
+            out = mla.fp6_rows(sl.numpy())
         else:
             out = sl.to(torch.float64).numpy()
         for r, v in self.appended.items():

@@ -68,10 +68,12 @@ def test_quantized_rows_within_half_a_step():
     rng = np.random.default_rng(3)
     rows = rng.standard_normal((40, 576)) * np.exp(rng.uniform(-3, 3, (40, 1)))
     rows[5, :32] = 0.0                                  # an all-zero block
-    packed, scales, deq = oracle.quantize_rows(rows, "fp6")
-    assert packed.shape == (40, 432) and packed.dtype == np.uint8
-    assert scales.shape == (40, 18) and scales.dtype == np.uint8
-    assert np.array_equal(oracle.fp6_rows(packed, scales), deq)
+    stored, none, deq = oracle.quantize_rows(rows, "fp6")
+    assert none is None and stored.shape == (40, 464) and stored.dtype == np.uint8
+    assert np.all(stored[:, 450:] == 0)
+    scales = stored[:, 432:450]
+    assert np.array_equal(oracle.fp6_rows(stored), deq)
+    assert np.array_equal(oracle.unpack6(stored[:, :432]).reshape(40, 18, 32)[5, 0], np.zeros(32))
     assert np.all(deq[5, :32] == 0) and scales[5, 0] == 0
     X = scales.astype(np.int64) - 127
     q = np.repeat(np.ldexp(1.0, X), 32, axis=1)          # the block's unit

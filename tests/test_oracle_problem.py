@@ -11,14 +11,14 @@ from oracle import mla
 def test_workload_shapes_and_lengths():
     for wl in W.WORKLOADS.values():
         p = W.make_problem(wl, B=2, lengths=np.array([3, 5]), H=16)
-        assert p.rows.shape == (p.total_rows, 432 if wl.cache == "fp6" else 576)
+        assert p.rows.shape == (p.total_rows, 464 if wl.cache == "fp6" else 576)
         assert p.q_nope.shape == (2, 16, 128) and p.q_pe.shape == (2, 16, 64)
         assert p.w_uk.shape == (16, 128, 512) and p.w_uv.shape == (16, 512, 128)
         assert np.all(p.seq_capacity >= p.seq_len)
         assert p.seq_start[1] == p.seq_capacity[0]
-        assert (p.row_scale is not None) == (wl.cache in ("fp8", "fp6"))
+        assert (p.row_scale is not None) == (wl.cache == "fp8")
         if wl.cache == "fp6":
-            assert p.row_scale.shape == (p.total_rows, 18) and p.row_scale.dtype == torch.uint8
+            assert p.rows.dtype == torch.uint8 and np.all(p.rows[:, 450:].numpy() == 0)
     # seeded: the same seed draws the same lengths and values
     a = W.make_problem(W.WORKLOADS["v2lite_bf16"], B=3)
     b = W.make_problem(W.WORKLOADS["v2lite_bf16"], B=3)
@@ -148,18 +148,17 @@ def test_oracle_view_selects_sequence_rows():
 
 def test_fp6_view_unpacks_codes_and_block_scales():
     """OracleView's fp6 rows: element i of a row is the 6-bit field at bits
-    6i .. 6i+5 of the row's bytes, times 2^(its block's scale code - 127);
-    checked on a row built by hand."""
+    6i .. 6i+5 of the row's first 432 bytes, times 2^(its block's scale code
+    - 127), the scale codes being bytes 432..449; checked on a hand-made row."""
     p = W.make_problem(W.WORKLOADS["fp6_cache"], B=1, lengths=np.array([2]), H=16)
-    row = np.zeros(432, dtype=np.uint8)
+    row = np.zeros(464, dtype=np.uint8)
     row[0] = 0b001000          # element 0: code 8 = 1.0
     row[0] |= 0b01 << 6        # element 1: low two bits of code 0b011001 ...
     row[1] = 0b0110            # ... high four bits: code 25 = 4.5
     row[24] = 0b100001         # element 32 (block 1): code 33 = -0.125
+    row[432:450] = 127
+    row[433] = 125             # block 1 scaled by 1/4
     p.rows[0] = torch.from_numpy(row)
-    sc = np.full(18, 127, dtype=np.uint8)
-    sc[1] = 125                # block 1 scaled by 1/4
-    p.row_scale[0] = torch.from_numpy(sc)
     r = OracleView(p).rows64(0)[0]
     assert r[0] == 1.0 and r[1] == 4.5 and r[32] == -0.125 / 4
     assert np.all(r[2:32] == 0) and np.all(r[33:] == 0)

@@ -61,8 +61,8 @@ WORKLOADS = {
     ]
 }
 # bytes of a stored row (and of its scale record) per cache format
-ROW_BYTES = {"f32": 2304, "bf16": 1152, "fp8": 576, "fp6": 432}
-FP6_SCALES_PER_ROW = 18
+ROW_BYTES = {"f32": 2304, "bf16": 1152, "fp8": 576, "fp6": 464}
+FP6_CODE_BYTES, FP6_SCALES_PER_ROW = 432, 18     # an fp6 row: codes, block scales, padding
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
@@ -145,11 +145,13 @@ def make_problem(wl: Workload, seed: Optional[int] = None, *, B: Optional[int] =
 
     row_scale = None
     if wl.cache == "fp6":
-        # any byte string is a valid packed row of 6-bit codes; block scale
-        # codes 120..127 (2^-7 .. 1)
-        rows = torch.from_numpy(rng.integers(0, 256, size=(total_rows, ROW_BYTES["fp6"]), dtype=np.uint8))
-        row_scale = torch.from_numpy(rng.integers(120, 128, size=(total_rows, FP6_SCALES_PER_ROW),
-                                                  dtype=np.uint8))
+        # any byte string is a valid packed run of 6-bit codes; block scale
+        # codes 120..127 (2^-7 .. 1); zero padding
+        r = np.zeros((total_rows, ROW_BYTES["fp6"]), dtype=np.uint8)
+        r[:, :FP6_CODE_BYTES] = rng.integers(0, 256, size=(total_rows, FP6_CODE_BYTES), dtype=np.uint8)
+        r[:, FP6_CODE_BYTES:FP6_CODE_BYTES + FP6_SCALES_PER_ROW] = rng.integers(
+            120, 128, size=(total_rows, FP6_SCALES_PER_ROW), dtype=np.uint8)
+        rows = torch.from_numpy(r)
     else:
         z = _normal(rng, (total_rows, D_ROW))
         if wl.cache == "fp8":
@@ -194,7 +196,7 @@ def algorithmic_bytes(p: Problem) -> dict:
     """Bytes the decode must move (cache rows + scales, both weights, q, out)."""
     e_a = {"f32": 4, "bf16": 2}[p.wl.act]
     B, H = p.q_nope.shape[0], p.q_nope.shape[1]
-    scale_bytes = {"fp8": 4, "fp6": FP6_SCALES_PER_ROW}.get(p.wl.cache, 0)
+    scale_bytes = {"fp8": 4}.get(p.wl.cache, 0)            # (fp6 rows hold their scales)
     cache = p.T * (ROW_BYTES[p.wl.cache] + scale_bytes)
     weights = 2 * H * D_NOPE * D_C * e_a
     q = B * H * (D_NOPE + D_R) * e_a
