@@ -29,6 +29,8 @@ MLA_ERR_HIP = 4
 MLA_DTYPE_F32 = 0
 MLA_DTYPE_BF16 = 1
 MLA_DTYPE_FP8_E4M3 = 2
+MLA_DTYPE_FP6_E2M3_MX = 3
+FP6_ROW_BYTES = 464        # 432 code bytes, 18 e8m0 block scales, padding
 
 D_C, D_R, D_ROW, D_NOPE, D_V = 512, 64, 576, 128, 128
 
@@ -150,6 +152,15 @@ def dtype_code(t: torch.dtype) -> int:
     raise TypeError(f"no libmla dtype for {t}")
 
 
+def _cache_dtype(rows: torch.Tensor) -> int:
+    """Cache format from the storage tensor: fp6 rows are 464 bytes."""
+    if rows.dtype == torch.uint8 and rows.dim() == 2 and rows.shape[1] == FP6_ROW_BYTES:
+        return MLA_DTYPE_FP6_E2M3_MX
+    if rows.dim() == 2 and rows.shape[1] == FP6_ROW_BYTES:
+        raise TypeError("fp6 rows are uint8 bytes")
+    return dtype_code(rows.dtype)
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     if t is None:
         return None
@@ -245,7 +256,7 @@ class LatentCache:
 
     @property
     def dtype(self) -> int:
-        return dtype_code(self.rows.dtype)
+        return _cache_dtype(self.rows)
 
     @property
     def num_seqs(self) -> int:
@@ -253,8 +264,8 @@ class LatentCache:
 
     def check(self) -> None:
         """Shapes, dtypes and devices of the cache tensors."""
-        if self.rows.dim() != 2 or self.rows.shape[1] != D_ROW:
-            raise ValueError("rows must be [total_rows, 576]")
+        if self.rows.dim() != 2 or self.rows.shape[1] not in (D_ROW, FP6_ROW_BYTES):
+            raise ValueError("rows must be [total_rows, 576] (fp6: [total_rows, 464] bytes)")
         dev = self.rows.device
         B = self.seq_start.shape[0] if self.seq_start.dim() == 1 else -1
         if B < 1:
@@ -285,7 +296,7 @@ class PagedLatentCache:
 
     @property
     def dtype(self) -> int:
-        return dtype_code(self.rows.dtype)
+        return _cache_dtype(self.rows)
 
     @property
     def num_seqs(self) -> int:
@@ -293,8 +304,8 @@ class PagedLatentCache:
 
     def check(self) -> None:
         """Shapes, dtypes and devices of the cache tensors."""
-        if self.rows.dim() != 2 or self.rows.shape[1] != D_ROW:
-            raise ValueError("rows must be [total_pages * page_tokens, 576]")
+        if self.rows.dim() != 2 or self.rows.shape[1] not in (D_ROW, FP6_ROW_BYTES):
+            raise ValueError("rows must be [total_pages * page_tokens, 576] (fp6: 464 bytes)")
         if self.page_tokens < 32 or self.page_tokens % 32 or self.rows.shape[0] % self.page_tokens:
             raise ValueError("page_tokens must be a multiple of 32 dividing the row count")
         dev = self.rows.device

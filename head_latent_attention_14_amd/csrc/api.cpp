@@ -35,7 +35,7 @@ DecodePlan make_plan(int ct, int B, int H) {
     p.h32 = true;
     p.nstage = 4;
     p.head_groups = H / 128;
-  } else if (ct != kF32 && H % 32 == 0) {
+  } else if ((ct == kBF16 || ct == kFP8) && H % 32 == 0) {
     // pair kernel: up to 128 heads (8 waves) per workgroup; the ring depth is
     // what fits in LDS beside the score-exchange buffer
     p.pair = true;
@@ -54,7 +54,7 @@ DecodePlan make_plan(int ct, int B, int H) {
     p.nstage = (ct == kF32) ? 2 : 4;
     p.head_groups = H / 16;
   }
-  p.tile = (ct == kF32) ? 16 : 32;
+  p.tile = (ct == kF32) ? 16 : 32;   // (fp6 tiles: the block kernel over widened rows)
   // what a segment start costs in tiles of work: queries in and a partial
   // out; the pair kernel moves 147 KB of queries and 128 KB of partial per
   // segment and drains its copy queue (measured best: 1 for the streaming
@@ -104,18 +104,21 @@ PrefillLayout prefill_layout(int B, int H, int64_t max_kv_rows) {
 using namespace mla;
 
 static bool valid_dtype(int d) {
-  return d == MLA_DTYPE_F32 || d == MLA_DTYPE_BF16 || d == MLA_DTYPE_FP8_E4M3;
+  return d == MLA_DTYPE_F32 || d == MLA_DTYPE_BF16 || d == MLA_DTYPE_FP8_E4M3 ||
+         d == MLA_DTYPE_FP6_E2M3_MX;
 }
 
 // supported (cache, activation) dtype pairs
 static bool supported_pair(int cache, int act) {
   return (cache == MLA_DTYPE_F32 && act == MLA_DTYPE_F32) ||
          (cache == MLA_DTYPE_BF16 && act == MLA_DTYPE_BF16) ||
-         (cache == MLA_DTYPE_FP8_E4M3 && act == MLA_DTYPE_BF16);
+         (cache == MLA_DTYPE_FP8_E4M3 && act == MLA_DTYPE_BF16) ||
+         (cache == MLA_DTYPE_FP6_E2M3_MX && act == MLA_DTYPE_BF16);
 }
 
 static int cache_type(int dtype) {
-  return dtype == MLA_DTYPE_F32 ? kF32 : (dtype == MLA_DTYPE_BF16 ? kBF16 : kFP8);
+  return dtype == MLA_DTYPE_F32 ? kF32 : dtype == MLA_DTYPE_BF16 ? kBF16
+       : dtype == MLA_DTYPE_FP8_E4M3 ? kFP8 : kFP6;
 }
 
 // The cache as the launchers see it: contiguous per-sequence row ranges
@@ -142,6 +145,7 @@ static mla_status_t check_common(int32_t dtype, int32_t d_c, int32_t d_r, int32_
   if (num_seqs > kMaxSeqs) return MLA_ERR_UNSUPPORTED;
   if (!rows) return MLA_ERR_INVALID_ARGUMENT;
   if (dtype == MLA_DTYPE_FP8_E4M3 && !row_scale) return MLA_ERR_INVALID_ARGUMENT;
+  if (dtype == MLA_DTYPE_FP6_E2M3_MX && row_scale) return MLA_ERR_INVALID_ARGUMENT;  // scales are in the rows
   return MLA_OK;
 }
 

@@ -19,11 +19,17 @@ constexpr int kNumGroups = kDrow / kColGroup;  // 36
 // One workgroup computes 16 output columns (all 576 for the fp8 cache, whose
 // per-row scale needs the whole row) for 16 tokens; its four waves split the
 // d_model contraction into quarters and reduce through LDS.
+struct Tr6 {
+  static constexpr int kRowBytes = 464;                // fp6 row: 432 code bytes, 18 scales, padding
+};
+
 template <int CT>
 __global__ void __launch_bounds__(256)
 mla_append_kernel(AppendArgs a) {
   using E = typename std::conditional<CT == kF32, float, __bf16>::type;
-  constexpr bool FP8 = (CT == kFP8);
+  // fp8 (one scale per row) and fp6 (scales per block of 32) quantise whole
+  // rows: one workgroup computes all 576 columns of its 16 tokens
+  constexpr bool FP8 = (CT == kFP8 || CT == kFP6);
   constexpr int KPL = (CT == kF32) ? 1 : 8;        // k elements per lane per MFMA
   constexpr int KSTEP = 4 * KPL;                   // k per MFMA
   constexpr int U = 16;                            // MFMAs per load round
@@ -173,6 +179,43 @@ mla_append_kernel(AppendArgs a) {
             ((uint16_t*)a.rows)[row * kDrow + c] = f32_to_bf16_bits(rowt[t][c]);
         }
       }
+    }
+  } else if constexpr (CT == kFP6) {
+    // one token per 16 lanes; lane sl quantises blocks sl and sl + 16 (< 18)
+    // of 32 elements: shared exponent X = floor(log2(amax)) - 2 (0 for an
+    // all-zero block: scale code 0), e2m3 codes rounded to nearest even with
+    // saturation at 7.5, packed little-endian (element e at bits 6e .. 6e+5
+    // of the block's 24 bytes), then the scale codes and zero padding
+    const int t = tid >> 4, sl = tid & 15;
+    const int tok = tok0 + t;
+    const int64_t row = tok < a.n_tok ? trow[t] : -1;
+    if (row >= 0) {
+      uint8_t* dst = (uint8_t*)a.rows + row * Tr6::kRowBytes;
+      for (int blk = sl; blk < 18; blk += 16) {
+        const float* v = &rowt[t][32 * blk];
+        float amax = 0.f;
+        for (int e = 0; e < 32; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[e]));
+        int x = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 2 : -127;   // amax = m 2^(x+3), m in [1, 2)
+        x = x < -127 ? -127 : (x > 127 ? 127 : x);
+        uint32_t w[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+        for (int e = 0; e < 32; ++e) {
+          const float q = __builtin_fabsf(__builtin_amdgcn_ldexpf(v[e], -x));   // exact
+          float c;                                     // code magnitude, round to nearest even
+          if (q < 2.f) c = __builtin_rintf(q * 8.f);                      // step 1/8: codes 0..16
+          else if (q < 4.f) c = 16.f + __builtin_rintf((q - 2.f) * 4.f);  // step 1/4: codes 16..24
+          else c = 24.f + __builtin_rintf((q - 4.f) * 2.f);               // step 1/2: codes 24..32
+          uint32_t code = c > 31.f ? 31u : (uint32_t)c;                   // saturate at 7.5
+          if (__builtin_signbit(v[e])) code |= 32u;
+          const int bit = 6 * e;
+          w[bit >> 5] |= code << (bit & 31);
+          if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+        }
+        uint32_t* d32 = (uint32_t*)(dst + 24 * blk);
+        for (int k = 0; k < 6; ++k) d32[k] = w[k];
+        dst[432 + blk] = (uint8_t)(x + 127);
+      }
+      if (sl == 0)
+        for (int k = 450; k < Tr6::kRowBytes; ++k) dst[k] = 0;
     }
   } else {
     // one token per 16 lanes: amax, scale, then 36 codes per lane
@@ -448,11 +491,12 @@ bool append_absorb_fits(int cache_type, const AppendArgs& a, const DecodeArgs& d
 }
 
 hipError_t launch_append(int ct, const AppendArgs& a, hipStream_t s) {
-  dim3 grid((a.n_tok + 15) / 16, ct == kFP8 ? 1 : kNumGroups);
+  dim3 grid((a.n_tok + 15) / 16, (ct == kFP8 || ct == kFP6) ? 1 : kNumGroups);
   switch (ct) {
     case kF32: hipLaunchKernelGGL(mla_append_kernel<kF32>, grid, dim3(256), 0, s, a); break;
     case kBF16: hipLaunchKernelGGL(mla_append_bf16_kernel<8>, grid, dim3(512), 0, s, a); break;
     case kFP8: hipLaunchKernelGGL(mla_append_kernel<kFP8>, grid, dim3(256), 0, s, a); break;
+    case kFP6: hipLaunchKernelGGL(mla_append_kernel<kFP6>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -38,6 +38,9 @@ template <int CT> struct Tr;
 template <> struct Tr<kBF16> { static constexpr int kRowBytes = 1152, kPad = 1168, kTile = 32; };
 template <> struct Tr<kFP8> { static constexpr int kRowBytes = 576, kPad = 592, kTile = 32; };
 template <> struct Tr<kF32> { static constexpr int kRowBytes = 2304, kPad = 2320, kTile = 16; };
+// fp6 rows (464 bytes: packed codes, block scales, padding) are only read by
+// the widening pass, which needs no padding
+template <> struct Tr<kFP6> { static constexpr int kRowBytes = 464, kPad = 464, kTile = 32; };
 constexpr int kConvPad = 1168;   // padded bf16 row of the widened fp8 tile
 constexpr float kSlack = 8.f;    // lazy-rescale slack of the running max (log2 units)
 
@@ -303,6 +306,31 @@ __device__ __forceinline__ void widen_fp8_tile(const char* stage, char* conv) {
     const uint2 c2 = fp8x4_to_bf16x4(v[2]), c3 = fp8x4_to_bf16x4(v[3]);
     *(u32x4*)(conv + r * kConvPad + j * 32) = u32x4{c0.x, c0.y, c1.x, c1.y};
     *(u32x4*)(conv + r * kConvPad + j * 32 + 16) = u32x4{c2.x, c2.y, c3.x, c3.y};
+  }
+}
+
+// Widen a staged fp6 tile (464-byte rows: 576 packed e2m3 codes, then the
+// 18 e8m0 block scales) to bf16 rows at pitch kConvPad, all threads of the
+// workgroup cooperating: one block of 32 codes (24 bytes) and its scale per
+// conversion (v_cvt_scalef32_pk32_bf16_fp6: element i from bits 6i .. 6i+5,
+// times the scale; an e2m3 value times a power of two is exact in bf16).
+template <int NT>
+__device__ __forceinline__ void widen_fp6_tile(const char* stage, char* conv) {
+  typedef int i32x6 __attribute__((ext_vector_type(6)));
+  typedef __bf16 bf16x32 __attribute__((ext_vector_type(32)));
+  constexpr int RB = Tr<kFP6>::kRowBytes;
+  for (int i = threadIdx.x; i < 32 * 18; i += NT) {
+    const int r = i / 18;
+    const int j = i - r * 18;
+    const char* src = stage + r * RB + 24 * j;
+    const uint2 w0 = *(const uint2*)src, w1 = *(const uint2*)(src + 8), w2 = *(const uint2*)(src + 16);
+    const int e = (int)*(const uint8_t*)(stage + r * RB + 432 + j);
+    const i32x6 codes = {(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y, (int)w2.x, (int)w2.y};
+    const bf16x32 v = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(codes, __builtin_amdgcn_ldexpf(1.f, e - 127));
+    const u32x4* vv = (const u32x4*)&v;
+    char* dst = conv + r * kConvPad + 64 * j;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *(u32x4*)(dst + 16 * k) = vv[k];
   }
 }
 

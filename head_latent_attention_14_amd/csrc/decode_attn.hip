@@ -28,7 +28,8 @@ mla_attn_kernel(AttnParams p) {
   constexpr int RP = Tr<CT>::kPad;
   constexpr int STAGE_DATA = TileCopy<CT, NW>::STAGE_DATA;
   constexpr int STAGE_BYTES = TileCopy<CT, NW>::STAGE_BYTES;
-  constexpr int CONV_BYTES = (CT == kFP8) ? TILE * kConvPad : 0;
+  constexpr bool WIDEN = (CT == kFP8 || CT == kFP6);     // codes widened to bf16 in LDS
+  constexpr int CONV_BYTES = WIDEN ? TILE * kConvPad : 0;
   constexpr int CPW = TileCopy<CT, NW>::CPW;             // copies per wave per tile
   constexpr int DSLICE = kDc / DS;
   constexpr int NB = DSLICE / 16;
@@ -114,7 +115,7 @@ mla_attn_kernel(AttnParams p) {
   for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // per-lane operand bases (bytes from the tile start)
-  constexpr int TP = (CT == kFP8) ? kConvPad : RP;       // row pitch of the tile computed on
+  constexpr int TP = WIDEN ? kConvPad : RP;              // row pitch of the tile computed on
   const uint32_t s_base = (uint32_t)(l16 * TP + g * 16);                   // score A rows
   const uint32_t v_base = (uint32_t)(4 * g * TP + (ds * DSLICE + l16) * (CT == kF32 ? 4 : 2));
   // transposing value reads: source lane (g, l16) points at row 4g + l16/4,
@@ -144,10 +145,11 @@ mla_attn_kernel(AttnParams p) {
     const int nvalid = left < TILE ? (int)left : TILE;
 
     const char* tb = stage;                              // bf16/f32 rows of this tile
-    if constexpr (CT == kFP8) {
-      // widen the fp8 codes to bf16 once for all waves
+    if constexpr (WIDEN) {
+      // widen the codes to bf16 once for all waves (fp6: block scales applied)
       char* conv = smem + NSTAGE * STAGE_BYTES;
-      widen_fp8_tile<64 * NW>(stage, conv);
+      if constexpr (CT == kFP8) widen_fp8_tile<64 * NW>(stage, conv);
+      else widen_fp6_tile<64 * NW>(stage, conv);
       barrier_lds();
       tb = conv;
     }
@@ -782,6 +784,7 @@ hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipS
   MLA_CASE(kF32, 1, 4, 2)
   MLA_CASE(kBF16, 1, 4, 4)
   MLA_CASE(kFP8, 1, 4, 4)
+  MLA_CASE(kFP6, 1, 4, 4)
   MLA_PAIR(kBF16, 4, 3)
   MLA_PAIR(kBF16, 2, 3)
   MLA_PAIR(kBF16, 1, 4)

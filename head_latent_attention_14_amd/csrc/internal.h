@@ -7,7 +7,7 @@
 
 namespace mla {
 
-enum CacheType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+enum CacheType : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kFP6 = 3 };
 
 constexpr int kTargetCUs = 256;   // MI355X compute units
 

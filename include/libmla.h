@@ -73,7 +73,8 @@ typedef int32_t mla_dtype_t;
 enum {
   MLA_DTYPE_F32 = 0,
   MLA_DTYPE_BF16 = 1,
-  MLA_DTYPE_FP8_E4M3 = 2          /* OCP e4m3fn codes (max 448, no infinities) */
+  MLA_DTYPE_FP8_E4M3 = 2,         /* OCP e4m3fn codes (max 448, no infinities) */
+  MLA_DTYPE_FP6_E2M3_MX = 3       /* 6-bit e2m3 codes in blocks of 32 with e8m0 scales */
 };
 
 /*
@@ -83,16 +84,25 @@ enum {
  * Sequence b owns rows [seq_start[b], seq_start[b] + seq_capacity[b]) of
  * `rows`. Row r is c_KV (elements 0..511) followed by k_pe (512..575), stored
  * in `dtype`. For MLA_DTYPE_FP8_E4M3 the value of element i of row r is
- * e4m3(rows[r][i]) * row_scale[r]; one fp32 scale covers the whole row. Row
- * ranges of different sequences must not overlap.
+ * e4m3(rows[r][i]) * row_scale[r]; one fp32 scale covers the whole row.
+ * MLA_DTYPE_FP6_E2M3_MX is the ~6-bit cache (the pages quantise the deployed
+ * cache to about 6 bits per element on average without naming a format:
+ * DeepSeek-V2 reading card, "Method adaptation"): OCP microscaling FP6. A
+ * row is 464 bytes: bytes 0..431 hold the 576 six-bit e2m3 codes (sign,
+ * 2-bit exponent with bias 1, 3-bit mantissa; largest 7.5) packed
+ * little-endian, element i in bits 6i .. 6i+5; bytes 432..449 the 18 e8m0
+ * scale codes of the blocks of 32 elements; bytes 450..463 padding (written
+ * as zero by mla_append). Element i's value is e2m3(code_i) *
+ * 2^(scale[i / 32] - 127); row_scale must be NULL. Row ranges of different
+ * sequences must not overlap.
  */
 typedef struct {
-  mla_dtype_t dtype;             /* element type of rows: F32, BF16 or FP8_E4M3 */
+  mla_dtype_t dtype;             /* element type of rows: F32, BF16, FP8_E4M3 or FP6_E2M3_MX */
   int32_t d_c;                   /* must be 512 */
   int32_t d_r;                   /* must be 64 */
   int32_t num_seqs;              /* B >= 1 */
   int64_t total_rows;            /* rows allocated in `rows` (>= 1) */
-  void* rows;                    /* (device) [total_rows][576] */
+  void* rows;                    /* (device) [total_rows][576] elements (FP6: [total_rows][464] bytes) */
   float* row_scale;              /* (device) [total_rows] for FP8_E4M3, else NULL */
   const int64_t* seq_start;      /* (device) [B] first row of sequence b */
   const int32_t* seq_capacity;   /* (device) [B] rows reserved for sequence b */
@@ -114,14 +124,14 @@ typedef struct {
  * different sequences must not overlap where rows are written.
  */
 typedef struct {
-  mla_dtype_t dtype;             /* element type of rows: F32, BF16 or FP8_E4M3 */
+  mla_dtype_t dtype;             /* element type of rows: F32, BF16, FP8_E4M3 or FP6_E2M3_MX */
   int32_t d_c;                   /* must be 512 */
   int32_t d_r;                   /* must be 64 */
   int32_t num_seqs;              /* B >= 1 */
   int32_t page_tokens;           /* rows per page: a positive multiple of 32 */
   int32_t max_pages;             /* block-table columns (pages per sequence) >= 1 */
   int64_t total_pages;           /* pages in `rows` >= 1 */
-  void* rows;                    /* (device) [total_pages * page_tokens][576] */
+  void* rows;                    /* (device) [total_pages * page_tokens][576] (FP6: [..][464] bytes) */
   float* row_scale;              /* (device) [total_pages * page_tokens] for FP8_E4M3, else NULL */
   const int32_t* block_table;    /* (device) [B][max_pages] page of each block */
 } mla_paged_cache_t;
@@ -137,13 +147,16 @@ typedef struct {
  *                                        pos * rope_base^(-2i/64); the angle is
  *                                        formed and reduced to [-pi, pi] in fp64,
  *                                        its sine and cosine taken in fp32 (BF16
- *                                        cache) or fp64 (F32, FP8_E4M3)
+ *                                        cache) or fp64 (F32, FP8_E4M3, FP6)
  *   row    = c || k_pe, stored at row seq_start[s] + pos of the cache, where
  *            s = tok_seq[n] and pos = tok_pos[n] (pos is both the slot and the
  *            RoPE position, 0-based within the sequence).
  * Storage: F32 as computed; BF16 rounded to nearest even; FP8_E4M3 with
  * row_scale = max|row| / 448 (1 for an all-zero row) and codes rounded to
- * nearest even with saturation at +-448.
+ * nearest even with saturation at +-448; FP6_E2M3_MX per block of 32
+ * elements with scale 2^X, X = floor(log2(max|block|)) - 2 (scale code 0 for
+ * an all-zero block), codes rounded to nearest even with saturation at
+ * +-7.5.
  * Arithmetic: products in `act_dtype`, fp32 accumulation.
  *
  *   h        (device) [n_tok][d_model] in act_dtype
@@ -151,8 +164,8 @@ typedef struct {
  *   w_kr     (device) [64][d_model] in act_dtype
  *   tok_seq  (device) [n_tok] sequence of each token
  *   tok_pos  (device) [n_tok] slot/position of each token
- * act_dtype must be F32 (with an F32 cache) or BF16 (with a BF16 or FP8
- * cache); d_model must be a positive multiple of 64. A token whose sequence
+ * act_dtype must be F32 (with an F32 cache) or BF16 (with a BF16, FP8 or
+ * FP6 cache); d_model must be a positive multiple of 64. A token whose sequence
  * is outside [0, B) or whose position is outside [0, seq_capacity) is not
  * written. Two tokens naming the same slot race. n_tok == 0 is a no-op.
  * The call does not change any length: the caller passes lengths to decode.
@@ -236,7 +249,9 @@ mla_status_t mla_decode_workspace_size(int32_t num_seqs, int32_t n_heads,
  *   workspace(device) at least mla_decode_workspace_size(...) bytes, 256-byte
  *            aligned; contents on entry are ignored.
  * Supported (cache dtype, act_dtype): (F32, F32), (BF16, BF16),
- * (FP8_E4M3, BF16). n_heads must be a positive multiple of 16. Arithmetic:
+ * (FP8_E4M3, BF16), (FP6_E2M3_MX, BF16). n_heads must be a positive multiple
+ * of 16. FP6 rows are widened exactly to bf16 (block scales applied) once per
+ * tile in LDS. Arithmetic:
  * bf16 (or fp32 for F32) matrix products with fp32 accumulation; softmax in
  * fp32. The result is deterministic: no floating-point atomics.
  */

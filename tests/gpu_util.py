@@ -10,11 +10,11 @@ import torch
 
 import workloads as W
 
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 4e-2}     # rel-L2 bounds on o[B,H,128]
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 4e-2, "fp6": 4e-2}     # rel-L2 bounds on o[B,H,128]
 
 # Unit roundoff of the absorbed query q_lat = W_UK[h]^T q_nope as the kernels
 # hold it: fp32 for the f32 cache, bf16 (8 significant bits) otherwise.
-Q_LAT_U = {"f32": 2.0 ** -24, "bf16": 2.0 ** -8, "fp8": 2.0 ** -8}
+Q_LAT_U = {"f32": 2.0 ** -24, "bf16": 2.0 ** -8, "fp8": 2.0 ** -8, "fp6": 2.0 ** -8}
 
 
 def log(msg: str):

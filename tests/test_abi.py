@@ -445,3 +445,28 @@ def test_prefill_binding_checks_shapes():
                 dict(w_uv=torch.zeros(H, 128, 512, dtype=torch.bfloat16))]:
         with pytest.raises((ValueError, TypeError)):
             call(**bad)
+
+
+def test_fp6_cache_validation():
+    """The fp6 cache carries its scales in the rows: row_scale must be NULL;
+    it pairs with bf16 activations only; the workspace is sized as for the
+    other 8/16-bit caches."""
+    E = mla
+    assert _decode(_cache(dtype=E.MLA_DTYPE_FP6_E2M3_MX, scale=FAKE)) == E.MLA_ERR_INVALID_ARGUMENT
+    assert _decode(_cache(dtype=E.MLA_DTYPE_FP6_E2M3_MX), act=E.MLA_DTYPE_F32) == E.MLA_ERR_UNSUPPORTED
+    need = mla.mla_decode_workspace_size(4, 16, E.MLA_DTYPE_FP6_E2M3_MX, E.MLA_DTYPE_BF16)
+    assert need > 0
+    assert _decode(_cache(dtype=E.MLA_DTYPE_FP6_E2M3_MX), ws_bytes=need - 1) == E.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert _append(_cache(dtype=E.MLA_DTYPE_FP6_E2M3_MX, scale=FAKE)) == E.MLA_ERR_INVALID_ARGUMENT
+    assert _decode(_cache(dtype=4)) == E.MLA_ERR_INVALID_ARGUMENT
+    torch = pytest.importorskip("torch")
+    c = mla.LatentCache(rows=torch.zeros(8, 464, dtype=torch.uint8),
+                        seq_start=torch.tensor([0], dtype=torch.int64),
+                        seq_capacity=torch.tensor([8], dtype=torch.int32))
+    assert c.dtype == E.MLA_DTYPE_FP6_E2M3_MX
+    c.check()
+    with pytest.raises((ValueError, TypeError)):
+        mla.LatentCache(rows=torch.zeros(8, 464, dtype=torch.uint8),
+                        seq_start=torch.tensor([0], dtype=torch.int64),
+                        seq_capacity=torch.tensor([8], dtype=torch.int32),
+                        row_scale=torch.zeros(8)).check()

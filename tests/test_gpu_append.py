@@ -32,6 +32,9 @@ def _cache(dtype, caps, fill=None):
     if dtype == "fp8":
         rows = torch.randint(0, 0x7E, (total, 576), dtype=torch.uint8)
         scale = torch.rand(total) + 0.5
+    elif dtype == "fp6":
+        rows = torch.randint(0, 256, (total, 464), dtype=torch.uint8)
+        scale = None
     else:
         rows = torch.randn(total, 576).to(W.TORCH_DTYPE[dtype])
         scale = None
@@ -174,6 +177,51 @@ def test_append_fp8_codes_and_scales():
     assert not (diff & ~tie).any()
     rel = np.linalg.norm(got - exact) / np.linalg.norm(exact)
     assert rel <= 4e-2
+
+
+def test_append_fp6_codes_scales_and_padding():
+    """fp6 append: every block's scale code and every element code equal the
+    oracle's, except where the exact value lies within the fp32 accumulation
+    error of a decision: a block maximum within 1e-5 (relative) of a power of
+    two (the shared exponent), an element within 2% of a step of a rounding
+    midpoint (the code); the padding bytes are zero."""
+    rng = np.random.default_rng(4)
+    dm = 512
+    n_tok = 40
+    cache, starts = _cache("fp6", [64, 64])
+    h = torch.from_numpy(rng.standard_normal((n_tok, dm)).astype(np.float32)).bfloat16()
+    wd = torch.from_numpy((rng.standard_normal((512, dm)) * rng.uniform(0.01, 0.2)).astype(np.float32)).bfloat16()
+    wk = torch.from_numpy((rng.standard_normal((64, dm)) * 0.05).astype(np.float32)).bfloat16()
+    seq = [i % 2 for i in range(n_tok)]
+    pos = [i // 2 for i in range(n_tok)]
+    _append(cache, h, wd, wk, seq, pos, 10000.0)
+    exact = omla.append_rows_exact(h.double().numpy(), wd.double().numpy(), wk.double().numpy(),
+                                   np.array(pos, dtype=np.float64), 10000.0)
+    ref, _, deq_ref = omla.quantize_rows(exact, "fp6")
+    idx = [int(starts[s]) + p for s, p in zip(seq, pos)]
+    got = cache.rows.cpu().numpy()[idx]
+    assert np.all(got[:, 450:] == 0)
+    # shared exponents
+    amax = np.abs(exact).reshape(n_tok, 18, 32).max(axis=2)
+    near_pow2 = np.abs(np.log2(amax) - np.round(np.log2(amax))) < 1e-5
+    sdiff = got[:, 432:450] != ref[:, 432:450]
+    log(f"  fp6 append: {int(sdiff.sum())} of {sdiff.size} block scales differ")
+    assert not (sdiff & ~near_pow2).any()
+    # element codes, in blocks whose exponent agrees
+    from oracle.numerics import unpack6
+    gc, rc = unpack6(got[:, :432]), unpack6(ref[:, :432])
+    X = np.repeat(ref[:, 432:450].astype(np.int64) - 127, 32, axis=1)
+    mag = np.abs(exact) / np.ldexp(1.0, X)
+    step = np.where(mag < 2, 1 / 8, np.where(mag < 4, 1 / 4, 1 / 2))
+    frac = (mag / step) % 1.0
+    tie = np.abs(frac - 0.5) < 0.02
+    same_x = np.repeat(~sdiff, 32, axis=1)
+    cdiff = (gc != rc) & same_x
+    log(f"  fp6 append: {int(cdiff.sum())} of {cdiff.size} codes differ ({int((cdiff & ~tie).sum())} off-tie)")
+    assert not (cdiff & ~tie).any()
+    deq = omla.fp6_rows(got)
+    err, err_ref = (np.linalg.norm(deq - exact), np.linalg.norm(deq_ref - exact))
+    assert err <= 1.01 * err_ref + 1e-12
 
 
 def test_append_skips_invalid_tokens():

@@ -98,7 +98,8 @@ def test_decode_full_size_all_heads(name):
 
 @pytest.mark.parametrize("name,lengths", [("v2lite_bf16", [700, 5, 1300]),
                                           ("v2_bf16", [3000, 5, 1300, 64]),
-                                          ("fp8_cache", [900, 33, 2000])])
+                                          ("fp8_cache", [900, 33, 2000]),
+                                          ("fp6_cache", [900, 33, 2000])])
 def test_decode_deterministic_and_repeatable(name, lengths):
     # no floating-point atomics: two runs over poisoned outputs and workspace
     # are bitwise equal, at 16 and at 128 heads (bf16 and fp8 caches)
@@ -260,7 +261,8 @@ GAPPY = [0, 0, 1, 0, 32, 0, 0, 33, 64, 0, 1, 0]
 
 
 @pytest.mark.parametrize("name,H", [("v2lite_bf16", 16), ("v2_bf16", 32), ("v2_bf16", 128),
-                                    ("fp8_cache", 16), ("fp8_cache", 128), ("tiny_fp32", 16)])
+                                    ("fp8_cache", 16), ("fp8_cache", 128), ("fp6_cache", 16),
+                                    ("fp6_cache", 128), ("tiny_fp32", 16)])
 def test_empty_sequences_between_others(name, H):
     wl = W.WORKLOADS[name]
     make = np.array([max(n, 1) for n in GAPPY])

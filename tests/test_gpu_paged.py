@@ -43,7 +43,7 @@ def _page(dp, P, seed):
         dst.append(table[b, t // P].astype(np.int64) * P + t % P)
     src, dst = np.concatenate(src), np.concatenate(dst)
     rows = dp.cache.rows
-    pool = torch.empty((total * P, 576), dtype=rows.dtype, device=rows.device)
+    pool = torch.empty((total * P, rows.shape[1]), dtype=rows.dtype, device=rows.device)
     if rows.dtype == torch.uint8:
         pool.random_(0, 0x7E)
     else:
@@ -78,6 +78,7 @@ CASES = [
     ("v2lite_bf16", [1, 33, 300, 64, 129], 96),
     ("v2_bf16", [1, 33, 200, 97], 64),               # pair kernel (128 heads)
     ("fp8_cache", [1, 33, 200, 97], 32),             # fp8 pair kernel
+    ("fp6_cache", [1, 33, 200, 97], 32),             # fp6: block kernel over widened rows
     ("tiny_fp32", [256, 40], 64),                    # f32 kernel (16-token tiles)
 ]
 
