@@ -35,12 +35,13 @@ DecodePlan make_plan(int ct, int B, int H) {
     p.h32 = true;
     p.nstage = 4;
     p.head_groups = H / 128;
-  } else if ((ct == kBF16 || ct == kFP8) && H % 32 == 0) {
+  } else if ((ct == kBF16 || ct == kFP8 || ct == kFP6) && H % 32 == 0) {
     // pair kernel: up to 128 heads (8 waves) per workgroup; the ring depth is
-    // what fits in LDS beside the score-exchange buffer
+    // what fits in LDS beside the score-exchange buffer (and, for fp6, the
+    // widened bf16 tile)
     p.pair = true;
     p.np = (H % 128 == 0) ? 4 : (H % 64 == 0) ? 2 : 1;
-    p.nstage = (ct == kFP8 || p.np == 1) ? 4 : 3;
+    p.nstage = (ct != kBF16 || p.np == 1) ? 4 : 3;
     p.head_groups = H / (32 * p.np);
     p.f8 = ct == kFP8 && getenv_flag("MLA_FP8_MFMA");
   } else if (ct == kBF16) {
@@ -54,7 +55,7 @@ DecodePlan make_plan(int ct, int B, int H) {
     p.nstage = (ct == kF32) ? 2 : 4;
     p.head_groups = H / 16;
   }
-  p.tile = (ct == kF32) ? 16 : 32;   // (fp6 tiles: the block kernel over widened rows)
+  p.tile = (ct == kF32) ? 16 : 32;
   // what a segment start costs in tiles of work: queries in and a partial
   // out; the pair kernel moves 147 KB of queries and 128 KB of partial per
   // segment and drains its copy queue (measured best: 1 for the streaming

@@ -334,6 +334,42 @@ __device__ __forceinline__ void widen_fp6_tile(const char* stage, char* conv) {
   }
 }
 
+// The same widening for kernels whose stage buffers are filled by
+// asynchronous copies: the staged codes and scales are read in asm blocks
+// that wait inside, so the compiler does not make them wait for every copy in
+// flight (the converted rows are ordinary LDS stores).
+template <int NT>
+__device__ __forceinline__ void widen_fp6_tile_async(const char* stage, char* conv) {
+  typedef int i32x6 __attribute__((ext_vector_type(6)));
+  typedef __bf16 bf16x32 __attribute__((ext_vector_type(32)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  constexpr int RB = Tr<kFP6>::kRowBytes;
+  for (int i = threadIdx.x; i < 32 * 18; i += NT) {
+    const int r = i / 18;
+    const int j = i - r * 18;
+    const uint32_t a = (uint32_t)(size_t)(stage + r * RB + 24 * j);
+    const uint32_t as = (uint32_t)(size_t)(stage + r * RB + 432 + j);
+    u32x2 w0, w1, w2;
+    uint32_t e;
+    asm volatile(
+        "ds_read_b64 %0, %4\n"
+        "ds_read_b64 %1, %4 offset:8\n"
+        "ds_read_b64 %2, %4 offset:16\n"
+        "ds_read_u8 %3, %5\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(e)
+        : "v"(a), "v"(as)
+        : "memory");
+    const unsigned x0 = w0[0], x1 = w0[1], x2 = w1[0], x3 = w1[1], x4 = w2[0], x5 = w2[1];
+    const i32x6 codes = {(int)x0, (int)x1, (int)x2, (int)x3, (int)x4, (int)x5};
+    const bf16x32 v = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(codes, __builtin_amdgcn_ldexpf(1.f, (int)e - 127));
+    const u32x4* vv = (const u32x4*)&v;
+    char* dst = conv + r * kConvPad + 64 * j;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *(u32x4*)(dst + 16 * k) = vv[k];
+  }
+}
+
 // Value operands of four 16-dim blocks starting at block NB0: the low half
 // covers tile rows 0..15, the high half rows 16..31 (row pitch TP bytes).
 template <int TP, int NB0>

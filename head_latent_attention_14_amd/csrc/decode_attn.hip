@@ -333,8 +333,12 @@ mla_attn_kernel(AttnParams p) {
 template <int CT, int NP, int NSTAGE, bool PAGED, bool F8>
 __global__ void __launch_bounds__(128 * NP)
 mla_attn_pair_kernel(AttnParams p) {
-  static_assert(CT == kBF16 || CT == kFP8, "pair kernel: bf16 or fp8 cache");
+  static_assert(CT == kBF16 || CT == kFP8 || CT == kFP6, "pair kernel: bf16, fp8 or fp6 cache");
   static_assert(!F8 || CT == kFP8, "fp8 MFMA needs the fp8 cache");
+  // fp6: each tile is widened once into a bf16 tile in LDS (block scales
+  // applied, exact), and the bf16 contraction runs on it
+  constexpr int CC = (CT == kFP6) ? kBF16 : CT;          // element type the contractions read
+  constexpr int CONV_BYTES = (CT == kFP6) ? 32 * kConvPad : 0;
   constexpr int kF8Lift = 4;
   constexpr float kSlackP = F8 ? (float)(8 - kF8Lift) : kSlack;
   constexpr int NW = 2 * NP;
@@ -344,12 +348,12 @@ mla_attn_pair_kernel(AttnParams p) {
   constexpr int STAGE_BYTES = TileCopy<CT, NW>::STAGE_BYTES;
   constexpr int CPW = TileCopy<CT, NW>::CPW;
   constexpr int X_BYTES = NW * 4096;                     // one 32x32 fp32 partial per wave
-  constexpr int TP = RP;                                 // row pitch of the staged tile
-  constexpr int EB = (CT == kFP8) ? 1 : 2;               // bytes per staged element
+  constexpr int TP = (CT == kFP6) ? kConvPad : RP;       // row pitch of the tile computed on
+  constexpr int EB = (CC == kFP8) ? 1 : 2;               // bytes per element of that tile
   static_assert(NSTAGE >= 2, "ring needs two stages");
   static_assert(Tr<CT>::kTile == TILE, "32-token tiles");
 
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + X_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + X_BYTES + CONV_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -377,7 +381,7 @@ mla_attn_pair_kernel(AttnParams p) {
   // one 16-byte read of the codes feeds both; k-step 8 is 256 + 8g .. +7.
   // The contraction runs over the same elements either way.
   auto q_elem = [&](int j, int gg) {
-    if (CT == kFP8 && j < 8) return 288 * half + 64 * (j >> 1) + 16 * gg + 8 * (j & 1);
+    if (CC == kFP8 && j < 8) return 288 * half + 64 * (j >> 1) + 16 * gg + 8 * (j & 1);
     return 288 * half + 32 * j + 8 * gg;
   };
   bf16x8 q[2][9];
@@ -456,6 +460,8 @@ mla_attn_pair_kernel(AttnParams p) {
       (CT == kFP8) ? (uint32_t)(((tq < 4 ? 4 * g + tq : 16 + 4 * g + tq - 4)) * TP + 256 * half + 8 * (l16 & 1))
                    : (uint32_t)((4 * g + (l16 >> 2)) * TP + 2 * 256 * half + 8 * (l16 & 3));
   char* xbuf = smem + NSTAGE * STAGE_BYTES;
+  char* conv = xbuf + X_BYTES;                           // fp6: the widened tile
+  (void)conv;
   // F8: exponent G of the value weights (a large start: the first tile of a
   // segment lowers it)
   constexpr int kGStart = 127;
@@ -487,6 +493,11 @@ mla_attn_pair_kernel(AttnParams p) {
     const int64_t left = cc.t_end - cc.t;
     const int nvalid = left < TILE ? (int)left : TILE;
     const char* tb = stage;
+    if constexpr (CT == kFP6) {                          // whole tile widened to bf16 once
+      widen_fp6_tile_async<128 * NP>(stage, conv);
+      barrier_lds();
+      tb = conv;
+    }
 
     // ---------------- scores: this wave's half of the contraction ----------------
     f32x4 acc[2][2];                                     // [token block][head block]
@@ -791,6 +802,9 @@ hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipS
   MLA_PAIR(kFP8, 4, 4)
   MLA_PAIR(kFP8, 2, 4)
   MLA_PAIR(kFP8, 1, 4)
+  MLA_PAIR(kFP6, 4, 4)
+  MLA_PAIR(kFP6, 2, 4)
+  MLA_PAIR(kFP6, 1, 4)
 #undef MLA_PAIR
 #undef MLA_CASE
   return hipErrorInvalidValue;

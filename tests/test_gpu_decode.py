@@ -225,6 +225,26 @@ def test_other_head_counts():
         assert rel_l2(o, ro) <= TOL["bf16"], H
 
 
+@pytest.mark.parametrize("H", [32, 64, 96, 128])
+def test_fp6_cache_pair_kernel_widths(H):
+    # fp6 rows are widened tile by tile into bf16 in LDS inside the pair
+    # kernel: 32, 64 and 128 heads per workgroup (96 heads: three 32-head
+    # groups); every output against the oracle on the dequantised rows
+    p = W.make_problem(W.WORKLOADS["fp6_cache"], B=4, lengths=np.array([1, 33, 200, 1000]), H=H)
+    log(f"[fp6 pair] H={H} lengths={p.seq_len.tolist()}")
+    dp = DeviceProblem(p)
+    o, lse = dp.step(poison=True)
+    view = OracleView(p)
+    ro, rl = view.decode()
+    err = rel_l2(o, ro)
+    log(f"  rel-L2 {err:.3e} (bound {TOL['fp6']})")
+    assert np.all(np.isfinite(o))
+    assert err <= TOL["fp6"]
+    for b in range(4):
+        assert rel_l2(o[b], ro[b]) <= TOL["fp6"], b
+    check_lse(lse, rl, view, [(b, h) for b in range(4) for h in range(H)], "fp6")
+
+
 def test_prepared_calls_match_direct_calls():
     # the prepared binding marshals the same arguments once; results are bitwise equal
     import head_latent_attention_14_amd as mla

@@ -78,7 +78,7 @@ CASES = [
     ("v2lite_bf16", [1, 33, 300, 64, 129], 96),
     ("v2_bf16", [1, 33, 200, 97], 64),               # pair kernel (128 heads)
     ("fp8_cache", [1, 33, 200, 97], 32),             # fp8 pair kernel
-    ("fp6_cache", [1, 33, 200, 97], 32),             # fp6: block kernel over widened rows
+    ("fp6_cache", [1, 33, 200, 97], 32),             # fp6 pair kernel (tiles widened in LDS)
     ("tiny_fp32", [256, 40], 64),                    # f32 kernel (16-token tiles)
 ]
 
