@@ -17,8 +17,8 @@ against the bf16 MFMA peak, with a sampled parity check against the oracle.
 
 The headline workload is the DeepSeek-V2-shaped decode (B=32, H=128,
 L ~ U[2048, 8192], bf16 cache). The DeepSeek-V2-Lite step (B=64, H=16, with
-append), the 128K-token decode (B=4, H=128) and the fp8-cache decode (B=128,
-H=128) are measured the same way and reported under "workloads", each with
+append), the 128K-token decode (B=4, H=128) and the fp8- and fp6-cache
+decodes (B=128, H=128) are measured the same way and reported under "workloads", each with
 its own roofline block; they run first, so the headline is timed with the
 chip at its sustained clock. For each workload: W untimed warmup steps, then
 exactly K timed steps with events only at the ends of the timed region
@@ -51,7 +51,7 @@ METRIC = "MLA decode latent-cache GB/s + TFLOP/s, % of MI355X roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # dense, MI355X
 HEADLINE = "v2_bf16"
-OTHERS = ["v2lite_bf16", "long_bf16", "fp8_cache"]
+OTHERS = ["v2lite_bf16", "long_bf16", "fp8_cache", "fp6_cache"]
 PREFILLS = ["prefill_bf16", "prefill_chunk_fp8"]
 # every source that decides what the attention launch reads and writes: the
 # kernels, the work split (api.cpp, gemm_tile.h) and the shared headers
@@ -124,8 +124,8 @@ def cpu_baseline(p, seconds: float):
     blas, blas_threads = blas_info()
     view = OracleView(p)
     B, H = p.q_nope.shape[:2]
-    e_c = {"f32": 4, "bf16": 2, "fp8": 1}[p.wl.cache]
-    sf = 4 if p.wl.cache == "fp8" else 0
+    import workloads as W
+    row = W.ROW_BYTES[p.wl.cache] + (4 if p.wl.cache == "fp8" else 0)   # row (+ fp8 scale)
     e_a = {"f32": 4, "bf16": 2}[p.wl.act]
     t0 = time.perf_counter()
     done = 0           # sequences decoded (passes over the batch repeat it)
@@ -137,7 +137,7 @@ def cpu_baseline(p, seconds: float):
         done += 1
     el = time.perf_counter() - t0
     # the sample's share of the step's algorithmic bytes
-    by = tokens * (576 * e_c + sf) + 2 * H * 128 * 512 * e_a * done / B + done * H * (192 + 128) * e_a
+    by = tokens * row + 2 * H * 128 * 512 * e_a * done / B + done * H * (192 + 128) * e_a
     # the unabsorbed oracle's own fp64 work: K and V expansions plus scores and values
     flops = tokens * H * (4 * 128 * 512 + 2 * (128 + 64) + 2 * 128)
     cores = len(os.sched_getaffinity(0))
@@ -195,7 +195,7 @@ def parity_sample(p, o, lse, n_seq: int = 2):
     got = np.stack([o[b, h] for b, h in pairs])
     gl = np.array([lse[b, h] for b, h in pairs])
     err = float(np.linalg.norm(got - ro) / np.linalg.norm(ro))
-    bound = {"f32": 1e-5, "bf16": 2e-2, "fp8": 4e-2}[p.wl.cache]
+    bound = {"f32": 1e-5, "bf16": 2e-2, "fp8": 4e-2, "fp6": 4e-2}[p.wl.cache]
     return {"rel_l2": float(f"{err:.4g}"), "bound": bound, "ok": bool(err <= bound),
             "max_abs": float(f"{np.abs(got - ro).max():.4g}"),
             "lse_max_abs": float(f"{np.abs(gl - rl).max():.4g}"),
@@ -213,11 +213,10 @@ def measure(mla, W, torch, name: str, steps: int, warmup: int, replicas: int = 0
     ab = W.algorithmic_bytes(p)
     fl = W.algorithmic_flops(p)
     e_a = {"f32": 4, "bf16": 2}[wl.act]
-    e_c = {"f32": 4, "bf16": 2, "fp8": 1}[wl.cache]
     append_bytes = 0
     if wl.append:
         # h, W_DKV, W_KR read; one row written per token
-        append_bytes = B * wl.d_model * e_a + 576 * wl.d_model * e_a + B * 576 * e_c
+        append_bytes = B * wl.d_model * e_a + 576 * wl.d_model * e_a + B * W.ROW_BYTES[wl.cache]
     step_bytes = ab["total"] + append_bytes
     step_flops = fl["total"] + (2 * B * wl.d_model * 576 if wl.append else 0)
 
@@ -428,20 +427,34 @@ def describe(wl, m) -> str:
 
 
 def roofline(m, name: str) -> dict:
-    """The attention kernel against the HBM roofline (the binding bound at
-    every shape: its flop per cached byte is below the MFMA ridge), with its
-    matrix rate against the MFMA peak of the arithmetic it runs."""
+    """The attention kernel against the roofline that binds it: HBM when its
+    matrix flop per algorithmic byte is below the MFMA ridge (peak flop/s over
+    peak bytes/s), else the MFMA peak of the arithmetic it runs (bf16 MFMA
+    for bf16, fp8 and fp6 caches, whose rows are widened to bf16 in LDS).
+    Both rates are reported either way."""
     wl = m["wl"]
     gbs = m["attn_bytes"] / (m["attn_ms"] * 1e-3) / 1e9
     tf = m["attn_flops"] / (m["attn_ms"] * 1e-3) / 1e12
     mfma_dtype = "f32" if wl.cache == "f32" else "bf16"
-    return {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(name),
+    mfma_peak = MFMA_PEAK_TFLOPS[mfma_dtype]
+    t_hbm = m["attn_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = m["attn_flops"] / (mfma_peak * 1e12)
+    if t_mfma > t_hbm:
+        head = {"bound": "mfma", "achieved": round(tf, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(tf / mfma_peak, 4)}
+    else:
+        head = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return {**head, "traffic": recorded_traffic(name),
             "kernel": "attention (mla_decode_attend)",
             "kernel_avg_us": round(m["attn_ms"] * 1e3, 3),
             "algorithmic_bytes_per_launch": int(m["attn_bytes"]),
+            "algorithmic_flops_per_launch": int(m["attn_flops"]),
+            "flop_per_byte": round(m["attn_flops"] / m["attn_bytes"], 1),
+            "ridge_flop_per_byte": round(mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9), 1),
+            "gbs": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "tflops": round(tf, 2), "mfma_dtype": mfma_dtype,
-            "mfma_frac": round(tf / MFMA_PEAK_TFLOPS[mfma_dtype], 4)}
+            "mfma_frac": round(tf / mfma_peak, 4)}
 
 
 def main():
@@ -509,7 +522,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-cache/bf16"}[wl.cache],
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-cache/bf16", "fp6": "fp6-cache/bf16"}[wl.cache],
         "data": "synthetic (seeded normal draws; random-init weights of the DeepSeek-V2(-Lite) "
                 "MLA shapes)",
         "config": {"workload": describe(wl, m),
