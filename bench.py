@@ -52,7 +52,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # dense, MI355X
 HEADLINE = "v2_bf16"
 OTHERS = ["v2lite_bf16", "long_bf16", "fp8_cache", "fp6_cache"]
-PREFILLS = ["prefill_bf16", "prefill_chunk_fp8"]
+PREFILLS = ["prefill_bf16", "prefill_chunk_fp8", "prefill_chunk_fp6"]
 # every source that decides what the attention launch reads and writes: the
 # kernels, the work split (api.cpp, gemm_tile.h) and the shared headers
 KERNEL_SOURCES = sorted(glob.glob(os.path.join(ROOT, "head_latent_attention_14_amd", "csrc", "*")))

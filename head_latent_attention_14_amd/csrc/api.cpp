@@ -631,7 +631,8 @@ mla_status_t mla_prefill(const mla_cache_t* cache, const int32_t* seq_len, const
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARGUMENT;
   if (((uintptr_t)workspace & 255) != 0) return MLA_ERR_INVALID_ARGUMENT;
   if (act_dtype != MLA_DTYPE_BF16 ||
-      (cv.dtype != MLA_DTYPE_BF16 && cv.dtype != MLA_DTYPE_FP8_E4M3))
+      (cv.dtype != MLA_DTYPE_BF16 && cv.dtype != MLA_DTYPE_FP8_E4M3 &&
+       cv.dtype != MLA_DTYPE_FP6_E2M3_MX))
     return MLA_ERR_UNSUPPORTED;
   const PrefillLayout wl = prefill_layout(cv.num_seqs, n_heads, max_kv_rows);
   if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE_TOO_SMALL;

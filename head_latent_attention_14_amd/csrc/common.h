@@ -11,6 +11,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// microscaling FP6: 32 packed e2m3 codes (element i in bits 6i..6i+5) and
+// the 32 bf16 values the scaled hardware conversion makes of them
+typedef int fp6x32_words __attribute__((ext_vector_type(6)));
+typedef __bf16 bf16x32 __attribute__((ext_vector_type(32)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 

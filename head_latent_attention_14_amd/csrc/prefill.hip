@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
   const int L = ld_const(a.lenc, b);
   const int t0 = (int)(r0 - ld_const(a.kv_row0, b));
   const int64_t crow0 = ld_const(a.seq_start, b) + t0;   // cache row of packed row r0
-  constexpr int RB = (CT == kFP8) ? kDrow : kDrow * 2;   // bytes of a cache row
+  constexpr int RB = (CT == kFP8) ? kDrow : (CT == kFP6) ? 464 : kDrow * 2;   // bytes of a cache row
   const char* rows = (const char*)a.rows;
 
   if constexpr (CT == kFP8) {
@@ -142,12 +142,27 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
   constexpr int NX = (CT == kFP8) ? 2 : 4;             // 16-byte pieces of latent per thread
   struct Chunk {
     u32x4 x[NX];
+    uint2 c6[3];                                       // fp6: one 32-element block's codes
+    uint32_t e6;                                       //      and its scale code
     u32x4 k[4];
     u32x4 v[4];
   };
   auto load = [&](int k0, Chunk& c) {
+    if constexpr (CT == kFP6) {                        // thread: row tid/2, block k0/32 + tid%2
+      const int r = tid >> 1;
+      const int j = (k0 >> 5) + (tid & 1);
+      c.c6[0] = c.c6[1] = c.c6[2] = uint2{0u, 0u};
+      c.e6 = 127u;
+      if (t0 + r < L) {
+        const char* rp = rows + (crow0 + r) * RB;
+#pragma unroll
+        for (int m = 0; m < 3; ++m) c.c6[m] = *(const uint2*)(rp + 24 * j + 8 * m);
+        c.e6 = *(const unsigned char*)(rp + 432 + j);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NX; ++j) {
+      if constexpr (CT == kFP6) break;
       const int i = tid + 256 * j;
       const int r = (CT == kFP8) ? (i >> 2) : (i >> 3);
       const int p = (CT == kFP8) ? (i & 3) : (i & 7);
@@ -165,8 +180,20 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
     }
   };
   auto store = [&](const Chunk& c) {
+    if constexpr (CT == kFP6) {                        // 32 codes -> 32 exact bf16 values
+      const int r = tid >> 1;
+      const fp6x32_words codes = {(int)c.c6[0].x, (int)c.c6[0].y, (int)c.c6[1].x,
+                                  (int)c.c6[1].y, (int)c.c6[2].x, (int)c.c6[2].y};
+      const bf16x32 v = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(
+          codes, __builtin_amdgcn_ldexpf(1.f, (int)c.e6 - 127));
+      const u32x4* vv = (const u32x4*)&v;
+      char* dst = xs + r * XP + 64 * (tid & 1);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) *(u32x4*)(dst + 16 * m) = vv[m];
+    }
 #pragma unroll
     for (int j = 0; j < NX; ++j) {
+      if constexpr (CT == kFP6) break;
       const int i = tid + 256 * j;
       if constexpr (CT == kFP8) {                      // 16 codes -> 16 exact bf16 values
         const int r = i >> 2, p = i & 3;
@@ -250,7 +277,26 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
 
   // ---- the RoPE key of the 128 rows after K[h]'s 128 dims (bf16; fp8 codes
   // times the row scale, rounded once) ----
-  {
+  if constexpr (CT == kFP6) {                          // thread: row tid/2, block 16 + tid%2
+    char* kpe = (char*)a.k + ((int64_t)h * a.kv_rows + r0) * KW * 2 + 128 * 2;
+    const int r = tid >> 1;
+    const int j = 16 + (tid & 1);
+    u32x4 out[4] = {};
+    if (t0 + r < L) {
+      const char* rp = rows + (crow0 + r) * RB;
+      uint2 c[3];
+#pragma unroll
+      for (int m = 0; m < 3; ++m) c[m] = *(const uint2*)(rp + 24 * j + 8 * m);
+      const unsigned e = *(const unsigned char*)(rp + 432 + j);
+      const fp6x32_words codes = {(int)c[0].x, (int)c[0].y, (int)c[1].x, (int)c[1].y, (int)c[2].x, (int)c[2].y};
+      const bf16x32 v = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(codes, __builtin_amdgcn_ldexpf(1.f, (int)e - 127));
+      const u32x4* vv = (const u32x4*)&v;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) out[m] = vv[m];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) *(u32x4*)(kpe + (r * KW + 32 * (tid & 1) + 8 * m) * 2) = out[m];
+  } else {
     char* kpe = (char*)a.k + ((int64_t)h * a.kv_rows + r0) * KW * 2 + 128 * 2;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -546,6 +592,8 @@ hipError_t launch_prefill(int ct, const PrefillArgs& a, hipStream_t s) {
   const int64_t tiles = a.kv_rows / kPfRows;
   if (ct == kFP8)
     hipLaunchKernelGGL(mla_prefill_kv_kernel<kFP8>, dim3((unsigned)tiles, a.H), dim3(256), 0, s, a);
+  else if (ct == kFP6)
+    hipLaunchKernelGGL(mla_prefill_kv_kernel<kFP6>, dim3((unsigned)tiles, a.H), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(mla_prefill_kv_kernel<kBF16>, dim3((unsigned)tiles, a.H), dim3(256), 0, s, a);
   const int64_t items = (int64_t)a.H * ((a.n_q + kPfQ - 1) / kPfQ + a.B);

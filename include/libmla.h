@@ -387,7 +387,8 @@ mla_status_t mla_decode_noalloc(const mla_cache_t* cache, const int32_t* seq_len
  * s_t = softmax_scale * (q_nope . W_UK[h] c_t + q_pe . k_pe,t); it is computed
  * in the unabsorbed form (each cached row up-projected once to per-head K and
  * V, rounded to bf16 in the workspace).
- *   cache          contiguous cache, BF16 or FP8_E4M3 (F32: MLA_ERR_UNSUPPORTED).
+ *   cache          contiguous cache, BF16, FP8_E4M3 or FP6_E2M3_MX (F32:
+ *                  MLA_ERR_UNSUPPORTED).
  *   seq_len        device int32 [num_seqs], in [0, capacity].
  *   q_start        device int32 [num_seqs + 1], non-decreasing from 0 to n_q,
  *                  with n_b <= seq_len[b].

@@ -89,6 +89,8 @@ class PrefillOracleView:
         sl = p.rows[s:s + L]
         if self.dtype == "fp8":
             return e4m3_decode(sl.numpy()) * p.row_scale[s:s + L].to(torch.float64).numpy()[:, None]
+        if self.dtype == "fp6":
+            return mla.fp6_rows(sl.numpy())
         return sl.to(torch.float64).numpy()
 
     def prefill(self, heads=None):

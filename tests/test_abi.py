@@ -405,6 +405,9 @@ def test_prefill_validation():
     # f32 caches and non-bf16 activations are not supported
     assert pf(_cache(dtype=E.MLA_DTYPE_F32)) == E.MLA_ERR_UNSUPPORTED
     assert pf(_cache(), act=E.MLA_DTYPE_F32) == E.MLA_ERR_UNSUPPORTED
+    # fp6 caches pass validation up to the workspace check; their scales are in the rows
+    assert pf(_cache(dtype=E.MLA_DTYPE_FP6_E2M3_MX), ws_bytes=1) == E.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert pf(_cache(dtype=E.MLA_DTYPE_FP6_E2M3_MX, scale=FAKE)) == E.MLA_ERR_INVALID_ARGUMENT
     assert pf(_cache(), act=9) == E.MLA_ERR_INVALID_ARGUMENT
     # any head count; the workspace grows with heads and rows
     n1 = mla.mla_prefill_workspace_size(4, 1, 64, 1000)

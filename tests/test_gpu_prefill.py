@@ -4,10 +4,10 @@ oracle, through the C ABI.
 Small cases compare every output: whole-prompt prefill over ragged lengths
 (1 row, partial and several 64-row blocks), chunks after a cached prefix,
 several 256-query blocks per sequence, sequences without queries between
-others, fp8 caches, odd head counts. The full-size case (the benchmark's
+others, fp8 and fp6 caches, odd head counts. The full-size case (the benchmark's
 shape: 128 heads, four prompts of 2K-4K tokens) compares every query of
 sampled (sequence, head) pairs. Bounds: rel-L2 2e-2 on o (bf16 cache), 4e-2
-(fp8 cache, against the oracle on the dequantised rows); |lse error|
+(fp8 and fp6 caches, against the oracle on the dequantised rows); |lse error|
 <= 1e-2 + 1e-3 |lse|."""
 import math
 
@@ -79,9 +79,9 @@ def _check(p, o, lse, heads=None, label=""):
     return err
 
 
-@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+@pytest.mark.parametrize("cache", ["bf16", "fp8", "fp6"])
 def test_prefill_whole_prompts_small(cache):
-    name = "prefill_bf16" if cache == "bf16" else "prefill_chunk_fp8"
+    name = {"bf16": "prefill_bf16", "fp8": "prefill_chunk_fp8", "fp6": "prefill_chunk_fp6"}[cache]
     p = W.make_prefill_problem(W.PREFILL_WORKLOADS[name], lengths=[1, 37, 300, 64],
                                n_queries=[1, 37, 300, 64], H=16)
     log(f"[prefill small] {cache} lengths={p.seq_len.tolist()} H=16")
@@ -128,6 +128,16 @@ def test_prefill_fp8_chunk_small():
     log("[prefill fp8 chunk]")
     o, lse = DevicePrefill(p).run()
     _check(p, o, lse, label="fp8 chunk")
+
+
+def test_prefill_fp6_chunk_small():
+    # rows widened from microscaling FP6 (block scales applied) before the
+    # up-projection; the RoPE key from the last two blocks of each row
+    p = W.make_prefill_problem(W.PREFILL_WORKLOADS["prefill_chunk_fp6"], lengths=[900, 300, 129],
+                               n_queries=[300, 300, 1], H=16, seed=9)
+    log("[prefill fp6 chunk]")
+    o, lse = DevicePrefill(p).run()
+    _check(p, o, lse, label="fp6 chunk")
 
 
 def test_prefill_repeatable():

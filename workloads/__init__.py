@@ -145,13 +145,7 @@ def make_problem(wl: Workload, seed: Optional[int] = None, *, B: Optional[int] =
 
     row_scale = None
     if wl.cache == "fp6":
-        # any byte string is a valid packed run of 6-bit codes; block scale
-        # codes 120..127 (2^-7 .. 1); zero padding
-        r = np.zeros((total_rows, ROW_BYTES["fp6"]), dtype=np.uint8)
-        r[:, :FP6_CODE_BYTES] = rng.integers(0, 256, size=(total_rows, FP6_CODE_BYTES), dtype=np.uint8)
-        r[:, FP6_CODE_BYTES:FP6_CODE_BYTES + FP6_SCALES_PER_ROW] = rng.integers(
-            120, 128, size=(total_rows, FP6_SCALES_PER_ROW), dtype=np.uint8)
-        rows = torch.from_numpy(r)
+        rows = fp6_rows_random(rng, total_rows)
     else:
         z = _normal(rng, (total_rows, D_ROW))
         if wl.cache == "fp8":
@@ -212,6 +206,16 @@ def algorithmic_flops(p: Problem) -> dict:
     return {"attention": attn, "absorb_project": absorb, "total": attn + absorb}
 
 
+def fp6_rows_random(rng, n: int) -> torch.Tensor:
+    """n stored fp6 rows of random content: any byte string is a valid packed
+    run of 6-bit codes; block scale codes 120..127 (2^-7 .. 1); zero padding."""
+    r = np.zeros((n, ROW_BYTES["fp6"]), dtype=np.uint8)
+    r[:, :FP6_CODE_BYTES] = rng.integers(0, 256, size=(n, FP6_CODE_BYTES), dtype=np.uint8)
+    r[:, FP6_CODE_BYTES:FP6_CODE_BYTES + FP6_SCALES_PER_ROW] = rng.integers(
+        120, 128, size=(n, FP6_SCALES_PER_ROW), dtype=np.uint8)
+    return torch.from_numpy(r)
+
+
 # ----------------------------------------------------------------------------
 # prefill / multi-query problems: the last n_b positions of each sequence are
 # queries (n_b = L_b: a whole prompt; n_b < L_b: a chunk after a cached prefix)
@@ -224,7 +228,7 @@ class PrefillWorkload:
     H: int
     lo: int                # sequence length drawn uniformly in [lo, hi]
     hi: int
-    cache: str             # "bf16" | "fp8"
+    cache: str             # "bf16" | "fp8" | "fp6"
     chunk: int = 0         # 0: every position is a query; else n_b = min(chunk, L_b)
 
 
@@ -234,6 +238,9 @@ PREFILL_WORKLOADS = {
         PrefillWorkload("prefill_bf16", 10, B=4, H=128, lo=2048, hi=4096, cache="bf16"),
         # a 512-token chunk after a cached prefix, fp8 cache
         PrefillWorkload("prefill_chunk_fp8", 11, B=8, H=128, lo=1024, hi=6144, cache="fp8",
+                        chunk=512),
+        # the same chunked shape over the ~6-bit (microscaling FP6) cache
+        PrefillWorkload("prefill_chunk_fp6", 12, B=8, H=128, lo=1024, hi=6144, cache="fp6",
                         chunk=512),
     ]
 }
@@ -269,7 +276,8 @@ def make_prefill_problem(wl: PrefillWorkload, seed: Optional[int] = None, *,
                          n_queries: Optional[Sequence[int]] = None,
                          H: Optional[int] = None, canary: int = CANARY_ROWS) -> PrefillProblem:
     """Draw a prefill problem. Draw order (fixed): lengths, cache rows (fp8:
-    then one uniform per row for the scale), q_nope, q_pe, W_UK, W_UV."""
+    then one uniform per row for the scale; fp6: code bytes, then scale codes),
+    q_nope, q_pe, W_UK, W_UV."""
     rng = np.random.Generator(np.random.PCG64(wl.index if seed is None else seed))
     H = wl.H if H is None else H
     if lengths is None:
@@ -289,15 +297,18 @@ def make_prefill_problem(wl: PrefillWorkload, seed: Optional[int] = None, *,
     if B > 1:
         seq_start[1:] = np.cumsum(cap)[:-1]
     total_rows = int(cap.sum())
-    z = _normal(rng, (total_rows, D_ROW))
     row_scale = None
-    if wl.cache == "fp8":
-        rows = fp8_codes_from_normal(z)
-        u = rng.uniform(-0.5, 0.5, size=total_rows)
-        row_scale = torch.from_numpy((np.exp(u) / FP8_SPREAD).astype(np.float32))
+    if wl.cache == "fp6":
+        rows = fp6_rows_random(rng, total_rows)
     else:
-        rows = _to(z, wl.cache)
-    del z
+        z = _normal(rng, (total_rows, D_ROW))
+        if wl.cache == "fp8":
+            rows = fp8_codes_from_normal(z)
+            u = rng.uniform(-0.5, 0.5, size=total_rows)
+            row_scale = torch.from_numpy((np.exp(u) / FP8_SPREAD).astype(np.float32))
+        else:
+            rows = _to(z, wl.cache)
+        del z
     n_q = int(q_start[-1])
     w_std = 1.0 / np.sqrt(D_C)
     q_nope = _to(_normal(rng, (n_q, H, D_NOPE)), "bf16")
