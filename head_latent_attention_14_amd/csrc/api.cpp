@@ -36,12 +36,12 @@ DecodePlan make_plan(int ct, int B, int H) {
     p.nstage = 4;
     p.head_groups = H / 128;
   } else if ((ct == kBF16 || ct == kFP8 || ct == kFP6) && H % 32 == 0) {
-    // pair kernel: up to 128 heads (8 waves) per workgroup; the ring depth is
-    // what fits in LDS beside the score-exchange buffer (and, for fp6, the
-    // widened bf16 tile)
+    // pair kernels: up to 128 heads (8 waves) per workgroup; the ring depth
+    // is what fits in LDS beside the exchange buffers (and, for fp6, two
+    // widened bf16 tiles)
     p.pair = true;
     p.np = (H % 128 == 0) ? 4 : (H % 64 == 0) ? 2 : 1;
-    p.nstage = (ct != kBF16 || p.np == 1) ? 4 : 3;
+    p.nstage = (ct == kFP8 || (ct == kBF16 && p.np == 1)) ? 4 : 3;
     p.head_groups = H / (32 * p.np);
     p.f8 = ct == kFP8 && getenv_flag("MLA_FP8_MFMA");
   } else if (ct == kBF16) {

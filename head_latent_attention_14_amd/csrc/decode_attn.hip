@@ -311,7 +311,9 @@ mla_attn_kernel(AttnParams p) {
   }
 }
 
-// Pair kernel, for head counts that are multiples of 32 (bf16 or fp8 cache).
+// Pair kernel, for head counts that are multiples of 32 over an fp8 cache
+// (bf16 and fp6 caches run mla_attn_pair2_kernel below, which shares the
+// softmax between the two waves of a pair).
 // Two waves share 32 heads (two 16-head MFMA blocks): for the scores each
 // wave contracts one half of the 576-wide rows (k-steps 0..8 or 9..17) and
 // the two fp32 partials meet in LDS; for the values each wave accumulates
@@ -333,12 +335,7 @@ mla_attn_kernel(AttnParams p) {
 template <int CT, int NP, int NSTAGE, bool PAGED, bool F8>
 __global__ void __launch_bounds__(128 * NP)
 mla_attn_pair_kernel(AttnParams p) {
-  static_assert(CT == kBF16 || CT == kFP8 || CT == kFP6, "pair kernel: bf16, fp8 or fp6 cache");
-  static_assert(!F8 || CT == kFP8, "fp8 MFMA needs the fp8 cache");
-  // fp6: each tile is widened once into a bf16 tile in LDS (block scales
-  // applied, exact), and the bf16 contraction runs on it
-  constexpr int CC = (CT == kFP6) ? kBF16 : CT;          // element type the contractions read
-  constexpr int CONV_BYTES = (CT == kFP6) ? 32 * kConvPad : 0;
+  static_assert(CT == kFP8, "pair kernel: fp8 cache");
   constexpr int kF8Lift = 4;
   constexpr float kSlackP = F8 ? (float)(8 - kF8Lift) : kSlack;
   constexpr int NW = 2 * NP;
@@ -348,12 +345,11 @@ mla_attn_pair_kernel(AttnParams p) {
   constexpr int STAGE_BYTES = TileCopy<CT, NW>::STAGE_BYTES;
   constexpr int CPW = TileCopy<CT, NW>::CPW;
   constexpr int X_BYTES = NW * 4096;                     // one 32x32 fp32 partial per wave
-  constexpr int TP = (CT == kFP6) ? kConvPad : RP;       // row pitch of the tile computed on
-  constexpr int EB = (CC == kFP8) ? 1 : 2;               // bytes per element of that tile
+  constexpr int TP = RP;                                 // row pitch of the staged tile
   static_assert(NSTAGE >= 2, "ring needs two stages");
   static_assert(Tr<CT>::kTile == TILE, "32-token tiles");
 
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + X_BYTES + CONV_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE_BYTES + X_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -375,13 +371,13 @@ mla_attn_pair_kernel(AttnParams p) {
   };
 
   // query fragments (B operand of the score MFMA): head block hb, k-step j of
-  // this wave's half of the row (elements 288*half ..). bf16: lane group g
-  // holds elements 32j + 8g .. +7 of the half. fp8: k-steps 2m and 2m+1
-  // (m < 4) hold elements 64m + 16g .. +7 and 64m + 16g + 8 .. +15, so that
-  // one 16-byte read of the codes feeds both; k-step 8 is 256 + 8g .. +7.
-  // The contraction runs over the same elements either way.
+  // this wave's half of the row (elements 288*half ..): k-steps 2m and 2m+1
+  // (m < 4) hold elements 64m + 16g .. +7 and 64m + 16g + 8 .. +15 for lane
+  // group g, so that one 16-byte read of the codes feeds both; k-step 8 is
+  // 256 + 8g .. +7 (the contraction runs over the row's elements in another
+  // order than mla_attn_pair2_kernel's, with the same result up to rounding)
   auto q_elem = [&](int j, int gg) {
-    if (CC == kFP8 && j < 8) return 288 * half + 64 * (j >> 1) + 16 * gg + 8 * (j & 1);
+    if (j < 8) return 288 * half + 64 * (j >> 1) + 16 * gg + 8 * (j & 1);
     return 288 * half + 32 * j + 8 * gg;
   };
   bf16x8 q[2][9];
@@ -447,21 +443,15 @@ mla_attn_pair_kernel(AttnParams p) {
     for (int nb = 0; nb < 16; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // score A operand: tile row l16 (+16 for the second token block), k-step 9*half
-  const uint32_t s_base = (CT == kFP8) ? (uint32_t)(l16 * TP + half * 288)
-                                       : (uint32_t)(l16 * TP + g * 8 * EB + half * 9 * 32 * EB);
-  // transposing value reads. bf16: source lane (g, l16) points at row
-  // 4g + l16/4, dims 256*half + 4*(l16%4) .. +3. fp8: source lane (g, l16)
-  // points at row T(g, l16/2), dims 256*half + 8*(l16%2) .. +7, with
-  // T(g, q) = 4g + q for q < 4 and 16 + 4g + (q - 4) otherwise, so that lane
-  // (n, g) receives dim n of tokens 4g..4g+3 and 16+4g..16+4g+3: the token
-  // order of the bf16 reads and of the P operand
+  const uint32_t s_base = (uint32_t)(l16 * TP + half * 288);
+  // transposing value reads: source lane (g, l16) points at row T(g, l16/2),
+  // dims 256*half + 8*(l16%2) .. +7, with T(g, q) = 4g + q for q < 4 and
+  // 16 + 4g + (q - 4) otherwise, so that lane (n, g) receives dim n of
+  // tokens 4g..4g+3 and 16+4g..16+4g+3: the token order of the P operand
   const int tq = l16 >> 1;
   const uint32_t tr_lane =
-      (CT == kFP8) ? (uint32_t)(((tq < 4 ? 4 * g + tq : 16 + 4 * g + tq - 4)) * TP + 256 * half + 8 * (l16 & 1))
-                   : (uint32_t)((4 * g + (l16 >> 2)) * TP + 2 * 256 * half + 8 * (l16 & 3));
+      (uint32_t)(((tq < 4 ? 4 * g + tq : 16 + 4 * g + tq - 4)) * TP + 256 * half + 8 * (l16 & 1));
   char* xbuf = smem + NSTAGE * STAGE_BYTES;
-  char* conv = xbuf + X_BYTES;                           // fp6: the widened tile
-  (void)conv;
   // F8: exponent G of the value weights (a large start: the first tile of a
   // segment lowers it)
   constexpr int kGStart = 127;
@@ -493,11 +483,6 @@ mla_attn_pair_kernel(AttnParams p) {
     const int64_t left = cc.t_end - cc.t;
     const int nvalid = left < TILE ? (int)left : TILE;
     const char* tb = stage;
-    if constexpr (CT == kFP6) {                          // whole tile widened to bf16 once
-      widen_fp6_tile_async<128 * NP>(stage, conv);
-      barrier_lds();
-      tb = conv;
-    }
 
     // ---------------- scores: this wave's half of the contraction ----------------
     f32x4 acc[2][2];                                     // [token block][head block]
@@ -516,7 +501,7 @@ mla_attn_pair_kernel(AttnParams p) {
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
       bf16x8 a0, a1;
-      if constexpr (CT == kFP8) {                        // codes widened in registers
+      {                                                  // codes widened in registers
         uint2 u0, u1;
         if (k < 8) {
           if (k == 0) lds_read_b128_x2<0, 16 * TP>(a16, c8[0][0], c8[1][0]);
@@ -531,9 +516,6 @@ mla_attn_pair_kernel(AttnParams p) {
         }
         a0 = fp8x8_to_bf16x8(u0);
         a1 = fp8x8_to_bf16x8(u1);
-      } else {
-        a0 = *(const bf16x8*)(sa + k * 64);
-        a1 = *(const bf16x8*)(sa + 16 * TP + k * 64);
       }
       acc[0][0] = mfma_bf16_k32(a0, q[0][k], acc[0][0]);
       acc[0][1] = mfma_bf16_k32(a0, q[1][k], acc[0][1]);
@@ -556,23 +538,17 @@ mla_attn_pair_kernel(AttnParams p) {
     for (int i = 0; i < 4; ++i) acc[i >> 1][i & 1] += *(const f32x4*)(xp + i * 1024);
 
     // ---------------- online softmax per head block ----------------
-    // fp8 row scales of tokens 4g.. and 16 + 4g.. (1 otherwise)
+    // row scales of tokens 4g.. and 16 + 4g..
     u32x4 scl8[2];
-    if constexpr (CT == kFP8)
-      lds_read_b128_x2<0, 64>((uint32_t)(size_t)(stage + STAGE_DATA) + 16 * g, scl8[0], scl8[1]);
-    float tsc[8];                                        // fp8 row scales (1 otherwise)
+    lds_read_b128_x2<0, 64>((uint32_t)(size_t)(stage + STAGE_DATA) + 16 * g, scl8[0], scl8[1]);
+    float tsc[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if constexpr (CT == kFP8) {
-        // (the element goes through a plain variable: a bit cast of a vector
-        // element expression read the vector's first element here)
-        const unsigned int w0 = scl8[0][r], w1 = scl8[1][r];
-        tsc[r] = __builtin_bit_cast(float, w0);
-        tsc[4 + r] = __builtin_bit_cast(float, w1);
-      } else {
-        tsc[r] = 1.f;
-        tsc[4 + r] = 1.f;
-      }
+      // (the element goes through a plain variable: a bit cast of a vector
+      // element expression read the vector's first element here)
+      const unsigned int w0 = scl8[0][r], w1 = scl8[1][r];
+      tsc[r] = __builtin_bit_cast(float, w0);
+      tsc[4 + r] = __builtin_bit_cast(float, w1);
     }
     float sc[2][8];
     float tmax[2];
@@ -669,19 +645,11 @@ mla_attn_pair_kernel(AttnParams p) {
         continue;
       }
       bf16x8 a[4];
-      if constexpr (CT == kFP8) {
+      {
         uint2 v[4];
         lds_tr8_x4<0, 16, 32, 48>(tr_addr + n0 * 16, v[0], v[1], v[2], v[3]);
 #pragma unroll
         for (int k = 0; k < 4; ++k) a[k] = fp8x8_to_bf16x8(v[k]);
-      } else {
-        s16x4 lo[4], hi[4];
-        pv_read4<TP, 0>(tr_addr + n0 * 32, lo, hi);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const s16x8 a8 = {lo[k][0], lo[k][1], lo[k][2], lo[k][3], hi[k][0], hi[k][1], hi[k][2], hi[k][3]};
-          a[k] = __builtin_bit_cast(bf16x8, a8);
-        }
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -730,13 +698,335 @@ mla_attn_pair_kernel(AttnParams p) {
   }
 }
 
+// Pair kernel with the softmax shared between the two waves of a pair and
+// the value product one tile behind the scores. Same contractions and the
+// same work split as mla_attn_pair_kernel; what changes:
+//  * each wave runs the online softmax of one of the pair's two 16-head
+//    blocks (wave half 0: heads 0..15 of the pair, half 1: heads 16..31):
+//    the score partials cross in LDS only for the other wave's block, and
+//    the probabilities (bf16), the rescale factor and the running sum of
+//    each block go to the other wave through LDS;
+//  * the values of tile t run after the barrier that opens tile t+1, so
+//    that barrier also publishes tile t's probabilities (no extra barrier);
+//    tile t's stage (and, for fp6, its widened copy) stays in LDS until
+//    then, and the copies into that stage go out after the score exchange
+//    of tile t+1, which every wave reaches only after its values of tile t;
+//  * a segment's last tile loads the next segment's queries right after its
+//    score MFMAs, so they arrive during the exchange and the softmax.
+template <int CT, int NP, int NSTAGE, bool PAGED>
+__global__ void __launch_bounds__(128 * NP)
+mla_attn_pair2_kernel(AttnParams p) {
+  static_assert(CT == kBF16 || CT == kFP6, "shared-softmax pair kernel: bf16 or fp6 cache");
+  constexpr int CONV_BYTES = (CT == kFP6) ? 2 * 32 * kConvPad : 0;   // two widened tiles
+  constexpr int NW = 2 * NP;
+  constexpr int TILE = 32;
+  constexpr int RP = Tr<CT>::kPad;
+  constexpr int STAGE_BYTES = TileCopy<CT, NW>::STAGE_BYTES;
+  constexpr int CPW = TileCopy<CT, NW>::CPW;
+  constexpr int X_BYTES = NW * 2048;                     // the other block's 32x16 fp32 partial
+  constexpr int P_BYTES = NW * 1536;                     // probabilities, alpha, running sum
+  constexpr int TP = (CT == kFP6) ? kConvPad : RP;       // row pitch of the tile computed on
+  static_assert(NSTAGE >= 3, "a tile stays until the next tile's exchange");
+  static_assert(Tr<CT>::kTile == TILE, "32-token tiles");
+
+  __shared__ __attribute__((aligned(1024)))
+      char smem[NSTAGE * STAGE_BYTES + X_BYTES + P_BYTES + CONV_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int half = wave & 1;                             // also this wave's softmax head block
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int H = p.H;
+  const int B = p.B;
+  const int hp = (blockIdx.y * NP + (wave >> 1)) * 32;  // first head of the pair
+  const int64_t w = blockIdx.x;
+  int64_t r_hi;
+  const Cursor c0 = cursor_start<TILE, PAGED>(p, w, lane, r_hi);
+  if (c0.b < 0) return;                                  // whole workgroup
+
+  TileCopy<CT, NW> cp;
+  cp.init(wave, lane);
+  auto issue = [&](const Cursor& c, int stage) {
+    cp.issue(p.rows, p.row_scale, c, smem + stage * STAGE_BYTES, lane);
+  };
+
+  // query fragments (B operand of the score MFMA): head block hb, k-step j of
+  // this wave's half of the row (elements 288*half ..): lane group g holds
+  // elements 32j + 8g .. +7 of the half
+  auto q_elem = [&](int j, int gg) { return 288 * half + 32 * j + 8 * gg; };
+  bf16x8 q[2][9];
+  auto load_q = [&](int b) {
+    const int ln = opaque(lane);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int64_t base = (int64_t)b * H + hp + 16 * hb + (ln & 15);
+      const __bf16* ql = (const __bf16*)p.q_lat + base * kDc;
+      const __bf16* qp = (const __bf16*)p.q_pe + base * kDr;
+#pragma unroll
+      for (int j = 0; j < 9; ++j) {
+        const int e = q_elem(j, ln >> 4);
+        const __bf16* src = e < kDc ? ql + e : qp + (e - kDc);
+        q[hb][j] = *(const bf16x8*)src;
+      }
+    }
+  };
+  auto settle_q = [&]() {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int j = 0; j < 9; ++j) asm volatile("" : "+v"(q[hb][j]));
+  };
+  Cursor lc = c0;
+  issue(lc, 0);
+  bool lvalid = advance<TILE, PAGED>(lc, p, r_hi, lane);
+  {
+    int b0 = c0.b;
+    asm volatile("" : "+s"(b0) :: "memory");
+    load_q(b0);
+  }
+#pragma unroll
+  for (int i = 1; i < NSTAGE - 1; ++i) {
+    issue(lvalid ? lc : c0, i);
+    if (lvalid) lvalid = advance<TILE, PAGED>(lc, p, r_hi, lane);
+  }
+  int issued = NSTAGE - 1;
+  wait_vmcnt<(NSTAGE - 2) * CPW>();
+  settle_q();
+
+  float m_own = -INFINITY;     // running max of this wave's head block (log2 domain)
+  float l_own = 0.f;           // this lane's share of its running sum
+  f32x4 o[2][16];              // O^T: dims 256*half + 16*nb + 4g + r, head l16 of block hb
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // score A operand: tile row l16 (+16 for the second token block), k-step 9*half
+  const uint32_t s_base = (uint32_t)(l16 * TP + g * 16 + half * 9 * 64);
+  // transposing value reads: source lane (g, l16) points at row 4g + l16/4,
+  // dims 256*half + 4*(l16%4) .. +3
+  const uint32_t tr_lane = (uint32_t)((4 * g + (l16 >> 2)) * TP + 2 * 256 * half + 8 * (l16 & 3));
+  char* xbuf = smem + NSTAGE * STAGE_BYTES;
+  char* pbuf = xbuf + X_BYTES;
+  char* conv = pbuf + P_BYTES;                           // fp6: two widened tiles
+  (void)conv;
+  // this wave's slots: partial for the other block, probabilities (16 B per
+  // lane), alpha and running sum (4 B per lane each)
+  char* xw = xbuf + wave * 2048 + lane * 16;
+  const char* xp = xbuf + (wave ^ 1) * 2048 + lane * 16;
+  char* pw = pbuf + wave * 1536;
+  const char* pp = pbuf + (wave ^ 1) * 1536;
+
+  // the previous tile, whose values are still to be added
+  bool have_prev = false;
+  const char* prev_tb = nullptr;
+  bf16x8 pb_own = {};
+  bool prev_seg_end = false;
+  int prev_b = 0;
+
+  // values of the previous tile (both head blocks of this wave's 256 dims),
+  // then, at its segment's end, the partial
+  auto finish_prev = [&]() {
+    const bf16x8 pb_oth = *(const bf16x8*)(pp + lane * 16);
+    const float a_oth = *(const float*)(pp + 1024 + lane * 4);
+    const float l_oth = *(const float*)(pp + 1280 + lane * 4);
+    if (__any(a_oth != 1.f)) {                           // the other block's max moved
+      const float a0 = half ? a_oth : 1.f, a1 = half ? 1.f : a_oth;
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb) {
+        o[0][nb] *= a0;
+        o[1][nb] *= a1;
+      }
+    }
+    const bf16x8 pb0 = half ? pb_oth : pb_own;
+    const bf16x8 pb1 = half ? pb_own : pb_oth;
+    const uint32_t tr_addr = (uint32_t)(size_t)prev_tb + tr_lane;
+#pragma unroll
+    for (int n0 = 0; n0 < 16; n0 += 4) {
+      bf16x8 a[4];
+      {
+        s16x4 lo[4], hi[4];
+        pv_read4<TP, 0>(tr_addr + n0 * 32, lo, hi);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const s16x8 a8 = {lo[k][0], lo[k][1], lo[k][2], lo[k][3], hi[k][0], hi[k][1], hi[k][2], hi[k][3]};
+          a[k] = __builtin_bit_cast(bf16x8, a8);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o[0][n0 + k] = mfma_bf16_k32(a[k], pb0, o[0][n0 + k]);
+        o[1][n0 + k] = mfma_bf16_k32(a[k], pb1, o[1][n0 + k]);
+      }
+    }
+    if (prev_seg_end) {
+      const int64_t slot = w + prev_b;
+      const int ln = opaque(lane);
+      const float ls_own = sum_over_groups(l_own);
+      const float ls_oth = sum_over_groups(l_oth);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const float lsum = (hb == half) ? ls_own : ls_oth;
+        const int h = hp + 16 * hb + (ln & 15);
+        const float inv = inv_or_zero(lsum);
+        const int64_t po = (slot * H + h) * kDc + 256 * half + 4 * (ln >> 4);
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) store_part4<CT>(p.part_o, po + nb * 16, o[hb][nb], inv);
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      if ((ln >> 4) == 0) {                              // the block's owner writes (m, l)
+        const int h = hp + 16 * half + (ln & 15);
+        p.part_ml[(slot * H + h) * 2 + 0] = m_own;
+        p.part_ml[(slot * H + h) * 2 + 1] = ls_own;
+      }
+      m_own = -INFINITY;
+      l_own = 0.f;
+    }
+  };
+
+  Cursor cc = c0;
+  int it = 0;
+  while (true) {
+    // this wave's copies of tile `it` landed
+    wait_tiles<CPW, NSTAGE - 2>(issued - 1 - it);
+    barrier_lds();            // tile `it` and the previous tile's probabilities visible
+    const bool do_copy = lvalid;
+    typename TileCopy<CT, NW>::Pending pend;
+    if (do_copy) {
+      pend = cp.prepare(p.rows, p.row_scale, lc, smem + (issued % NSTAGE) * STAGE_BYTES);
+      ++issued;
+      lvalid = advance<TILE, PAGED>(lc, p, r_hi, lane);
+    }
+    const char* stage = smem + (it % NSTAGE) * STAGE_BYTES;
+    const int64_t left = cc.t_end - cc.t;
+    const int nvalid = left < TILE ? (int)left : TILE;
+    const char* tb = stage;
+    if constexpr (CT == kFP6) {
+      char* cv = conv + (it & 1) * (32 * kConvPad);
+      widen_fp6_tile_async<128 * NP>(stage, cv);
+      barrier_lds();
+      tb = cv;
+    }
+    if (have_prev) finish_prev();
+
+    // ---------------- scores: this wave's half of the contraction ----------------
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const char* sa = tb + s_base;
+    // one batch of nine k-steps; the compiler places the 18 operand reads
+    // among the 36 MFMAs as registers allow
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const bf16x8 a0 = *(const bf16x8*)(sa + k * 64);
+      const bf16x8 a1 = *(const bf16x8*)(sa + 16 * TP + k * 64);
+      acc[0][0] = mfma_bf16_k32(a0, q[0][k], acc[0][0]);
+      acc[0][1] = mfma_bf16_k32(a0, q[1][k], acc[0][1]);
+      acc[1][0] = mfma_bf16_k32(a1, q[0][k], acc[1][0]);
+      acc[1][1] = mfma_bf16_k32(a1, q[1][k], acc[1][1]);
+    }
+    // a segment's last tile: the next segment's queries go out now
+    const bool seg_end = (cc.t + TILE >= cc.t_end);
+    const int nseq = seg_end ? next_segment_seq<PAGED>(cc, p, r_hi) : -1;
+    if (nseq >= 0) load_q(nseq);
+    __builtin_amdgcn_sched_barrier(0);
+    // the other block's partial to the other wave; its partial of this block back
+    const f32x4 x0 = half ? acc[0][0] : acc[0][1];
+    const f32x4 x1 = half ? acc[1][0] : acc[1][1];
+    *(f32x4*)(xw) = x0;
+    *(f32x4*)(xw + 1024) = x1;
+    barrier_lds();            // every wave's values of the previous tile are done
+    f32x4 s0 = half ? acc[0][1] : acc[0][0];
+    f32x4 s1 = half ? acc[1][1] : acc[1][0];
+    s0 += *(const f32x4*)(xp);
+    s1 += *(const f32x4*)(xp + 1024);
+    // the freed stage (the previous tile's) takes the next tile
+    if (do_copy) {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) cp.copy(pend, i);
+    }
+
+    // ---------------- online softmax of this wave's head block ----------------
+    float sc[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[r] = s0[r] * p.scale_log2;
+      sc[4 + r] = s1[r] * p.scale_log2;
+    }
+    if (nvalid < TILE) {
+      const int g4 = 4 * (opaque(lane) >> 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (g4 >= nvalid - r) sc[r] = -INFINITY;
+        if (g4 >= nvalid - 16 - r) sc[4 + r] = -INFINITY;
+      }
+    }
+    float t = sc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) t = __builtin_fmaxf(t, sc[i]);
+    const float tmax = max_over_groups(t);
+    float alpha = 1.f;
+    if (__any(tmax > m_own + kSlack)) {                  // lazy rescale (see the pair kernel)
+      const float m_new = __builtin_fmaxf(m_own, tmax);
+      alpha = __builtin_amdgcn_exp2f(m_own - m_new);
+      l_own *= alpha;
+      const float a0 = half ? 1.f : alpha, a1 = half ? alpha : 1.f;
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb) {
+        o[0][nb] *= a0;
+        o[1][nb] *= a1;
+      }
+      m_own = m_new;
+    }
+    const float m_use = (m_own == -INFINITY) ? 0.f : m_own;
+    float pv[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e = __builtin_amdgcn_exp2f(sc[i] - m_use);
+      psum += e;
+      pv[i] = e;
+    }
+    l_own += psum;
+    pb_own = pack_bf16x8(pv);
+    *(bf16x8*)(pw + lane * 16) = pb_own;
+    *(float*)(pw + 1024 + lane * 4) = alpha;
+    *(float*)(pw + 1280 + lane * 4) = l_own;
+
+    have_prev = true;
+    prev_tb = tb;
+    prev_seg_end = seg_end;
+    prev_b = (int)cc.b;
+    if (!advance<TILE, PAGED>(cc, p, r_hi, lane)) break;
+    if (seg_end) {
+      // the next segment's queries have landed (the copies just issued, if
+      // any, may stay in flight)
+      if (do_copy) wait_vmcnt<CPW>();
+      else wait_vmcnt<0>();
+      settle_q();
+    }
+    ++it;
+  }
+  barrier_lds();              // the last tile's probabilities visible
+  finish_prev();
+}
+
 // ------------------------------------------------------------------ launch
 template <int CT, int NP, int NSTAGE, bool F8>
 static void launch_pair_f(const AttnParams& prm, dim3 grid, dim3 block, hipStream_t s) {
-  if (prm.block_table)
-    hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE, true, F8>), grid, block, 0, s, prm);
-  else
-    hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE, false, F8>), grid, block, 0, s, prm);
+  if constexpr (!F8 && CT != kFP8) {                   // bf16, fp6: the shared-softmax kernel
+    if (prm.block_table)
+      hipLaunchKernelGGL((mla_attn_pair2_kernel<CT, NP, NSTAGE, true>), grid, block, 0, s, prm);
+    else
+      hipLaunchKernelGGL((mla_attn_pair2_kernel<CT, NP, NSTAGE, false>), grid, block, 0, s, prm);
+  } else {                                               // fp8 (and its fp8-MFMA variant)
+    if (prm.block_table)
+      hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE, true, F8>), grid, block, 0, s, prm);
+    else
+      hipLaunchKernelGGL((mla_attn_pair_kernel<CT, NP, NSTAGE, false, F8>), grid, block, 0, s, prm);
+  }
 }
 template <int CT, int NP, int NSTAGE>
 static hipError_t launch_pair_t(const AttnParams& prm, bool f8, int workers, int head_groups,
@@ -802,9 +1092,9 @@ hipError_t launch_attn(int ct, const DecodePlan& plan, const DecodeArgs& a, hipS
   MLA_PAIR(kFP8, 4, 4)
   MLA_PAIR(kFP8, 2, 4)
   MLA_PAIR(kFP8, 1, 4)
-  MLA_PAIR(kFP6, 4, 4)
-  MLA_PAIR(kFP6, 2, 4)
-  MLA_PAIR(kFP6, 1, 4)
+  MLA_PAIR(kFP6, 4, 3)
+  MLA_PAIR(kFP6, 2, 3)
+  MLA_PAIR(kFP6, 1, 3)
 #undef MLA_PAIR
 #undef MLA_CASE
   return hipErrorInvalidValue;
