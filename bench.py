@@ -427,15 +427,18 @@ def describe(wl, m) -> str:
 
 
 def roofline(m, name: str) -> dict:
-    """The attention kernel against the roofline that binds it: HBM when its
-    matrix flop per algorithmic byte is below the MFMA ridge (peak flop/s over
-    peak bytes/s), else the MFMA peak of the arithmetic it runs (bf16 MFMA
-    for bf16, fp8 and fp6 caches, whose rows are widened to bf16 in LDS).
-    Both rates are reported either way."""
+    """The attention kernel against the roofline that binds the workload: HBM
+    when its matrix flop per algorithmic byte is below the MFMA ridge (peak
+    flop/s over peak bytes/s), else the MFMA peak. The MFMA peak is that of
+    the narrowest matrix arithmetic the cache format allows (bf16 for a bf16
+    cache, fp8 for the fp8 and fp6 caches, fp32 for fp32), whatever
+    instructions the kernel runs; both rates are reported either way, and the
+    matrix rate also against the bf16 peak (the fp8 and fp6 caches are
+    contracted on bf16 MFMA after widening)."""
     wl = m["wl"]
     gbs = m["attn_bytes"] / (m["attn_ms"] * 1e-3) / 1e9
     tf = m["attn_flops"] / (m["attn_ms"] * 1e-3) / 1e12
-    mfma_dtype = "f32" if wl.cache == "f32" else "bf16"
+    mfma_dtype = {"f32": "f32", "bf16": "bf16"}.get(wl.cache, "fp8")
     mfma_peak = MFMA_PEAK_TFLOPS[mfma_dtype]
     t_hbm = m["attn_bytes"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = m["attn_flops"] / (mfma_peak * 1e12)
@@ -445,6 +448,7 @@ def roofline(m, name: str) -> dict:
     else:
         head = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    used = "f32" if wl.cache == "f32" else "bf16"
     return {**head, "traffic": recorded_traffic(name),
             "kernel": "attention (mla_decode_attend)",
             "kernel_avg_us": round(m["attn_ms"] * 1e3, 3),
@@ -454,7 +458,8 @@ def roofline(m, name: str) -> dict:
             "ridge_flop_per_byte": round(mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9), 1),
             "gbs": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "tflops": round(tf, 2), "mfma_dtype": mfma_dtype,
-            "mfma_frac": round(tf / mfma_peak, 4)}
+            "mfma_frac": round(tf / mfma_peak, 4),
+            "mfma_used": used, "mfma_used_frac": round(tf / MFMA_PEAK_TFLOPS[used], 4)}
 
 
 def main():
