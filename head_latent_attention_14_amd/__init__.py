@@ -38,7 +38,7 @@ EXPORTED = ["mla_append", "mla_decode_workspace_size", "mla_decode", "mla_decode
             "mla_decode_attend", "mla_decode_combine", "mla_decode_attend_combine",
             "mla_append_absorb", "mla_decode_noalloc", "mla_append_yarn",
             "mla_yarn_softmax_factor", "mla_append_paged", "mla_decode_paged",
-            "mla_prefill_workspace_size", "mla_prefill", "mla_status_string",
+            "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_paged", "mla_status_string",
             "mla_abi_version"]
 DECODE_STAGES = ["mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
                  "mla_decode_attend_combine"]
@@ -120,7 +120,10 @@ def _load(path: str = LIB_PATH):
     lib.mla_prefill_workspace_size.restype = ctypes.c_int
     lib.mla_prefill.argtypes = [C, P, P, I64, I64, P, P, P, P, ctypes.c_int, I32, F32, P, P,
                                 P, SZ, P]
+    lib.mla_prefill_paged.argtypes = [PC, P, P, I64, I64, P, P, P, P, ctypes.c_int, I32, F32, P,
+                                      P, P, SZ, P]
     lib.mla_prefill.restype = ctypes.c_int
+    lib.mla_prefill_paged.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -577,12 +580,13 @@ def alloc_prefill_workspace(cache: LatentCache, n_heads: int, n_q: int, max_kv_r
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device or cache.rows.device)
 
 
-def mla_prefill(cache: LatentCache, seq_len: torch.Tensor, q_start: torch.Tensor,
+def mla_prefill(cache, seq_len: torch.Tensor, q_start: torch.Tensor,
                 max_kv_rows: int, q_nope: torch.Tensor, q_pe: torch.Tensor, w_uk: torch.Tensor,
                 w_uv: torch.Tensor, softmax_scale: float, out: torch.Tensor,
                 lse: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
     """Causal multi-query attention: query rows q_start[b]..q_start[b+1]-1 are
-    sequence b's last positions (see libmla.h)."""
+    sequence b's last positions (see libmla.h). A PagedLatentCache runs
+    mla_prefill_paged."""
     cache.check()
     dev = cache.rows.device
     B = cache.num_seqs
@@ -604,7 +608,9 @@ def mla_prefill(cache: LatentCache, seq_len: torch.Tensor, q_start: torch.Tensor
             or workspace.dim() != 1 or workspace.device != dev:
         raise ValueError(f"workspace must be a 1-D uint8 tensor on {dev}")
     st = ctypes.byref(cache.struct())
-    _check(lib.mla_prefill(st, _ptr(seq_len), _ptr(q_start), n_q, int(max_kv_rows), _ptr(q_nope),
-                           _ptr(q_pe), _ptr(w_uk), _ptr(w_uv), MLA_DTYPE_BF16, H,
-                           float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
-                           workspace.numel(), _stream(stream)), "mla_prefill")
+    fn, name = ((lib.mla_prefill_paged, "mla_prefill_paged") if isinstance(cache, PagedLatentCache)
+                else (lib.mla_prefill, "mla_prefill"))
+    _check(fn(st, _ptr(seq_len), _ptr(q_start), n_q, int(max_kv_rows), _ptr(q_nope),
+              _ptr(q_pe), _ptr(w_uk), _ptr(w_uv), MLA_DTYPE_BF16, H,
+              float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+              workspace.numel(), _stream(stream)), name)

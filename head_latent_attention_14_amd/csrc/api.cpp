@@ -613,18 +613,14 @@ static mla_status_t debug_check_prefill(const CacheView& c, const int32_t* seq_l
   return MLA_OK;
 }
 
-extern "C" {
-
-mla_status_t mla_prefill(const mla_cache_t* cache, const int32_t* seq_len, const int32_t* q_start,
-                         int64_t n_q, int64_t max_kv_rows, const void* q_nope, const void* q_pe,
-                         const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
-                         int32_t n_heads, float softmax_scale, void* out, float* lse,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-  CacheView cv;
-  mla_status_t st = view_of(cache, cv);
-  if (st != MLA_OK) return st;
+static mla_status_t prefill_view(const CacheView& cv, const int32_t* seq_len,
+                                 const int32_t* q_start, int64_t n_q, int64_t max_kv_rows,
+                                 const void* q_nope, const void* q_pe, const void* w_uk,
+                                 const void* w_uv, mla_dtype_t act_dtype, int32_t n_heads,
+                                 float softmax_scale, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   if (!valid_dtype(act_dtype)) return MLA_ERR_INVALID_ARGUMENT;
-  st = prefill_shape(cv.num_seqs, n_heads, n_q, max_kv_rows);
+  mla_status_t st = prefill_shape(cv.num_seqs, n_heads, n_q, max_kv_rows);
   if (st != MLA_OK) return st;
   if (!seq_len || !q_start || !q_nope || !q_pe || !w_uk || !w_uv || !out || !workspace)
     return MLA_ERR_INVALID_ARGUMENT;
@@ -647,6 +643,10 @@ mla_status_t mla_prefill(const mla_cache_t* cache, const int32_t* seq_len, const
   a.row_scale = cv.row_scale;
   a.seq_start = cv.seq_start;
   a.seq_cap = cv.seq_cap;
+  a.block_table = cv.block_table;
+  a.max_pages = cv.max_pages;
+  a.page_tokens = cv.page_tokens;
+  a.page_limit = (uint32_t)(cv.total_pages < (int64_t)1 << 31 ? cv.total_pages : (int64_t)1 << 31);
   a.seq_len = seq_len;
   a.q_start = q_start;
   a.n_q = n_q;
@@ -668,6 +668,33 @@ mla_status_t mla_prefill(const mla_cache_t* cache, const int32_t* seq_len, const
   a.v = ws + wl.v;
   const hipError_t e = launch_prefill(cache_type(cv.dtype), a, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+extern "C" {
+
+mla_status_t mla_prefill(const mla_cache_t* cache, const int32_t* seq_len, const int32_t* q_start,
+                         int64_t n_q, int64_t max_kv_rows, const void* q_nope, const void* q_pe,
+                         const void* w_uk, const void* w_uv, mla_dtype_t act_dtype,
+                         int32_t n_heads, float softmax_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  CacheView cv;
+  const mla_status_t st = view_of(cache, cv);
+  if (st != MLA_OK) return st;
+  return prefill_view(cv, seq_len, q_start, n_q, max_kv_rows, q_nope, q_pe, w_uk, w_uv, act_dtype,
+                      n_heads, softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+mla_status_t mla_prefill_paged(const mla_paged_cache_t* cache, const int32_t* seq_len,
+                               const int32_t* q_start, int64_t n_q, int64_t max_kv_rows,
+                               const void* q_nope, const void* q_pe, const void* w_uk,
+                               const void* w_uv, mla_dtype_t act_dtype, int32_t n_heads,
+                               float softmax_scale, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  CacheView cv;
+  const mla_status_t st = view_of(cache, cv);
+  if (st != MLA_OK) return st;
+  return prefill_view(cv, seq_len, q_start, n_q, max_kv_rows, q_nope, q_pe, w_uk, w_uv, act_dtype,
+                      n_heads, softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -164,10 +164,14 @@ struct PrefillLayout {
 PrefillLayout prefill_layout(int B, int H, int64_t max_kv_rows);
 
 struct PrefillArgs {
-  const void* rows;           // contiguous cache storage
+  const void* rows;           // cache storage (contiguous rows or the page pool)
   const float* row_scale;     // fp8 only
-  const int64_t* seq_start;   // [B]
-  const int32_t* seq_cap;     // [B]
+  const int64_t* seq_start;   // [B] (contiguous)
+  const int32_t* seq_cap;     // [B] (contiguous)
+  const int32_t* block_table; // [B][max_pages] (paged; null: contiguous)
+  int32_t max_pages;
+  int32_t page_tokens;
+  uint32_t page_limit;        // pages in the pool, at most 2^31
   const int32_t* seq_len;     // [B]
   const int32_t* q_start;     // [B+1]
   int64_t n_q;

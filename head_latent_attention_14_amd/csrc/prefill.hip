@@ -40,7 +40,8 @@ __global__ void __launch_bounds__(256) mla_prefill_plan_kernel(PrefillArgs a) {
     int64_t kvr = 0;
     int32_t qb = 0;
     if (b < a.B) {
-      const int cap = a.seq_cap[b] > 0 ? a.seq_cap[b] : 0;
+      const int cap = a.block_table ? a.max_pages * a.page_tokens
+                                    : (a.seq_cap[b] > 0 ? a.seq_cap[b] : 0);
       len = a.seq_len[b];
       len = len < 0 ? 0 : (len > cap ? cap : len);
       int64_t q0 = a.q_start[b], q1 = a.q_start[b + 1];
@@ -130,12 +131,23 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
   const int b = search_seq(a.kv_row0, a.B, r0);
   const int L = ld_const(a.lenc, b);
   const int t0 = (int)(r0 - ld_const(a.kv_row0, b));
-  const int64_t crow0 = ld_const(a.seq_start, b) + t0;   // cache row of packed row r0
+  // cache row of position t0 + r: contiguous, seq_start[b] + t0 + r; paged,
+  // through the block table (an entry outside the pool reads page 0 of it,
+  // as the decode kernels do: a wrong page, never outside the pool)
+  const bool paged = a.block_table != nullptr;
+  const int64_t crow0 = paged ? 0 : ld_const(a.seq_start, b) + t0;
+  auto crow = [&](int r) -> int64_t {
+    if (!paged) return crow0 + r;
+    const int t = t0 + r;
+    const int j = t / a.page_tokens;
+    const int32_t pg = a.block_table[(int64_t)b * a.max_pages + j];
+    return (int64_t)((uint32_t)pg < a.page_limit ? pg : 0) * a.page_tokens + (t - j * a.page_tokens);
+  };
   constexpr int RB = (CT == kFP8) ? kDrow : (CT == kFP6) ? 464 : kDrow * 2;   // bytes of a cache row
   const char* rows = (const char*)a.rows;
 
   if constexpr (CT == kFP8) {
-    if (tid < kPfRows) s_scale[tid] = (t0 + tid < L) ? a.row_scale[crow0 + tid] : 0.f;
+    if (tid < kPfRows) s_scale[tid] = (t0 + tid < L) ? a.row_scale[crow(tid)] : 0.f;
   }
 
   // ---- global loads of one chunk into registers ----
@@ -154,7 +166,7 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
       c.c6[0] = c.c6[1] = c.c6[2] = uint2{0u, 0u};
       c.e6 = 127u;
       if (t0 + r < L) {
-        const char* rp = rows + (crow0 + r) * RB;
+        const char* rp = rows + crow(r) * RB;
 #pragma unroll
         for (int m = 0; m < 3; ++m) c.c6[m] = *(const uint2*)(rp + 24 * j + 8 * m);
         c.e6 = *(const unsigned char*)(rp + 432 + j);
@@ -168,7 +180,7 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
       const int p = (CT == kFP8) ? (i & 3) : (i & 7);
       c.x[j] = u32x4{0u, 0u, 0u, 0u};
       if (t0 + r < L)
-        c.x[j] = *(const u32x4*)(rows + (crow0 + r) * RB + (CT == kFP8 ? k0 : 2 * k0) + 16 * p);
+        c.x[j] = *(const u32x4*)(rows + crow(r) * RB + (CT == kFP8 ? k0 : 2 * k0) + 16 * p);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -283,7 +295,7 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
     const int j = 16 + (tid & 1);
     u32x4 out[4] = {};
     if (t0 + r < L) {
-      const char* rp = rows + (crow0 + r) * RB;
+      const char* rp = rows + crow(r) * RB;
       uint2 c[3];
 #pragma unroll
       for (int m = 0; m < 3; ++m) c[m] = *(const uint2*)(rp + 24 * j + 8 * m);
@@ -305,7 +317,7 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
       u32x4 out = u32x4{0u, 0u, 0u, 0u};
       if (t0 + r < L) {
         if constexpr (CT == kFP8) {
-          const uint2 c = *(const uint2*)(rows + (crow0 + r) * RB + kDc + 8 * p);
+          const uint2 c = *(const uint2*)(rows + crow(r) * RB + kDc + 8 * p);
           const float sc = s_scale[r];
           float f[8];
 #pragma unroll
@@ -322,7 +334,7 @@ __global__ void __launch_bounds__(256) mla_prefill_kv_kernel(PrefillArgs a) {
           out = u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
                       pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
         } else {
-          out = *(const u32x4*)(rows + (crow0 + r) * RB + kDc * 2 + 16 * p);
+          out = *(const u32x4*)(rows + crow(r) * RB + kDc * 2 + 16 * p);
         }
       }
       *(u32x4*)(kpe + (r * KW + 8 * p) * 2) = out;

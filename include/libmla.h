@@ -420,6 +420,21 @@ mla_status_t mla_prefill(const mla_cache_t* cache, const int32_t* seq_len, const
                          int32_t n_heads, float softmax_scale, void* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mla_prefill_paged -- mla_prefill over a paged cache (the layout of
+ * mla_decode_paged: each sequence's capacity max_pages * page_tokens, its rows
+ * found through the block table): same arguments, rules and workspace, and
+ * the same result as mla_prefill over those rows laid out contiguously, bit
+ * for bit. A table entry outside the page pool reads page 0 of the pool (as
+ * the paged decode does); MLA_DEBUG=1 rejects such entries instead.
+ */
+mla_status_t mla_prefill_paged(const mla_paged_cache_t* cache, const int32_t* seq_len,
+                               const int32_t* q_start, int64_t n_q, int64_t max_kv_rows,
+                               const void* q_nope, const void* q_pe, const void* w_uk,
+                               const void* w_uv, mla_dtype_t act_dtype, int32_t n_heads,
+                               float softmax_scale, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Static English text for a status code (host); "unknown status" for any
  * other value. */
 const char* mla_status_string(mla_status_t status);

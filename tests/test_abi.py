@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
                           "mla_decode_attend_combine",
                           "mla_append_absorb", "mla_decode_noalloc", "mla_append_yarn",
                           "mla_yarn_softmax_factor", "mla_append_paged", "mla_decode_paged",
-                          "mla_prefill_workspace_size", "mla_prefill",
+                          "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_paged",
                           "mla_status_string", "mla_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -340,7 +340,12 @@ def test_paged_validation():
         return lib.mla_append_paged(ctypes.byref(c) if c is not None else None, FAKE, n_tok, 128,
                                     FAKE, FAKE, E.MLA_DTYPE_BF16, FAKE, FAKE, 10000.0, None)
 
-    for f in (dec, app):
+    def pf(c, H=16, ws_bytes=1 << 40):
+        return lib.mla_prefill_paged(ctypes.byref(c) if c is not None else None, FAKE, FAKE, 64,
+                                     1000, FAKE, FAKE, FAKE, FAKE, E.MLA_DTYPE_BF16, H, 0.07, FAKE,
+                                     None, FAKE, ws_bytes, None)
+
+    for f in (dec, app, pf):
         assert f(None) == E.MLA_ERR_INVALID_ARGUMENT
         assert f(_paged(P=48)) == E.MLA_ERR_INVALID_ARGUMENT        # not a multiple of 32
         assert f(_paged(P=0)) == E.MLA_ERR_INVALID_ARGUMENT
@@ -356,6 +361,10 @@ def test_paged_validation():
     need = mla.mla_decode_workspace_size(4, 16, E.MLA_DTYPE_BF16, E.MLA_DTYPE_BF16)
     assert dec(_paged(), ws_bytes=need - 1) == E.MLA_ERR_WORKSPACE_TOO_SMALL
     assert app(_paged(), n_tok=0) == E.MLA_OK                      # a no-op
+    # paged prefill: any head count, the prefill workspace, f32 pools unsupported
+    need = mla.mla_prefill_workspace_size(4, 3, 64, 1000)
+    assert pf(_paged(), H=3, ws_bytes=need - 1) == E.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert pf(_paged(dtype=E.MLA_DTYPE_F32)) == E.MLA_ERR_UNSUPPORTED
 
 
 def test_paged_binding_checks_shapes():

@@ -4,7 +4,8 @@ oracle, through the C ABI.
 Small cases compare every output: whole-prompt prefill over ragged lengths
 (1 row, partial and several 64-row blocks), chunks after a cached prefix,
 several 256-query blocks per sequence, sequences without queries between
-others, fp8 and fp6 caches, odd head counts. The full-size case (the benchmark's
+others, fp8 and fp6 caches, odd head counts, paged caches (bit for bit equal
+to the contiguous ones). The full-size case (the benchmark's
 shape: 128 heads, four prompts of 2K-4K tokens) compares every query of
 sampled (sequence, head) pairs. Bounds: rel-L2 2e-2 on o (bf16 cache), 4e-2
 (fp8 and fp6 caches, against the oracle on the dequantised rows); |lse error|
@@ -138,6 +139,30 @@ def test_prefill_fp6_chunk_small():
     log("[prefill fp6 chunk]")
     o, lse = DevicePrefill(p).run()
     _check(p, o, lse, label="fp6 chunk")
+
+
+@pytest.mark.parametrize("name,P", [("prefill_bf16", 32), ("prefill_chunk_fp8", 64),
+                                    ("prefill_chunk_fp6", 32)])
+def test_prefill_paged_equals_contiguous(name, P):
+    # the same rows in shuffled P-row pages of a larger pool (unused rows
+    # random): mla_prefill_paged equals mla_prefill bit for bit
+    from tests.test_gpu_paged import _page
+    p = W.make_prefill_problem(W.PREFILL_WORKLOADS[name], lengths=[700, 33, 300, 129],
+                               n_queries=[300, 33, 1, 129], H=16, seed=10)
+    d = DevicePrefill(p)
+    o, lse = d.run()
+    pc = _page(d, P, seed=P)
+    out = torch.full_like(d.out, float("nan"))
+    lse_p = torch.full_like(d.lse, float("nan"))
+    ws = d.mla.alloc_prefill_workspace(pc, d.H, out.shape[0], d.max_kv_rows)
+    ws.fill_(0xFF)
+    d.mla.mla_prefill(pc, d.seq_len, d.q_start, d.max_kv_rows, d.q_nope, d.q_pe, d.w_uk, d.w_uv,
+                      1.0 / math.sqrt(192.0), out, lse_p, ws)
+    torch.cuda.synchronize()
+    log(f"[prefill paged] {name} P={P}")
+    assert np.array_equal(out.double().cpu().numpy(), o)
+    assert np.array_equal(lse_p.double().cpu().numpy(), lse)
+    _check(p, o, lse, label=f"{name} paged")
 
 
 def test_prefill_repeatable():
