@@ -38,6 +38,7 @@ EXPORTED = ["mla_append", "mla_decode_workspace_size", "mla_decode", "mla_decode
             "mla_decode_attend", "mla_decode_combine", "mla_decode_attend_combine",
             "mla_append_absorb", "mla_decode_noalloc", "mla_append_yarn",
             "mla_yarn_softmax_factor", "mla_append_paged", "mla_decode_paged",
+            "mla_append_yarn_paged",
             "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_paged", "mla_status_string",
             "mla_abi_version"]
 DECODE_STAGES = ["mla_decode_absorb", "mla_decode_attend", "mla_decode_combine",
@@ -112,6 +113,9 @@ def _load(path: str = LIB_PATH):
     lib.mla_yarn_softmax_factor.argtypes = [F32]
     lib.mla_yarn_softmax_factor.restype = F32
     PC = ctypes.POINTER(mla_paged_cache_t)
+    lib.mla_append_yarn_paged.argtypes = [PC, P, I32, I32, P, P, ctypes.c_int, P, P,
+                                          ctypes.POINTER(mla_yarn_t), P]
+    lib.mla_append_yarn_paged.restype = ctypes.c_int
     lib.mla_append_paged.argtypes = [PC, P, I32, I32, P, P, ctypes.c_int, P, P, F32, P]
     lib.mla_append_paged.restype = ctypes.c_int
     lib.mla_decode_paged.argtypes = [PC, P, P, P, P, P, ctypes.c_int, I32, F32, P, P, P, SZ, P]
@@ -372,19 +376,20 @@ def mla_append(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: t
                           float(rope_base), _stream(stream)), "mla_append")
 
 
-def mla_append_yarn(cache: LatentCache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor,
+def mla_append_yarn(cache, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: torch.Tensor,
                     tok_seq: torch.Tensor, tok_pos: torch.Tensor, base: float = 10000.0,
                     scale: float = 40.0, alpha: float = 1.0, beta: float = 32.0,
                     orig_context: int = 4096, stream=None) -> None:
     """mla_append with the RoPE key at YaRN frequencies (see libmla.h); the
-    defaults are DeepSeek-V2's."""
+    defaults are DeepSeek-V2's. A PagedLatentCache runs mla_append_yarn_paged."""
     check_append_args(cache, h, w_dkv, w_kr, tok_seq, tok_pos)
     n_tok, d_model = h.shape
     st = ctypes.byref(cache.struct())
     rope = mla_yarn_t(float(base), float(scale), float(alpha), float(beta), int(orig_context))
-    _check(lib.mla_append_yarn(st, _ptr(h), n_tok, d_model, _ptr(w_dkv), _ptr(w_kr),
-                               dtype_code(h.dtype), _ptr(tok_seq), _ptr(tok_pos),
-                               ctypes.byref(rope), _stream(stream)), "mla_append_yarn")
+    fn, name = ((lib.mla_append_yarn_paged, "mla_append_yarn_paged")
+                if isinstance(cache, PagedLatentCache) else (lib.mla_append_yarn, "mla_append_yarn"))
+    _check(fn(st, _ptr(h), n_tok, d_model, _ptr(w_dkv), _ptr(w_kr), dtype_code(h.dtype),
+              _ptr(tok_seq), _ptr(tok_pos), ctypes.byref(rope), _stream(stream)), name)
 
 
 def mla_yarn_softmax_factor(scale: float) -> float:

@@ -396,6 +396,18 @@ mla_status_t mla_append_paged(const mla_paged_cache_t* cache, const void* h, int
                      nullptr, stream);
 }
 
+mla_status_t mla_append_yarn_paged(const mla_paged_cache_t* cache, const void* h, int32_t n_tok,
+                                   int32_t d_model, const void* w_dkv, const void* w_kr,
+                                   mla_dtype_t act_dtype, const int32_t* tok_seq,
+                                   const int32_t* tok_pos, const mla_yarn_t* rope, void* stream) {
+  CacheView cv;
+  const mla_status_t st = view_of(cache, cv);
+  if (st != MLA_OK) return st;
+  if (!valid_yarn(rope)) return MLA_ERR_INVALID_ARGUMENT;
+  return append_impl(cv, h, n_tok, d_model, w_dkv, w_kr, act_dtype, tok_seq, tok_pos, rope->base,
+                     rope, stream);
+}
+
 float mla_yarn_softmax_factor(float scale) {
   if (!(scale > 1.f) || !isfinite(scale)) return 1.f;
   const double m = 0.1 * log((double)scale) + 1.0;

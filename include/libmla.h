@@ -282,6 +282,16 @@ mla_status_t mla_decode_paged(const mla_paged_cache_t* cache, const int32_t* seq
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_append_yarn_paged -- mla_append_yarn into a paged cache: the rows of
+ * mla_append_paged with the RoPE key at the YaRN frequencies of `rope`.
+ */
+mla_status_t mla_append_yarn_paged(const mla_paged_cache_t* cache,
+                                   const void* h, int32_t n_tok, int32_t d_model,
+                                   const void* w_dkv, const void* w_kr, mla_dtype_t act_dtype,
+                                   const int32_t* tok_seq, const int32_t* tok_pos,
+                                   const mla_yarn_t* rope, void* stream);
+
+/*
  * The three stages mla_decode runs, exposed so a caller can time or
  * interleave them. Same arguments and rules as mla_decode; calling
  * absorb, attend and combine in this order on one stream with the same

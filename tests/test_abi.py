@@ -28,6 +28,7 @@ def test_exports_every_declared_symbol():
                           "mla_decode_attend_combine",
                           "mla_append_absorb", "mla_decode_noalloc", "mla_append_yarn",
                           "mla_yarn_softmax_factor", "mla_append_paged", "mla_decode_paged",
+                          "mla_append_yarn_paged",
                           "mla_prefill_workspace_size", "mla_prefill", "mla_prefill_paged",
                           "mla_status_string", "mla_abi_version"}
     for n in names:
@@ -315,6 +316,20 @@ def test_append_yarn_validation_and_softmax_factor():
     assert call(mla.mla_yarn_t(**good), n_tok=-1) == E.MLA_ERR_INVALID_ARGUMENT
     # n_tok == 0 is a valid no-op that touches nothing
     assert call(mla.mla_yarn_t(**good), n_tok=0) == E.MLA_OK
+    # the paged form checks the pool first, then the same frequency parameters
+    pc = _paged()
+
+    def call_p(rope, n_tok=4):
+        r = ctypes.byref(rope) if rope is not None else None
+        return lib.mla_append_yarn_paged(ctypes.byref(pc), FAKE, n_tok, 128, FAKE, FAKE,
+                                         E.MLA_DTYPE_BF16, FAKE, FAKE, r, None)
+
+    assert call_p(None) == E.MLA_ERR_INVALID_ARGUMENT
+    assert call_p(mla.mla_yarn_t(**dict(good, beta=0.5))) == E.MLA_ERR_INVALID_ARGUMENT
+    assert call_p(mla.mla_yarn_t(**good), n_tok=0) == E.MLA_OK
+    assert lib.mla_append_yarn_paged(None, FAKE, 4, 128, FAKE, FAKE, E.MLA_DTYPE_BF16, FAKE, FAKE,
+                                     ctypes.byref(mla.mla_yarn_t(**good)), None) \
+        == E.MLA_ERR_INVALID_ARGUMENT
     import math
     assert mla.mla_yarn_softmax_factor(1.0) == 1.0
     assert mla.mla_yarn_softmax_factor(0.25) == 1.0

@@ -108,8 +108,8 @@ def test_paged_decode_full_size_v2():
     assert _same_bits(out, dp.out) and _same_bits(lse, dp.lse)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_paged_append_matches_contiguous_rows(dtype):
+@pytest.mark.parametrize("dtype,yarn", [("bf16", False), ("fp8", False), ("bf16", True)])
+def test_paged_append_matches_contiguous_rows(dtype, yarn):
     mla = _mla()
     rng = np.random.default_rng(5)
     dm, n_tok, P = 256, 24, 64
@@ -144,8 +144,12 @@ def test_paged_append_matches_contiguous_rows(dtype):
     seq = torch.tensor([int(s[0]) for s in slots], dtype=torch.int32).cuda()
     pos = torch.tensor([int(s[1]) for s in slots], dtype=torch.int32).cuda()
     before = pool.clone()
-    mla.mla_append_paged(pc, h, wd, wk, seq, pos, 10000.0)
-    mla.mla_append(cc, h, wd, wk, seq, pos, 10000.0)
+    if yarn:                                       # YaRN frequencies (DeepSeek-V2's constants)
+        mla.mla_append_yarn(pc, h, wd, wk, seq, pos)
+        mla.mla_append_yarn(cc, h, wd, wk, seq, pos)
+    else:
+        mla.mla_append_paged(pc, h, wd, wk, seq, pos, 10000.0)
+        mla.mla_append(cc, h, wd, wk, seq, pos, 10000.0)
     torch.cuda.synchronize()
     written = set()
     for (b, t) in slots:
