@@ -217,7 +217,9 @@ def test_combine_row_blocks(B, H, maxlen):
 
 
 def test_other_head_counts():
-    for H in [32, 64]:
+    # 32 and 64 heads: one pair-kernel workgroup of 2 or 4 waves per worker;
+    # 160 and 256 heads: several head groups per worker (5 x 32, 2 x 128)
+    for H in [32, 64, 160, 256]:
         p = W.make_problem(W.WORKLOADS["v2_bf16"], B=2, lengths=np.array([77, 300]), H=H)
         dp = DeviceProblem(p)
         o, _ = dp.step()
@@ -225,11 +227,12 @@ def test_other_head_counts():
         assert rel_l2(o, ro) <= TOL["bf16"], H
 
 
-@pytest.mark.parametrize("H", [32, 64, 96, 128])
+@pytest.mark.parametrize("H", [32, 64, 96, 128, 192])
 def test_fp6_cache_pair_kernel_widths(H):
     # fp6 rows are widened tile by tile into bf16 in LDS inside the pair
     # kernel: 32, 64 and 128 heads per workgroup (96 heads: three 32-head
-    # groups); every output against the oracle on the dequantised rows
+    # groups; 192: three 64-head groups); every output against the oracle on
+    # the dequantised rows
     p = W.make_problem(W.WORKLOADS["fp6_cache"], B=4, lengths=np.array([1, 33, 200, 1000]), H=H)
     log(f"[fp6 pair] H={H} lengths={p.seq_len.tolist()}")
     dp = DeviceProblem(p)
