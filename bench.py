@@ -152,7 +152,8 @@ def cpu_baseline(p, seconds: float):
 
 
 def gpu_clock_mhz():
-    """Current shader clock as the driver reports it (sysfs, else rocm-smi)."""
+    """Current shader clock as the amdgpu kernel driver reports it (sysfs pp_dpm_sclk, else
+    rocm-smi)."""
     for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
         try:
             for line in open(f):
